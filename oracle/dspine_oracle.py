@@ -1,0 +1,469 @@
+"""CPU oracle for the DSpine draft-block hot path.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg may import this module.  The product path (the HIP library and its
+binding) never calls it, and it imports nothing from the product package.
+
+Everything is float64 numpy, written step by step from the sources below,
+with no fusion, blocking or reordering beyond what the definitions state.
+The only roundings are the ones the sources fix for stored context K/V.
+
+Sources (cited by tag):
+  [FLZ] "DSpine for Qwen3.8-27B: Causal Features Through Depth" (flozi.net guide)
+  [PHY] "DSpine 完全拆解：相邻因果注入如何让并行草稿沿网络深度建立 token 依赖"
+        (pinghaoyang.com.cn article)
+  [DSP] "DSpark, every bolt and rivet" (lab-artifacts tutorial)
+  [NIF] NInfer maintainer notes, "DFlash" (docs/maintainer/dflash.md)
+
+Tensor conventions: uint16 arrays hold bfloat16 bit patterns; matrices are
+``[out, in]`` (y = W x).  A model is the dict made by ``synth.make_weights``
+plus its ``synth.Geometry``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+def widen(a: np.ndarray) -> np.ndarray:
+    """bf16 bits (uint16) or floats -> float64 (exact)."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 value, ties to even (done in exact integer
+    arithmetic on the float64 bit pattern).  Returns float64 values."""
+    x = np.asarray(x, dtype=np.float64)
+    bits = x.view(np.uint64)
+    # bf16 keeps 7 fraction bits; float64 has 52: drop 45 bits with RNE.
+    drop = np.uint64(45)
+    half = np.uint64(1) << (drop - np.uint64(1))
+    lsb = (bits >> drop) & np.uint64(1)
+    rounded = (bits + half - np.uint64(1) + lsb) >> drop << drop
+    out = rounded.view(np.float64).copy()
+    # exponent range: bf16 shares float32's range; values beyond it overflow.
+    big = np.abs(out) > 3.3895313892515355e38
+    out[big] = np.sign(out[big]) * np.inf
+    small = np.abs(x) < 2.0 ** -126   # bf16 subnormals: a fixed step of 2^-133
+    if np.any(small):
+        step = 2.0 ** -133
+        out[small] = np.round(x[small] / step) * step   # numpy rounds halves to even
+    return out
+
+
+def round_fp16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest IEEE half value (ties to even); float64 out."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# elementary operations
+# ---------------------------------------------------------------------------
+def plain_rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """[NIF, context conditioning]: w * x / sqrt(mean(x^2) + eps) over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    return widen(w) * x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def head_rmsnorm(x: np.ndarray, w: np.ndarray, eps: float, head_dim: int) -> np.ndarray:
+    """[NIF, layer equations]: plain RMSNorm over each head of width D, one
+    weight vector [D] shared by all heads of the projection."""
+    shp = x.shape
+    xh = x.reshape(shp[:-1] + (shp[-1] // head_dim, head_dim))
+    return plain_rmsnorm(xh, w, eps).reshape(shp)
+
+
+def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
+    """inverse frequency of rotation pair j: theta^(-2j/D), j < D/2."""
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * j / head_dim)
+
+
+def rope_1d(x: np.ndarray, positions: np.ndarray, theta: float, head_dim: int) -> np.ndarray:
+    """[NIF, context K/V and layer equations]: one-dimensional RoPE over the
+    full head in split-half form: pair (j, j + D/2) is rotated by the angle
+    position * theta^(-2j/D).
+
+    x: [T, n_heads*D]; positions: [T] absolute integer positions."""
+    T = x.shape[0]
+    half = head_dim // 2
+    xh = x.reshape(T, -1, head_dim)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * rope_inv_freq(head_dim, theta)[None, :]
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    x1 = xh[..., :half]
+    x2 = xh[..., half:]
+    out = np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+    return out.reshape(x.shape)
+
+
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y = W x for rows of x; W is [out, in]."""
+    return np.asarray(x, dtype=np.float64) @ widen(w).T
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row softmax; entries equal to -inf get zero weight."""
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# context: a1-a3
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class LayerContext:
+    """Context K/V of one draft layer for one request, by absolute position.
+
+    ``k[p - lo]`` / ``v[p - lo]`` hold position p for p in [lo, frontier):
+    exactly the live interval [NIF, ring storage]."""
+    lo: int
+    k: np.ndarray          # [n, nkv*D] float64 (already rounded to storage type)
+    v: np.ndarray
+
+
+@dataclasses.dataclass
+class RequestContext:
+    frontier: int
+    layers: List[LayerContext]
+
+
+def empty_context(g, frontier: int = 0) -> RequestContext:
+    """A context whose frontier is ``frontier`` with nothing stored (positions
+    below the frontier that are never materialized are simply absent)."""
+    return RequestContext(frontier, [LayerContext(frontier, np.zeros((0, g.kv_dim)),
+                                                  np.zeros((0, g.kv_dim)))
+                                     for _ in range(g.n_layers)])
+
+
+def live_lo(window: int, frontier: int) -> int:
+    """[NIF, ring storage]: live interval is [max(0, F - S), F) for a local
+    layer of window S; a full layer (S = 0) keeps every position."""
+    if window == 0:
+        return 0
+    return max(0, frontier - window)
+
+
+def context_features(g, wts: Dict[str, np.ndarray], feats: np.ndarray) -> np.ndarray:
+    """a1 [NIF, context conditioning]; [DSP §5.1]: s_t is the concatenation
+    of the recorded target residuals; c_t = plain_rmsnorm(W_feature s_t,
+    context_norm), no bias."""
+    u = linear(widen(feats), wts["w_feat"])
+    return plain_rmsnorm(u, wts["g_ctx"], g.eps)
+
+
+def context_kv(g, wts, layer: int, c: np.ndarray, positions: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """a2 [NIF, context K/V]: k = rope_1d(head_rmsnorm(W_k c, key_norm), t),
+    v = W_v c, using the layer's own K/V weights.  Storage [NIF, fused
+    context materializer]: K is stored as BF16 (no rounding before the head
+    norm) and V as FP16_RNE(BF16(v)).  A float32 model stores both unrounded
+    beyond float32 (reading: the BF16/FP16 contract belongs to the BF16
+    drafter)."""
+    p = f"l{layer}."
+    k = rope_1d(head_rmsnorm(linear(c, wts[p + "wk"]), wts[p + "gk"], g.eps, g.head_dim),
+                positions, g.rope_theta, g.head_dim)
+    v = linear(c, wts[p + "wv"])
+    if g.dtype == "bf16":
+        k = round_bf16(k)
+        v = round_fp16(round_bf16(v))
+    else:
+        k = k.astype(np.float32).astype(np.float64)
+        v = v.astype(np.float32).astype(np.float64)
+    return k, v
+
+
+def materialize(g, wts, ctx: RequestContext, feats: np.ndarray) -> RequestContext:
+    """a1-a3 for one request and one chunk of n new positions [F, F+n).
+
+    [NIF, context prefill]: only the feature and K/V projections run.  A
+    chunk longer than a local ring stores only its final live window while
+    the frontier still advances by the whole chunk.  Returns a new context."""
+    n = feats.shape[0]
+    F0 = ctx.frontier
+    F1 = F0 + n
+    new_layers = []
+    # positions that some layer keeps
+    need_lo = F1
+    for l in range(g.n_layers):
+        need_lo = min(need_lo, max(F0, live_lo(g.windows[l], F1)))
+    c = None
+    if need_lo < F1:
+        c_rows = context_features(g, wts, feats[need_lo - F0:])
+    for l in range(g.n_layers):
+        lo_new = live_lo(g.windows[l], F1)
+        old = ctx.layers[l]
+        keep_from = max(F0, lo_new)
+        if keep_from < F1:
+            pos = np.arange(keep_from, F1)
+            k_new, v_new = context_kv(g, wts, l, c_rows[keep_from - need_lo:], pos)
+        else:
+            k_new = np.zeros((0, g.kv_dim))
+            v_new = np.zeros((0, g.kv_dim))
+        # surviving old positions: [max(old.lo, lo_new), F0)
+        s = max(old.lo, lo_new)
+        k_old = old.k[max(0, s - old.lo):]
+        v_old = old.v[max(0, s - old.lo):]
+        lo = s if k_old.shape[0] > 0 else keep_from
+        new_layers.append(LayerContext(lo, np.concatenate([k_old, k_new]),
+                                       np.concatenate([v_old, v_new])))
+    return RequestContext(F1, new_layers)
+
+
+def ring_image(g, ctx: RequestContext, layer: int, capacity: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Ring storage view [NIF, ring storage]: position p sits in slot p mod S
+    of a local layer (slot p of a full layer).  Layout [nkv, capacity, D];
+    slots holding no live position are NaN."""
+    lc = ctx.layers[layer]
+    S = g.windows[layer]
+    K = np.full((g.n_kv_heads, capacity, g.head_dim), np.nan)
+    V = np.full((g.n_kv_heads, capacity, g.head_dim), np.nan)
+    for i in range(lc.k.shape[0]):
+        p = lc.lo + i
+        slot = p % S if S > 0 else p
+        K[:, slot, :] = lc.k[i].reshape(g.n_kv_heads, g.head_dim)
+        V[:, slot, :] = lc.v[i].reshape(g.n_kv_heads, g.head_dim)
+    return K, V
+
+
+# ---------------------------------------------------------------------------
+# a3: visibility
+# ---------------------------------------------------------------------------
+def key_visible(window: int, block_causal: bool, p_query: int, p_key: int,
+                key_is_block: bool, q_index: int = 0, k_index: int = 0) -> bool:
+    """[NIF, draft attention]: a local layer allows |p_key - p_query| < S
+    (distance S-1 in, S out); a full layer allows every populated key.
+    [PHY, 块因果注意力] / [FLZ]: the block-causal variant additionally hides
+    block keys after the query row."""
+    if window > 0 and abs(p_key - p_query) >= window:
+        return False
+    if key_is_block and block_causal and k_index > q_index:
+        return False
+    return True
+
+
+def visible_context_interval(window: int, frontier: int, row: int) -> Tuple[int, int]:
+    """Closed form of the context positions row i (at F+i) sees: the
+    predicate clipped to the populated positions [0, F)."""
+    if window == 0:
+        return 0, frontier
+    lo = max(0, frontier + row - window + 1)
+    return min(lo, frontier), frontier
+
+
+# ---------------------------------------------------------------------------
+# a6: attention
+# ---------------------------------------------------------------------------
+def block_attention(g, layer: int, ctx: RequestContext, q: np.ndarray, k: np.ndarray,
+                    v: np.ndarray) -> np.ndarray:
+    """[NIF, layer equations]: attention(q, concat(K_ctx, k), concat(V_ctx, v),
+    scale 1/sqrt(D), layer mask), vectorised.  q: [W, nq*D]; k, v: [W, nkv*D]
+    for block positions F..F+W-1.  Q head h reads KV head h // (nq/nkv)
+    (reading: contiguous grouping)."""
+    W = q.shape[0]
+    F = ctx.frontier
+    S = g.windows[layer]
+    lc = ctx.layers[layer]
+    D = g.head_dim
+    grp = g.n_q_heads // g.n_kv_heads
+    ctx_pos = np.arange(lc.lo, lc.lo + lc.k.shape[0])
+    blk_pos = F + np.arange(W)
+    key_pos = np.concatenate([ctx_pos, blk_pos])
+    K = np.concatenate([lc.k, k]).reshape(-1, g.n_kv_heads, D)
+    V = np.concatenate([lc.v, v]).reshape(-1, g.n_kv_heads, D)
+    n_ctx = ctx_pos.shape[0]
+    # mask [W, n_keys]
+    qpos = blk_pos[:, None]
+    allowed = np.ones((W, key_pos.shape[0]), dtype=bool)
+    if S > 0:
+        allowed &= np.abs(key_pos[None, :] - qpos) < S
+    if g.block_causal:
+        jj = np.arange(W)[None, :]
+        ii = np.arange(W)[:, None]
+        allowed[:, n_ctx:] &= jj <= ii
+    out = np.zeros((W, g.n_q_heads, D))
+    qh = q.reshape(W, g.n_q_heads, D)
+    for h in range(g.n_q_heads):
+        kvh = h // grp
+        s = qh[:, h, :] @ K[:, kvh, :].T / math.sqrt(D)
+        s = np.where(allowed, s, -np.inf)
+        out[:, h, :] = softmax_rows(s) @ V[:, kvh, :]
+    return out.reshape(W, -1)
+
+
+def block_attention_bruteforce(g, layer: int, ctx: RequestContext, q: np.ndarray,
+                               k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Second attention for tiny inputs: explicit loops over (head, query,
+    key), the predicate evaluated per pair through ``key_visible``, keys read
+    from their logical positions, softmax accumulated in float64."""
+    W = q.shape[0]
+    F = ctx.frontier
+    S = g.windows[layer]
+    lc = ctx.layers[layer]
+    D = g.head_dim
+    grp = g.n_q_heads // g.n_kv_heads
+    out = np.zeros((W, g.n_q_heads * D))
+    for h in range(g.n_q_heads):
+        kvh = h // grp
+        for i in range(W):
+            qi = q[i, h * D:(h + 1) * D]
+            keys = []
+            for p in range(0, F):
+                if p < lc.lo or p >= lc.lo + lc.k.shape[0]:
+                    continue
+                if key_visible(S, g.block_causal, F + i, p, False):
+                    r = p - lc.lo
+                    keys.append((lc.k[r, kvh * D:(kvh + 1) * D], lc.v[r, kvh * D:(kvh + 1) * D]))
+            for j in range(W):
+                if key_visible(S, g.block_causal, F + i, F + j, True, i, j):
+                    keys.append((k[j, kvh * D:(kvh + 1) * D], v[j, kvh * D:(kvh + 1) * D]))
+            scores = [float(np.dot(qi, kk)) / math.sqrt(D) for kk, _ in keys]
+            mx = max(scores)
+            wsum = 0.0
+            acc = np.zeros(D)
+            for sc, (_, vv) in zip(scores, keys):
+                e = math.exp(sc - mx)
+                wsum += e
+                acc += e * vv
+            out[i, h * D:(h + 1) * D] = acc / wsum
+    return out
+
+
+# ---------------------------------------------------------------------------
+# a9-a11: the bridge
+# ---------------------------------------------------------------------------
+def bridge_codes(g, wts, layer: int, x: np.ndarray, anchor_id: int) -> Tuple[np.ndarray, np.ndarray]:
+    """a9 [FLZ, "The bridge", equations for r, z, c]; [PHY, 统一转移空间]:
+    rho_t = sqrt(mean_i x_{t,i}^2) (no floor), z_t = R_l x_t / (rho_t + eps),
+    c_t = sqrt(r) z_t / (||z_t||_2 + eps).  The anchor row takes sqrt(r) times
+    its token's codebook row instead.  Returns (rho [W], c [W, r])."""
+    r = g.code_dim
+    rho = np.sqrt(np.mean(x * x, axis=-1))
+    z = linear(x / (rho[:, None] + g.eps), wts[f"l{layer}.R"])
+    c = math.sqrt(r) * z / (np.linalg.norm(z, axis=-1, keepdims=True) + g.eps)
+    c[0] = math.sqrt(r) * widen(wts["codebook"][anchor_id])
+    return rho, c
+
+
+def bridge_write(g, wts, layer: int, x: np.ndarray, rho: np.ndarray, c: np.ndarray,
+                 pred_codes: Optional[np.ndarray] = None) -> np.ndarray:
+    """a10-a11 [FLZ, "The bridge", equations for m and x']; [PHY, 门控与写回]:
+    g_t = sigmoid(G c_t + G_p c_{t-1} + b), m_t = g_t * (A c_{t-1}),
+    x'_t = x_t + rho_t W_l m_t for t >= 1.  The anchor row (t = 0) gets no
+    message [FLZ]; [PHY]: the anchor only sends.  All codes come from the
+    pre-write states, so every row is written from the same inputs.
+
+    ``pred_codes`` [W, r], when given, replaces c_{t-1} for receiver t (row 0
+    unused): the hook used to redo the last write with a known predecessor."""
+    W = x.shape[0]
+    out = x.copy()
+    for t in range(1, W):
+        cp = c[t - 1] if pred_codes is None else pred_codes[t]
+        gate = sigmoid(linear(c[t][None], wts["bridge_G"])[0]
+                       + linear(cp[None], wts["bridge_Gp"])[0] + widen(wts["bridge_b"]))
+        m = gate * linear(cp[None], wts["bridge_A"])[0]
+        out[t] = x[t] + rho[t] * linear(m[None], wts[f"l{layer}.W_l"])[0]
+    return out
+
+
+def bridge(g, wts, layer: int, x: np.ndarray, anchor_id: int,
+           pred_codes: Optional[np.ndarray] = None) -> np.ndarray:
+    """One bridge on one request block x [W, H] (read, then write)."""
+    rho, c = bridge_codes(g, wts, layer, x, anchor_id)
+    return bridge_write(g, wts, layer, x, rho, c, pred_codes)
+
+
+# ---------------------------------------------------------------------------
+# a4-a12: the draft forward
+# ---------------------------------------------------------------------------
+def block_input(g, wts, anchor_id: int, W: int) -> np.ndarray:
+    """a4 [NIF, draft input]: target embeddings of the anchor followed by W-1
+    MASK tokens at positions F..F+W-1."""
+    emb = wts["embed"]
+    rows = [anchor_id] + [g.mask_token_id] * (W - 1)
+    return widen(emb[rows])
+
+
+def decoder_layer(g, wts, layer: int, ctxs: Sequence[RequestContext], x: np.ndarray, W: int,
+                  attn_fn=block_attention) -> np.ndarray:
+    """a5-a8 [NIF, layer equations]: n = plain_rmsnorm(x, input_norm); q and k
+    are head-RMSNormed and rotated; attention over context plus block; y = x +
+    W_o a; m = plain_rmsnorm(y, post_attention_norm); x_next = y +
+    W_down(SiLU(W_gate m) * W_up m).  x is [B*W, H]: rows of all requests are
+    stacked for the row-wise linear maps; attention runs per request."""
+    p = f"l{layer}."
+    B = len(ctxs)
+    n = plain_rmsnorm(x, wts[p + "g_in"], g.eps)
+    pos = np.concatenate([np.arange(c.frontier, c.frontier + W) for c in ctxs])
+    q = rope_1d(head_rmsnorm(linear(n, wts[p + "wq"]), wts[p + "gq"], g.eps, g.head_dim),
+                pos, g.rope_theta, g.head_dim)
+    k = rope_1d(head_rmsnorm(linear(n, wts[p + "wk"]), wts[p + "gk"], g.eps, g.head_dim),
+                pos, g.rope_theta, g.head_dim)
+    v = linear(n, wts[p + "wv"])
+    a = np.zeros((B * W, g.q_dim))
+    for b in range(B):
+        sl = slice(b * W, (b + 1) * W)
+        a[sl] = attn_fn(g, layer, ctxs[b], q[sl], k[sl], v[sl])
+    y = x + linear(a, wts[p + "wo"])
+    m = plain_rmsnorm(y, wts[p + "g_post"], g.eps)
+    return y + linear(silu(linear(m, wts[p + "w_gate"])) * linear(m, wts[p + "w_up"]),
+                      wts[p + "w_down"])
+
+
+def draft_forward(g, wts, ctxs: Sequence[RequestContext], anchor_ids: Sequence[int], W: int,
+                  attn_fn=block_attention, return_layers: bool = False):
+    """a4-a12: one masked-block forward over B requests.
+
+    After every decoder layer (the last one included) the bridge writes
+    predecessor messages [FLZ, "The bridge"]; [PHY, 融合 kernel]; then the
+    next stage normalises: the next layer's input norm, or the final plain
+    RMSNorm [NIF, after the layers].  With code_dim == 0 there is no bridge
+    and this is the plain DFlash forward.  Returns [B, W, H]."""
+    B = len(ctxs)
+    x = np.concatenate([block_input(g, wts, int(anchor_ids[b]), W) for b in range(B)])
+    states = []
+    for l in range(g.n_layers):
+        x = decoder_layer(g, wts, l, ctxs, x, W, attn_fn)
+        if g.bridge:
+            for b in range(B):
+                sl = slice(b * W, (b + 1) * W)
+                x[sl] = bridge(g, wts, l, x[sl], int(anchor_ids[b]))
+        states.append(x.copy())
+    out = plain_rmsnorm(x, wts["g_final"], g.eps).reshape(B, W, g.hidden)
+    if return_layers:
+        return out, states
+    return out
+
+
+# ---------------------------------------------------------------------------
+# size arithmetic
+# ---------------------------------------------------------------------------
+def ring_bytes_per_position(g) -> int:
+    """Bytes of stored context K/V per retained position over all layers:
+    2-byte K and 2-byte V per KV head coordinate [FLZ, cache section];
+    [NIF, ring storage]."""
+    elt = 2 if g.dtype == "bf16" else 4
+    return g.n_layers * 2 * elt * g.n_kv_heads * g.head_dim
+
+
+def bridge_parameter_count(hidden: int, n_layers: int, code_dim: int, msg_dim: int) -> int:
+    """Per layer R_l [r, H] and W_l [H, a]; shared G, G_p, A [a, r] and b [a]
+    [FLZ, "The bridge"]; [PHY, 门控与写回]."""
+    return n_layers * (code_dim * hidden + hidden * msg_dim) + 3 * msg_dim * code_dim + msg_dim
