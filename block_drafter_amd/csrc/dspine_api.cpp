@@ -1,0 +1,941 @@
+// C ABI of the DSpine draft-block library: argument checks, workspace plan and
+// the launch sequences of the three hot-path calls.  All arithmetic runs in
+// the HIP kernels; this file only validates and enqueues.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dspine_internal.hpp"
+
+struct dspine_model {
+  dspine_geometry g;
+  dspine_weights w;
+};
+
+using namespace dspine;
+
+namespace {
+
+thread_local std::string t_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_err = buf;
+  return code;
+}
+int ok() {
+  t_err.clear();
+  return DSPINE_OK;
+}
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(DSPINE_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int elt_bytes(const dspine_geometry& g) { return g.dtype == DSPINE_BF16 ? 2 : 4; }
+// activation (MFMA operand) bytes: fp16 for BF16 models, float for F32 models
+int act_bytes(const dspine_geometry& g) { return g.dtype == DSPINE_BF16 ? 2 : 4; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// CU count of the current device, cached per device.
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing: event pairs around launches of selected classes
+// ---------------------------------------------------------------------------
+struct Profiler {
+  std::mutex mu;
+  uint32_t mask = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[DSPINE_PROF_KINDS];
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+// Records a start event now and a stop event when it goes out of scope.
+class ProfScope {
+ public:
+  ProfScope(int kind, hipStream_t s) : kind_(kind), s_(s) {
+    Profiler& p = prof();
+    if (!(p.mask & (1u << kind))) return;
+    std::lock_guard<std::mutex> lk(p.mu);
+    a_ = p.get();
+    b_ = p.get();
+    if (a_ && b_) hipEventRecord(a_, s_);
+  }
+  ~ProfScope() {
+    if (!a_ || !b_) return;
+    hipEventRecord(b_, s_);
+    Profiler& p = prof();
+    std::lock_guard<std::mutex> lk(p.mu);
+    p.rec[kind_].emplace_back(a_, b_);
+  }
+ private:
+  int kind_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
+// first context position block row 0 sees (host twin of ctx_row_lo)
+int64_t row0_lo(int64_t F, int S) {
+  if (S == 0) return 0;
+  return std::min(F, std::max<int64_t>(0, F - S + 1));
+}
+// live interval start of a layer after frontier F [NIF, ring storage]
+int64_t live_lo(int S, int64_t F) { return S == 0 ? 0 : std::max<int64_t>(0, F - S); }
+
+// ---------------------------------------------------------------------------
+// workspace plan.  Counters sit first at fixed offsets so that they stay
+// zero from call to call whatever else the calls put in the buffer.
+// ---------------------------------------------------------------------------
+struct Plan {
+  size_t gemm_cnt, attn_cnt;              // u32 counters
+  size_t gemm_part, attn_part;            // f32 partials
+  size_t x, act_h, act_q, act_f, act_r, act_r2, qkv, z, P, P2, rho, rope;
+  size_t c_raw, c_act, kv_raw;            // materialize, per row block
+  size_t total;
+};
+
+Plan make_plan(const dspine_geometry& g, int64_t M, int64_t rows) {
+  Plan p{};
+  const size_t eb = elt_bytes(g);
+  const int64_t Mp = ((std::max<int64_t>(M, 1) + 15) / 16) * 16;
+  const int qd = g.n_q_heads * g.head_dim, kvd = g.n_kv_heads * g.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  p.gemm_cnt = take(sizeof(uint32_t) * kMaxTiles);
+  p.attn_cnt = take(sizeof(uint32_t) * DSPINE_MAX_BATCH * g.n_q_heads);
+  p.gemm_part = take(sizeof(float) * gemm_stream_partial_floats(kMaxGrid));
+  p.attn_part = take(sizeof(float) * attn_partial_floats(DSPINE_MAX_BATCH, g.n_q_heads, g.head_dim));
+  p.x = take(4 * Mp * g.hidden);
+  p.act_h = take(eb * Mp * g.hidden);
+  p.act_q = take(eb * Mp * qd);
+  p.act_f = take(eb * Mp * g.ffn);
+  const int r = std::max(g.code_dim, 1), a = std::max(g.msg_dim, 1);
+  p.act_r = take(eb * Mp * r);
+  p.act_r2 = take(eb * Mp * r);
+  p.qkv = take(4 * Mp * (qd + 2 * kvd));
+  p.z = take(4 * Mp * r);
+  p.P = take(4 * Mp * 3 * a);
+  p.P2 = take(4 * Mp * 3 * a);
+  p.rho = take(4 * Mp);
+  p.rope = take(4 * Mp * g.head_dim);
+  const int64_t R = std::max<int64_t>(rows, 0);
+  p.c_raw = take(4 * R * g.hidden);
+  p.c_act = take(eb * R * g.hidden);
+  p.kv_raw = take(4 * R * (int64_t)g.n_layers * 2 * kvd);
+  p.total = off;
+  return p;
+}
+// materialize row-block capacity of a workspace of `bytes`
+int64_t rows_capacity(const dspine_geometry& g, size_t bytes) {
+  const Plan base = make_plan(g, 1, 0);
+  if (bytes <= base.total) return 0;
+  const size_t per_row = 4 * (size_t)g.hidden + elt_bytes(g) * (size_t)g.hidden +
+                         4 * (size_t)g.n_layers * 2 * g.n_kv_heads * g.head_dim;
+  int64_t r = (int64_t)((bytes - base.total) / per_row);
+  while (r > 0 && make_plan(g, 1, r).total > bytes) --r;   // alignment slack
+  return r;
+}
+
+int check_geometry(const dspine_geometry& g) {
+  if (g.dtype != DSPINE_F32 && g.dtype != DSPINE_BF16) return fail(DSPINE_E_UNSUPPORTED, "dtype %d", g.dtype);
+  if (g.n_layers < 1 || g.n_layers > DSPINE_MAX_LAYERS)
+    return fail(DSPINE_E_UNSUPPORTED, "n_layers %d not in 1..%d", g.n_layers, DSPINE_MAX_LAYERS);
+  if (g.hidden <= 0 || g.hidden % 64) return fail(DSPINE_E_UNSUPPORTED, "hidden %d not a positive multiple of 64", g.hidden);
+  if (g.head_dim != 64 && g.head_dim != 128) return fail(DSPINE_E_UNSUPPORTED, "head_dim %d not 64 or 128", g.head_dim);
+  if (g.n_kv_heads < 1 || g.n_q_heads < g.n_kv_heads || g.n_q_heads % g.n_kv_heads)
+    return fail(DSPINE_E_UNSUPPORTED, "heads %d/%d", g.n_q_heads, g.n_kv_heads);
+  const int grp = g.n_q_heads / g.n_kv_heads;
+  if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
+    return fail(DSPINE_E_UNSUPPORTED, "query heads per KV head %d not in {1,2,4,8}", grp);
+  if (g.n_q_heads > 256) return fail(DSPINE_E_UNSUPPORTED, "n_q_heads %d > 256", g.n_q_heads);
+  if (g.ffn <= 0 || g.ffn % 64) return fail(DSPINE_E_UNSUPPORTED, "ffn %d not a positive multiple of 64", g.ffn);
+  if (g.n_feat_layers < 1) return fail(DSPINE_E_UNSUPPORTED, "n_feat_layers %d", g.n_feat_layers);
+  if ((g.code_dim == 0) != (g.msg_dim == 0) || g.code_dim < 0 || g.msg_dim < 0)
+    return fail(DSPINE_E_UNSUPPORTED, "code_dim %d / msg_dim %d: both zero or both positive", g.code_dim, g.msg_dim);
+  if (g.code_dim % 32 || g.msg_dim % 32)
+    return fail(DSPINE_E_UNSUPPORTED, "code_dim %d and msg_dim %d must be multiples of 32", g.code_dim, g.msg_dim);
+  if (g.vocab < 1 || g.mask_token_id < 0 || g.mask_token_id >= g.vocab)
+    return fail(DSPINE_E_UNSUPPORTED, "vocab %d / mask_token_id %d", g.vocab, g.mask_token_id);
+  if (g.block_causal != 0 && g.block_causal != 1) return fail(DSPINE_E_UNSUPPORTED, "block_causal %d", g.block_causal);
+  for (int l = 0; l < g.n_layers; ++l)
+    if (g.window[l] < 0) return fail(DSPINE_E_UNSUPPORTED, "window[%d] = %d", l, g.window[l]);
+  if (!(g.eps >= 0.f) || !(g.rope_theta > 0.f)) return fail(DSPINE_E_UNSUPPORTED, "eps / rope_theta");
+  return DSPINE_OK;
+}
+
+int check_weights(const dspine_geometry& g, const dspine_weights& w) {
+  auto need = [&](const void* p, const char* name, int layer) -> int {
+    if (!p) return fail(DSPINE_E_ARG, "weight %s (layer %d) is NULL", name, layer);
+    if (!aligned16(p)) return fail(DSPINE_E_ARG, "weight %s (layer %d) not 16-byte aligned", name, layer);
+    return DSPINE_OK;
+  };
+  int rc;
+#define NEED(ptr, name, layer) if ((rc = need(ptr, name, layer)) != DSPINE_OK) return rc
+  NEED(w.embed, "embed", -1);
+  NEED(w.w_feat, "w_feat", -1);
+  NEED(w.g_ctx, "g_ctx", -1);
+  NEED(w.g_final, "g_final", -1);
+  if (g.code_dim > 0) {
+    NEED(w.codebook, "codebook", -1);
+    NEED(w.bridge_G, "bridge_G", -1);
+    NEED(w.bridge_Gp, "bridge_Gp", -1);
+    NEED(w.bridge_A, "bridge_A", -1);
+    NEED(w.bridge_b, "bridge_b", -1);
+  }
+  for (int l = 0; l < g.n_layers; ++l) {
+    const dspine_layer_weights& L = w.layer[l];
+    NEED(L.g_in, "g_in", l);
+    NEED(L.wq, "wq", l);
+    NEED(L.wk, "wk", l);
+    NEED(L.wv, "wv", l);
+    NEED(L.gq, "gq", l);
+    NEED(L.gk, "gk", l);
+    NEED(L.wo, "wo", l);
+    NEED(L.g_post, "g_post", l);
+    NEED(L.w_gate, "w_gate", l);
+    NEED(L.w_up, "w_up", l);
+    NEED(L.w_down, "w_down", l);
+    if (g.code_dim > 0) {
+      NEED(L.R, "R", l);
+      NEED(L.W_l, "W_l", l);
+    }
+  }
+#undef NEED
+  return DSPINE_OK;
+}
+
+int check_ctx_rings(const dspine_model& m, const dspine_ctx& c, int b, int64_t need_full) {
+  const dspine_geometry& g = m.g;
+  if (c.frontier < 0) return fail(DSPINE_E_STATE, "request %d: frontier %lld < 0", b, (long long)c.frontier);
+  for (int l = 0; l < g.n_layers; ++l) {
+    if (!c.k_ring[l] || !c.v_ring[l]) return fail(DSPINE_E_ARG, "request %d layer %d: ring pointer NULL", b, l);
+    if (!aligned16(c.k_ring[l]) || !aligned16(c.v_ring[l]))
+      return fail(DSPINE_E_ARG, "request %d layer %d: ring not 16-byte aligned", b, l);
+    const int S = g.window[l];
+    if (S > 0 && c.capacity[l] != S)
+      return fail(DSPINE_E_STATE, "request %d layer %d: ring capacity %lld != window %d", b, l,
+                  (long long)c.capacity[l], S);
+    if (S == 0 && c.capacity[l] < need_full)
+      return fail(DSPINE_E_STATE, "request %d layer %d: full-layer capacity %lld < %lld", b, l,
+                  (long long)c.capacity[l], (long long)need_full);
+  }
+  return DSPINE_OK;
+}
+
+// streamed GEMM helpers -------------------------------------------------------
+GemmParams gemm_base(const Plan& P, char* ws, int K, int M) {
+  GemmParams gp;
+  memset(&gp, 0, sizeof gp);
+  gp.K = K;
+  gp.M = M;
+  gp.partials = reinterpret_cast<float*>(ws + P.gemm_part);
+  gp.counters = reinterpret_cast<uint32_t*>(ws + P.gemm_cnt);
+  return gp;
+}
+void set_segments(GemmParams& gp, std::initializer_list<std::pair<const void*, int>> segs) {
+  int blk = 0, s = 0;
+  for (const auto& sg : segs) {
+    gp.seg_ptr[s] = sg.first;
+    gp.seg_blk0[s] = blk;
+    blk += sg.second / 16;
+    ++s;
+  }
+  gp.nseg = s;
+  gp.nblk = blk;
+}
+
+}  // namespace
+
+// =============================================================================
+extern "C" {
+
+const char* dspine_last_error(void) { return t_err.c_str(); }
+
+int dspine_profile_enable(uint32_t kind_mask) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.mask = kind_mask & ((1u << DSPINE_PROF_KINDS) - 1);
+  return ok();
+}
+
+int dspine_profile_read(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= DSPINE_PROF_KINDS || !total_ms || !launches)
+    return fail(DSPINE_E_ARG, "profile_read: bad argument");
+  Profiler& p = prof();
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec;
+  {
+    std::lock_guard<std::mutex> lk(p.mu);
+    rec.swap(p.rec[kind]);
+  }
+  double sum = 0.0;
+  int rc = DSPINE_OK;
+  for (auto& ab : rec) {
+    float ms = 0.f;
+    if (hipEventSynchronize(ab.second) != hipSuccess || hipEventElapsedTime(&ms, ab.first, ab.second) != hipSuccess)
+      rc = fail(DSPINE_E_HIP, "profile_read: event query failed");
+    sum += ms;
+  }
+  {
+    std::lock_guard<std::mutex> lk(p.mu);
+    for (auto& ab : rec) {
+      p.pool.push_back(ab.first);
+      p.pool.push_back(ab.second);
+    }
+  }
+  *total_ms = sum;
+  *launches = (int64_t)rec.size();
+  return rc ? rc : ok();
+}
+const char* dspine_version(void) { return "dspine-mi355x 0.1 (gfx950)"; }
+
+int dspine_model_create(const dspine_geometry* geom, const dspine_weights* weights, dspine_model** out) {
+  if (!geom || !weights || !out) return fail(DSPINE_E_ARG, "model_create: NULL argument");
+  *out = nullptr;
+  int rc = check_geometry(*geom);
+  if (rc) return rc;
+  if ((rc = check_weights(*geom, *weights))) return rc;
+  dspine_model* m = new (std::nothrow) dspine_model;
+  if (!m) return fail(DSPINE_E_ARG, "out of host memory");
+  m->g = *geom;
+  m->w = *weights;
+  *out = m;
+  return ok();
+}
+
+void dspine_model_destroy(dspine_model* model) { delete model; }
+
+size_t dspine_ring_bytes(const dspine_model* model, int layer, int64_t capacity) {
+  if (!model || layer < 0 || layer >= model->g.n_layers || capacity < 0) {
+    fail(DSPINE_E_ARG, "ring_bytes: bad argument");
+    return 0;
+  }
+  const int S = model->g.window[layer];
+  if (S > 0 && capacity != S) {
+    fail(DSPINE_E_STATE, "ring_bytes: local layer %d needs capacity %d", layer, S);
+    return 0;
+  }
+  return (size_t)model->g.n_kv_heads * capacity * model->g.head_dim * elt_bytes(model->g);
+}
+
+size_t dspine_workspace_bytes(const dspine_model* model, int max_batch, int max_width, int64_t max_rows) {
+  if (!model || max_batch < 1 || max_batch > DSPINE_MAX_BATCH || max_width < DSPINE_MIN_WIDTH ||
+      max_width > DSPINE_MAX_WIDTH || max_rows < 0) {
+    fail(DSPINE_E_ARG, "workspace_bytes: bad argument");
+    return 0;
+  }
+  return make_plan(model->g, (int64_t)max_batch * max_width, max_rows).total;
+}
+
+// -----------------------------------------------------------------------------
+// a1-a3
+// -----------------------------------------------------------------------------
+int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx, const void* const* feats,
+                           const int64_t* n_tok, void* workspace, size_t workspace_bytes,
+                           dspine_stream_t stream_) {
+  if (!model || !ctx || !feats || !n_tok) return fail(DSPINE_E_ARG, "materialize: NULL argument");
+  if (n_req < 1 || n_req > DSPINE_MAX_BATCH) return fail(DSPINE_E_UNSUPPORTED, "materialize: n_req %d", n_req);
+  const dspine_geometry& g = model->g;
+  const dspine_weights& wt = model->w;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const int L = g.n_layers, H = g.hidden, kvd = g.n_kv_heads * g.head_dim;
+
+  // rows each request must compute: [need_lo, F1)
+  int64_t need_lo[DSPINE_MAX_BATCH], F1[DSPINE_MAX_BATCH], total_rows = 0;
+  for (int b = 0; b < n_req; ++b) {
+    if (n_tok[b] < 0) return fail(DSPINE_E_ARG, "materialize: n_tok[%d] = %lld", b, (long long)n_tok[b]);
+    const int64_t F0 = ctx[b].frontier;
+    F1[b] = F0 + n_tok[b];
+    int rc = check_ctx_rings(*model, ctx[b], b, F1[b]);
+    if (rc) return rc;
+    if (n_tok[b] > 0 && !feats[b]) return fail(DSPINE_E_ARG, "materialize: feats[%d] is NULL", b);
+    if (n_tok[b] > 0 && !aligned16(feats[b])) return fail(DSPINE_E_ARG, "materialize: feats[%d] not aligned", b);
+    int64_t lo = F1[b];
+    for (int l = 0; l < L; ++l) lo = std::min(lo, std::max(F0, live_lo(g.window[l], F1[b])));
+    need_lo[b] = lo;
+    total_rows += F1[b] - lo;
+  }
+  if (total_rows > 0) {
+    if (!workspace || !aligned16(workspace)) return fail(DSPINE_E_ARG, "materialize: workspace NULL or unaligned");
+    const int64_t cap_rows = rows_capacity(g, workspace_bytes);
+    if (cap_rows < 1)
+      return fail(DSPINE_E_WORKSPACE, "materialize: workspace of %zu bytes holds no row block", workspace_bytes);
+    char* ws = static_cast<char*>(workspace);
+    const int cus = num_cus();
+    const int64_t blk_rows = std::min<int64_t>(cap_rows, total_rows);
+    const Plan P = make_plan(g, 1, blk_rows);
+    float* c_raw = reinterpret_cast<float*>(ws + P.c_raw);
+    void* c_act = ws + P.c_act;
+    float* kv_raw = reinterpret_cast<float*>(ws + P.kv_raw);
+    const int ldkv = L * 2 * kvd;
+
+    // walk the concatenated row list in blocks
+    int64_t done = 0;
+    while (done < total_rows) {
+      const int64_t nrows = std::min(blk_rows, total_rows - done);
+      // requests intersecting [done, done + nrows)
+      int nsrc = 0;
+      const void* src[DSPINE_MAX_BATCH];
+      int32_t row0[DSPINE_MAX_BATCH + 1];
+      int64_t skip[DSPINE_MAX_BATCH], pos0[DSPINE_MAX_BATCH];
+      int req_of[DSPINE_MAX_BATCH];
+      int64_t acc = 0;
+      for (int b = 0; b < n_req; ++b) {
+        const int64_t rb = F1[b] - need_lo[b];
+        const int64_t s0 = std::max(acc, done), s1 = std::min(acc + rb, done + nrows);
+        if (s1 > s0) {
+          src[nsrc] = feats[b];
+          row0[nsrc] = (int32_t)(s0 - done);
+          const int64_t first_pos = need_lo[b] + (s0 - acc);
+          skip[nsrc] = first_pos - ctx[b].frontier;      // feature row of that position
+          pos0[nsrc] = first_pos;
+          req_of[nsrc] = b;
+          ++nsrc;
+        }
+        acc += rb;
+      }
+      row0[nsrc] = (int32_t)nrows;
+
+      // GEMM 1: c_raw = s W_feat^T  (a1)
+      const bool tile = g.dtype == DSPINE_BF16 && nrows > kMaxRows && H % 128 == 0 &&
+                        (g.n_feat_layers * H) % 64 == 0 && kvd % 128 == 0 && H % 64 == 0;
+      if (tile) {
+        TileGemmParams tp;
+        memset(&tp, 0, sizeof tp);
+        tp.seg_ptr[0] = wt.w_feat;
+        tp.seg_rows0[0] = 0;
+        tp.seg_rows0[1] = H;
+        tp.nseg = 1;
+        tp.N = H;
+        tp.K = g.n_feat_layers * H;
+        tp.M = (int)nrows;
+        tp.pro = PRO_GATHER;
+        tp.a_bf16 = 1;
+        tp.lda = g.n_feat_layers * H;
+        for (int s = 0; s < nsrc; ++s) {
+          tp.g_src[s] = src[s];
+          tp.g_row0[s] = row0[s];
+          tp.g_skip[s] = skip[s];
+        }
+        tp.g_row0[nsrc] = row0[nsrc];
+        tp.g_n = nsrc;
+        tp.out = c_raw;
+        tp.ldo = H;
+        ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
+        HIP_TRY(launch_gemm_tile(tp, g.dtype, cus, stream));
+      } else {
+        for (int64_t r0 = 0; r0 < nrows; r0 += kMaxRows) {
+          const int mr = (int)std::min<int64_t>(kMaxRows, nrows - r0);
+          GemmParams gp = gemm_base(P, ws, g.n_feat_layers * H, mr);
+          set_segments(gp, {{wt.w_feat, H}});
+          gp.pro = PRO_GATHER;
+          gp.a_bf16 = 1;                    // target features are bf16 inputs
+          gp.lda = g.n_feat_layers * H;
+          int n = 0;
+          for (int s = 0; s < nsrc; ++s) {
+            const int64_t a0 = std::max<int64_t>(row0[s], r0), a1 = std::min<int64_t>(row0[s + 1], r0 + mr);
+            if (a1 <= a0) continue;
+            gp.g_src[n] = src[s];
+            gp.g_row0[n] = (int32_t)(a0 - r0);
+            gp.g_skip[n] = skip[s] + (a0 - row0[s]);
+            ++n;
+          }
+          gp.g_row0[n] = mr;
+          gp.g_n = n;
+          gp.epi = EPI_STORE;
+          gp.out = c_raw + r0 * H;
+          gp.ldo = H;
+          ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
+          HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+        }
+      }
+      // c = plain_rmsnorm(c_raw, context_norm)
+      RowParams rp;
+      memset(&rp, 0, sizeof rp);
+      rp.M = (int)nrows;
+      rp.H = H;
+      rp.x = c_raw;
+      rp.act = c_act;
+      rp.gain = wt.g_ctx;
+      rp.eps = g.eps;
+      {
+        ProfScope ps(DSPINE_PROF_CTX_STORE, stream);
+        HIP_TRY(launch_rmsnorm(rp, g.dtype, false, stream));
+      }
+
+      // GEMM 2: every layer's K and V projections of c  (a2)
+      if (tile) {
+        TileGemmParams tp;
+        memset(&tp, 0, sizeof tp);
+        for (int l = 0; l < L; ++l) {
+          tp.seg_ptr[2 * l] = wt.layer[l].wk;
+          tp.seg_ptr[2 * l + 1] = wt.layer[l].wv;
+          tp.seg_rows0[2 * l] = 2 * l * kvd;
+          tp.seg_rows0[2 * l + 1] = (2 * l + 1) * kvd;
+        }
+        tp.seg_rows0[2 * L] = 2 * L * kvd;
+        tp.nseg = 2 * L;
+        tp.N = ldkv;
+        tp.K = H;
+        tp.M = (int)nrows;
+        tp.pro = PRO_COPY;
+        tp.a = c_act;
+        tp.lda = H;
+        tp.out = kv_raw;
+        tp.ldo = ldkv;
+        ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
+        HIP_TRY(launch_gemm_tile(tp, g.dtype, cus, stream));
+      } else {
+        for (int64_t r0 = 0; r0 < nrows; r0 += kMaxRows) {
+          const int mr = (int)std::min<int64_t>(kMaxRows, nrows - r0);
+          GemmParams gp = gemm_base(P, ws, H, mr);
+          int blk = 0;
+          for (int l = 0; l < L; ++l) {
+            gp.seg_ptr[2 * l] = wt.layer[l].wk;
+            gp.seg_blk0[2 * l] = blk;
+            blk += kvd / 16;
+            gp.seg_ptr[2 * l + 1] = wt.layer[l].wv;
+            gp.seg_blk0[2 * l + 1] = blk;
+            blk += kvd / 16;
+          }
+          gp.nseg = 2 * L;
+          gp.nblk = blk;
+          gp.pro = PRO_COPY;
+          gp.a = static_cast<char*>(c_act) + (size_t)r0 * H * act_bytes(g);
+          gp.lda = H;
+          gp.epi = EPI_STORE;
+          gp.out = kv_raw + r0 * ldkv;
+          gp.ldo = ldkv;
+          ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
+          HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+        }
+      }
+      // per layer: head norm + RoPE + storage rounding + ring scatter
+      for (int l = 0; l < L; ++l) {
+        KvStoreParams kp;
+        memset(&kp, 0, sizeof kp);
+        kp.rows = (int)nrows;
+        kp.nkv = g.n_kv_heads;
+        kp.D = g.head_dim;
+        kp.S = g.window[l];
+        kp.n_req = nsrc;
+        kp.kv = kv_raw;
+        kp.ld = ldkv;
+        kp.k_col = 2 * l * kvd;
+        kp.v_col = (2 * l + 1) * kvd;
+        kp.gk = wt.layer[l].gk;
+        kp.eps = g.eps;
+        kp.rope_theta = g.rope_theta;
+        for (int s = 0; s <= nsrc; ++s) kp.row0[s] = row0[s];
+        for (int s = 0; s < nsrc; ++s) {
+          const int b = req_of[s];
+          kp.pos0[s] = pos0[s];
+          kp.keep_lo[s] = std::max(ctx[b].frontier, live_lo(g.window[l], F1[b]));
+          kp.kring[s] = ctx[b].k_ring[l];
+          kp.vring[s] = ctx[b].v_ring[l];
+          kp.cap[s] = ctx[b].capacity[l];
+        }
+        ProfScope ps(DSPINE_PROF_CTX_STORE, stream);
+        HIP_TRY(launch_kv_store(kp, g.dtype, stream));
+      }
+      done += nrows;
+    }
+  }
+  for (int b = 0; b < n_req; ++b) ctx[b].frontier = F1[b];
+  return ok();
+}
+
+// -----------------------------------------------------------------------------
+// bridge (a9-a11) on x [M, H] fp32 in place
+// -----------------------------------------------------------------------------
+namespace {
+int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const int32_t* anchor_ids,
+               const float* pred_codes, char* ws, const Plan& P, int cus, hipStream_t stream) {
+  const dspine_geometry& g = m.g;
+  const dspine_weights& wt = m.w;
+  const int M = B * W, H = g.hidden, r = g.code_dim, a = g.msg_dim;
+  void* act_h = ws + P.act_h;
+  void* act_r = ws + P.act_r;
+  float* z = reinterpret_cast<float*>(ws + P.z);
+  float* Pb = reinterpret_cast<float*>(ws + P.P);
+  float* P2 = reinterpret_cast<float*>(ws + P.P2);
+  float* rho = reinterpret_cast<float*>(ws + P.rho);
+
+  RowParams rp;
+  memset(&rp, 0, sizeof rp);
+  rp.M = M;
+  rp.W = W;
+  rp.H = H;
+  rp.x = x;
+  rp.act = act_h;
+  rp.eps = g.eps;
+  rp.rho = rho;
+  HIP_TRY(launch_bridge_read(rp, g.dtype, stream));                 // rho, x/(rho+eps)
+
+  GemmParams gp = gemm_base(P, ws, H, M);                             // z = R (x/(rho+eps))
+  set_segments(gp, {{wt.layer[layer].R, r}});
+  gp.pro = PRO_COPY;
+  gp.a = act_h;
+  gp.lda = H;
+  gp.epi = EPI_STORE;
+  gp.out = z;
+  gp.ldo = r;
+  HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+
+  RowParams cp;
+  memset(&cp, 0, sizeof cp);
+  cp.M = M;
+  cp.W = W;
+  cp.eps = g.eps;
+  cp.z = z;
+  cp.r = r;
+  cp.codebook = wt.codebook;
+  cp.act = act_r;
+  for (int b = 0; b < B; ++b) cp.anchor[b] = anchor_ids[b];
+  HIP_TRY(launch_bridge_code(cp, g.dtype, stream));                   // c (anchor: sqrt(r) C[a])
+
+  gp = gemm_base(P, ws, r, M);                                         // [G; G_p; A] c, one GEMM
+  set_segments(gp, {{wt.bridge_G, a}, {wt.bridge_Gp, a}, {wt.bridge_A, a}});
+  gp.pro = PRO_COPY;
+  gp.a = act_r;
+  gp.lda = r;
+  gp.epi = EPI_STORE;
+  gp.out = Pb;
+  gp.ldo = 3 * a;
+  HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+
+  const float* Ppred = Pb;
+  int shift = 1;
+  if (pred_codes) {                                                    // predecessor override
+    RowParams op;
+    memset(&op, 0, sizeof op);
+    op.M = M;
+    op.r = r;
+    op.pred_in = pred_codes;
+    op.pred_act = ws + P.act_r2;
+    HIP_TRY(launch_copy_codes(op, g.dtype, stream));
+    gp = gemm_base(P, ws, r, M);
+    set_segments(gp, {{wt.bridge_G, a}, {wt.bridge_Gp, a}, {wt.bridge_A, a}});
+    gp.pro = PRO_COPY;
+    gp.a = ws + P.act_r2;
+    gp.lda = r;
+    gp.epi = EPI_STORE;
+    gp.out = P2;
+    gp.ldo = 3 * a;
+    HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+    Ppred = P2;
+    shift = 0;
+  }
+
+  gp = gemm_base(P, ws, a, M);                                         // x += rho W_l (g * m)
+  set_segments(gp, {{wt.layer[layer].W_l, H}});
+  gp.pro = PRO_BRIDGE_MSG;
+  gp.P = Pb;
+  gp.Ppred = Ppred;
+  gp.bias = wt.bridge_b;
+  gp.a_dim = a;
+  gp.W = W;
+  gp.pred_shift = shift;
+  gp.epi = EPI_ADD_ROWSCALE;
+  gp.row_scale = rho;
+  gp.out = x;
+  gp.ldo = H;
+  HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+  return DSPINE_OK;
+}
+
+int check_call(const dspine_model* model, int B, int W, const int32_t* anchor_ids, const void* ws,
+               size_t ws_bytes, size_t* need) {
+  if (!model || !anchor_ids) return fail(DSPINE_E_ARG, "NULL argument");
+  if (B < 1 || B > DSPINE_MAX_BATCH) return fail(DSPINE_E_UNSUPPORTED, "B = %d not in 1..%d", B, DSPINE_MAX_BATCH);
+  if (W < DSPINE_MIN_WIDTH || W > DSPINE_MAX_WIDTH)
+    return fail(DSPINE_E_UNSUPPORTED, "W = %d not in %d..%d", W, DSPINE_MIN_WIDTH, DSPINE_MAX_WIDTH);
+  for (int b = 0; b < B; ++b)
+    if (anchor_ids[b] < 0 || anchor_ids[b] >= model->g.vocab)
+      return fail(DSPINE_E_ARG, "anchor_ids[%d] = %d outside [0, %d)", b, anchor_ids[b], model->g.vocab);
+  *need = make_plan(model->g, (int64_t)B * W, 0).total;
+  if (!ws || !aligned16(ws)) return fail(DSPINE_E_ARG, "workspace NULL or not 16-byte aligned");
+  if (ws_bytes < *need) return fail(DSPINE_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, *need);
+  return DSPINE_OK;
+}
+}  // namespace
+
+int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x, const int32_t* anchor_ids,
+                  const float* pred_codes, void* workspace, size_t workspace_bytes, dspine_stream_t stream) {
+  size_t need = 0;
+  int rc = check_call(model, B, W, anchor_ids, workspace, workspace_bytes, &need);
+  if (rc) return rc;
+  if (model->g.code_dim == 0) return fail(DSPINE_E_UNSUPPORTED, "bridge: the geometry has no bridge (code_dim 0)");
+  if (layer < 0 || layer >= model->g.n_layers) return fail(DSPINE_E_ARG, "bridge: layer %d", layer);
+  if (!x || !aligned16(x)) return fail(DSPINE_E_ARG, "bridge: x NULL or unaligned");
+  if (pred_codes && !aligned16(pred_codes)) return fail(DSPINE_E_ARG, "bridge: pred_codes unaligned");
+  const Plan P = make_plan(model->g, (int64_t)B * W, 0);
+  rc = run_bridge(*model, layer, B, W, x, anchor_ids, pred_codes, static_cast<char*>(workspace), P, num_cus(),
+                  reinterpret_cast<hipStream_t>(stream));
+  return rc ? rc : ok();
+}
+
+// -----------------------------------------------------------------------------
+// a4-a12
+// -----------------------------------------------------------------------------
+int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_ctx* ctx, const int32_t* anchor_ids,
+                         float* out, void* workspace, size_t workspace_bytes, dspine_stream_t stream_) {
+  size_t need = 0;
+  int rc = check_call(model, B, W, anchor_ids, workspace, workspace_bytes, &need);
+  if (rc) return rc;
+  if (!ctx) return fail(DSPINE_E_ARG, "forward: ctx NULL");
+  if (!out || !aligned16(out)) return fail(DSPINE_E_ARG, "forward: out NULL or unaligned");
+  for (int b = 0; b < B; ++b)
+    if ((rc = check_ctx_rings(*model, ctx[b], b, ctx[b].frontier))) return rc;
+
+  const dspine_geometry& g = model->g;
+  const dspine_weights& wt = model->w;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const int M = B * W, H = g.hidden, D = g.head_dim;
+  const int qd = g.n_q_heads * D, kvd = g.n_kv_heads * D;
+  const Plan P = make_plan(g, M, 0);
+  const int cus = num_cus();
+  float* x = reinterpret_cast<float*>(ws + P.x);
+  void* act_h = ws + P.act_h;
+  void* act_q = ws + P.act_q;
+  void* act_f = ws + P.act_f;
+  float* qkv = reinterpret_cast<float*>(ws + P.qkv);
+  float* rope = reinterpret_cast<float*>(ws + P.rope);
+
+  // a4 + first input norm (+ rotation table of positions F_b + i)
+  RowParams rp;
+  memset(&rp, 0, sizeof rp);
+  rp.M = M;
+  rp.W = W;
+  rp.H = H;
+  rp.x_out = x;
+  rp.act = act_h;
+  rp.gain = wt.layer[0].g_in;
+  rp.eps = g.eps;
+  rp.embed = wt.embed;
+  for (int b = 0; b < B; ++b) {
+    rp.anchor[b] = anchor_ids[b];
+    rp.F[b] = ctx[b].frontier;
+  }
+  rp.mask_id = g.mask_token_id;
+  rp.rope = rope;
+  rp.head_dim = D;
+  rp.rope_theta = g.rope_theta;
+  {
+    ProfScope ps(DSPINE_PROF_NORM, stream);
+    HIP_TRY(launch_embed_norm(rp, g.dtype, stream));
+  }
+
+  for (int l = 0; l < g.n_layers; ++l) {
+    const dspine_layer_weights& Lw = wt.layer[l];
+    if (l > 0) {
+      RowParams np;
+      memset(&np, 0, sizeof np);
+      np.M = M;
+      np.H = H;
+      np.x = x;
+      np.act = act_h;
+      np.gain = Lw.g_in;
+      np.eps = g.eps;
+      ProfScope ps(DSPINE_PROF_NORM, stream);
+      HIP_TRY(launch_rmsnorm(np, g.dtype, false, stream));
+    }
+    // a5: q | k | v projections of n
+    GemmParams gp = gemm_base(P, ws, H, M);
+    set_segments(gp, {{Lw.wq, qd}, {Lw.wk, kvd}, {Lw.wv, kvd}});
+    gp.pro = PRO_COPY;
+    gp.a = act_h;
+    gp.lda = H;
+    gp.epi = EPI_STORE;
+    gp.out = qkv;
+    gp.ldo = qd + 2 * kvd;
+    {
+      ProfScope ps(DSPINE_PROF_GEMM_QKV, stream);
+      HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+    }
+
+    // a6 (with the q/k head norm + RoPE of a5)
+    AttnParams ap;
+    memset(&ap, 0, sizeof ap);
+    ap.B = B;
+    ap.W = W;
+    ap.nq = g.n_q_heads;
+    ap.nkv = g.n_kv_heads;
+    ap.M = M;
+    ap.qkv = qkv;
+    ap.ld_qkv = qd + 2 * kvd;
+    ap.gq = Lw.gq;
+    ap.gk = Lw.gk;
+    ap.eps = g.eps;
+    ap.rope = rope;
+    ap.S = g.window[l];
+    ap.causal = g.block_causal;
+    int64_t max_splits = 1;
+    const int64_t base_split = ceil_div(256, (int64_t)B * g.n_kv_heads);
+    for (int b = 0; b < B; ++b) {
+      ap.kring[b] = ctx[b].k_ring[l];
+      ap.vring[b] = ctx[b].v_ring[l];
+      ap.cap[b] = ctx[b].capacity[l];
+      ap.F[b] = ctx[b].frontier;
+      ap.lo0[b] = row0_lo(ctx[b].frontier, g.window[l]);
+      const int64_t nctx = ap.F[b] - ap.lo0[b];
+      const int64_t want = std::max<int64_t>(1, std::min(ceil_div(nctx, 128), std::max(base_split, ceil_div(nctx, 2048))));
+      max_splits = std::max(max_splits, want);
+    }
+    ap.nsplit = (int)std::min<int64_t>(max_splits, kMaxSplit);
+    for (int b = 0; b < B; ++b) {
+      const int64_t nctx = ap.F[b] - ap.lo0[b];
+      ap.kps[b] = (int32_t)(ceil_div(ceil_div(nctx, ap.nsplit), 32) * 32);
+    }
+    ap.out = act_q;
+    ap.ld_out = qd;
+    ap.partials = reinterpret_cast<float*>(ws + P.attn_part);
+    ap.counters = reinterpret_cast<uint32_t*>(ws + P.attn_cnt);
+    {
+      ProfScope ps(DSPINE_PROF_ATTENTION, stream);
+      HIP_TRY(launch_attention(ap, g.dtype, D, stream));
+    }
+
+    // a7: y = x + W_o a ; m = norm_post(y)
+    gp = gemm_base(P, ws, qd, M);
+    set_segments(gp, {{Lw.wo, H}});
+    gp.pro = PRO_COPY;
+    gp.a = act_q;
+    gp.lda = qd;
+    gp.epi = EPI_ADD;
+    gp.out = x;
+    gp.ldo = H;
+    {
+      ProfScope ps(DSPINE_PROF_GEMM_O, stream);
+      HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+    }
+    RowParams np;
+    memset(&np, 0, sizeof np);
+    np.M = M;
+    np.H = H;
+    np.x = x;
+    np.act = act_h;
+    np.gain = Lw.g_post;
+    np.eps = g.eps;
+    {
+      ProfScope ps(DSPINE_PROF_NORM, stream);
+      HIP_TRY(launch_rmsnorm(np, g.dtype, false, stream));
+    }
+
+    // a8: x = y + W_down(SiLU(W_gate m) * W_up m)
+    gp = gemm_base(P, ws, H, M);
+    gp.seg_ptr[0] = Lw.w_gate;
+    gp.seg_ptr[1] = Lw.w_up;
+    gp.nseg = 2;
+    gp.interleave = 1;
+    gp.nblk = 2 * (g.ffn / 16);
+    gp.pro = PRO_COPY;
+    gp.a = act_h;
+    gp.lda = H;
+    gp.epi = EPI_SWIGLU;
+    gp.out_act = act_f;
+    gp.ld_act = g.ffn;
+    {
+      ProfScope ps(DSPINE_PROF_GEMM_GATE_UP, stream);
+      HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+    }
+    gp = gemm_base(P, ws, g.ffn, M);
+    set_segments(gp, {{Lw.w_down, H}});
+    gp.pro = PRO_COPY;
+    gp.a = act_f;
+    gp.lda = g.ffn;
+    gp.epi = EPI_ADD;
+    gp.out = x;
+    gp.ldo = H;
+    {
+      ProfScope ps(DSPINE_PROF_GEMM_DOWN, stream);
+      HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+    }
+
+    // a9-a11
+    if (g.code_dim > 0) {
+      ProfScope ps(DSPINE_PROF_BRIDGE, stream);
+      rc = run_bridge(*model, l, B, W, x, anchor_ids, nullptr, ws, P, cus, stream);
+      if (rc) return rc;
+    }
+  }
+  // a12
+  RowParams fp;
+  memset(&fp, 0, sizeof fp);
+  fp.M = M;
+  fp.H = H;
+  fp.x = x;
+  fp.f32_out = out;
+  fp.gain = wt.g_final;
+  fp.eps = g.eps;
+  {
+    ProfScope ps(DSPINE_PROF_NORM, stream);
+    HIP_TRY(launch_rmsnorm(fp, g.dtype, true, stream));
+  }
+  return ok();
+}
+
+int dspine_debug_visible(const dspine_model* model, int layer, int B, int W, const dspine_ctx* ctx,
+                         int64_t* lo_hi, int32_t* first_slot, int32_t* n_block, dspine_stream_t stream) {
+  if (!model || !ctx || !lo_hi || !first_slot || !n_block) return fail(DSPINE_E_ARG, "debug_visible: NULL argument");
+  if (layer < 0 || layer >= model->g.n_layers) return fail(DSPINE_E_ARG, "debug_visible: layer %d", layer);
+  if (B < 1 || B > DSPINE_MAX_BATCH || W < DSPINE_MIN_WIDTH || W > DSPINE_MAX_WIDTH)
+    return fail(DSPINE_E_UNSUPPORTED, "debug_visible: B %d W %d", B, W);
+  VisibleParams vp;
+  memset(&vp, 0, sizeof vp);
+  vp.B = B;
+  vp.W = W;
+  vp.S = model->g.window[layer];
+  vp.causal = model->g.block_causal;
+  for (int b = 0; b < B; ++b) {
+    if (ctx[b].frontier < 0) return fail(DSPINE_E_STATE, "debug_visible: frontier < 0");
+    vp.F[b] = ctx[b].frontier;
+  }
+  vp.lo_hi = lo_hi;
+  vp.first_slot = first_slot;
+  vp.n_block = n_block;
+  HIP_TRY(launch_debug_visible(vp, reinterpret_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+}  // extern "C"

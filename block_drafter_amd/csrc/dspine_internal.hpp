@@ -1,0 +1,168 @@
+// Internal interfaces between the C ABI (dspine_api.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dspine.h"
+
+namespace dspine {
+
+enum { DT_F32 = DSPINE_F32, DT_BF16 = DSPINE_BF16 };
+enum { PRO_COPY = 0, PRO_GATHER = 1, PRO_BRIDGE_MSG = 2 };
+enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2, EPI_ADD_ROWSCALE = 3 };
+
+constexpr int kMaxSeg = 32;        // weight segments of one streamed GEMM
+constexpr int kMaxGrid = 512;      // workgroups of one streamed GEMM
+constexpr int kMaxTiles = 8192;    // tile counters of one GEMM
+constexpr int kMaxSplit = 32;      // key splits of one attention launch
+constexpr int kMaxRows = 128;      // B*W rows of one forward
+
+// ---------------------------------------------------------------------------
+// streamed (skinny) GEMM: out[m, n] (op)= sum_k A[m, k] W[n, k]
+// ---------------------------------------------------------------------------
+struct GemmParams {
+  // weights: the virtual N space is a list of segments (or gate/up pairs)
+  const void* seg_ptr[kMaxSeg];   // each [rows_s, K] row-major, model dtype
+  int32_t seg_blk0[kMaxSeg];      // first 16-row block of each segment
+  int32_t nseg;
+  int32_t interleave;             // 1: block vb -> segment vb&1, row block vb>>1
+  int32_t nblk;                   // 16-row blocks in N
+  int32_t K, M;
+  // A operand: activation type of the model (fp16 for BF16 models), or bf16
+  // target features when a_bf16 is set
+  int32_t pro;
+  int32_t a_bf16;
+  const void* a;                  // PRO_COPY / PRO_GATHER: row stride lda
+  int32_t lda;
+  const void* g_src[DSPINE_MAX_BATCH];   // PRO_GATHER: rows [g_row0[s], g_row0[s+1])
+  int32_t g_row0[DSPINE_MAX_BATCH + 1];  //   come from g_src[s] starting at row g_skip[s]
+  int32_t g_n;
+  int64_t g_skip[DSPINE_MAX_BATCH];
+  const float* P;                 // PRO_BRIDGE_MSG: own-code projections [M, 3a]
+  const float* Ppred;             //   predecessor-code projections
+  const void* bias;               //   [a] model dtype
+  int32_t a_dim, W, pred_shift;
+  // epilogue
+  int32_t epi;
+  float* out;                     // EPI_STORE / EPI_ADD(_ROWSCALE): fp32 [M, ldo]
+  int32_t ldo;
+  const float* row_scale;         // EPI_ADD_ROWSCALE: out[m] += row_scale[m] * acc
+  void* out_act;                  // EPI_SWIGLU: model dtype [M, ld_act]
+  int32_t ld_act;
+  // filled by the launcher
+  int32_t tiles, ipt, xcd_remap;
+  float* partials;
+  uint32_t* counters;
+};
+hipError_t launch_gemm_stream(const GemmParams& p, int dtype, int num_cus, hipStream_t s);
+size_t gemm_stream_partial_floats(int grid_cap);
+int gemm_stream_grid_cap(int num_cus);
+
+// ---------------------------------------------------------------------------
+// tiled MFMA GEMM for many rows (prefill): out[m, n] = sum_k A[m, k] W[n, k]
+// ---------------------------------------------------------------------------
+struct TileGemmParams {
+  const void* seg_ptr[kMaxSeg];
+  int32_t seg_rows0[kMaxSeg + 1]; // first N row of each segment (prefix)
+  int32_t nseg;
+  int32_t N, K, M;
+  int32_t pro;                    // PRO_COPY or PRO_GATHER (same fields as above)
+  int32_t a_bf16;                 // 1: bf16 x bf16 (features); 0: fp16 operands
+  const void* a;
+  int32_t lda;
+  const void* g_src[DSPINE_MAX_BATCH];
+  int32_t g_row0[DSPINE_MAX_BATCH + 1];
+  int32_t g_n;
+  int64_t g_skip[DSPINE_MAX_BATCH];
+  float* out;                     // fp32 [M, ldo]
+  int32_t ldo;
+};
+hipError_t launch_gemm_tile(const TileGemmParams& p, int dtype, int num_cus, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// attention over ring context + block
+// ---------------------------------------------------------------------------
+struct AttnParams {
+  int32_t B, W, nq, nkv, M;
+  const float* qkv;               // raw projections [M, ld_qkv]: q | k | v
+  int32_t ld_qkv;
+  const void* gq;                 // [D] model dtype
+  const void* gk;
+  float eps;
+  const float* rope;              // [M, D/2, 2] cos, sin of each row's angles
+  int32_t S, causal;
+  const void* kring[DSPINE_MAX_BATCH];
+  const void* vring[DSPINE_MAX_BATCH];
+  int64_t cap[DSPINE_MAX_BATCH];
+  int64_t F[DSPINE_MAX_BATCH];
+  int64_t lo0[DSPINE_MAX_BATCH];  // first context position row 0 sees
+  int32_t kps[DSPINE_MAX_BATCH];  // context keys per split (multiple of 32)
+  int32_t nsplit;
+  void* out;                      // model dtype [M, ld_out]
+  int32_t ld_out;
+  float* partials;
+  uint32_t* counters;             // [B * nq]
+};
+hipError_t launch_attention(const AttnParams& p, int dtype, int head_dim, hipStream_t s);
+size_t attn_partial_floats(int max_b, int nq, int head_dim);
+
+// ---------------------------------------------------------------------------
+// row kernels
+// ---------------------------------------------------------------------------
+struct RowParams {
+  int32_t M, W, H;
+  const float* x;                 // fp32 [M, H] input
+  float* x_out;                   // fp32 residual written by embed gather
+  void* act;                      // model dtype [M, H] output
+  float* f32_out;                 // fp32 output (final norm)
+  const void* gain;               // [H] model dtype
+  float eps;
+  // embed gather
+  const void* embed;
+  int32_t anchor[DSPINE_MAX_BATCH];
+  int32_t mask_id;
+  // rope table side job
+  float* rope;                    // [M, D/2, 2]
+  int64_t F[DSPINE_MAX_BATCH];
+  int32_t head_dim;
+  float rope_theta;
+  // bridge
+  float* rho;                     // [M]
+  const float* z;                 // [M, r]
+  int32_t r;
+  const void* codebook;           // [vocab, r]
+  const float* pred_in;           // [M, r] fp32 override codes
+  void* pred_act;                 // [M, r] model dtype
+};
+hipError_t launch_embed_norm(const RowParams& p, int dtype, hipStream_t s);
+hipError_t launch_rmsnorm(const RowParams& p, int dtype, bool f32_output, hipStream_t s);
+hipError_t launch_bridge_read(const RowParams& p, int dtype, hipStream_t s);
+hipError_t launch_bridge_code(const RowParams& p, int dtype, hipStream_t s);
+hipError_t launch_copy_codes(const RowParams& p, int dtype, hipStream_t s);
+
+struct KvStoreParams {
+  int32_t rows, nkv, D, S, n_req;
+  const float* kv;                // fp32 [rows, ld]: k columns at k_col, v at v_col
+  int32_t ld, k_col, v_col;
+  const void* gk;
+  float eps, rope_theta;
+  int32_t row0[DSPINE_MAX_BATCH + 1];
+  int64_t pos0[DSPINE_MAX_BATCH];      // position of the request's first row
+  int64_t keep_lo[DSPINE_MAX_BATCH];   // rows at positions below are not stored
+  void* kring[DSPINE_MAX_BATCH];
+  void* vring[DSPINE_MAX_BATCH];
+  int64_t cap[DSPINE_MAX_BATCH];
+};
+hipError_t launch_kv_store(const KvStoreParams& p, int dtype, hipStream_t s);
+
+struct VisibleParams {
+  int32_t B, W, S, causal;
+  int64_t F[DSPINE_MAX_BATCH];
+  int64_t* lo_hi;
+  int32_t* first_slot;
+  int32_t* n_block;
+};
+hipError_t launch_debug_visible(const VisibleParams& p, hipStream_t s);
+
+}  // namespace dspine

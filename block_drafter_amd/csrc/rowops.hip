@@ -1,0 +1,243 @@
+// Row-wise kernels: input gather + norms (a4, a5 head, a7 norm, a12), the
+// bridge's read and code steps (a9), and the context K/V store epilogue (a2).
+// One workgroup per row; statistics in fp32.
+#include "dspine_device.hpp"
+#include "dspine_internal.hpp"
+
+namespace dspine {
+
+constexpr int kRowThreads = 256;
+
+// (cos, sin) of position * theta^(-2j/D), angle formed in double precision so
+// that positions of tens of thousands keep full float accuracy.
+__device__ __forceinline__ void rope_pair(int64_t pos, int j, int D, float theta, float& c, float& s) {
+  const double inv_freq = exp2(-(2.0 * j / D) * log2((double)theta));
+  const double ang = (double)pos * inv_freq;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// a4 + layer 0's input norm: x[m] = embed[token(m)], act[m] = g_in * x / rms(x).
+// [NIF, draft input]: row 0 of each request is the anchor, rows 1..W-1 the
+// mask token.  Side job: the rotation table of every row's position F + i.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const RowParams p) {
+  __shared__ float red[kRowThreads / 64];
+  const int m = blockIdx.x, b = m / p.W, i = m % p.W;
+  const int tok = i == 0 ? p.anchor[b] : p.mask_id;
+  const T* e = reinterpret_cast<const T*>(p.embed) + (size_t)tok * p.H;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < p.H; k += kRowThreads) {
+    const float v = Elt<T>::load(e, k);
+    p.x_out[(size_t)m * p.H + k] = v;
+    ss += v * v;
+  }
+  ss = block_sum<kRowThreads>(ss, red);
+  const float inv = rsqrtf(ss / p.H + p.eps);
+  using TA = typename ActOf<T>::type;
+  const T* gw = reinterpret_cast<const T*>(p.gain);
+  TA* act = reinterpret_cast<TA*>(p.act);
+  for (int k = threadIdx.x; k < p.H; k += kRowThreads)
+    Elt<TA>::store(act, (size_t)m * p.H + k, Elt<T>::load(e, k) * inv * Elt<T>::load(gw, k));
+  for (int j = threadIdx.x; j < p.head_dim / 2; j += kRowThreads) {
+    float c, s;
+    rope_pair(p.F[b] + i, j, p.head_dim, p.rope_theta, c, s);
+    p.rope[(size_t)m * p.head_dim + 2 * j] = c;
+    p.rope[(size_t)m * p.head_dim + 2 * j + 1] = s;
+  }
+}
+
+// plain_rmsnorm [NIF]: out = g * x / sqrt(mean(x^2) + eps); out in the model
+// dtype (GEMM operand) or fp32 (final hidden states).
+template <typename T, bool F32OUT>
+__global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const RowParams p) {
+  __shared__ float red[kRowThreads / 64];
+  const int m = blockIdx.x;
+  const float* x = p.x + (size_t)m * p.H;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < p.H; k += kRowThreads) ss += x[k] * x[k];
+  ss = block_sum<kRowThreads>(ss, red);
+  const float inv = rsqrtf(ss / p.H + p.eps);
+  const T* gw = reinterpret_cast<const T*>(p.gain);
+  for (int k = threadIdx.x; k < p.H; k += kRowThreads) {
+    const float v = x[k] * inv * Elt<T>::load(gw, k);
+    if (F32OUT) p.f32_out[(size_t)m * p.H + k] = v;
+    else Elt<typename ActOf<T>::type>::store(reinterpret_cast<typename ActOf<T>::type*>(p.act), (size_t)m * p.H + k, v);
+  }
+}
+
+// a9, first half [FLZ, "The bridge"]: rho_t = sqrt(mean(x_t^2)) (no floor)
+// and the read input x_t / (rho_t + eps) in the GEMM operand type.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void bridge_read_kernel(const RowParams p) {
+  __shared__ float red[kRowThreads / 64];
+  const int m = blockIdx.x;
+  const float* x = p.x + (size_t)m * p.H;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < p.H; k += kRowThreads) ss += x[k] * x[k];
+  ss = block_sum<kRowThreads>(ss, red);
+  const float rho = sqrtf(ss / p.H);
+  if (threadIdx.x == 0) p.rho[m] = rho;
+  const float inv = 1.f / (rho + p.eps);
+  using TA = typename ActOf<T>::type;
+  TA* act = reinterpret_cast<TA*>(p.act);
+  for (int k = threadIdx.x; k < p.H; k += kRowThreads) Elt<TA>::store(act, (size_t)m * p.H + k, x[k] * inv);
+}
+
+// a9, second half: c_t = sqrt(r) z_t / (||z_t||_2 + eps); the anchor row of
+// every request takes sqrt(r) C[anchor] instead [FLZ, "The bridge"].
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void bridge_code_kernel(const RowParams p) {
+  __shared__ float red[kRowThreads / 64];
+  const int m = blockIdx.x, b = m / p.W, i = m % p.W;
+  const float sr = sqrtf((float)p.r);
+  using TA = typename ActOf<T>::type;
+  TA* act = reinterpret_cast<TA*>(p.act);
+  if (i == 0) {
+    const T* cb = reinterpret_cast<const T*>(p.codebook) + (size_t)p.anchor[b] * p.r;
+    for (int k = threadIdx.x; k < p.r; k += kRowThreads)
+      Elt<TA>::store(act, (size_t)m * p.r + k, sr * Elt<T>::load(cb, k));
+    return;
+  }
+  const float* z = p.z + (size_t)m * p.r;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < p.r; k += kRowThreads) ss += z[k] * z[k];
+  ss = block_sum<kRowThreads>(ss, red);
+  const float scale = sr / (sqrtf(ss) + p.eps);
+  for (int k = threadIdx.x; k < p.r; k += kRowThreads) Elt<TA>::store(act, (size_t)m * p.r + k, z[k] * scale);
+}
+
+// caller-supplied predecessor codes (fp32) -> GEMM operand type
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void copy_codes_kernel(const RowParams p) {
+  const int m = blockIdx.x;
+  using TA = typename ActOf<T>::type;
+  TA* act = reinterpret_cast<TA*>(p.pred_act);
+  for (int k = threadIdx.x; k < p.r; k += kRowThreads)
+    Elt<TA>::store(act, (size_t)m * p.r + k, p.pred_in[(size_t)m * p.r + k]);
+}
+
+// a2 epilogue for one draft layer [NIF, context K/V; fused context
+// materializer]: k = rope_1d(head_rmsnorm(k_raw, gk), t) stored BF16 (no
+// rounding before the norm); v stored FP16_RNE(BF16(v_raw)).  F32 models
+// store float.  Rows at positions below keep_lo are not stored (chunk
+// truncation); position t goes to ring slot t mod S (t for a full layer).
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void kv_store_kernel(const KvStoreParams p) {
+  extern __shared__ float sm[];   // D/2 (cos, sin) pairs, nkv sums, nkv*D raw keys
+  const int row = blockIdx.x;
+  int b = 0;
+  while (b + 1 < p.n_req && row >= p.row0[b + 1]) ++b;
+  const int64_t t = p.pos0[b] + (row - p.row0[b]);
+  if (t < p.keep_lo[b]) return;
+  const int D = p.D, half = D / 2;
+  float* cs = sm;
+  float* ssum = sm + D;
+  float* kraw = ssum + p.nkv;
+  const float* kr = p.kv + (size_t)row * p.ld + p.k_col;
+  const float* vr = p.kv + (size_t)row * p.ld + p.v_col;
+  for (int j = threadIdx.x; j < half; j += kRowThreads) rope_pair(t, j, D, p.rope_theta, cs[2 * j], cs[2 * j + 1]);
+  for (int e = threadIdx.x; e < p.nkv * D; e += kRowThreads) kraw[e] = kr[e];
+  __syncthreads();
+  // per-head sum of squares in a fixed order (reproducible bits)
+  for (int hh = threadIdx.x; hh < p.nkv; hh += kRowThreads) {
+    float s = 0.f;
+    for (int d = 0; d < D; ++d) s += kraw[hh * D + d] * kraw[hh * D + d];
+    ssum[hh] = s;
+  }
+  __syncthreads();
+  const int64_t slot = ring_slot(t, p.S);
+  const int64_t cap = p.cap[b];
+  const T* gk = reinterpret_cast<const T*>(p.gk);
+  for (int e = threadIdx.x; e < p.nkv * half; e += kRowThreads) {
+    const int hh = e / half, j = e % half;
+    const float inv = rsqrtf(ssum[hh] / D + p.eps);
+    const float a = kraw[hh * D + j] * inv * Elt<T>::load(gk, j);
+    const float c = kraw[hh * D + j + half] * inv * Elt<T>::load(gk, j + half);
+    const float co = cs[2 * j], si = cs[2 * j + 1];
+    const size_t base = ((size_t)hh * cap + slot) * D;
+    if constexpr (Elt<T>::kBytes == 2) {
+      uint16_t* K = reinterpret_cast<uint16_t*>(p.kring[b]);
+      K[base + j] = f32_to_bf16_bits(a * co - c * si);
+      K[base + j + half] = f32_to_bf16_bits(c * co + a * si);
+    } else {
+      float* K = reinterpret_cast<float*>(p.kring[b]);
+      K[base + j] = a * co - c * si;
+      K[base + j + half] = c * co + a * si;
+    }
+  }
+  for (int e = threadIdx.x; e < p.nkv * D; e += kRowThreads) {
+    const int hh = e / D, d = e % D;
+    const size_t idx = ((size_t)hh * cap + slot) * D + d;
+    if constexpr (Elt<T>::kBytes == 2) {
+      reinterpret_cast<uint16_t*>(p.vring[b])[idx] = f32_to_f16_bits(bf16_bits_to_f32(f32_to_bf16_bits(vr[e])));
+    } else {
+      reinterpret_cast<float*>(p.vring[b])[idx] = vr[e];
+    }
+  }
+}
+
+// a3 as evaluated by the attention kernel (same device predicate)
+__global__ void debug_visible_kernel(const VisibleParams p) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= p.B * p.W) return;
+  const int b = m / p.W, i = m % p.W;
+  const int64_t F = p.F[b];
+  const int64_t lo = ctx_row_lo(F, p.S, i);
+  p.lo_hi[2 * m] = lo;
+  p.lo_hi[2 * m + 1] = F;
+  p.first_slot[m] = lo < F ? (int32_t)ring_slot(lo, p.S) : -1;
+  int n = 0;
+  for (int j = 0; j < p.W; ++j) n += block_key_visible(p.S, p.causal, i, j) ? 1 : 0;
+  p.n_block[m] = n;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+#define DSPINE_DISPATCH(dtype, KERNEL, ...)                                               \
+  do {                                                                                    \
+    if ((dtype) == DT_BF16) hipLaunchKernelGGL((KERNEL<bf16_t>), __VA_ARGS__);            \
+    else hipLaunchKernelGGL((KERNEL<float>), __VA_ARGS__);                                \
+  } while (0)
+
+hipError_t launch_embed_norm(const RowParams& p, int dtype, hipStream_t s) {
+  DSPINE_DISPATCH(dtype, embed_norm_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
+  return hipGetLastError();
+}
+hipError_t launch_rmsnorm(const RowParams& p, int dtype, bool f32_output, hipStream_t s) {
+  if (dtype == DT_BF16) {
+    if (f32_output) hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, true>), dim3(p.M), dim3(kRowThreads), 0, s, p);
+    else hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, false>), dim3(p.M), dim3(kRowThreads), 0, s, p);
+  } else {
+    if (f32_output) hipLaunchKernelGGL((rmsnorm_kernel<float, true>), dim3(p.M), dim3(kRowThreads), 0, s, p);
+    else hipLaunchKernelGGL((rmsnorm_kernel<float, false>), dim3(p.M), dim3(kRowThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+hipError_t launch_bridge_read(const RowParams& p, int dtype, hipStream_t s) {
+  DSPINE_DISPATCH(dtype, bridge_read_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
+  return hipGetLastError();
+}
+hipError_t launch_bridge_code(const RowParams& p, int dtype, hipStream_t s) {
+  DSPINE_DISPATCH(dtype, bridge_code_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
+  return hipGetLastError();
+}
+hipError_t launch_copy_codes(const RowParams& p, int dtype, hipStream_t s) {
+  DSPINE_DISPATCH(dtype, copy_codes_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
+  return hipGetLastError();
+}
+hipError_t launch_kv_store(const KvStoreParams& p, int dtype, hipStream_t s) {
+  const size_t smem = (size_t)(p.D + p.nkv + p.nkv * p.D) * sizeof(float);
+  DSPINE_DISPATCH(dtype, kv_store_kernel, dim3(p.rows), dim3(kRowThreads), smem, s, p);
+  return hipGetLastError();
+}
+hipError_t launch_debug_visible(const VisibleParams& p, hipStream_t s) {
+  const int n = p.B * p.W;
+  hipLaunchKernelGGL(debug_visible_kernel, dim3((n + 63) / 64), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace dspine

@@ -1,0 +1,276 @@
+/*
+ * dspine.h -- C ABI of the DSpine draft-block library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes one speculative-decoding draft round on the GPU:
+ *   - dspine_ctx_materialize: fuse committed target features into context
+ *     features and store every draft layer's context K/V in per-request rings;
+ *   - dspine_draft_forward:   one masked-block forward (anchor + masks) over
+ *     B requests, with the DSpine gated predecessor bridge after every layer;
+ *   - dspine_bridge:          the bridge alone on one layer's block states.
+ *
+ * Sources, cited by tag in the comments below:
+ *   [FLZ] "DSpine for Qwen3.8-27B: Causal Features Through Depth" (flozi.net guide)
+ *   [PHY] "DSpine 完全拆解：相邻因果注入如何让并行草稿沿网络深度建立 token 依赖"
+ *         (pinghaoyang.com.cn article)
+ *   [DSP] "DSpark, every bolt and rivet" (lab-artifacts tutorial)
+ *   [NIF] NInfer maintainer notes, "DFlash" (docs/maintainer/dflash.md)
+ *
+ * Conventions for every call:
+ *   - "device" pointers address GPU memory of the current HIP device; "host"
+ *     pointers address CPU memory read during the call only.
+ *   - The caller owns every buffer (weights, rings, features, outputs,
+ *     workspace).  The library never allocates, frees or synchronises; calls
+ *     only enqueue kernels on the given stream and return.
+ *   - Matrices are row-major [out, in] (y = W x).  BF16 tensors are IEEE
+ *     bfloat16 bit patterns; FP16 is IEEE binary16.
+ *   - Return value: DSPINE_OK (0) or a negative DSPINE_E_* code.  Every
+ *     argument check happens before the first launch: on error nothing is
+ *     enqueued and no context frontier changes.  dspine_last_error() gives
+ *     a message for the calling thread's last failure.
+ *   - A kernel fault surfaces as DSPINE_E_HIP on a later call (or on the
+ *     caller's own stream synchronisation).
+ */
+#ifndef DSPINE_H
+#define DSPINE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dspine_stream_t;   /* same object as hipStream_t */
+
+#define DSPINE_MAX_LAYERS 16
+#define DSPINE_MAX_BATCH 8
+#define DSPINE_MIN_WIDTH 2
+#define DSPINE_MAX_WIDTH 16
+
+/* status codes */
+#define DSPINE_OK 0
+#define DSPINE_E_ARG (-1)          /* null pointer, negative size, bad index */
+#define DSPINE_E_UNSUPPORTED (-2)  /* geometry, B or W outside what the kernels implement */
+#define DSPINE_E_WORKSPACE (-3)    /* workspace smaller than dspine_workspace_bytes() */
+#define DSPINE_E_STATE (-4)        /* context state inconsistent with the request */
+#define DSPINE_E_HIP (-5)          /* a HIP runtime call failed */
+
+/* element type of weights, features and the residual stream's inputs */
+#define DSPINE_F32 0
+#define DSPINE_BF16 1
+
+/*
+ * Draft geometry.  [NIF, draft config table]: hidden width, layers, FFN
+ * width, Q/KV heads and head width, norm epsilon, 1-D RoPE theta, per-layer
+ * attention type and window, target feature layers, mask token.  [FLZ, "The
+ * bridge"]: code width r and message width a (r = a = 0: no bridge, which
+ * is plain DFlash).
+ *
+ * Kernel limits (DSPINE_E_UNSUPPORTED otherwise): hidden, ffn, code_dim and
+ * n_q_heads*head_dim multiples of 32 (hidden and ffn also of 64); msg_dim a
+ * multiple of 32; head_dim 64 or 128; n_q_heads/n_kv_heads in {1,2,4,8};
+ * 1 <= n_layers <= DSPINE_MAX_LAYERS; window[l] >= 0 (0 = full attention).
+ */
+typedef struct {
+    int32_t hidden;            /* H */
+    int32_t n_layers;          /* L */
+    int32_t n_q_heads;         /* nq */
+    int32_t n_kv_heads;        /* nkv */
+    int32_t head_dim;          /* D */
+    int32_t ffn;               /* SwiGLU intermediate width */
+    int32_t n_feat_layers;     /* Lf: target layers concatenated into features */
+    int32_t code_dim;          /* r; 0 disables the bridge */
+    int32_t msg_dim;           /* a; 0 iff code_dim == 0 */
+    int32_t vocab;             /* rows of the embedding table and the codebook */
+    int32_t mask_token_id;     /* embedding row used for every mask position */
+    int32_t block_causal;      /* 0: bidirectional block [NIF]; 1: block-causal [PHY, 块因果注意力] */
+    int32_t window[DSPINE_MAX_LAYERS];  /* S_l; 0 = full attention layer */
+    float eps;                 /* RMSNorm epsilon, also the bridge floor */
+    float rope_theta;
+    int32_t dtype;             /* DSPINE_F32 or DSPINE_BF16 */
+} dspine_geometry;
+
+/* Per-layer weights (device, borrowed; element type = geometry.dtype). */
+typedef struct {
+    const void* g_in;          /* [H]    input RMSNorm gain */
+    const void* wq;            /* [nq*D, H] */
+    const void* wk;            /* [nkv*D, H]  used for block and context keys [NIF] */
+    const void* wv;            /* [nkv*D, H]  used for block and context values */
+    const void* gq;            /* [D]    query head-norm gain */
+    const void* gk;            /* [D]    key head-norm gain */
+    const void* wo;            /* [H, nq*D] */
+    const void* g_post;        /* [H]    post-attention RMSNorm gain */
+    const void* w_gate;        /* [ffn, H] */
+    const void* w_up;          /* [ffn, H] */
+    const void* w_down;        /* [H, ffn] */
+    const void* R;             /* [r, H]  bridge read [FLZ]; NULL when r == 0 */
+    const void* W_l;           /* [H, a]  bridge write;     NULL when r == 0 */
+} dspine_layer_weights;
+
+/* All model weights (device, borrowed, element type = geometry.dtype).  They
+ * must stay valid and unchanged while the model handle is used. */
+typedef struct {
+    const void* embed;         /* [vocab, H]  target input embedding */
+    const void* w_feat;        /* [H, Lf*H]   context feature projection, no bias [NIF] */
+    const void* g_ctx;         /* [H]         context_norm gain */
+    const void* g_final;       /* [H]         final RMSNorm gain */
+    const void* codebook;      /* [vocab, r]  token codes C [FLZ]; NULL when r == 0 */
+    const void* bridge_G;      /* [a, r]  receiver gate, shared by layers [FLZ] */
+    const void* bridge_Gp;     /* [a, r]  predecessor gate, shared */
+    const void* bridge_A;      /* [a, r]  predecessor value map, shared */
+    const void* bridge_b;      /* [a]     gate bias, shared */
+    dspine_layer_weights layer[DSPINE_MAX_LAYERS];
+} dspine_weights;
+
+/*
+ * One request's draft context (host struct).  [NIF, ring storage]: a local
+ * layer of window S keeps positions [max(0, F-S), F) in a ring of exactly S
+ * slots, position p in slot p mod S; a full layer keeps [0, F) with
+ * position p at index p (capacity >= every frontier it will reach).
+ *
+ * Ring layout per layer, head-major: K [n_kv_heads][capacity][head_dim] and
+ * V [n_kv_heads][capacity][head_dim].  Element types [NIF, fused context
+ * materializer]: BF16 model -> K bfloat16, V binary16 (FP16_RNE(BF16(v)));
+ * F32 model -> both float32.  Only live slots are ever read.
+ *
+ * frontier F: positions [0, F) are processed and materialized; the anchor
+ * token sits at position F [NIF, frontier].  dspine_ctx_materialize
+ * advances it; nothing else changes it.
+ */
+typedef struct {
+    void* k_ring[DSPINE_MAX_LAYERS];
+    void* v_ring[DSPINE_MAX_LAYERS];
+    int64_t capacity[DSPINE_MAX_LAYERS];
+    int64_t frontier;
+} dspine_ctx;
+
+typedef struct dspine_model dspine_model;
+
+/* Checks the geometry and weight pointers and makes a host-side handle that
+ * borrows them.  Errors: E_ARG (null), E_UNSUPPORTED (limits above). */
+int dspine_model_create(const dspine_geometry* geom, const dspine_weights* weights,
+                        dspine_model** out);
+void dspine_model_destroy(dspine_model* model);
+
+/* Bytes of one ring (K or V, same size) of `layer` for one request with the
+ * given capacity (must be window[layer] for a local layer).  0 on error. */
+size_t dspine_ring_bytes(const dspine_model* model, int layer, int64_t capacity);
+
+/* Workspace bytes a call needs for up to max_batch requests of width up to
+ * max_width and up to max_rows materialized positions per call (summed over
+ * the call's requests, after truncation to the live windows).  The buffer
+ * must be zero-filled once before its first use; the library leaves its
+ * internal counters at zero when each call's work completes.  Calls that
+ * share a workspace must be ordered on one stream.  0 on error. */
+size_t dspine_workspace_bytes(const dspine_model* model, int max_batch, int max_width,
+                              int64_t max_rows);
+
+/*
+ * a1-a3: materialize committed target features into the draft context.
+ * [NIF, context conditioning / context K/V / fused context materializer]:
+ *   c_t = plain_rmsnorm(W_feat s_t, g_ctx);
+ *   per layer: k = rope_1d(head_rmsnorm(W_k c_t, gk), t) stored BF16,
+ *              v = W_v c_t stored FP16_RNE(BF16(v)).
+ * A chunk longer than a local ring stores only its final live window; the
+ * frontier still advances by the whole chunk.
+ *
+ *   n_req          number of requests (1..DSPINE_MAX_BATCH)
+ *   ctx            host [n_req]; ctx[b].frontier += n_tok[b] on success
+ *   feats          host [n_req] of device pointers, each [n_tok[b], Lf*H]
+ *                  in the model dtype (positions F..F+n-1 in order)
+ *   n_tok          host [n_req], each >= 0
+ * Errors: E_ARG, E_STATE (local capacity != window, full capacity < F+n),
+ * E_WORKSPACE (rows after truncation exceed the workspace's max_rows).
+ */
+int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx,
+                           const void* const* feats, const int64_t* n_tok,
+                           void* workspace, size_t workspace_bytes, dspine_stream_t stream);
+
+/*
+ * a4-a12: one masked-block draft forward for B requests of width W.
+ * [NIF, draft input]: row i of request b is the embedding of the anchor
+ * (i = 0) or of the mask token (i > 0), at position F_b + i.
+ * [NIF, layer equations] per layer, then the bridge [FLZ, "The bridge"]
+ * after every layer when code_dim > 0, then the final plain RMSNorm.
+ * Attention [NIF, draft attention]: key at position p is visible to the
+ * row at q iff |p - q| < S (local) plus, with block_causal, block key j <=
+ * row i; context keys are the ring positions [max(0, q-S+1), F).
+ *
+ *   B, W           1..8 and 2..16
+ *   ctx            host [B]; read only (frontiers and rings)
+ *   anchor_ids     host [B], each in [0, vocab)
+ *   out            device float32 [B, W, H]: final-normed hidden states
+ * Errors: E_ARG, E_UNSUPPORTED, E_STATE (full-layer capacity < F + W is
+ * allowed; a frontier < 0 is not), E_WORKSPACE.
+ */
+int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_ctx* ctx,
+                         const int32_t* anchor_ids, float* out,
+                         void* workspace, size_t workspace_bytes, dspine_stream_t stream);
+
+/*
+ * a9-a11 alone on one layer's block states.  [FLZ, "The bridge"]:
+ *   rho_t = rms(x_t), z_t = R_l x_t / (rho_t + eps),
+ *   c_t = sqrt(r) z_t / (||z_t|| + eps), anchor row: c_0 = sqrt(r) C[a_b];
+ *   x_t += rho_t W_l (sigmoid(G c_t + G_p p_t + b) * (A p_t)) for t >= 1,
+ * with predecessor code p_t = c_{t-1}, or pred_codes[b][t] when given (the
+ * hook for redoing the last write with a chosen predecessor token [PHY,
+ * last-write refinement]).  Row 0 is never written.
+ *
+ *   layer          0..L-1 (selects R_l and W_l)
+ *   x              device float32 [B, W, H], updated in place
+ *   anchor_ids     host [B]
+ *   pred_codes     device float32 [B, W, r] or NULL; entry t = 0 unused
+ * Errors: E_ARG, E_UNSUPPORTED (no bridge in the geometry), E_WORKSPACE.
+ */
+int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x,
+                  const int32_t* anchor_ids, const float* pred_codes,
+                  void* workspace, size_t workspace_bytes, dspine_stream_t stream);
+
+/*
+ * a3 as the attention kernel evaluates it, for exact comparison: for every
+ * block row, the half-open interval of visible context positions, the ring
+ * slot of its first position, and the number of visible block keys.  The
+ * values come from the same device predicate the attention kernel uses.
+ *
+ *   lo_hi          device int64 [B, W, 2]
+ *   first_slot     device int32 [B, W]   (-1 for an empty interval)
+ *   n_block        device int32 [B, W]
+ */
+int dspine_debug_visible(const dspine_model* model, int layer, int B, int W,
+                         const dspine_ctx* ctx, int64_t* lo_hi, int32_t* first_slot,
+                         int32_t* n_block, dspine_stream_t stream);
+
+/*
+ * Kernel timing (tracing).  While enabled, the calls record a pair of HIP
+ * events on their stream around every launch of the selected kernel classes;
+ * dspine_profile_read waits for the recorded events of one class, returns
+ * their summed duration and count, and forgets them.  Intended for
+ * measurement runs: the event records add a few microseconds per launch.
+ */
+#define DSPINE_PROF_GEMM_QKV 0      /* a5 q|k|v projection */
+#define DSPINE_PROF_ATTENTION 1     /* a6 */
+#define DSPINE_PROF_GEMM_O 2        /* a7 output projection + residual */
+#define DSPINE_PROF_GEMM_GATE_UP 3  /* a8 gate/up projection + SwiGLU */
+#define DSPINE_PROF_GEMM_DOWN 4     /* a8 down projection + residual */
+#define DSPINE_PROF_BRIDGE 5        /* a9-a11, all kernels of one bridge */
+#define DSPINE_PROF_NORM 6          /* input/post/final norms and the embedding gather */
+#define DSPINE_PROF_CTX_GEMM 7      /* a1-a2 feature and K/V projections */
+#define DSPINE_PROF_CTX_STORE 8     /* a1 norm, a2 head norm + RoPE + ring scatter */
+#define DSPINE_PROF_KINDS 9
+
+/* kind_mask: bit k enables class k; 0 disables recording.  Process-wide. */
+int dspine_profile_enable(uint32_t kind_mask);
+/* Waits for the recorded events of class `kind` (host-blocking), writes the
+ * summed milliseconds and the number of launches, and clears the class. */
+int dspine_profile_read(int kind, double* total_ms, int64_t* launches);
+
+/* Message for the calling thread's last nonzero status ("" if none). */
+const char* dspine_last_error(void);
+
+/* Library version string. */
+const char* dspine_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPINE_H */

@@ -27,7 +27,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-CHUNK = 1 << 22
+CHUNK = 1 << 20
 
 
 # ---------------------------------------------------------------------------
@@ -152,32 +152,38 @@ def _pool() -> _cf.ThreadPoolExecutor:
 
 
 def normal(seed: int, index: int, shape, scale: float = 1.0, shift: float = 0.0,
-           out_dtype: str = "bf16") -> np.ndarray:
-    """N(shift, scale^2) values of ``shape``; rounded once to ``out_dtype``."""
+           out_dtype: str = "bf16", rows: Optional[tuple] = None) -> np.ndarray:
+    """N(shift, scale^2) values of ``shape``; rounded once to ``out_dtype``.
+
+    ``rows=(r0, r1)`` returns only rows r0..r1-1 of the leading axis, with
+    exactly the values the whole tensor has there."""
     n = int(np.prod(shape)) if len(shape) else 1
-    if out_dtype == "bf16":
-        out = np.empty(n, dtype=np.uint16)
-    else:
-        out = np.empty(n, dtype=np.float32)
-    nchunks = (n + CHUNK - 1) // CHUNK
+    row_elems = int(np.prod(shape[1:])) if len(shape) > 1 else 1
+    r0, r1 = rows if rows is not None else (0, shape[0] if len(shape) else 1)
+    e0, e1 = r0 * row_elems, r1 * row_elems
+    m = e1 - e0
+    out = np.empty(m, dtype=np.uint16 if out_dtype == "bf16" else np.float32)
+    c_first, c_last = e0 // CHUNK, (e1 - 1) // CHUNK if m > 0 else -1
 
     def work(c):
-        lo = c * CHUNK
-        hi = min(n, lo + CHUNK)
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
         g = np.random.default_rng([seed, index, c])
         v = g.standard_normal(hi - lo, dtype=np.float32)
         if scale != 1.0:
             v *= np.float32(scale)
         if shift != 0.0:
             v += np.float32(shift)
-        out[lo:hi] = f32_to_bf16_bits(v) if out_dtype == "bf16" else v
+        a, b = max(lo, e0), min(hi, e1)
+        v = v[a - lo:b - lo]
+        out[a - e0:b - e0] = f32_to_bf16_bits(v) if out_dtype == "bf16" else v
 
-    if nchunks <= 1:
-        for c in range(nchunks):
+    chunks = range(c_first, c_last + 1)
+    if len(chunks) <= 1:
+        for c in chunks:
             work(c)
     else:
-        list(_pool().map(work, range(nchunks)))
-    return out.reshape(shape)
+        list(_pool().map(work, chunks))
+    return out.reshape(((r1 - r0),) + tuple(shape[1:]) if len(shape) else ())
 
 
 def unit_rows(seed: int, index: int, rows: int, cols: int, out_dtype: str) -> np.ndarray:
@@ -256,11 +262,17 @@ FEATURE_INDEX_BASE = 10_000
 ANCHOR_INDEX = 20_000
 
 
-def make_features(g: Geometry, seed: int, request: int, n_tok: int,
-                  stream: int = 0) -> np.ndarray:
-    """Target residual features ``[n_tok, Lf*H]`` ~ N(0,1) for one request."""
-    return normal(seed, FEATURE_INDEX_BASE + 97 * stream + request,
-                  (n_tok, g.n_feat_layers * g.hidden), 1.0, 0.0, g.dtype)
+# Every request has one feature sequence of FEATURE_ROWS positions; the
+# features of positions [p0, p1) are rows p0..p1-1 of it, whatever chunking
+# a test or the bench materializes them in.
+FEATURE_ROWS = 1 << 20
+
+
+def make_features(g: Geometry, seed: int, request: int, n_tok: int, start: int = 0) -> np.ndarray:
+    """Target residual features ~ N(0,1) of positions [start, start + n_tok)
+    of one request: ``[n_tok, Lf*H]``."""
+    return normal(seed, FEATURE_INDEX_BASE + request, (FEATURE_ROWS, g.n_feat_layers * g.hidden),
+                  1.0, 0.0, g.dtype, rows=(start, start + n_tok))
 
 
 def make_anchor_ids(g: Geometry, seed: int, B: int, stream: int = 0) -> np.ndarray:
