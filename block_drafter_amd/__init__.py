@@ -56,6 +56,9 @@ class LayerWeights_c(ctypes.Structure):
 
 _GLOBAL_FIELDS = ["embed", "w_feat", "g_ctx", "g_final", "codebook", "bridge_G", "bridge_Gp",
                   "bridge_A", "bridge_b"]
+# matrices the library streams from its packed copy
+_PROJECTIONS = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "R", "W_l", "w_feat",
+                "bridge_G", "bridge_Gp", "bridge_A"}
 
 
 class Weights_c(ctypes.Structure):
@@ -72,6 +75,9 @@ EXPORTS = {
     "dspine_model_create": (ctypes.c_int, [ctypes.POINTER(Geometry_c), ctypes.POINTER(Weights_c),
                                            ctypes.POINTER(ctypes.c_void_p)]),
     "dspine_model_destroy": (None, [ctypes.c_void_p]),
+    "dspine_packed_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "dspine_pack_weights": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]),
     "dspine_ring_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64]),
     "dspine_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int64]),
@@ -152,7 +158,7 @@ def to_device(a: np.ndarray, device="cuda"):
 class Model:
     """A model handle over device weights (borrowed by the library)."""
 
-    def __init__(self, geom, weights: Dict[str, "torch.Tensor"]):
+    def __init__(self, geom, weights: Dict[str, "torch.Tensor"], drop_row_major: bool = True):
         self.geom = geom
         self.weights = weights               # keeps the tensors alive
         self._gs = geometry_struct(geom)
@@ -169,7 +175,18 @@ class Model:
         _check(lib().dspine_model_create(ctypes.byref(self._gs), ctypes.byref(ws), ctypes.byref(h)))
         self.handle = h
         self._workspace = None
-        self._ws_key = None
+        # projections in fragment order (the library's streaming layout); the
+        # row-major matrices are dropped once the packing kernels have run
+        torch = _torch()
+        nbytes = lib().dspine_packed_bytes(self.handle)
+        self.packed = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        _check(lib().dspine_pack_weights(self.handle, self.packed.data_ptr(), nbytes,
+                                         torch.cuda.current_stream().cuda_stream))
+        if drop_row_major:
+            torch.cuda.current_stream().synchronize()
+            for name in list(self.weights):
+                if name.split(".")[-1] in _PROJECTIONS:
+                    del self.weights[name]
 
     @classmethod
     def from_numpy(cls, geom, wts: Dict[str, np.ndarray], device="cuda"):

@@ -253,20 +253,18 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
   float* base = p.partials + (size_t)((b * p.nq + h) * p.nsplit) * PSZ;
   float* mine = base + (size_t)split * PSZ;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(mine + (dt * 64 + lane) * 4) = o[dt];
+  for (int dt = 0; dt < D / 16; ++dt) store_coherent(mine + (dt * 64 + lane) * 4, o[dt]);
   if (lane < 16) {
-    mine[64 * (D / 4) + lane] = m_run;
-    mine[64 * (D / 4) + 16 + lane] = lrow;
+    store_coherent(mine + 64 * (D / 4) + lane, m_run);
+    store_coherent(mine + 64 * (D / 4) + 16 + lane, lrow);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  drain_own_stores();
   uint32_t old = 0;
-  if (lane == 0)
-    old = __hip_atomic_fetch_add(p.counters + b * p.nq + h, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) old = count_arrival(p.counters + b * p.nq + h);
   old = __shfl(old, 0, 64);
   if ((int)old != p.nsplit - 1) return;
-  acquire_partials();
   float mstar = -INFINITY;
-  for (int sp = 0; sp < p.nsplit; ++sp) mstar = fmaxf(mstar, base[(size_t)sp * PSZ + 64 * (D / 4) + qrow]);
+  for (int sp = 0; sp < p.nsplit; ++sp) mstar = fmaxf(mstar, load_coherent(base + (size_t)sp * PSZ + 64 * (D / 4) + qrow));
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
@@ -274,13 +272,12 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
   if (mstar != -INFINITY) {
     for (int sp = 0; sp < p.nsplit; ++sp) {
       const float* part = base + (size_t)sp * PSZ;
-      const float ms = part[64 * (D / 4) + qrow];
+      const float ms = load_coherent(part + 64 * (D / 4) + qrow);
       if (ms == -INFINITY) continue;
       const float wgt = exp2f(ms - mstar);
-      L += wgt * part[64 * (D / 4) + 16 + qrow];
+      L += wgt * load_coherent(part + 64 * (D / 4) + 16 + qrow);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        acc[dt] += wgt * *reinterpret_cast<const f32x4*>(part + (dt * 64 + lane) * 4);
+      for (int dt = 0; dt < D / 16; ++dt) acc[dt] += wgt * load_coherent4(part + (dt * 64 + lane) * 4);
     }
   }
   if (L > 0.f) write_row(acc, 1.f / L);

@@ -15,7 +15,9 @@
 
 struct dspine_model {
   dspine_geometry g;
-  dspine_weights w;
+  dspine_weights w;    // as given: projection matrices row-major [out, in]
+  dspine_weights pw;   // the same with projection matrices in fragment order
+  bool packed = false;
 };
 
 using namespace dspine;
@@ -262,6 +264,41 @@ int check_ctx_rings(const dspine_model& m, const dspine_ctx& c, int b, int64_t n
   return DSPINE_OK;
 }
 
+// Projection matrices of a model (the operands streamed by the GEMMs), each
+// with its rows and columns; `global` / `layer` select the pointer field.
+struct Proj {
+  const void* dspine_weights::*global;
+  const void* dspine_layer_weights::*layer;
+  int rows, cols;
+};
+std::vector<Proj> projections(const dspine_geometry& g) {
+  const int H = g.hidden, qd = g.n_q_heads * g.head_dim, kvd = g.n_kv_heads * g.head_dim;
+  std::vector<Proj> v = {
+      {nullptr, &dspine_layer_weights::wq, qd, H},      {nullptr, &dspine_layer_weights::wk, kvd, H},
+      {nullptr, &dspine_layer_weights::wv, kvd, H},     {nullptr, &dspine_layer_weights::wo, H, qd},
+      {nullptr, &dspine_layer_weights::w_gate, g.ffn, H}, {nullptr, &dspine_layer_weights::w_up, g.ffn, H},
+      {nullptr, &dspine_layer_weights::w_down, H, g.ffn}};
+  if (g.code_dim > 0) {
+    v.push_back({nullptr, &dspine_layer_weights::R, g.code_dim, H});
+    v.push_back({nullptr, &dspine_layer_weights::W_l, H, g.msg_dim});
+  }
+  v.push_back({&dspine_weights::w_feat, nullptr, H, g.n_feat_layers * H});
+  if (g.code_dim > 0) {
+    v.push_back({&dspine_weights::bridge_G, nullptr, g.msg_dim, g.code_dim});
+    v.push_back({&dspine_weights::bridge_Gp, nullptr, g.msg_dim, g.code_dim});
+    v.push_back({&dspine_weights::bridge_A, nullptr, g.msg_dim, g.code_dim});
+  }
+  return v;
+}
+size_t packed_bytes(const dspine_geometry& g) {
+  size_t total = 0;
+  for (const Proj& pr : projections(g)) {
+    const size_t one = align256((size_t)pr.rows * pr.cols * elt_bytes(g));
+    total += pr.layer ? one * g.n_layers : one;
+  }
+  return total;
+}
+
 // streamed GEMM helpers -------------------------------------------------------
 GemmParams gemm_base(const Plan& P, char* ws, int K, int M) {
   GemmParams gp;
@@ -344,6 +381,42 @@ int dspine_model_create(const dspine_geometry* geom, const dspine_weights* weigh
 
 void dspine_model_destroy(dspine_model* model) { delete model; }
 
+size_t dspine_packed_bytes(const dspine_model* model) {
+  if (!model) {
+    fail(DSPINE_E_ARG, "packed_bytes: NULL model");
+    return 0;
+  }
+  return packed_bytes(model->g);
+}
+
+int dspine_pack_weights(dspine_model* model, void* dst, size_t dst_bytes, dspine_stream_t stream) {
+  if (!model || !dst) return fail(DSPINE_E_ARG, "pack_weights: NULL argument");
+  if (((uintptr_t)dst & 255u) != 0) return fail(DSPINE_E_ARG, "pack_weights: dst not 256-byte aligned");
+  const size_t need = packed_bytes(model->g);
+  if (dst_bytes < need) return fail(DSPINE_E_WORKSPACE, "pack_weights: %zu bytes < %zu needed", dst_bytes, need);
+  const dspine_geometry& g = model->g;
+  dspine_weights pw = model->w;
+  char* out = static_cast<char*>(dst);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (const Proj& pr : projections(g)) {
+    const size_t one = align256((size_t)pr.rows * pr.cols * elt_bytes(g));
+    if (pr.layer) {
+      for (int l = 0; l < g.n_layers; ++l) {
+        HIP_TRY(launch_pack(model->w.layer[l].*pr.layer, out, pr.rows, pr.cols, g.dtype, s));
+        pw.layer[l].*pr.layer = out;
+        out += one;
+      }
+    } else {
+      HIP_TRY(launch_pack(model->w.*pr.global, out, pr.rows, pr.cols, g.dtype, s));
+      pw.*pr.global = out;
+      out += one;
+    }
+  }
+  model->pw = pw;
+  model->packed = true;
+  return ok();
+}
+
 size_t dspine_ring_bytes(const dspine_model* model, int layer, int64_t capacity) {
   if (!model || layer < 0 || layer >= model->g.n_layers || capacity < 0) {
     fail(DSPINE_E_ARG, "ring_bytes: bad argument");
@@ -376,6 +449,7 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
   if (n_req < 1 || n_req > DSPINE_MAX_BATCH) return fail(DSPINE_E_UNSUPPORTED, "materialize: n_req %d", n_req);
   const dspine_geometry& g = model->g;
   const dspine_weights& wt = model->w;
+  const dspine_weights& pw = model->pw;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   const int L = g.n_layers, H = g.hidden, kvd = g.n_kv_heads * g.head_dim;
 
@@ -399,6 +473,7 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
     const int64_t cap_rows = rows_capacity(g, workspace_bytes);
     if (cap_rows < 1)
       return fail(DSPINE_E_WORKSPACE, "materialize: workspace of %zu bytes holds no row block", workspace_bytes);
+    if (!model->packed) return fail(DSPINE_E_STATE, "weights not packed: call dspine_pack_weights first");
     char* ws = static_cast<char*>(workspace);
     const int cus = num_cus();
     const int64_t blk_rows = std::min<int64_t>(cap_rows, total_rows);
@@ -441,7 +516,7 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
       if (tile) {
         TileGemmParams tp;
         memset(&tp, 0, sizeof tp);
-        tp.seg_ptr[0] = wt.w_feat;
+        tp.seg_ptr[0] = pw.w_feat;
         tp.seg_rows0[0] = 0;
         tp.seg_rows0[1] = H;
         tp.nseg = 1;
@@ -466,7 +541,7 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
         for (int64_t r0 = 0; r0 < nrows; r0 += kMaxRows) {
           const int mr = (int)std::min<int64_t>(kMaxRows, nrows - r0);
           GemmParams gp = gemm_base(P, ws, g.n_feat_layers * H, mr);
-          set_segments(gp, {{wt.w_feat, H}});
+          set_segments(gp, {{pw.w_feat, H}});
           gp.pro = PRO_GATHER;
           gp.a_bf16 = 1;                    // target features are bf16 inputs
           gp.lda = g.n_feat_layers * H;
@@ -507,8 +582,8 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
         TileGemmParams tp;
         memset(&tp, 0, sizeof tp);
         for (int l = 0; l < L; ++l) {
-          tp.seg_ptr[2 * l] = wt.layer[l].wk;
-          tp.seg_ptr[2 * l + 1] = wt.layer[l].wv;
+          tp.seg_ptr[2 * l] = pw.layer[l].wk;
+          tp.seg_ptr[2 * l + 1] = pw.layer[l].wv;
           tp.seg_rows0[2 * l] = 2 * l * kvd;
           tp.seg_rows0[2 * l + 1] = (2 * l + 1) * kvd;
         }
@@ -530,10 +605,10 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
           GemmParams gp = gemm_base(P, ws, H, mr);
           int blk = 0;
           for (int l = 0; l < L; ++l) {
-            gp.seg_ptr[2 * l] = wt.layer[l].wk;
+            gp.seg_ptr[2 * l] = pw.layer[l].wk;
             gp.seg_blk0[2 * l] = blk;
             blk += kvd / 16;
-            gp.seg_ptr[2 * l + 1] = wt.layer[l].wv;
+            gp.seg_ptr[2 * l + 1] = pw.layer[l].wv;
             gp.seg_blk0[2 * l + 1] = blk;
             blk += kvd / 16;
           }
@@ -612,7 +687,7 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const i
   HIP_TRY(launch_bridge_read(rp, g.dtype, stream));                 // rho, x/(rho+eps)
 
   GemmParams gp = gemm_base(P, ws, H, M);                             // z = R (x/(rho+eps))
-  set_segments(gp, {{wt.layer[layer].R, r}});
+  set_segments(gp, {{m.pw.layer[layer].R, r}});
   gp.pro = PRO_COPY;
   gp.a = act_h;
   gp.lda = H;
@@ -634,7 +709,7 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const i
   HIP_TRY(launch_bridge_code(cp, g.dtype, stream));                   // c (anchor: sqrt(r) C[a])
 
   gp = gemm_base(P, ws, r, M);                                         // [G; G_p; A] c, one GEMM
-  set_segments(gp, {{wt.bridge_G, a}, {wt.bridge_Gp, a}, {wt.bridge_A, a}});
+  set_segments(gp, {{m.pw.bridge_G, a}, {m.pw.bridge_Gp, a}, {m.pw.bridge_A, a}});
   gp.pro = PRO_COPY;
   gp.a = act_r;
   gp.lda = r;
@@ -654,7 +729,7 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const i
     op.pred_act = ws + P.act_r2;
     HIP_TRY(launch_copy_codes(op, g.dtype, stream));
     gp = gemm_base(P, ws, r, M);
-    set_segments(gp, {{wt.bridge_G, a}, {wt.bridge_Gp, a}, {wt.bridge_A, a}});
+    set_segments(gp, {{m.pw.bridge_G, a}, {m.pw.bridge_Gp, a}, {m.pw.bridge_A, a}});
     gp.pro = PRO_COPY;
     gp.a = ws + P.act_r2;
     gp.lda = r;
@@ -667,7 +742,7 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const i
   }
 
   gp = gemm_base(P, ws, a, M);                                         // x += rho W_l (g * m)
-  set_segments(gp, {{wt.layer[layer].W_l, H}});
+  set_segments(gp, {{m.pw.layer[layer].W_l, H}});
   gp.pro = PRO_BRIDGE_MSG;
   gp.P = Pb;
   gp.Ppred = Ppred;
@@ -697,6 +772,11 @@ int check_call(const dspine_model* model, int B, int W, const int32_t* anchor_id
   if (ws_bytes < *need) return fail(DSPINE_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, *need);
   return DSPINE_OK;
 }
+// last check before the first launch of a call
+int check_packed(const dspine_model* model) {
+  if (!model->packed) return fail(DSPINE_E_STATE, "weights not packed: call dspine_pack_weights first");
+  return DSPINE_OK;
+}
 }  // namespace
 
 int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x, const int32_t* anchor_ids,
@@ -708,6 +788,7 @@ int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x, 
   if (layer < 0 || layer >= model->g.n_layers) return fail(DSPINE_E_ARG, "bridge: layer %d", layer);
   if (!x || !aligned16(x)) return fail(DSPINE_E_ARG, "bridge: x NULL or unaligned");
   if (pred_codes && !aligned16(pred_codes)) return fail(DSPINE_E_ARG, "bridge: pred_codes unaligned");
+  if ((rc = check_packed(model))) return rc;
   const Plan P = make_plan(model->g, (int64_t)B * W, 0);
   rc = run_bridge(*model, layer, B, W, x, anchor_ids, pred_codes, static_cast<char*>(workspace), P, num_cus(),
                   reinterpret_cast<hipStream_t>(stream));
@@ -726,6 +807,7 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
   if (!out || !aligned16(out)) return fail(DSPINE_E_ARG, "forward: out NULL or unaligned");
   for (int b = 0; b < B; ++b)
     if ((rc = check_ctx_rings(*model, ctx[b], b, ctx[b].frontier))) return rc;
+  if ((rc = check_packed(model))) return rc;
 
   const dspine_geometry& g = model->g;
   const dspine_weights& wt = model->w;
@@ -768,6 +850,7 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
 
   for (int l = 0; l < g.n_layers; ++l) {
     const dspine_layer_weights& Lw = wt.layer[l];
+    const dspine_layer_weights& Pw = model->pw.layer[l];
     if (l > 0) {
       RowParams np;
       memset(&np, 0, sizeof np);
@@ -782,7 +865,7 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
     }
     // a5: q | k | v projections of n
     GemmParams gp = gemm_base(P, ws, H, M);
-    set_segments(gp, {{Lw.wq, qd}, {Lw.wk, kvd}, {Lw.wv, kvd}});
+    set_segments(gp, {{Pw.wq, qd}, {Pw.wk, kvd}, {Pw.wv, kvd}});
     gp.pro = PRO_COPY;
     gp.a = act_h;
     gp.lda = H;
@@ -838,7 +921,7 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
 
     // a7: y = x + W_o a ; m = norm_post(y)
     gp = gemm_base(P, ws, qd, M);
-    set_segments(gp, {{Lw.wo, H}});
+    set_segments(gp, {{Pw.wo, H}});
     gp.pro = PRO_COPY;
     gp.a = act_q;
     gp.lda = qd;
@@ -864,8 +947,8 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
 
     // a8: x = y + W_down(SiLU(W_gate m) * W_up m)
     gp = gemm_base(P, ws, H, M);
-    gp.seg_ptr[0] = Lw.w_gate;
-    gp.seg_ptr[1] = Lw.w_up;
+    gp.seg_ptr[0] = Pw.w_gate;
+    gp.seg_ptr[1] = Pw.w_up;
     gp.nseg = 2;
     gp.interleave = 1;
     gp.nblk = 2 * (g.ffn / 16);
@@ -880,7 +963,7 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
     }
     gp = gemm_base(P, ws, g.ffn, M);
-    set_segments(gp, {{Lw.w_down, H}});
+    set_segments(gp, {{Pw.w_down, H}});
     gp.pro = PRO_COPY;
     gp.a = act_f;
     gp.lda = g.ffn;

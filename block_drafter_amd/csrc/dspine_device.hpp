@@ -71,6 +71,18 @@ template <> struct Elt<bf16_t> {
   }
 };
 
+// Global-address-space view of a pointer.  Loads through it are global_load
+// (vector-memory counter only); loads through a generic pointer become
+// flat_load, which also counts on the LDS counter, so any later LDS wait
+// would drain every in-flight global load with it.
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ gptr<T> as_global(const T* p) {
+  return (gptr<T>)(p);
+}
+__device__ __forceinline__ u32x4 gload16(gptr<void> p) { return *(gptr<u32x4>)(p); }
+
 // ---------------------------------------------------------------------------
 // MFMA fragments: 8 consecutive K elements of one row, per lane.
 // ---------------------------------------------------------------------------
@@ -78,6 +90,7 @@ template <typename T> struct Frag;
 template <> struct Frag<bf16_t> {
   u32x4 v;  // 8 bf16
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void gload(gptr<bf16_t> p) { v = gload16((gptr<void>)p); }
   __device__ __forceinline__ void zero() { v = u32x4{0, 0, 0, 0}; }
 };
 template <> struct Frag<float> {
@@ -85,6 +98,10 @@ template <> struct Frag<float> {
   __device__ __forceinline__ void load(const float* p) {
     v[0] = reinterpret_cast<const u32x4*>(p)[0];
     v[1] = reinterpret_cast<const u32x4*>(p)[1];
+  }
+  __device__ __forceinline__ void gload(gptr<float> p) {
+    v[0] = gload16((gptr<void>)p);
+    v[1] = gload16((gptr<void>)(p + 4));
   }
   __device__ __forceinline__ void zero() { v[0] = u32x4{0, 0, 0, 0}; v[1] = v[0]; }
 };
@@ -177,18 +194,47 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // ---------------------------------------------------------------------------
-// memory ordering for last-arriver reductions across workgroups
+// Cross-workgroup handoff of partial results (last arriver finishes).
+//
+// Each XCD has its own L2, so a plain store from one workgroup need not be
+// visible to a workgroup on another XCD.  An agent-scope release/acquire
+// fence pair would write back and invalidate a whole L2 per handoff, which
+// stalls every wave of that XCD.  Instead the partials travel with
+// agent-scope relaxed atomic stores and loads (global_store/global_load with
+// the sc1 bit: written through to, and read from, the device coherence
+// point), the writer waits until its own stores have completed before it
+// counts its arrival, and the counter is an agent-scope atomic.
 // ---------------------------------------------------------------------------
-// Publish this workgroup's partial results (device scope), then count one
-// arrival; returns the previous count.  Called by one thread after a
-// __syncthreads() that follows the partial stores.
-__device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_coherent(float* p, const f32x4& v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  const uint64_t a = ((uint64_t)__float_as_uint(v[1]) << 32) | __float_as_uint(v[0]);
+  const uint64_t b = ((uint64_t)__float_as_uint(v[3]) << 32) | __float_as_uint(v[2]);
+  __hip_atomic_store(q, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Make other workgroups' published partials visible to this thread.
-__device__ __forceinline__ void acquire_partials() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_coherent4(const float* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+               __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed (its
+// write-through stores included).  The empty asm keeps the compiler from
+// moving memory operations across the wait.
+__device__ __forceinline__ void drain_own_stores() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ uint32_t count_arrival(uint32_t* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void reset_counter(uint32_t* counter) {
   __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -165,4 +165,7 @@ struct VisibleParams {
 };
 hipError_t launch_debug_visible(const VisibleParams& p, hipStream_t s);
 
+// projection matrix [rows, cols] row-major -> fragment order (see pack_kernel)
+hipError_t launch_pack(const void* src, void* dst, int rows, int cols, int dtype, hipStream_t s);
+
 }  // namespace dspine

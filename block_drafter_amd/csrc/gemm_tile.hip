@@ -72,11 +72,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(const TileGemmP
       const int col = (c % (BK / 8)) * 8;
       ra[q] = arow[q] ? *reinterpret_cast<const u32x4*>(arow[q] + k0 + col) : u32x4{0, 0, 0, 0};
     }
+    // weights are fragment-ordered: block i (16 rows), 32-K step ks holds 64
+    // lane fragments (row i*16 + l%16, K 8*(l/16)..+8) in 1 KB
 #pragma unroll
     for (int q = 0; q < BCH; ++q) {
       const int c = tid + q * NT;
-      const int row = c / (BK / 8), col = (c % (BK / 8)) * 8;
-      rb[q] = *reinterpret_cast<const u32x4*>(wbase + (size_t)row * p.K + k0 + col);
+      const int blk = c / 128, sub = (c / 64) % 2, l = c % 64;
+      rb[q] = *reinterpret_cast<const u32x4*>(wbase + (size_t)blk * 16 * p.K + (size_t)(k0 / 32 + sub) * 512 + l * 8);
     }
   };
   auto store_stage = [&](int buf) {
@@ -88,7 +90,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(const TileGemmP
 #pragma unroll
     for (int q = 0; q < BCH; ++q) {
       const int c = tid + q * NT;
-      *reinterpret_cast<u32x4*>(&sB[buf][(c / (BK / 8)) * LDK + (c % (BK / 8)) * 8]) =
+      const int blk = c / 128, sub = (c / 64) % 2, l = c % 64;
+      *reinterpret_cast<u32x4*>(&sB[buf][(blk * 16 + (l & 15)) * LDK + sub * 32 + 8 * (l >> 4)]) =
           F16 ? bf16x8_to_f16x8(rb[q]) : rb[q];
     }
   };

@@ -1,6 +1,8 @@
 // Row-wise kernels: input gather + norms (a4, a5 head, a7 norm, a12), the
 // bridge's read and code steps (a9), and the context K/V store epilogue (a2).
 // One workgroup per row; statistics in fp32.
+#include <algorithm>
+
 #include "dspine_device.hpp"
 #include "dspine_internal.hpp"
 
@@ -179,6 +181,27 @@ __global__ __launch_bounds__(kRowThreads) void kv_store_kernel(const KvStorePara
   }
 }
 
+// Fragment order of a projection matrix W [R, K] (R % 16 == 0, K % 32 == 0):
+// block b (rows 16b..16b+15) keeps its place; inside it, 32-wide K step ks
+// holds 64 lane fragments, lane l = row 16b + l%16, columns ks*32 + 8*(l/16)
+// .. +8, at element offset (b*(K/32) + ks)*512 + 8*l.  This is the order in
+// which a wave's MFMA fragments are loaded, so each load reads 1 KB
+// (bf16; 2 KB for float) of consecutive memory.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_kernel(const T* src, T* dst, int R, int K) {
+  const size_t nfrag = (size_t)(R / 16) * (K / 32) * 64;
+  for (size_t f = blockIdx.x * (size_t)blockDim.x + threadIdx.x; f < nfrag; f += (size_t)gridDim.x * blockDim.x) {
+    const size_t blk = f / 64;
+    const int l = (int)(f % 64);
+    const size_t rb = blk / (K / 32);
+    const int ks = (int)(blk % (K / 32));
+    const T* s = src + (rb * 16 + (l & 15)) * (size_t)K + ks * 32 + 8 * (l >> 4);
+    T* d = dst + blk * 512 + l * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = s[j];
+  }
+}
+
 // a3 as evaluated by the attention kernel (same device predicate)
 __global__ void debug_visible_kernel(const VisibleParams p) {
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
@@ -234,6 +257,18 @@ hipError_t launch_kv_store(const KvStoreParams& p, int dtype, hipStream_t s) {
   DSPINE_DISPATCH(dtype, kv_store_kernel, dim3(p.rows), dim3(kRowThreads), smem, s, p);
   return hipGetLastError();
 }
+hipError_t launch_pack(const void* src, void* dst, int rows, int cols, int dtype, hipStream_t s) {
+  const size_t nfrag = (size_t)(rows / 16) * (cols / 32) * 64;
+  const int grid = (int)std::min<size_t>((nfrag + 255) / 256, 8192);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL((pack_kernel<uint16_t>), dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), rows, cols);
+  else
+    hipLaunchKernelGGL((pack_kernel<float>), dim3(grid), dim3(256), 0, s,
+                       static_cast<const float*>(src), static_cast<float*>(dst), rows, cols);
+  return hipGetLastError();
+}
+
 hipError_t launch_debug_visible(const VisibleParams& p, hipStream_t s) {
   const int n = p.B * p.W;
   hipLaunchKernelGGL(debug_visible_kernel, dim3((n + 63) / 64), dim3(64), 0, s, p);

@@ -152,6 +152,22 @@ int dspine_model_create(const dspine_geometry* geom, const dspine_weights* weigh
                         dspine_model** out);
 void dspine_model_destroy(dspine_model* model);
 
+/*
+ * Projection weights in fragment order.  The GEMMs stream every projection
+ * matrix (wq, wk, wv, wo, w_gate, w_up, w_down, R, W_l per layer; w_feat,
+ * bridge_G, bridge_Gp, bridge_A) in the order their MFMA fragments are
+ * loaded: inside each block of 16 rows, 32-wide column step ks holds the 64
+ * lane fragments (row 16b + l%16, columns 32ks + 8(l/16) .. +8) in
+ * consecutive memory.  dspine_pack_weights writes that copy into `dst`
+ * (device, 256-byte aligned, dspine_packed_bytes bytes, caller-owned) with
+ * kernels on `stream`; from then on the model reads projections only from
+ * `dst`, which must outlive the model (the row-major matrices may be freed
+ * once those kernels have run).  Every other call returns DSPINE_E_STATE
+ * until the model is packed.  Errors: E_ARG, E_WORKSPACE (dst too small).
+ */
+size_t dspine_packed_bytes(const dspine_model* model);
+int dspine_pack_weights(dspine_model* model, void* dst, size_t dst_bytes, dspine_stream_t stream);
+
 /* Bytes of one ring (K or V, same size) of `layer` for one request with the
  * given capacity (must be window[layer] for a local layer).  0 on error. */
 size_t dspine_ring_bytes(const dspine_model* model, int layer, int64_t capacity);

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import synth
@@ -175,6 +176,25 @@ def test_materialize_rejections(L):
     n[0] = 0
     assert L.dspine_ctx_materialize(h, 1, arr, feats, n, None, 0, None) == 0
     assert arr[0].frontier == 0
+    L.dspine_model_destroy(h)
+
+
+def test_unpacked_model_refuses_valid_calls(L):
+    """Projection weights must be packed (fragment order) before any call
+    that launches work; argument errors are still reported first."""
+    g = synth.G_27B
+    h = make_model(L, g)
+    assert L.dspine_packed_bytes(h) == sum(
+        int(np.prod(synth.weight_shape(g, n))) * 2
+        for n in synth.weight_names(g) if n.split(".")[-1] in bd._PROJECTIONS)
+    c = fake_ctx(g, 4096)
+    assert call_forward(L, h, 1, 16, [c], [5]) == bd.E_STATE
+    assert b"pack" in L.dspine_last_error()
+    assert call_forward(L, h, 1, 17, [c], [5]) == bd.E_UNSUPPORTED
+    aid = (ctypes.c_int32 * 1)(3)
+    assert L.dspine_bridge(h, 0, 1, 16, FAKE, aid, None, FAKE, 1 << 40, None) == bd.E_STATE
+    assert L.dspine_pack_weights(h, FAKE + 16, 1 << 40, None) == bd.E_ARG     # misaligned dst
+    assert L.dspine_pack_weights(h, FAKE, 1024, None) == bd.E_WORKSPACE
     L.dspine_model_destroy(h)
 
 

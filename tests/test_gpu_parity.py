@@ -10,7 +10,7 @@ import pytest
 
 import synth
 from oracle import dspine_oracle as O
-from tests.gpu_cases import Case, Run, bf16_ulp, rel_err, tol_for, to_np64
+from tests.gpu_cases import Case, Run, rel_err, storage_err, tol_for, to_np64
 
 pytestmark = pytest.mark.gpu
 
@@ -87,7 +87,10 @@ def test_chunked_and_truncated_materialization():
                 c = to_np64(getattr(run.ctxs[b], ring)[l])
                 assert np.array_equal(np.isnan(a), np.isnan(c))
                 m = ~np.isnan(a)
-                assert np.all(np.abs(a[m] - c[m]) <= bf16_ulp(a[m]))
+                # GEMM rounding scales with the row's rms, so beyond one
+                # storage step an element may differ by a small multiple of
+                # the fp32 error of the raw projection (measured vs rms)
+                assert storage_err(c[m], a[m], True) <= 1e-3, (l, ring, b)
                 assert np.mean(a[m] == c[m]) > 0.99
 
 
