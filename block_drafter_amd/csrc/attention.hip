@@ -80,33 +80,96 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
   const int row_base = b * W;
   const float* rope = p.rope;
 
+  // ---- context keys [cbeg, cend) in tiles of 32 ---------------------------
+  // PF tiles are in flight in registers at any time: the slot of tile i is
+  // refilled with tile i + PF as soon as tile i is in LDS, so a split's keys
+  // cost about one memory latency, not one per tile.  Loads past cend read
+  // position cend-1 (in bounds); those keys are masked and their values
+  // zeroed when the tile is written to LDS.
+  const gptr<TW> kring = as_global(reinterpret_cast<const TW*>(p.kring[b]));
+  const gptr<TV> vring = as_global(reinterpret_cast<const TV*>(p.vring[b]));
+  const int64_t cap = p.cap[b];
+  constexpr int KCH = D * EQ / 16, KEPC = 16 / EQ;     // 16-byte chunks per key row
+  constexpr int VCH = D * EV / 16, VEPC = 16 / EV;
+  // chunks per thread; with more threads than chunks the spare threads load
+  // a duplicate chunk and store nothing
+  constexpr int KPT = (32 * KCH + NT - 1) / NT, VPT = (32 * VCH + NT - 1) / NT;
+  constexpr int PF = (16 / (KPT + VPT)) < 1 ? 1 : (16 / (KPT + VPT)) > 8 ? 8 : 16 / (KPT + VPT);
+  u32x4 kreg[PF][KPT], vreg[PF][VPT];
+  const int n_tiles = cend > cbeg ? (int)((cend - cbeg + 31) / 32) : 0;
+  auto load_tile = [&](u32x4 (&kr_)[KPT], u32x4 (&vr_)[VPT], int i) {
+    const int64_t t0 = cbeg + 32 * (int64_t)i;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int c = (tid + q * NT) % (32 * KCH), kr = c / KCH, part = c % KCH;
+      const int64_t pos = t0 + kr < cend ? t0 + kr : cend - 1;
+      kr_[q] = gload16((gptr<void>)(kring + ((size_t)g * cap + ring_slot(pos, S)) * D + part * KEPC));
+    }
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+      const int c = (tid + q * NT) % (32 * VCH), kr = c / VCH, part = c % VCH;
+      const int64_t pos = t0 + kr < cend ? t0 + kr : cend - 1;
+      vr_[q] = gload16((gptr<void>)(vring + ((size_t)g * cap + ring_slot(pos, S)) * D + part * VEPC));
+    }
+  };
+  auto store_tile = [&](const u32x4 (&kr_)[KPT], const u32x4 (&vr_)[VPT], int i) {
+    const int64_t t0 = cbeg + 32 * (int64_t)i;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int c = tid + q * NT, kr = c / KCH, part = c % KCH;
+      if (c < 32 * KCH)
+        *reinterpret_cast<u32x4*>(&sK[0][kr * LDQ + part * KEPC]) = key_chunk(kr_[q], (TW*)nullptr, (TQ*)nullptr);
+    }
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+      const int c = tid + q * NT, kr = c / VCH, part = c % VCH;
+      if (c >= 32 * VCH) continue;
+      alignas(16) TV val[VEPC];
+      *reinterpret_cast<u32x4*>(val) = t0 + kr < cend ? vr_[q] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < VEPC; ++e) sVt[0][(part * VEPC + e) * LDV + kr] = val[e];
+    }
+  };
+  // first PF tiles in flight during the prologue below (clamped, in bounds)
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) load_tile(kreg[j], vreg[j], j < n_tiles ? j : n_tiles - 1);
+  }
+
   // ---- prologue: head RMSNorm + RoPE of this wave's query head ------------
+  // Every operand is loaded into registers before the first use, through
+  // global-address-space pointers, so the row's loads share one latency.
   auto prep_rows = [&](int col0, const void* gain, TQ* dst) {
     const int r = lane >> 2, part = lane & 3;
     constexpr int NP = D / 8;               // rotation pairs per lane
-    float xa[NP], xb[NP];
-    float ss = 0.f;
     const bool live = r < W;
-    const float* src = p.qkv + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + col0;
+    const gptr<float> src = as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + col0;
+    const gptr<float> cs = as_global(rope) + (size_t)(row_base + (live ? r : 0)) * D;   // (cos, sin) x D/2
+    const gptr<TW> gw = as_global(reinterpret_cast<const TW*>(gain));
+    float xa[NP], xb[NP], ga[NP], gb[NP], co[NP], si[NP];
 #pragma unroll
     for (int jj = 0; jj < NP; ++jj) {
       const int j = part * NP + jj;
-      xa[jj] = live ? src[j] : 0.f;
-      xb[jj] = live ? src[j + D / 2] : 0.f;
-      ss += xa[jj] * xa[jj] + xb[jj] * xb[jj];
+      xa[jj] = src[j];
+      xb[jj] = src[j + D / 2];
+      ga[jj] = Elt<TW>::gload(gw, j);
+      gb[jj] = Elt<TW>::gload(gw, j + D / 2);
+      co[jj] = cs[2 * j];
+      si[jj] = cs[2 * j + 1];
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < NP; ++jj) ss += xa[jj] * xa[jj] + xb[jj] * xb[jj];
     ss += __shfl_xor(ss, 1, 64);
     ss += __shfl_xor(ss, 2, 64);
     const float inv = rsqrtf(ss / D + p.eps);
-    const float* cs = rope + (size_t)(row_base + (live ? r : 0)) * D;   // (cos, sin) x D/2
 #pragma unroll
     for (int jj = 0; jj < NP; ++jj) {
       const int j = part * NP + jj;
-      const float a = xa[jj] * inv * Elt<TW>::load(reinterpret_cast<const TW*>(gain), j);
-      const float c = xb[jj] * inv * Elt<TW>::load(reinterpret_cast<const TW*>(gain), j + D / 2);
-      const float co = cs[2 * j], si = cs[2 * j + 1];
-      Elt<TQ>::store(dst, r * LDQ + j, live ? a * co - c * si : 0.f);
-      Elt<TQ>::store(dst, r * LDQ + j + D / 2, live ? c * co + a * si : 0.f);
+      const float a = xa[jj] * inv * ga[jj];
+      const float c = xb[jj] * inv * gb[jj];
+      Elt<TQ>::store(dst, r * LDQ + j, live ? a * co[jj] - c * si[jj] : 0.f);
+      Elt<TQ>::store(dst, r * LDQ + j + D / 2, live ? c * co[jj] + a * si[jj] : 0.f);
     }
   };
   prep_rows(h * D, p.gq, sQ[w]);
@@ -121,9 +184,12 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
     if (w == (GRP > 1 ? 1 : 0)) {
       const int r = lane >> 2, part = lane & 3;
       const bool live = r < W;
-      const float* src = p.qkv + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + vcol;
-      for (int d = part * (D / 4); d < (part + 1) * (D / 4); ++d)
-        put_v(&sVt[1][d * LDV + r], live ? src[d] : 0.f);
+      const gptr<float> src = as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + vcol + part * (D / 4);
+      float vv[D / 4];
+#pragma unroll
+      for (int d = 0; d < D / 4; ++d) vv[d] = src[d];
+#pragma unroll
+      for (int d = 0; d < D / 4; ++d) put_v(&sVt[1][(part * (D / 4) + d) * LDV + r], live ? vv[d] : 0.f);
       for (int e = lane; e < 16 * D; e += 64) put_v(&sVt[1][(e / 16) * LDV + 16 + (e % 16)], 0.f);
     }
   }
@@ -199,38 +265,19 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
     }
   };
 
-  // ---- context keys [cbeg, cend) in tiles of 32 ---------------------------
-  const TW* kring = reinterpret_cast<const TW*>(p.kring[b]);
-  const TV* vring = reinterpret_cast<const TV*>(p.vring[b]);
-  const int64_t cap = p.cap[b];
-  for (int64_t t0 = cbeg; t0 < cend; t0 += 32) {
-    constexpr int KCH = D * EQ / 16, KEPC = 16 / EQ;
-    for (int c = tid; c < 32 * KCH; c += NT) {
-      const int kr = c / KCH, part = c % KCH;
-      const int64_t pos = t0 + kr;
-      u32x4 val = {0, 0, 0, 0};
-      if (pos < cend)
-        val = key_chunk(*reinterpret_cast<const u32x4*>(kring + ((size_t)g * cap + ring_slot(pos, S)) * D + part * KEPC),
-                        (TW*)nullptr, (TQ*)nullptr);
-      *reinterpret_cast<u32x4*>(&sK[0][kr * LDQ + part * KEPC]) = val;
-    }
-    constexpr int VCH = D * EV / 16, VEPC = 16 / EV;
-    for (int c = tid; c < 32 * VCH; c += NT) {
-      const int kr = c / VCH, part = c % VCH;
-      const int64_t pos = t0 + kr;
-      alignas(16) TV val[VEPC];
-      if (pos < cend) {
-        *reinterpret_cast<u32x4*>(val) =
-            *reinterpret_cast<const u32x4*>(vring + ((size_t)g * cap + ring_slot(pos, S)) * D + part * VEPC);
-      } else {
-        *reinterpret_cast<u32x4*>(val) = u32x4{0, 0, 0, 0};
-      }
+  // Every trip issues the same loads (refills past the end re-read the last
+  // tile), so the wait before each LDS store covers exactly one slot.
+  for (int i0 = 0; i0 < n_tiles; i0 += PF) {
 #pragma unroll
-      for (int e = 0; e < VEPC; ++e) sVt[0][(part * VEPC + e) * LDV + kr] = val[e];
+    for (int j = 0; j < PF; ++j) {
+      const int i = i0 + j;
+      const bool live = i < n_tiles;
+      if (live) store_tile(kreg[j], vreg[j], i);
+      __syncthreads();
+      load_tile(kreg[j], vreg[j], i + PF < n_tiles ? i + PF : n_tiles - 1);
+      if (live) process(0, cbeg + 32 * (int64_t)i, false);
+      __syncthreads();
     }
-    __syncthreads();
-    process(0, t0, false);
-    __syncthreads();
   }
   if (has_block) process(1, 0, true);
 
@@ -263,21 +310,46 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
   if (lane == 0) old = count_arrival(p.counters + b * p.nq + h);
   old = __shfl(old, 0, 64);
   if ((int)old != p.nsplit - 1) return;
+  // Merge: the splits' row maxima first (8 loads in flight at a time), then
+  // their partial sums four splits at a time, every load issued before use.
+  // Indexes past the last split repeat it; those copies are not added.
   float mstar = -INFINITY;
-  for (int sp = 0; sp < p.nsplit; ++sp) mstar = fmaxf(mstar, load_coherent(base + (size_t)sp * PSZ + 64 * (D / 4) + qrow));
+  for (int sp0 = 0; sp0 < p.nsplit; sp0 += 8) {
+    float mv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sp = sp0 + j < p.nsplit ? sp0 + j : p.nsplit - 1;
+      mv[j] = load_coherent(base + (size_t)sp * PSZ + 64 * (D / 4) + qrow);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mstar = fmaxf(mstar, mv[j]);
+  }
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
   float L = 0.f;
   if (mstar != -INFINITY) {
-    for (int sp = 0; sp < p.nsplit; ++sp) {
-      const float* part = base + (size_t)sp * PSZ;
-      const float ms = load_coherent(part + 64 * (D / 4) + qrow);
-      if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - mstar);
-      L += wgt * load_coherent(part + 64 * (D / 4) + 16 + qrow);
+    constexpr int MB = 256 / D;              // splits merged per batch of loads
+    for (int sp0 = 0; sp0 < p.nsplit; sp0 += MB) {
+      float mv[MB], lv[MB];
+      f32x4 ov[MB][D / 16];
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) acc[dt] += wgt * load_coherent4(part + (dt * 64 + lane) * 4);
+      for (int j = 0; j < MB; ++j) {
+        const int sp = sp0 + j < p.nsplit ? sp0 + j : p.nsplit - 1;
+        const float* part = base + (size_t)sp * PSZ;
+        mv[j] = load_coherent(part + 64 * (D / 4) + qrow);
+        lv[j] = load_coherent(part + 64 * (D / 4) + 16 + qrow);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) ov[j][dt] = load_coherent4(part + (dt * 64 + lane) * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        if (sp0 + j >= p.nsplit || mv[j] == -INFINITY) continue;
+        const float wgt = exp2f(mv[j] - mstar);
+        L += wgt * lv[j];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) acc[dt] += wgt * ov[j][dt];
+      }
     }
   }
   if (L > 0.f) write_row(acc, 1.f / L);

@@ -893,19 +893,20 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
     ap.rope = rope;
     ap.S = g.window[l];
     ap.causal = g.block_causal;
-    int64_t max_splits = 1;
-    const int64_t base_split = ceil_div(256, (int64_t)B * g.n_kv_heads);
+    // Key splits: enough workgroups to spread the reads (about 256, or one
+    // split per 2048 keys on long contexts) but at least 256 keys per split,
+    // since every split adds a partial the merge has to read back.
+    int64_t max_ctx = 0;
     for (int b = 0; b < B; ++b) {
       ap.kring[b] = ctx[b].k_ring[l];
       ap.vring[b] = ctx[b].v_ring[l];
       ap.cap[b] = ctx[b].capacity[l];
       ap.F[b] = ctx[b].frontier;
       ap.lo0[b] = row0_lo(ctx[b].frontier, g.window[l]);
-      const int64_t nctx = ap.F[b] - ap.lo0[b];
-      const int64_t want = std::max<int64_t>(1, std::min(ceil_div(nctx, 128), std::max(base_split, ceil_div(nctx, 2048))));
-      max_splits = std::max(max_splits, want);
+      max_ctx = std::max(max_ctx, ap.F[b] - ap.lo0[b]);
     }
-    ap.nsplit = (int)std::min<int64_t>(max_splits, kMaxSplit);
+    const int64_t spread = std::max(ceil_div(256, (int64_t)B * g.n_kv_heads), ceil_div(max_ctx, 2048));
+    ap.nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({spread, ceil_div(max_ctx, 256), (int64_t)kMaxSplit}));
     for (int b = 0; b < B; ++b) {
       const int64_t nctx = ap.F[b] - ap.lo0[b];
       ap.kps[b] = (int32_t)(ceil_div(ceil_div(nctx, ap.nsplit), 32) * 32);

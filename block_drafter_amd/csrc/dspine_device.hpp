@@ -50,27 +50,6 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
 template <typename TW> struct ActOf;
 
 // Element traits: the storage type of weights/activations for each model dtype.
-template <typename T> struct Elt;
-template <> struct Elt<float> {
-  static constexpr int kBytes = 4;
-  __device__ static __forceinline__ float load(const float* p, size_t i) { return p[i]; }
-  __device__ static __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
-};
-template <> struct Elt<f16_t> {
-  static constexpr int kBytes = 2;
-  __device__ static __forceinline__ float load(const f16_t* p, size_t i) { return f16_bits_to_f32(p[i].bits); }
-  __device__ static __forceinline__ void store(f16_t* p, size_t i, float v) { p[i].bits = f32_to_f16_bits(v); }
-};
-template <> struct Elt<bf16_t> {
-  static constexpr int kBytes = 2;
-  __device__ static __forceinline__ float load(const bf16_t* p, size_t i) {
-    return bf16_bits_to_f32(p[i].bits);
-  }
-  __device__ static __forceinline__ void store(bf16_t* p, size_t i, float v) {
-    p[i].bits = f32_to_bf16_bits(v);
-  }
-};
-
 // Global-address-space view of a pointer.  Loads through it are global_load
 // (vector-memory counter only); loads through a generic pointer become
 // flat_load, which also counts on the LDS counter, so any later LDS wait
@@ -82,6 +61,31 @@ __device__ __forceinline__ gptr<T> as_global(const T* p) {
   return (gptr<T>)(p);
 }
 __device__ __forceinline__ u32x4 gload16(gptr<void> p) { return *(gptr<u32x4>)(p); }
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  __device__ static __forceinline__ float gload(gptr<float> p, size_t i) { return p[i]; }
+  __device__ static __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elt<f16_t> {
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ float load(const f16_t* p, size_t i) { return f16_bits_to_f32(p[i].bits); }
+  __device__ static __forceinline__ float gload(gptr<f16_t> p, size_t i) { return f16_bits_to_f32(p[i].bits); }
+  __device__ static __forceinline__ void store(f16_t* p, size_t i, float v) { p[i].bits = f32_to_f16_bits(v); }
+};
+template <> struct Elt<bf16_t> {
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ float load(const bf16_t* p, size_t i) {
+    return bf16_bits_to_f32(p[i].bits);
+  }
+  __device__ static __forceinline__ float gload(gptr<bf16_t> p, size_t i) { return bf16_bits_to_f32(p[i].bits); }
+  __device__ static __forceinline__ void store(bf16_t* p, size_t i, float v) {
+    p[i].bits = f32_to_bf16_bits(v);
+  }
+};
+
 
 // ---------------------------------------------------------------------------
 // MFMA fragments: 8 consecutive K elements of one row, per lane.

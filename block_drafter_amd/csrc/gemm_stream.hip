@@ -230,22 +230,36 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
           for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0, 0, 0, 0};
         return;
       }
-      // add the contributions in workgroup order, whoever finishes, so the
-      // result does not depend on arrival order (bit-reproducible runs)
+      // Add the contributions in workgroup order, whoever finishes, so the
+      // result does not depend on arrival order (bit-reproducible runs).  The
+      // own partial is read back like the others (the same values).  Loads go
+      // out FB contributors at a time so their latencies overlap; indexes past
+      // the last contributor repeat it and are not added.
+      constexpr int FB = NWB * MT <= 2 ? 8 : NWB * MT <= 4 ? 4 : NWB * MT <= 8 ? 2 : 1;
       f32x4 sum[NWB][MT];
 #pragma unroll
       for (int nb = 0; nb < NWB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < MT; ++mb) sum[nb][mb] = f32x4{0, 0, 0, 0};
-      for (int gg = g_first; gg <= g_last; ++gg) {
-        const float* other = p.partials + (size_t)slot_of(gg) * (NWB * MT * 256 * 4);
+      for (int g0 = g_first; g0 <= g_last; g0 += FB) {
+        f32x4 part[FB][NWB][MT];
 #pragma unroll
-        for (int nb = 0; nb < NWB; ++nb)
+        for (int j = 0; j < FB; ++j) {
+          const int gg = g0 + j <= g_last ? g0 + j : g_last;
+          const float* other = p.partials + (size_t)slot_of(gg) * (NWB * MT * 256 * 4);
 #pragma unroll
-          for (int mb = 0; mb < MT; ++mb) {
-            if (gg == g) sum[nb][mb] += acc[nb][mb];
-            else sum[nb][mb] += load_coherent4(other + ((nb * MT + mb) * 256 + tid) * 4);
-          }
+          for (int nb = 0; nb < NWB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MT; ++mb) part[j][nb][mb] = load_coherent4(other + ((nb * MT + mb) * 256 + tid) * 4);
+        }
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+          if (g0 + j > g_last) break;
+#pragma unroll
+          for (int nb = 0; nb < NWB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MT; ++mb) sum[nb][mb] += part[j][nb][mb];
+        }
       }
 #pragma unroll
       for (int nb = 0; nb < NWB; ++nb)
