@@ -102,7 +102,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
                     help="after the timed region, time every kernel class for a few steps")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times and exit (calibrates "
+                         "hardware byte counters against a known traffic)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the draft round is "
@@ -187,6 +201,26 @@ def main():
     gu_avg_ms = gu_ms / max(1, gu_n)
     achieved = gu_bytes / (gu_avg_ms * 1e-3) / 1e9
 
+    # the draft forward alone (same inputs, after the timed steps)
+    fwd_ev0 = torch.cuda.Event(enable_timing=True)
+    fwd_ev1 = torch.cuda.Event(enable_timing=True)
+    fwd_ev0.record()
+    for _ in range(args.steps):
+        model.forward(ctxs, anchors, W, out=out, workspace=ws)
+    fwd_ev1.record()
+    torch.cuda.synchronize()
+    fwd_ms = fwd_ev0.elapsed_time(fwd_ev1) / args.steps
+
+    # HBM traffic of the same kernel from the PMC runs summarised under
+    # profiles/ (null unless they were taken on this workload with the
+    # current kernel sources)
+    traffic = None
+    if wl.name == "dspine27b_b1":
+        from block_drafter_amd import profsum
+        rec = profsum.read_traffic(os.path.join(ROOT, "profiles", "traffic_gemm_stream_gate_up_dspine27b_b1.md"))
+        if rec is not None and rec[1] == profsum.source_hash():
+            traffic = rec[0]
+
     breakdown = None
     if args.breakdown:
         bd.profile_enable(bd.PROF_KINDS)
@@ -232,6 +266,9 @@ def main():
             "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "bytes_forward_weights": fwd_bytes, "bytes_context_kv": ctx_bytes,
             "bytes_materialize": mat_bytes, "wall_s": round(wall, 3),
+            "forward_only_ms": round(fwd_ms, 4),
+            "forward_only_per_s": round(1000.0 / fwd_ms, 3),
+            "forward_only_GBps": round((fwd_bytes + ctx_bytes + B * W * g.hidden * 4) / (fwd_ms * 1e-3) / 1e9, 1),
             "operands": "bf16 weights widened to fp16 in registers x fp16 activations, fp32 accumulate",
         },
         "roofline": {
@@ -241,7 +278,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "bytes per launch (HBM, PMC FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "bytes_per_launch": gu_bytes,
             "avg_launch_us": round(gu_avg_ms * 1000, 2),
             "launches": gu_n,

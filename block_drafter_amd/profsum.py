@@ -1,0 +1,127 @@
+"""Summaries of rocprofv3 output for this library's kernels.
+
+  python -m block_drafter_amd.profsum stats KERNEL_STATS_CSV [--top N]
+      Markdown table of a ``--kernel-trace --stats --output-format csv`` run.
+
+  python -m block_drafter_amd.profsum traffic --fetch CSV --write CSV
+        --fetch-copy CSV --write-copy CSV --kernel REGEX --algorithmic BYTES
+      HBM traffic per launch of the kernels whose name matches REGEX, from two
+      ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs (KiB per dispatch).
+      Each counter is scaled by the factor that turns its reading on a plain
+      device copy of known size into the copy's true bytes (the copy runs
+      come from ``bench.py --copy-probe BYTES``).  The summary records a hash
+      of the kernel sources, so a reader can tell when it has gone stale.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import re
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+# sources whose change invalidates a traffic figure of the streamed GEMM
+GEMM_SOURCES = ["csrc/gemm_stream.hip", "csrc/dspine_device.hpp", "csrc/dspine_internal.hpp"]
+
+
+def source_hash(paths=GEMM_SOURCES) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(HERE, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    name = name.split("(")[0]
+    return name.replace("void ", "").replace("dspine::", "")
+
+
+def stats_table(path: str, top: int = 20) -> str:
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows[:top]:
+        out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(out)
+
+
+def _counter(path: str, regex: str):
+    vals = []
+    for r in csv.DictReader(open(path)):
+        if re.search(regex, r["Kernel_Name"]):
+            vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def copy_factor(path: str, copy_bytes: int) -> float:
+    vals = _counter(path, r"copyBuffer|elementwise_kernel.*copy|CopyKernel|copy_kernel")
+    if not vals:
+        raise SystemExit(f"no copy dispatch in {path}")
+    return copy_bytes / (statistics.median(vals) * 1024.0)
+
+
+def traffic(args) -> str:
+    fetch = _counter(args.fetch, args.kernel)
+    write = _counter(args.write, args.kernel)
+    if not fetch or not write:
+        raise SystemExit("kernel regex matched no dispatch")
+    ff = copy_factor(args.fetch_copy, args.copy_bytes)
+    wf = copy_factor(args.write_copy, args.copy_bytes)
+    fb = statistics.median(fetch) * 1024.0 * ff
+    wb = statistics.median(write) * 1024.0 * wf
+    t = fb + wb
+    lines = [
+        f"kernel regex: `{args.kernel}`",
+        f"dispatches: {len(fetch)} (FETCH_SIZE run), {len(write)} (WRITE_SIZE run)",
+        f"copy calibration: FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {wf:.4f} (plain copy of {args.copy_bytes} bytes)",
+        f"fetched bytes per launch: {fb:.0f}",
+        f"written bytes per launch: {wb:.0f}",
+        f"algorithmic bytes per launch: {args.algorithmic}",
+        f"traffic / algorithmic: {t / args.algorithmic:.4f}",
+        f"traffic_bytes_per_launch: {t:.0f}",
+        f"source_hash: {source_hash()}",
+    ]
+    return "\n".join(lines)
+
+
+def read_traffic(md_path: str):
+    """(traffic bytes per launch, source hash) recorded in a traffic summary,
+    or None when the file is missing or names other sources."""
+    if not os.path.exists(md_path):
+        return None
+    txt = open(md_path).read()
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", txt)
+    h = re.search(r"source_hash: ([0-9a-f]+)", txt)
+    if not m or not h:
+        return None
+    return int(m.group(1)), h.group(1)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--top", type=int, default=20)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--fetch-copy", required=True)
+    t.add_argument("--write-copy", required=True)
+    t.add_argument("--copy-bytes", type=int, default=1 << 30)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--algorithmic", type=int, required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(stats_table(a.csv, a.top))
+    else:
+        print(traffic(a))
+
+
+if __name__ == "__main__":
+    sys.exit(main())
