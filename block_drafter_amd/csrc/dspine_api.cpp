@@ -127,10 +127,14 @@ int64_t live_lo(int S, int64_t F) { return S == 0 ? 0 : std::max<int64_t>(0, F -
 struct Plan {
   size_t gemm_cnt, attn_cnt;              // u32 counters
   size_t gemm_part, attn_part;            // f32 partials
-  size_t x, act_h, act_q, act_f, act_r, act_r2, qkv, z, P, P2, rho, rope;
+  size_t x, act_q, act_f, qkv, z, P, P2, rope;
+  size_t act_h, act_r, act_m;             // pre-scaled operands (large blocks)
+  size_t st0, st1, stz, stc;              // row statistics [lists][kMaxRows]
   size_t c_raw, c_act, kv_raw;            // materialize, per row block
   size_t total;
 };
+// row-statistics lists a GEMM writes for `width` output columns (one per 64)
+int stat_tiles(int width) { return gemm_stream_stat_lists(width); }
 
 Plan make_plan(const dspine_geometry& g, int64_t M, int64_t rows) {
   Plan p{};
@@ -148,18 +152,21 @@ Plan make_plan(const dspine_geometry& g, int64_t M, int64_t rows) {
   p.gemm_part = take(sizeof(float) * gemm_stream_partial_floats(kMaxGrid));
   p.attn_part = take(sizeof(float) * attn_partial_floats(DSPINE_MAX_BATCH, g.n_q_heads, g.head_dim));
   p.x = take(4 * Mp * g.hidden);
-  p.act_h = take(eb * Mp * g.hidden);
   p.act_q = take(eb * Mp * qd);
   p.act_f = take(eb * Mp * g.ffn);
   const int r = std::max(g.code_dim, 1), a = std::max(g.msg_dim, 1);
-  p.act_r = take(eb * Mp * r);
-  p.act_r2 = take(eb * Mp * r);
   p.qkv = take(4 * Mp * (qd + 2 * kvd));
   p.z = take(4 * Mp * r);
   p.P = take(4 * Mp * 3 * a);
   p.P2 = take(4 * Mp * 3 * a);
-  p.rho = take(4 * Mp);
   p.rope = take(4 * Mp * g.head_dim);
+  p.act_h = take(eb * Mp * g.hidden);
+  p.act_r = take(eb * Mp * r);
+  p.act_m = take(eb * Mp * a);
+  p.st0 = take(4 * (size_t)kMaxRows * stat_tiles(g.hidden));
+  p.st1 = take(4 * (size_t)kMaxRows * stat_tiles(g.hidden));
+  p.stz = take(4 * (size_t)kMaxRows * stat_tiles(r));
+  p.stc = take(4 * (size_t)kMaxRows * stat_tiles(g.hidden));
   const int64_t R = std::max<int64_t>(rows, 0);
   p.c_raw = take(4 * R * g.hidden);
   p.c_act = take(eb * R * g.hidden);
@@ -319,6 +326,51 @@ void set_segments(GemmParams& gp, std::initializer_list<std::pair<const void*, i
   }
   gp.nseg = s;
   gp.nblk = blk;
+}
+
+// A operand of a streamed GEMM: fp32 rows x[m, :K] (stride ldx) times the
+// per-row scale `mode` formed from the row statistics `st` (`lists` lists),
+// times `gain` when given.  Small blocks form it in the GEMM prologue; large
+// ones through the pre-scale kernel into `act` (stride K).
+int set_scaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, const float* x, int ldx, int K, int mode,
+                 const float* st, int lists, float n, const void* gain, void* act, hipStream_t stream) {
+  gp.scale_n = n;
+  gp.eps = g.eps;
+  gp.code_scale = sqrtf((float)std::max(g.code_dim, 1));
+  gp.W = W;
+  if (M <= gemm_stream_fused_rows()) {
+    gp.pro = gain ? PRO_NORM : PRO_SCALE;
+    gp.xa = x;
+    gp.lda = ldx;
+    gp.gain = gain;
+    gp.scale_mode = mode;
+    gp.stats_in = st;
+    gp.stats_tiles = lists;
+    gp.stats_ld = kMaxRows;
+    return DSPINE_OK;
+  }
+  ScaleParams sp;
+  memset(&sp, 0, sizeof sp);
+  sp.M = M;
+  sp.K = K;
+  sp.W = W;
+  sp.mode = mode;
+  sp.stats = st;
+  sp.lists = lists;
+  sp.ld = kMaxRows;
+  sp.n = n;
+  sp.eps = g.eps;
+  sp.code_scale = gp.code_scale;
+  sp.x = x;
+  sp.ldx = ldx;
+  sp.gain = gain;
+  sp.act = act;
+  sp.ld_act = K;
+  HIP_TRY(launch_scale_rows(sp, g.dtype, stream));
+  gp.pro = PRO_COPY;
+  gp.a = act;
+  gp.lda = K;
+  return DSPINE_OK;
 }
 
 }  // namespace
@@ -481,6 +533,7 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
     float* c_raw = reinterpret_cast<float*>(ws + P.c_raw);
     void* c_act = ws + P.c_act;
     float* kv_raw = reinterpret_cast<float*>(ws + P.kv_raw);
+    float* stc = reinterpret_cast<float*>(ws + P.stc);
     const int ldkv = L * 2 * kvd;
 
     // walk the concatenated row list in blocks
@@ -510,10 +563,12 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
       }
       row0[nsrc] = (int32_t)nrows;
 
-      // GEMM 1: c_raw = s W_feat^T  (a1)
+      // a1: c_raw = W_feat s; a2: every layer's K and V projections of
+      // c = plain_rmsnorm(c_raw, g_ctx)
       const bool tile = g.dtype == DSPINE_BF16 && nrows > kMaxRows && H % 128 == 0 &&
                         (g.n_feat_layers * H) % 64 == 0 && kvd % 128 == 0 && H % 64 == 0;
       if (tile) {
+        // long blocks: MFMA tile GEMMs with the norm between them
         TileGemmParams tp;
         memset(&tp, 0, sizeof tp);
         tp.seg_ptr[0] = pw.w_feat;
@@ -535,9 +590,44 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
         tp.g_n = nsrc;
         tp.out = c_raw;
         tp.ldo = H;
+        {
+          ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
+          HIP_TRY(launch_gemm_tile(tp, g.dtype, cus, stream));
+        }
+        RowParams rp;
+        memset(&rp, 0, sizeof rp);
+        rp.M = (int)nrows;
+        rp.H = H;
+        rp.x = c_raw;
+        rp.act = c_act;
+        rp.gain = wt.g_ctx;
+        rp.eps = g.eps;
+        {
+          ProfScope ps(DSPINE_PROF_CTX_STORE, stream);
+          HIP_TRY(launch_rmsnorm(rp, g.dtype, false, stream));
+        }
+        memset(&tp, 0, sizeof tp);
+        for (int l = 0; l < L; ++l) {
+          tp.seg_ptr[2 * l] = pw.layer[l].wk;
+          tp.seg_ptr[2 * l + 1] = pw.layer[l].wv;
+          tp.seg_rows0[2 * l] = 2 * l * kvd;
+          tp.seg_rows0[2 * l + 1] = (2 * l + 1) * kvd;
+        }
+        tp.seg_rows0[2 * L] = 2 * L * kvd;
+        tp.nseg = 2 * L;
+        tp.N = ldkv;
+        tp.K = H;
+        tp.M = (int)nrows;
+        tp.pro = PRO_COPY;
+        tp.a = c_act;
+        tp.lda = H;
+        tp.out = kv_raw;
+        tp.ldo = ldkv;
         ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
         HIP_TRY(launch_gemm_tile(tp, g.dtype, cus, stream));
       } else {
+        // short blocks, in chunks of at most kMaxRows rows: streamed GEMMs,
+        // the norm formed in the K/V GEMM from the first one's statistics
         for (int64_t r0 = 0; r0 < nrows; r0 += kMaxRows) {
           const int mr = (int)std::min<int64_t>(kMaxRows, nrows - r0);
           GemmParams gp = gemm_base(P, ws, g.n_feat_layers * H, mr);
@@ -559,50 +649,13 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
           gp.epi = EPI_STORE;
           gp.out = c_raw + r0 * H;
           gp.ldo = H;
-          ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
-          HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
-        }
-      }
-      // c = plain_rmsnorm(c_raw, context_norm)
-      RowParams rp;
-      memset(&rp, 0, sizeof rp);
-      rp.M = (int)nrows;
-      rp.H = H;
-      rp.x = c_raw;
-      rp.act = c_act;
-      rp.gain = wt.g_ctx;
-      rp.eps = g.eps;
-      {
-        ProfScope ps(DSPINE_PROF_CTX_STORE, stream);
-        HIP_TRY(launch_rmsnorm(rp, g.dtype, false, stream));
-      }
-
-      // GEMM 2: every layer's K and V projections of c  (a2)
-      if (tile) {
-        TileGemmParams tp;
-        memset(&tp, 0, sizeof tp);
-        for (int l = 0; l < L; ++l) {
-          tp.seg_ptr[2 * l] = pw.layer[l].wk;
-          tp.seg_ptr[2 * l + 1] = pw.layer[l].wv;
-          tp.seg_rows0[2 * l] = 2 * l * kvd;
-          tp.seg_rows0[2 * l + 1] = (2 * l + 1) * kvd;
-        }
-        tp.seg_rows0[2 * L] = 2 * L * kvd;
-        tp.nseg = 2 * L;
-        tp.N = ldkv;
-        tp.K = H;
-        tp.M = (int)nrows;
-        tp.pro = PRO_COPY;
-        tp.a = c_act;
-        tp.lda = H;
-        tp.out = kv_raw;
-        tp.ldo = ldkv;
-        ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
-        HIP_TRY(launch_gemm_tile(tp, g.dtype, cus, stream));
-      } else {
-        for (int64_t r0 = 0; r0 < nrows; r0 += kMaxRows) {
-          const int mr = (int)std::min<int64_t>(kMaxRows, nrows - r0);
-          GemmParams gp = gemm_base(P, ws, H, mr);
+          gp.stats_out = stc;
+          gp.stats_out_ld = kMaxRows;
+          {
+            ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
+            HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+          }
+          gp = gemm_base(P, ws, H, mr);
           int blk = 0;
           for (int l = 0; l < L; ++l) {
             gp.seg_ptr[2 * l] = pw.layer[l].wk;
@@ -614,9 +667,9 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
           }
           gp.nseg = 2 * L;
           gp.nblk = blk;
-          gp.pro = PRO_COPY;
-          gp.a = static_cast<char*>(c_act) + (size_t)r0 * H * act_bytes(g);
-          gp.lda = H;
+          int rc2 = set_scaled_a(gp, g, mr, 1, c_raw + r0 * H, H, H, SCALE_RMSNORM, stc, stat_tiles(H), (float)H,
+                                 wt.g_ctx, c_act, stream);
+          if (rc2) return rc2;
           gp.epi = EPI_STORE;
           gp.out = kv_raw + r0 * ldkv;
           gp.ldo = ldkv;
@@ -663,56 +716,43 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
 // bridge (a9-a11) on x [M, H] fp32 in place
 // -----------------------------------------------------------------------------
 namespace {
-int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const int32_t* anchor_ids,
-               const float* pred_codes, char* ws, const Plan& P, int cus, hipStream_t stream) {
+// x [M, H] fp32 in place; `xst` holds the sums of squares of x's rows as
+// `xst_tiles` partial lists (ld kMaxRows).  Writes the new rows' statistics
+// to `st_out` (stat_tiles(H) lists).
+int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const float* xst, int xst_tiles,
+               float* st_out, const int32_t* anchor_ids, const float* pred_codes, char* ws, const Plan& P,
+               int cus, hipStream_t stream) {
   const dspine_geometry& g = m.g;
   const dspine_weights& wt = m.w;
   const int M = B * W, H = g.hidden, r = g.code_dim, a = g.msg_dim;
-  void* act_h = ws + P.act_h;
-  void* act_r = ws + P.act_r;
   float* z = reinterpret_cast<float*>(ws + P.z);
+  float* stz = reinterpret_cast<float*>(ws + P.stz);
   float* Pb = reinterpret_cast<float*>(ws + P.P);
   float* P2 = reinterpret_cast<float*>(ws + P.P2);
-  float* rho = reinterpret_cast<float*>(ws + P.rho);
 
-  RowParams rp;
-  memset(&rp, 0, sizeof rp);
-  rp.M = M;
-  rp.W = W;
-  rp.H = H;
-  rp.x = x;
-  rp.act = act_h;
-  rp.eps = g.eps;
-  rp.rho = rho;
-  HIP_TRY(launch_bridge_read(rp, g.dtype, stream));                 // rho, x/(rho+eps)
-
-  GemmParams gp = gemm_base(P, ws, H, M);                             // z = R (x/(rho+eps))
+  // z = R (x / (rho + eps)), rho = rms(x); the anchor rows of z take
+  // sqrt(r) C[anchor] (their code); statistics of z for the code norm
+  GemmParams gp = gemm_base(P, ws, H, M);
   set_segments(gp, {{m.pw.layer[layer].R, r}});
-  gp.pro = PRO_COPY;
-  gp.a = act_h;
-  gp.lda = H;
+  int rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RHO_INV, xst, xst_tiles, (float)H, nullptr, ws + P.act_h, stream);
+  if (rc) return rc;
   gp.epi = EPI_STORE;
   gp.out = z;
   gp.ldo = r;
+  gp.stats_out = stz;
+  gp.stats_out_ld = kMaxRows;
+  gp.code_anchor = 1;
+  gp.codebook = wt.codebook;
+  gp.code_scale = sqrtf((float)r);
+  gp.W = W;
+  for (int b = 0; b < B; ++b) gp.anchor[b] = anchor_ids[b];
   HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
 
-  RowParams cp;
-  memset(&cp, 0, sizeof cp);
-  cp.M = M;
-  cp.W = W;
-  cp.eps = g.eps;
-  cp.z = z;
-  cp.r = r;
-  cp.codebook = wt.codebook;
-  cp.act = act_r;
-  for (int b = 0; b < B; ++b) cp.anchor[b] = anchor_ids[b];
-  HIP_TRY(launch_bridge_code(cp, g.dtype, stream));                   // c (anchor: sqrt(r) C[a])
-
-  gp = gemm_base(P, ws, r, M);                                         // [G; G_p; A] c, one GEMM
+  // [G; G_p; A] c with c = sqrt(r) z / (||z|| + eps) (anchor rows: z as is)
+  gp = gemm_base(P, ws, r, M);
   set_segments(gp, {{m.pw.bridge_G, a}, {m.pw.bridge_Gp, a}, {m.pw.bridge_A, a}});
-  gp.pro = PRO_COPY;
-  gp.a = act_r;
-  gp.lda = r;
+  rc = set_scaled_a(gp, g, M, W, z, r, r, SCALE_CODE, stz, stat_tiles(r), (float)r, nullptr, ws + P.act_r, stream);
+  if (rc) return rc;
   gp.epi = EPI_STORE;
   gp.out = Pb;
   gp.ldo = 3 * a;
@@ -721,18 +761,10 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const i
   const float* Ppred = Pb;
   int shift = 1;
   if (pred_codes) {                                                    // predecessor override
-    RowParams op;
-    memset(&op, 0, sizeof op);
-    op.M = M;
-    op.r = r;
-    op.pred_in = pred_codes;
-    op.pred_act = ws + P.act_r2;
-    HIP_TRY(launch_copy_codes(op, g.dtype, stream));
     gp = gemm_base(P, ws, r, M);
     set_segments(gp, {{m.pw.bridge_G, a}, {m.pw.bridge_Gp, a}, {m.pw.bridge_A, a}});
-    gp.pro = PRO_COPY;
-    gp.a = ws + P.act_r2;
-    gp.lda = r;
+    rc = set_scaled_a(gp, g, M, W, pred_codes, r, r, SCALE_ONE, nullptr, 0, (float)r, nullptr, ws + P.act_r, stream);
+    if (rc) return rc;
     gp.epi = EPI_STORE;
     gp.out = P2;
     gp.ldo = 3 * a;
@@ -741,19 +773,44 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const i
     shift = 0;
   }
 
-  gp = gemm_base(P, ws, a, M);                                         // x += rho W_l (g * m)
+  // x += rho W_l (g * m), rho from the same statistics of x
+  gp = gemm_base(P, ws, a, M);
   set_segments(gp, {{m.pw.layer[layer].W_l, H}});
-  gp.pro = PRO_BRIDGE_MSG;
-  gp.P = Pb;
-  gp.Ppred = Ppred;
-  gp.bias = wt.bridge_b;
-  gp.a_dim = a;
+  if (M <= gemm_stream_fused_rows()) {
+    gp.pro = PRO_BRIDGE_MSG;
+    gp.P = Pb;
+    gp.Ppred = Ppred;
+    gp.bias = wt.bridge_b;
+    gp.a_dim = a;
+    gp.pred_shift = shift;
+  } else {
+    ScaleParams sp;
+    memset(&sp, 0, sizeof sp);
+    sp.M = M;
+    sp.K = a;
+    sp.W = W;
+    sp.P = Pb;
+    sp.Ppred = Ppred;
+    sp.bias = wt.bridge_b;
+    sp.pred_shift = shift;
+    sp.act = ws + P.act_m;
+    sp.ld_act = a;
+    HIP_TRY(launch_bridge_msg(sp, g.dtype, stream));
+    gp.pro = PRO_COPY;
+    gp.a = ws + P.act_m;
+    gp.lda = a;
+  }
   gp.W = W;
-  gp.pred_shift = shift;
+  gp.scale_mode = SCALE_RHO;
+  gp.stats_in = xst;
+  gp.stats_tiles = xst_tiles;
+  gp.stats_ld = kMaxRows;
+  gp.scale_n = (float)H;
   gp.epi = EPI_ADD_ROWSCALE;
-  gp.row_scale = rho;
   gp.out = x;
   gp.ldo = H;
+  gp.stats_out = st_out;
+  gp.stats_out_ld = kMaxRows;
   HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
   return DSPINE_OK;
 }
@@ -790,8 +847,18 @@ int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x, 
   if (pred_codes && !aligned16(pred_codes)) return fail(DSPINE_E_ARG, "bridge: pred_codes unaligned");
   if ((rc = check_packed(model))) return rc;
   const Plan P = make_plan(model->g, (int64_t)B * W, 0);
-  rc = run_bridge(*model, layer, B, W, x, anchor_ids, pred_codes, static_cast<char*>(workspace), P, num_cus(),
-                  reinterpret_cast<hipStream_t>(stream));
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* st1 = reinterpret_cast<float*>(ws + P.st1);
+  RowParams rp;
+  memset(&rp, 0, sizeof rp);
+  rp.M = B * W;
+  rp.H = model->g.hidden;
+  rp.x = x;
+  rp.stats = st1;
+  HIP_TRY(launch_rowstats(rp, s));
+  rc = run_bridge(*model, layer, B, W, x, st1, 1, reinterpret_cast<float*>(ws + P.st0), anchor_ids, pred_codes, ws,
+                  P, num_cus(), s);
   return rc ? rc : ok();
 }
 
@@ -818,22 +885,22 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
   const Plan P = make_plan(g, M, 0);
   const int cus = num_cus();
   float* x = reinterpret_cast<float*>(ws + P.x);
-  void* act_h = ws + P.act_h;
   void* act_q = ws + P.act_q;
   void* act_f = ws + P.act_f;
   float* qkv = reinterpret_cast<float*>(ws + P.qkv);
   float* rope = reinterpret_cast<float*>(ws + P.rope);
+  float* st0 = reinterpret_cast<float*>(ws + P.st0);
+  float* st1 = reinterpret_cast<float*>(ws + P.st1);
+  const int tH = stat_tiles(H);
 
-  // a4 + first input norm (+ rotation table of positions F_b + i)
+  // a4: x, its row statistics (one list) and the rotation table of F_b + i
   RowParams rp;
   memset(&rp, 0, sizeof rp);
   rp.M = M;
   rp.W = W;
   rp.H = H;
   rp.x_out = x;
-  rp.act = act_h;
-  rp.gain = wt.layer[0].g_in;
-  rp.eps = g.eps;
+  rp.stats = st1;
   rp.embed = wt.embed;
   for (int b = 0; b < B; ++b) {
     rp.anchor[b] = anchor_ids[b];
@@ -845,30 +912,21 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
   rp.rope_theta = g.rope_theta;
   {
     ProfScope ps(DSPINE_PROF_NORM, stream);
-    HIP_TRY(launch_embed_norm(rp, g.dtype, stream));
+    HIP_TRY(launch_embed(rp, g.dtype, stream));
   }
+  // statistics of the current x: list and its length
+  const float* xst = st1;
+  int xst_tiles = 1;
 
   for (int l = 0; l < g.n_layers; ++l) {
     const dspine_layer_weights& Lw = wt.layer[l];
     const dspine_layer_weights& Pw = model->pw.layer[l];
-    if (l > 0) {
-      RowParams np;
-      memset(&np, 0, sizeof np);
-      np.M = M;
-      np.H = H;
-      np.x = x;
-      np.act = act_h;
-      np.gain = Lw.g_in;
-      np.eps = g.eps;
-      ProfScope ps(DSPINE_PROF_NORM, stream);
-      HIP_TRY(launch_rmsnorm(np, g.dtype, false, stream));
-    }
-    // a5: q | k | v projections of n
+    // a5: q | k | v projections of n = input_norm(x) (norm formed in the GEMM)
     GemmParams gp = gemm_base(P, ws, H, M);
     set_segments(gp, {{Pw.wq, qd}, {Pw.wk, kvd}, {Pw.wv, kvd}});
-    gp.pro = PRO_COPY;
-    gp.a = act_h;
-    gp.lda = H;
+    if ((rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RMSNORM, xst, xst_tiles, (float)H, Lw.g_in, ws + P.act_h,
+                           stream)))
+      return rc;
     gp.epi = EPI_STORE;
     gp.out = qkv;
     gp.ldo = qd + 2 * kvd;
@@ -920,7 +978,7 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
       HIP_TRY(launch_attention(ap, g.dtype, D, stream));
     }
 
-    // a7: y = x + W_o a ; m = norm_post(y)
+    // a7: y = x + W_o a, with the row statistics of y
     gp = gemm_base(P, ws, qd, M);
     set_segments(gp, {{Pw.wo, H}});
     gp.pro = PRO_COPY;
@@ -929,33 +987,23 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
     gp.epi = EPI_ADD;
     gp.out = x;
     gp.ldo = H;
+    gp.stats_out = st0;
+    gp.stats_out_ld = kMaxRows;
     {
       ProfScope ps(DSPINE_PROF_GEMM_O, stream);
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
     }
-    RowParams np;
-    memset(&np, 0, sizeof np);
-    np.M = M;
-    np.H = H;
-    np.x = x;
-    np.act = act_h;
-    np.gain = Lw.g_post;
-    np.eps = g.eps;
-    {
-      ProfScope ps(DSPINE_PROF_NORM, stream);
-      HIP_TRY(launch_rmsnorm(np, g.dtype, false, stream));
-    }
 
-    // a8: x = y + W_down(SiLU(W_gate m) * W_up m)
+    // a8: x = y + W_down(SiLU(W_gate m) * W_up m), m = post_norm(y) formed
+    // in the gate/up GEMM
     gp = gemm_base(P, ws, H, M);
     gp.seg_ptr[0] = Pw.w_gate;
     gp.seg_ptr[1] = Pw.w_up;
     gp.nseg = 2;
     gp.interleave = 1;
     gp.nblk = 2 * (g.ffn / 16);
-    gp.pro = PRO_COPY;
-    gp.a = act_h;
-    gp.lda = H;
+    if ((rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RMSNORM, st0, tH, (float)H, Lw.g_post, ws + P.act_h, stream)))
+      return rc;
     gp.epi = EPI_SWIGLU;
     gp.out_act = act_f;
     gp.ld_act = g.ffn;
@@ -971,16 +1019,21 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
     gp.epi = EPI_ADD;
     gp.out = x;
     gp.ldo = H;
+    gp.stats_out = st1;
+    gp.stats_out_ld = kMaxRows;
     {
       ProfScope ps(DSPINE_PROF_GEMM_DOWN, stream);
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
     }
+    xst = st1;
+    xst_tiles = tH;
 
-    // a9-a11
+    // a9-a11 (statistics of the written rows go to st0)
     if (g.code_dim > 0) {
       ProfScope ps(DSPINE_PROF_BRIDGE, stream);
-      rc = run_bridge(*model, l, B, W, x, anchor_ids, nullptr, ws, P, cus, stream);
+      rc = run_bridge(*model, l, B, W, x, st1, tH, st0, anchor_ids, nullptr, ws, P, cus, stream);
       if (rc) return rc;
+      xst = st0;
     }
   }
   // a12

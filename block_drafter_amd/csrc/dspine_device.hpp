@@ -267,6 +267,18 @@ __device__ __forceinline__ bool block_key_visible(int S, int causal, int i, int 
 // ring slot of a stored position: p mod S for a local layer, p for a full one
 __device__ __forceinline__ int64_t ring_slot(int64_t p, int S) { return S > 0 ? p % S : p; }
 
+// Per-row scale of a row with sum of squares S (the SCALE_* modes of the
+// streamed GEMM and the row pre-scale kernel), rows of width n.
+__device__ __forceinline__ float row_scale(int mode, float S, float n, float eps, float code_scale, bool anchor) {
+  switch (mode) {
+    case 1: return rsqrtf(S / n + eps);                              // plain RMSNorm
+    case 2: return 1.f / (sqrtf(S / n) + eps);                       // bridge read 1/(rho+eps)
+    case 3: return anchor ? 1.f : code_scale / (sqrtf(S) + eps);     // bridge code
+    case 4: return sqrtf(S / n);                                     // rho
+    default: return 1.f;
+  }
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
 

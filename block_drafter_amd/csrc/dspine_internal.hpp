@@ -9,8 +9,26 @@
 namespace dspine {
 
 enum { DT_F32 = DSPINE_F32, DT_BF16 = DSPINE_BF16 };
-enum { PRO_COPY = 0, PRO_GATHER = 1, PRO_BRIDGE_MSG = 2 };
+// A-operand prologues of the streamed GEMM
+enum {
+  PRO_COPY = 0,        // activations as stored (model operand type)
+  PRO_GATHER = 1,      // bf16 target features gathered from several requests
+  PRO_BRIDGE_MSG = 2,  // bridge gate * message from the [G; G_p; A] projections
+  PRO_NORM = 3,        // fp32 rows x per-row scale x per-column gain
+  PRO_SCALE = 4,       // fp32 rows x per-row scale
+};
 enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2, EPI_ADD_ROWSCALE = 3 };
+// per-row scale s[m] formed in the kernel from the sum S of squares of the
+// row (a list of per-tile partial sums), over rows of width n:
+// (the values are the mode numbers of row_scale in dspine_device.hpp)
+enum {
+  SCALE_NONE = 0,
+  SCALE_RMSNORM = 1,   // 1 / sqrt(S / n + eps)              plain RMSNorm
+  SCALE_RHO_INV = 2,   // 1 / (sqrt(S / n) + eps)            bridge read
+  SCALE_CODE = 3,      // sqrt(r) / (sqrt(S) + eps); 1 at anchor rows (m % W == 0)
+  SCALE_RHO = 4,       // sqrt(S / n)                        bridge write
+  SCALE_ONE = 5,       // 1
+};
 
 constexpr int kMaxSeg = 32;        // weight segments of one streamed GEMM
 constexpr int kMaxGrid = 512;      // workgroups of one streamed GEMM
@@ -43,13 +61,25 @@ struct GemmParams {
   const float* Ppred;             //   predecessor-code projections
   const void* bias;               //   [a] model dtype
   int32_t a_dim, W, pred_shift;
+  const float* xa;                // PRO_NORM / PRO_SCALE: fp32 rows, stride lda
+  const void* gain;               // PRO_NORM: [K] model dtype
+  // per-row scale (prologue of PRO_NORM / PRO_SCALE, or EPI_ADD_ROWSCALE)
+  int32_t scale_mode;
+  const float* stats_in;          // [stats_tiles][stats_ld] per-64-column sums of squares
+  int32_t stats_tiles, stats_ld;
+  float scale_n, eps, code_scale;
   // epilogue
   int32_t epi;
   float* out;                     // EPI_STORE / EPI_ADD(_ROWSCALE): fp32 [M, ldo]
   int32_t ldo;
-  const float* row_scale;         // EPI_ADD_ROWSCALE: out[m] += row_scale[m] * acc
   void* out_act;                  // EPI_SWIGLU: model dtype [M, ld_act]
   int32_t ld_act;
+  float* stats_out;               // or NULL: [n / 64][stats_out_ld] sums of squares of the stored rows
+  int32_t stats_out_ld;
+  // EPI_STORE: rows m % W == 0 store code_scale * codebook[anchor[m / W]] instead
+  int32_t code_anchor;
+  const void* codebook;           // [vocab, N] model dtype
+  int32_t anchor[DSPINE_MAX_BATCH];
   // filled by the launcher
   int32_t tiles, ipt, xcd_remap;
   float* partials;
@@ -58,6 +88,8 @@ struct GemmParams {
 hipError_t launch_gemm_stream(const GemmParams& p, int dtype, int num_cus, hipStream_t s);
 size_t gemm_stream_partial_floats(int grid_cap);
 int gemm_stream_grid_cap(int num_cus);
+int gemm_stream_stat_lists(int n_columns);
+int gemm_stream_fused_rows();
 
 // ---------------------------------------------------------------------------
 // tiled MFMA GEMM for many rows (prefill): out[m, n] = sum_k A[m, k] W[n, k]
@@ -118,7 +150,7 @@ struct RowParams {
   float* f32_out;                 // fp32 output (final norm)
   const void* gain;               // [H] model dtype
   float eps;
-  // embed gather
+  // embedding gather
   const void* embed;
   int32_t anchor[DSPINE_MAX_BATCH];
   int32_t mask_id;
@@ -127,19 +159,36 @@ struct RowParams {
   int64_t F[DSPINE_MAX_BATCH];
   int32_t head_dim;
   float rope_theta;
-  // bridge
-  float* rho;                     // [M]
-  const float* z;                 // [M, r]
-  int32_t r;
-  const void* codebook;           // [vocab, r]
-  const float* pred_in;           // [M, r] fp32 override codes
-  void* pred_act;                 // [M, r] model dtype
+  float* stats;                   // [M] sum of squares of each row (one stats tile)
 };
-hipError_t launch_embed_norm(const RowParams& p, int dtype, hipStream_t s);
+// Operand pre-scale for large blocks: act[m, k] = x[m, k] * s[m] (* gain[k]),
+// s[m] from the row's statistics lists; or the bridge message
+// act[t, k] = sigmoid(P[t, k] + Pp[tp, a + k] + b[k]) * Pp[tp, 2a + k]
+// (zero at anchor rows).  act is in the model's operand type.
+struct ScaleParams {
+  int32_t M, K, W;
+  int32_t mode;                   // SCALE_* (scale_rows)
+  const float* stats;             // [lists][ld]
+  int32_t lists, ld;
+  float n, eps, code_scale;
+  const float* x;                 // fp32 [M, ldx]
+  int32_t ldx;
+  const void* gain;               // [K] model dtype, or NULL
+  const float* P;                 // bridge_msg: [M, 3a]
+  const float* Ppred;
+  const void* bias;               // [a] model dtype
+  int32_t pred_shift;
+  void* act;                      // [M, ld_act]
+  int32_t ld_act;
+};
+hipError_t launch_scale_rows(const ScaleParams& p, int dtype, hipStream_t s);
+hipError_t launch_bridge_msg(const ScaleParams& p, int dtype, hipStream_t s);
+
+// a4: x = embedding rows, their sums of squares, and the rotation table
+hipError_t launch_embed(const RowParams& p, int dtype, hipStream_t s);
 hipError_t launch_rmsnorm(const RowParams& p, int dtype, bool f32_output, hipStream_t s);
-hipError_t launch_bridge_read(const RowParams& p, int dtype, hipStream_t s);
-hipError_t launch_bridge_code(const RowParams& p, int dtype, hipStream_t s);
-hipError_t launch_copy_codes(const RowParams& p, int dtype, hipStream_t s);
+// sums of squares of the rows of x (one stats tile)
+hipError_t launch_rowstats(const RowParams& p, hipStream_t s);
 
 struct KvStoreParams {
   int32_t rows, nkv, D, S, n_req;

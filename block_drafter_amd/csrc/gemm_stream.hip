@@ -4,25 +4,36 @@
 //
 // The block has only B*W <= 128 activation rows, so every projection of the
 // draft layers is bound by reading W once from HBM.  Design for gfx950:
-//  * W rows stream straight from HBM into registers as MFMA fragments (16 B
-//    per lane per 32 K) and are double-buffered in registers across
-//    iterations; A (tiny) is staged once per workgroup iteration in LDS and
-//    shared by the four waves.
-//  * Stream-K: the (tile, k-iteration) space is cut into equal contiguous
-//    ranges, one per workgroup, so every CU streams the same number of bytes
-//    whatever N and K are.  A tile split between workgroups is finished by the
-//    last one to arrive (device-scope counter), which adds the published
-//    partials and runs the epilogue: no accumulator buffer needs zeroing and
-//    epilogues (residual add, SwiGLU) stay fused.
 //  * Weights are stored fragment-ordered (see the packing kernel): inside a
 //    16-row block, each 32-wide K step is 64 lane fragments of 16 bytes laid
 //    out contiguously, so every wave load reads 1 KB of consecutive memory.
-//  * Weights are the MFMA A operand (16 rows = 16 output columns n) and the
-//    activations the B operand (16 columns = 16 rows m), so each lane ends up
-//    with 4 consecutive n of one m: 16-byte epilogue stores.
+//    They are the MFMA A operand (16 rows = 16 output columns n); activations
+//    are the B operand (16 columns = 16 rows m), so each lane ends with 4
+//    consecutive n of one m: 16-byte epilogue stores.
+//  * Each wave streams NWB 16-row blocks.  Its weight fragments go through a
+//    ring of PD + 1 register stages: PD iterations are in flight while one is
+//    multiplied.  The activation chunk of an iteration travels in the same
+//    stage as its weights (the vector-memory counter retires in issue order,
+//    so a load issued after the weights could not be waited for alone), and
+//    is staged through LDS for the four waves.
+//  * A tile (4 * NWB blocks) is either streamed over its whole K by one
+//    workgroup (no reduction at all), or, when N has fewer tiles than there
+//    are CUs (one CU alone cannot pull its share of HBM bandwidth), the
+//    (tile, k-iteration) space is cut into equal contiguous ranges
+//    (stream-K).  A tile split between workgroups is finished by the
+//    last one to arrive, which adds the published partials in workgroup
+//    order (bit-reproducible) and runs the epilogue.
+//  * Prologues form the A operand: as stored, gathered bf16 target
+//    features, a row-scaled (and gained) fp32 residual whose norm comes from
+//    per-64-column sums of squares written by the producing GEMM, or the
+//    bridge gate * message.  Epilogues: store, residual add, SwiGLU (gate/up
+//    blocks interleaved), row-scaled add; the stored rows' sums of squares
+//    go out per 64 columns for the next norm.
 //  * Operand types: a BF16 model multiplies FP16 activations by its bf16
 //    weights widened to fp16 in registers (exact); bf16 target features are
 //    used as they are (bf16 x bf16).  A float32 model uses fp32 MFMAs.
+#include <type_traits>
+
 #include "dspine_device.hpp"
 #include "dspine_internal.hpp"
 
@@ -73,32 +84,23 @@ __device__ __forceinline__ const TA* a_row_ptr(const GemmParams& p, int m) {
   }
 }
 
-// PRO_BRIDGE_MSG chunk: A[t, k] = sigmoid(P[t, k] + Pp[tp, a + k] + b[k]) * Pp[tp, 2a + k]
-// for receivers t (zero at anchors); the receiver's rms scales the product
-// in the epilogue.
-template <typename TW, typename TA>
-__device__ __forceinline__ u32x4 bridge_msg_chunk(const GemmParams& p, int m, int k) {
-  constexpr int EPC = 16 / Elt<TA>::kBytes;
-  u32x4 r = {0, 0, 0, 0};
-  if (m >= p.M || k >= p.K || m % p.W == 0) return r;
-  const int tp = p.pred_shift ? m - 1 : m;
-  const int a3 = 3 * p.a_dim;
-  const float* P = p.P + (size_t)m * a3;
-  const float* Pp = p.Ppred + (size_t)tp * a3;
-  const TW* bias = reinterpret_cast<const TW*>(p.bias);
-  TA* out = reinterpret_cast<TA*>(&r);
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) {
-    const int kk = k + e;
-    const float gpre = P[kk] + Pp[p.a_dim + kk] + Elt<TW>::load(bias, kk);
-    Elt<TA>::store(out, e, sigmoid(gpre) * Pp[2 * p.a_dim + kk]);
-  }
-  return r;
+// Per-row scale from the row's sum of squares S (see the SCALE_* modes).
+__device__ __forceinline__ float row_scale_of(const GemmParams& p, int m, float S) {
+  return row_scale(p.scale_mode, S, p.scale_n, p.eps, p.code_scale, m % p.W == 0);
+}
+
+// 16-byte registers one activation chunk (EPC elements) occupies in a stage
+template <int PRO, int EPC>
+constexpr int a_regs() {
+  return PRO == PRO_NORM ? (EPC == 8 ? 3 : 2)           // fp32 x (+ gain)
+       : PRO == PRO_SCALE ? (EPC == 8 ? 2 : 1)          // fp32 x
+       : PRO == PRO_BRIDGE_MSG ? (EPC == 8 ? 7 : 4)     // P, Pp gate, Pp message (fp32) + bias
+       : 1;
 }
 
 }  // namespace
 
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PRO, int EPI>
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   using T = TA;                                 // LDS / MFMA operand type
   constexpr int EB = Elt<TA>::kBytes;
@@ -110,10 +112,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   constexpr int NCH = MP * CPR / 256;           // chunks per thread
   static_assert(NCH >= 1 && (MP * CPR) % 256 == 0, "A tile must split over 256 threads");
   constexpr int WG_BLKS = 4 * NWB;              // 16-row weight blocks per tile
+  constexpr int NST = PD + 1;                   // register stages
+  static_assert(NST >= 1 && NST <= 4, "stages");
+  constexpr int AR = a_regs<PRO, EPC>();
+  constexpr bool kScaledA = PRO == PRO_NORM || PRO == PRO_SCALE;
 
   __shared__ __attribute__((aligned(16))) T lds[2][MP * LDA];
   __shared__ uint32_t s_flag;
   __shared__ SegTable s_seg;
+  __shared__ float s_scale[MP];      // per-row scale (SCALE_* modes)
+  __shared__ float s_red[4][MP];     // per-wave row sums of squares (stats_out)
 
   const int tid = threadIdx.x;
   if (tid < p.nseg) {
@@ -140,29 +148,56 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0, 0, 0, 0};
 
   // per-thread A rows (fixed for the whole kernel)
-  gptr<TA> arow[NCH];
+  const void* arow[NCH];
 #pragma unroll
-  for (int q = 0; q < NCH; ++q) arow[q] = as_global(a_row_ptr<PRO, TA>(p, (tid + q * 256) / CPR));
+  for (int q = 0; q < NCH; ++q) {
+    const int m = (tid + q * 256) / CPR;
+    if constexpr (kScaledA) arow[q] = p.xa + (size_t)(m < p.M ? m : p.M - 1) * p.lda;
+    else if constexpr (PRO == PRO_BRIDGE_MSG) arow[q] = nullptr;
+    else arow[q] = a_row_ptr<PRO, TA>(p, m);
+  }
 
-  Frag<TW> wf0[NWB][KSUB], wf1[NWB][KSUB];
-  u32x4 areg[NCH];
+  Frag<TW> wf[NST][NWB][KSUB];
+  u32x4 areg[NST][NCH][AR];
 
-  // Nothing may consume a prefetched weight fragment before the MFMAs that
-  // need it: a use would make the wave wait for the whole prefetch.  So past
-  // the end of K the weight address is clamped (finite data, in bounds) and
-  // the matching activation chunk is zeroed when it is written to LDS.
-  auto load_iter = [&](int it, Frag<TW> (&wf)[NWB][KSUB]) {
+  // Stage j <- iteration it: activation chunk(s) first, then the weights.
+  // Nothing may consume a prefetched value before it is needed: past the
+  // end of K the addresses are clamped (finite data, in bounds) and the
+  // activation chunk is zeroed when it is written to LDS.
+  auto load_stage = [&](int j, int it) __attribute__((always_inline)) {
     const int tile = it / ipt;
     const int k0 = (it - tile * ipt) * KS;
-    // A tile chunks first: the LDS store waits only for these (older) loads
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
       const int c = tid + q * 256;
       const int k = k0 + (c % CPR) * EPC;
-      if constexpr (PRO == PRO_BRIDGE_MSG) {
-        areg[q] = bridge_msg_chunk<TW, TA>(p, c / CPR, k);
+      const int kc = k < p.K ? k : p.K - EPC;
+      if constexpr (kScaledA) {
+        const gptr<float> x = as_global(reinterpret_cast<const float*>(arow[q])) + kc;
+        areg[j][q][0] = gload16((gptr<void>)x);
+        if constexpr (EPC == 8) areg[j][q][1] = gload16((gptr<void>)(x + 4));
+        if constexpr (PRO == PRO_NORM)
+          areg[j][q][AR - 1] = gload16((gptr<void>)(as_global(reinterpret_cast<const TW*>(p.gain)) + kc));
+      } else if constexpr (PRO == PRO_BRIDGE_MSG) {
+        // A[t, k] = sigmoid(P[t, k] + Pp[tp, a + k] + b[k]) * Pp[tp, 2a + k]
+        int m = c / CPR;
+        m = m < p.M ? m : p.M - 1;
+        int tp = p.pred_shift ? m - 1 : m;
+        tp = tp < 0 ? 0 : tp;
+        const int a3 = 3 * p.a_dim;
+        const gptr<float> P = as_global(p.P) + (size_t)m * a3 + kc;
+        const gptr<float> Pg = as_global(p.Ppred) + (size_t)tp * a3 + p.a_dim + kc;
+        const gptr<float> Pm = as_global(p.Ppred) + (size_t)tp * a3 + 2 * p.a_dim + kc;
+        constexpr int H4 = EPC / 4;                // 16-byte pieces of EPC floats
+#pragma unroll
+        for (int h = 0; h < H4; ++h) {
+          areg[j][q][h] = gload16((gptr<void>)(P + 4 * h));
+          areg[j][q][H4 + h] = gload16((gptr<void>)(Pg + 4 * h));
+          areg[j][q][2 * H4 + h] = gload16((gptr<void>)(Pm + 4 * h));
+        }
+        areg[j][q][3 * H4] = gload16((gptr<void>)(as_global(reinterpret_cast<const TW*>(p.bias)) + kc));
       } else {
-        areg[q] = gload16((gptr<void>)(arow[q] + (k < p.K ? k : p.K - EPC)));
+        areg[j][q][0] = gload16((gptr<void>)(as_global(reinterpret_cast<const TA*>(arow[q])) + kc));
       }
     }
 #pragma unroll
@@ -173,26 +208,66 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 #pragma unroll
       for (int s = 0; s < KSUB; ++s) {
         const int ks = k0 / 32 + s;
-        wf[nb][s].gload(wr + (size_t)(ks < p.K / 32 ? ks : p.K / 32 - 1) * 512);
+        wf[j][nb][s].gload(wr + (size_t)(ks < p.K / 32 ? ks : p.K / 32 - 1) * 512);
       }
     }
   };
-  auto store_a = [&](int buf, int it) {
+  // activation chunk of stage j (iteration it) -> LDS buffer buf
+  auto store_a = [&](int buf, int j, int it) __attribute__((always_inline)) {
     const int k0 = (it - (it / ipt) * ipt) * KS;
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
       const int c = tid + q * 256;
+      const int m = c / CPR;
       const int k = k0 + (c % CPR) * EPC;
-      *reinterpret_cast<u32x4*>(&lds[buf][(c / CPR) * LDA + (c % CPR) * EPC]) =
-          k < p.K ? areg[q] : u32x4{0, 0, 0, 0};
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if constexpr (kScaledA) {
+        if (k < p.K) {
+          const float sc = s_scale[m];
+          alignas(16) float xv[EPC];
+          *reinterpret_cast<u32x4*>(&xv[0]) = areg[j][q][0];
+          if constexpr (EPC == 8) *reinterpret_cast<u32x4*>(&xv[4]) = areg[j][q][1];
+          alignas(16) TW gv[EPC];
+          if constexpr (PRO == PRO_NORM) *reinterpret_cast<u32x4*>(gv) = areg[j][q][AR - 1];
+          alignas(16) T tv[EPC];
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            const float gn = (PRO == PRO_NORM) ? Elt<TW>::load(gv, e) : 1.f;
+            Elt<T>::store(tv, e, xv[e] * sc * gn);
+          }
+          v = *reinterpret_cast<const u32x4*>(tv);
+        }
+      } else if constexpr (PRO == PRO_BRIDGE_MSG) {
+        // receivers only: zero at anchors (m % W == 0) and past M / K
+        if (k < p.K && m < p.M && m % p.W != 0) {
+          constexpr int H4 = EPC / 4;
+          alignas(16) float P[EPC], Pg[EPC], Pm[EPC];
+#pragma unroll
+          for (int h = 0; h < H4; ++h) {
+            *reinterpret_cast<u32x4*>(&P[4 * h]) = areg[j][q][h];
+            *reinterpret_cast<u32x4*>(&Pg[4 * h]) = areg[j][q][H4 + h];
+            *reinterpret_cast<u32x4*>(&Pm[4 * h]) = areg[j][q][2 * H4 + h];
+          }
+          alignas(16) TW bv[EPC];
+          *reinterpret_cast<u32x4*>(bv) = areg[j][q][3 * H4];
+          alignas(16) T tv[EPC];
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            Elt<T>::store(tv, e, sigmoid(P[e] + Pg[e] + Elt<TW>::load(bv, e)) * Pm[e]);
+          v = *reinterpret_cast<const u32x4*>(tv);
+        }
+      } else {
+        v = k < p.K ? areg[j][q][0] : u32x4{0, 0, 0, 0};
+      }
+      *reinterpret_cast<u32x4*>(&lds[buf][m * LDA + (c % CPR) * EPC]) = v;
     }
   };
-  auto compute = [&](int buf, Frag<TW> (&wf)[NWB][KSUB]) {
+  auto compute = [&](int buf, int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       Frag<T> wo[NWB];
 #pragma unroll
-      for (int nb = 0; nb < NWB; ++nb) wo[nb] = AsOperand<T, TW>::cvt(wf[nb][s]);
+      for (int nb = 0; nb < NWB; ++nb) wo[nb] = AsOperand<T, TW>::cvt(wf[j][nb][s]);
 #pragma unroll
       for (int mb = 0; mb < MT; ++mb) {
         Frag<T> af;
@@ -204,13 +279,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   };
 
   // Finish tile `tile` whose iterations [kb, ke) this workgroup has accumulated.
-  auto finish = [&](int tile, int kb, int ke) {
+  auto finish = [&](int tile, int kb, int ke) __attribute__((always_inline)) {
     if (!(kb == 0 && ke == ipt)) {
       const int t0 = tile * ipt;
       const int g_first = owner_of(t0, TI, G);
       const int g_last = owner_of(t0 + ipt - 1, TI, G);
       const int ncontrib = g_last - g_first + 1;
-      auto slot_of = [&](int gg) {
+      auto slot_of = [&](int gg) __attribute__((always_inline)) {
         const int first_tile = iter_begin(gg, TI, G) / ipt;
         return 2 * gg + (first_tile == tile ? 0 : 1);
       };
@@ -283,6 +358,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
         }
       }
     } else {
+      float sq[MT];
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb) sq[mb] = 0.f;
 #pragma unroll
       for (int nb = 0; nb < NWB; ++nb) {
         const int vb = tile * WG_BLKS + wave * NWB + nb;
@@ -292,10 +370,48 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
           const int m = mb * 16 + (lane & 15);
           if (m >= p.M) continue;
           f32x4* o = reinterpret_cast<f32x4*>(p.out + (size_t)m * p.ldo + vb * 16 + nl);
-          if constexpr (EPI == EPI_ADD) *o = *o + acc[nb][mb];
-          else if constexpr (EPI == EPI_ADD_ROWSCALE) *o = *o + p.row_scale[m] * acc[nb][mb];
-          else *o = acc[nb][mb];
+          f32x4 val;
+          if constexpr (EPI == EPI_ADD) {
+            val = *o + acc[nb][mb];
+          } else if constexpr (EPI == EPI_ADD_ROWSCALE) {
+            val = *o + s_scale[m] * acc[nb][mb];
+          } else {
+            val = acc[nb][mb];
+            if (p.code_anchor && m % p.W == 0) {      // anchor code: sqrt(r) C[anchor]
+              const gptr<TW> cb = as_global(reinterpret_cast<const TW*>(p.codebook)) +
+                                  (size_t)p.anchor[m / p.W] * p.ldo + vb * 16 + nl;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) val[v] = p.code_scale * Elt<TW>::gload(cb, v);
+            }
+          }
+          *o = val;
+          sq[mb] += ((val[0] * val[0] + val[1] * val[1]) + val[2] * val[2]) + val[3] * val[3];
         }
+      }
+      // Sums of squares per row over each 64 output columns, in a fixed
+      // order: lane values, the four lane groups, then the waves of the list.
+      if (p.stats_out != nullptr) {
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) {
+          sq[mb] += __shfl_xor(sq[mb], 16, 64);
+          sq[mb] += __shfl_xor(sq[mb], 32, 64);
+          if (lane < 16) s_red[wave][mb * 16 + lane] = sq[mb];
+        }
+        __syncthreads();
+        constexpr int WPL = 4 / NWB;                   // waves per 64-column list
+        const int nlists = (p.nblk + 3) / 4;
+        if (tid < p.M) {
+#pragma unroll
+          for (int jl = 0; jl < NWB; ++jl) {
+            const int list = tile * NWB + jl;
+            if (list >= nlists) break;
+            float sum = s_red[jl * WPL][tid];
+#pragma unroll
+            for (int w = 1; w < WPL; ++w) sum += s_red[jl * WPL + w][tid];
+            p.stats_out[(size_t)list * p.stats_out_ld + tid] = sum;
+          }
+        }
+        __syncthreads();
       }
     }
 #pragma unroll
@@ -304,56 +420,137 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0, 0, 0, 0};
   };
 
-  // prologue: first iteration's data
-  load_iter(it_beg, wf0);
-  store_a(0, it_beg);
+  // prologue: the per-row scales and the first NST iterations.  A row's
+  // statistics lists are split over Q = 256 / MP threads (thread jq takes
+  // lists jq, jq + Q, ...) and the Q partial sums are added in order, so the
+  // sum does not depend on timing.  The first batch of statistics loads goes
+  // out before the weight stages, so that waiting for it does not wait for
+  // the weights (the memory counter retires in issue order).
+  constexpr int Q = 256 / MP;
+  constexpr int LB = 8;                             // statistics loads per batch
+  const bool scaled = p.scale_mode != SCALE_NONE && p.scale_mode != SCALE_ONE;
+  const int sm = tid % MP, sq0 = tid / MP;
+  const gptr<float> st = as_global(p.stats_in) + (sm < p.M ? sm : 0);
+  float sv[LB];
+  if (scaled) {
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int t = sq0 + u * Q;
+      sv[u] = st[(size_t)(t < p.stats_tiles ? t : 0) * p.stats_ld];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NST; ++j) load_stage(j, it_beg + j < it_end ? it_beg + j : it_end - 1);
+  if (p.scale_mode == SCALE_ONE) {
+    if (tid < MP) s_scale[tid] = 1.f;
+    __syncthreads();
+  } else if (scaled) {
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < LB; ++u)
+      if (sq0 + u * Q < p.stats_tiles) part += sv[u];
+    for (int t0 = sq0 + LB * Q; t0 < p.stats_tiles; t0 += LB * Q) {    // large M only
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int t = t0 + u * Q;
+        sv[u] = st[(size_t)(t < p.stats_tiles ? t : 0) * p.stats_ld];
+      }
+#pragma unroll
+      for (int u = 0; u < LB; ++u)
+        if (t0 + u * Q < p.stats_tiles) part += sv[u];
+    }
+    float* s_part = reinterpret_cast<float*>(lds[1]);  // [Q][MP], free until the first step
+    s_part[sq0 * MP + sm] = part;
+    __syncthreads();
+    if (tid < MP) {
+      float S = 0.f;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) S += s_part[q * MP + tid];
+      s_scale[tid] = tid < p.M ? row_scale_of(p, tid, S) : 0.f;
+    }
+    __syncthreads();
+  }
+  store_a(0, 0, it_beg);
   __syncthreads();
 
-  // Stream the workgroup's range.  The register prefetch of iteration it+1
-  // overlaps the MFMAs of iteration it; two iterations per trip so that the
-  // two register buffers swap statically.  A tile is finished when its last
-  // iteration in this range has been accumulated.
+  // Stream the workgroup's range.  Step `it` uses stage it % NST: multiply,
+  // finish a tile whose last iteration this was, stage the next iteration's
+  // activations, then refill the stage with iteration it + NST (clamped to
+  // the range: a re-read of data this wave just fetched, an L2 hit).  The
+  // loop is unrolled over the stages so that every register index is static.
   int it = it_beg;
   int buf = 0;
   int seg_k0 = it_beg % ipt;
-  // The prefetch is issued on every iteration (the last one re-reads its own
-  // data, which sits in L2): with the same number of loads in flight on every
-  // path, the wait before the MFMAs covers exactly the previous iteration.
-  auto step = [&](Frag<TW> (&cur)[NWB][KSUB], Frag<TW> (&nxt)[NWB][KSUB]) -> bool {
+  auto step = [&](auto J) __attribute__((always_inline)) -> bool {
+    constexpr int j = decltype(J)::value;
+    constexpr int jn = (j + 1) % NST;
     const bool has_next = it + 1 < it_end;
-    const int it_next = has_next ? it + 1 : it;
-    load_iter(it_next, nxt);
-    compute(buf, cur);
+    compute(buf, j);
     const int tile = it / ipt;
     const int kk = it - tile * ipt;
     if (!has_next || kk == ipt - 1) {
       finish(tile, seg_k0, kk + 1);
       seg_k0 = 0;
     }
-    store_a(buf ^ 1, it_next);
+    if (!has_next) return false;
+    store_a(buf ^ 1, jn, it + 1);
+    load_stage(j, it + NST < it_end ? it + NST : it_end - 1);
     __syncthreads();
     buf ^= 1;
     ++it;
-    return has_next;
+    return true;
   };
   while (true) {
-    if (!step(wf0, wf1)) break;
-    if (!step(wf1, wf0)) break;
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if constexpr (NST > 1) {
+      if (!step(std::integral_constant<int, 1 % NST>{})) break;
+    }
+    if constexpr (NST > 2) {
+      if (!step(std::integral_constant<int, 2 % NST>{})) break;
+    }
+    if constexpr (NST > 3) {
+      if (!step(std::integral_constant<int, 3 % NST>{})) break;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PRO, int EPI>
-static hipError_t launch_t(GemmParams p, int grid_cap, hipStream_t s) {
+// Stream-K and whole-K tiles both assume every workgroup of the grid is
+// resident at once: the grid is capped at what the kernel's occupancy
+// allows on all CUs.
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI>
+static int resident_cap(int grid_cap, int num_cus) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI>,
+                                                      256, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  const int cap = per_cu * num_cus;
+  return cap < grid_cap ? cap : grid_cap;
+}
+
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI>
+static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t s) {
+  static_assert(NWB == 1 || NWB == 2, "tile widths");
   constexpr int KS = 32 * KSUB;
+  grid_cap = resident_cap<TW, TA, MT, NWB, KSUB, PD, PRO, EPI>(grid_cap, num_cus);
   p.ipt = (p.K + KS - 1) / KS;
   p.tiles = (p.nblk + 4 * NWB - 1) / (4 * NWB);
   const int64_t TI = (int64_t)p.tiles * p.ipt;
-  int G = (int)(TI < grid_cap ? TI : grid_cap);
+  // One CU streams only about 25 GB/s, so every CU must take part: whole-K
+  // tiles only when there are at least as many tiles as CUs (and all fit at
+  // once); otherwise stream-K over the resident grid.
+  int G;
+  if (p.tiles <= grid_cap && p.tiles >= num_cus) G = p.tiles;
+  else G = (int)(TI < grid_cap ? TI : grid_cap);
   p.xcd_remap = (G % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PRO, EPI>), dim3(G), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI>), dim3(G), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -364,40 +561,69 @@ size_t gemm_stream_partial_floats(int grid_cap) {
   return (size_t)2 * grid_cap * (2 * 8 * 256 * 4);
 }
 
+// statistics lists a GEMM of N output columns writes (one per 64 columns)
+int gemm_stream_stat_lists(int n) { return (n + 63) / 64; }
+
+// largest M whose prologues form scaled operands themselves
+int gemm_stream_fused_rows() { return 32; }
+
+// Tile shape and pipeline depth per row-tile count: a wave keeps about 32 KB
+// of weights in flight when M is small; large M spends its registers on the
+// accumulators and the activation stages instead.
 template <typename TW, typename TA, int PRO, int EPI>
-static hipError_t launch_mt(const GemmParams& p, int grid_cap, hipStream_t s) {
+static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipStream_t s) {
   const int mt = (p.M + 15) / 16;
   constexpr bool kHalf = Elt<TA>::kBytes == 2;
-  if (mt <= 1) return launch_t<TW, TA, 1, 2, kHalf ? 8 : 4, PRO, EPI>(p, grid_cap, s);
-  if (mt <= 2) return launch_t<TW, TA, 2, 2, kHalf ? 8 : 4, PRO, EPI>(p, grid_cap, s);
-  if (mt <= 4) return launch_t<TW, TA, 4, 2, kHalf ? 4 : 2, PRO, EPI>(p, grid_cap, s);
-  return launch_t<TW, TA, 8, 2, kHalf ? 4 : 1, PRO, EPI>(p, grid_cap, s);
+  constexpr int NWB1 = EPI == EPI_SWIGLU ? 2 : 1;   // narrow tiles: more of them
+  constexpr int PD_SMALL = PRO == PRO_BRIDGE_MSG ? 1 : (NWB1 == 2 ? 2 : 3);
+  if (mt <= 1) return launch_t<TW, TA, 1, NWB1, kHalf ? 8 : 4, PD_SMALL, PRO, EPI>(p, grid_cap, num_cus, s);
+  if (mt <= 2) return launch_t<TW, TA, 2, NWB1, kHalf ? 8 : 4, PD_SMALL, PRO, EPI>(p, grid_cap, num_cus, s);
+  if constexpr (PRO == PRO_COPY || PRO == PRO_GATHER) {
+    // 64 and 128 rows take pre-scaled operands (the launcher's caller forms
+    // them), in 128-column tiles so that each staged activation chunk feeds
+    // twice the weights
+    if (mt <= 4) return launch_t<TW, TA, 4, 2, kHalf ? 4 : 2, 1, PRO, EPI>(p, grid_cap, num_cus, s);
+    return launch_t<TW, TA, 8, 2, kHalf ? 4 : 1, 1, PRO, EPI>(p, grid_cap, num_cus, s);
+  }
+  return hipErrorInvalidValue;
 }
 
+// The (prologue, epilogue) pairs the hot path uses.
 template <typename TW, typename TA>
-static hipError_t launch_kind(const GemmParams& p, int grid_cap, hipStream_t s) {
-  if (p.pro == PRO_BRIDGE_MSG) {
-    if (p.epi != EPI_ADD_ROWSCALE) return hipErrorInvalidValue;
-    return launch_mt<TW, TA, PRO_BRIDGE_MSG, EPI_ADD_ROWSCALE>(p, grid_cap, s);
+static hipError_t launch_kind(const GemmParams& p, int grid_cap, int num_cus, hipStream_t s) {
+  switch (p.pro) {
+    case PRO_BRIDGE_MSG:
+      if (p.epi == EPI_ADD_ROWSCALE)
+        return launch_mt<TW, TA, PRO_BRIDGE_MSG, EPI_ADD_ROWSCALE>(p, grid_cap, num_cus, s);
+      break;
+    case PRO_COPY:
+      if (p.epi == EPI_STORE) return launch_mt<TW, TA, PRO_COPY, EPI_STORE>(p, grid_cap, num_cus, s);
+      if (p.epi == EPI_ADD) return launch_mt<TW, TA, PRO_COPY, EPI_ADD>(p, grid_cap, num_cus, s);
+      if (p.epi == EPI_SWIGLU) return launch_mt<TW, TA, PRO_COPY, EPI_SWIGLU>(p, grid_cap, num_cus, s);
+      if (p.epi == EPI_ADD_ROWSCALE) return launch_mt<TW, TA, PRO_COPY, EPI_ADD_ROWSCALE>(p, grid_cap, num_cus, s);
+      break;
+    case PRO_NORM:
+      if (p.epi == EPI_STORE) return launch_mt<TW, TA, PRO_NORM, EPI_STORE>(p, grid_cap, num_cus, s);
+      if (p.epi == EPI_SWIGLU) return launch_mt<TW, TA, PRO_NORM, EPI_SWIGLU>(p, grid_cap, num_cus, s);
+      break;
+    case PRO_SCALE:
+      if (p.epi == EPI_STORE) return launch_mt<TW, TA, PRO_SCALE, EPI_STORE>(p, grid_cap, num_cus, s);
+      break;
+    default:
+      break;
   }
-  if (p.pro != PRO_COPY) return hipErrorInvalidValue;
-  switch (p.epi) {
-    case EPI_STORE: return launch_mt<TW, TA, PRO_COPY, EPI_STORE>(p, grid_cap, s);
-    case EPI_ADD: return launch_mt<TW, TA, PRO_COPY, EPI_ADD>(p, grid_cap, s);
-    case EPI_SWIGLU: return launch_mt<TW, TA, PRO_COPY, EPI_SWIGLU>(p, grid_cap, s);
-    default: return hipErrorInvalidValue;
-  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_stream(const GemmParams& p, int dtype, int num_cus, hipStream_t s) {
   const int grid_cap = gemm_stream_grid_cap(num_cus);
   if (p.pro == PRO_GATHER) {          // target features, stored output only
     if (p.epi != EPI_STORE) return hipErrorInvalidValue;
-    if (dtype == DT_BF16) return launch_mt<bf16_t, bf16_t, PRO_GATHER, EPI_STORE>(p, grid_cap, s);
-    return launch_mt<float, float, PRO_GATHER, EPI_STORE>(p, grid_cap, s);
+    if (dtype == DT_BF16) return launch_mt<bf16_t, bf16_t, PRO_GATHER, EPI_STORE>(p, grid_cap, num_cus, s);
+    return launch_mt<float, float, PRO_GATHER, EPI_STORE>(p, grid_cap, num_cus, s);
   }
-  if (dtype == DT_BF16) return launch_kind<bf16_t, f16_t>(p, grid_cap, s);
-  return launch_kind<float, float>(p, grid_cap, s);
+  if (dtype == DT_BF16) return launch_kind<bf16_t, f16_t>(p, grid_cap, num_cus, s);
+  return launch_kind<float, float>(p, grid_cap, num_cus, s);
 }
 
 }  // namespace dspine

@@ -1,5 +1,6 @@
-// Row-wise kernels: input gather + norms (a4, a5 head, a7 norm, a12), the
-// bridge's read and code steps (a9), and the context K/V store epilogue (a2).
+// Row-wise kernels: the block input gather (a4), plain RMSNorm (a12 and the
+// context norm of long materialize blocks), row statistics, and the context
+// K/V store epilogue (a2).
 // One workgroup per row; statistics in fp32.
 #include <algorithm>
 
@@ -21,28 +22,25 @@ __device__ __forceinline__ void rope_pair(int64_t pos, int j, int D, float theta
   s = (float)sd;
 }
 
-// a4 + layer 0's input norm: x[m] = embed[token(m)], act[m] = g_in * x / rms(x).
-// [NIF, draft input]: row 0 of each request is the anchor, rows 1..W-1 the
-// mask token.  Side job: the rotation table of every row's position F + i.
+// a4 [NIF, draft input]: x[m] = embed[token(m)], row 0 of each request the
+// anchor and rows 1..W-1 the mask token.  Also the row's sum of squares (one
+// statistics tile, from which the first input norm is formed in the QKV
+// projection) and the rotation table of the row's position F + i.
 template <typename T>
-__global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const RowParams p) {
+__global__ __launch_bounds__(kRowThreads) void embed_kernel(const RowParams p) {
   __shared__ float red[kRowThreads / 64];
   const int m = blockIdx.x, b = m / p.W, i = m % p.W;
   const int tok = i == 0 ? p.anchor[b] : p.mask_id;
-  const T* e = reinterpret_cast<const T*>(p.embed) + (size_t)tok * p.H;
+  const gptr<T> e = as_global(reinterpret_cast<const T*>(p.embed)) + (size_t)tok * p.H;
   float ss = 0.f;
+#pragma unroll 4
   for (int k = threadIdx.x; k < p.H; k += kRowThreads) {
-    const float v = Elt<T>::load(e, k);
+    const float v = Elt<T>::gload(e, k);
     p.x_out[(size_t)m * p.H + k] = v;
     ss += v * v;
   }
   ss = block_sum<kRowThreads>(ss, red);
-  const float inv = rsqrtf(ss / p.H + p.eps);
-  using TA = typename ActOf<T>::type;
-  const T* gw = reinterpret_cast<const T*>(p.gain);
-  TA* act = reinterpret_cast<TA*>(p.act);
-  for (int k = threadIdx.x; k < p.H; k += kRowThreads)
-    Elt<TA>::store(act, (size_t)m * p.H + k, Elt<T>::load(e, k) * inv * Elt<T>::load(gw, k));
+  if (threadIdx.x == 0) p.stats[m] = ss;
   for (int j = threadIdx.x; j < p.head_dim / 2; j += kRowThreads) {
     float c, s;
     rope_pair(p.F[b] + i, j, p.head_dim, p.rope_theta, c, s);
@@ -51,74 +49,90 @@ __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const RowParams
   }
 }
 
+// Sum of squares of each row of x (one statistics tile): the bridge called
+// on its own receives x without statistics.
+__global__ __launch_bounds__(kRowThreads) void rowstats_kernel(const RowParams p) {
+  __shared__ float red[kRowThreads / 64];
+  const int m = blockIdx.x;
+  const gptr<float> x = as_global(p.x) + (size_t)m * p.H;
+  float ss = 0.f;
+#pragma unroll 4
+  for (int k = threadIdx.x; k < p.H; k += kRowThreads) ss += x[k] * x[k];
+  ss = block_sum<kRowThreads>(ss, red);
+  if (threadIdx.x == 0) p.stats[m] = ss;
+}
+
+// act[m, k] = x[m, k] * s[m] (* gain[k]) in the operand type.  One wave per
+// row forms s[m] from the row's statistics lists (a fixed split over lanes
+// and a fixed reduction order); grid (column blocks of 2048, rows).
+template <typename T>
+__global__ __launch_bounds__(256) void scale_rows_kernel(const ScaleParams p) {
+  __shared__ float s_row;
+  const int m = blockIdx.y;
+  if (threadIdx.x < 64) {
+    float v = 0.f;
+    if (p.mode != SCALE_ONE)
+      for (int t = threadIdx.x; t < p.lists; t += 64) v += p.stats[(size_t)t * p.ld + m];
+    v = wave_sum(v);
+    if (threadIdx.x == 0)
+      s_row = p.mode == SCALE_ONE ? 1.f : row_scale(p.mode, v, p.n, p.eps, p.code_scale, m % p.W == 0);
+  }
+  __syncthreads();
+  const float sc = s_row;
+  using TA = typename ActOf<T>::type;
+  constexpr int EPC = 8;
+  const int k = (blockIdx.x * 256 + threadIdx.x) * EPC;
+  if (k >= p.K) return;
+  const gptr<float> x = as_global(p.x) + (size_t)m * p.ldx + k;
+  const gptr<T> gn = as_global(reinterpret_cast<const T*>(p.gain)) + k;
+  TA* out = reinterpret_cast<TA*>(p.act) + (size_t)m * p.ld_act + k;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) {
+    const float g = p.gain ? Elt<T>::gload(gn, e) : 1.f;
+    Elt<TA>::store(out, e, x[e] * sc * g);
+  }
+}
+
+// act[t, k] = sigmoid(P[t, k] + Pp[tp, a + k] + b[k]) * Pp[tp, 2a + k] for
+// receiver rows t (tp = t - 1, or t with an override), zero at anchor rows
+// [FLZ, "The bridge"]; grid (column blocks of 256, rows).
+template <typename T>
+__global__ __launch_bounds__(256) void bridge_msg_kernel(const ScaleParams p) {
+  const int m = blockIdx.y;
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= p.K) return;
+  using TA = typename ActOf<T>::type;
+  TA* out = reinterpret_cast<TA*>(p.act) + (size_t)m * p.ld_act;
+  if (m % p.W == 0) {
+    Elt<TA>::store(out, k, 0.f);
+    return;
+  }
+  const int tp = p.pred_shift ? m - 1 : m;
+  const int a = p.K, a3 = 3 * p.K;
+  const float gpre = p.P[(size_t)m * a3 + k] + p.Ppred[(size_t)tp * a3 + a + k] +
+                     Elt<T>::load(reinterpret_cast<const T*>(p.bias), k);
+  Elt<TA>::store(out, k, sigmoid(gpre) * p.Ppred[(size_t)tp * a3 + 2 * a + k]);
+}
+
 // plain_rmsnorm [NIF]: out = g * x / sqrt(mean(x^2) + eps); out in the model
 // dtype (GEMM operand) or fp32 (final hidden states).
 template <typename T, bool F32OUT>
 __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const RowParams p) {
   __shared__ float red[kRowThreads / 64];
   const int m = blockIdx.x;
-  const float* x = p.x + (size_t)m * p.H;
+  const gptr<float> x = as_global(p.x) + (size_t)m * p.H;
   float ss = 0.f;
+#pragma unroll 4
   for (int k = threadIdx.x; k < p.H; k += kRowThreads) ss += x[k] * x[k];
   ss = block_sum<kRowThreads>(ss, red);
   const float inv = rsqrtf(ss / p.H + p.eps);
-  const T* gw = reinterpret_cast<const T*>(p.gain);
+  const gptr<T> gw = as_global(reinterpret_cast<const T*>(p.gain));
+#pragma unroll 4
   for (int k = threadIdx.x; k < p.H; k += kRowThreads) {
-    const float v = x[k] * inv * Elt<T>::load(gw, k);
+    const float v = x[k] * inv * Elt<T>::gload(gw, k);
     if (F32OUT) p.f32_out[(size_t)m * p.H + k] = v;
     else Elt<typename ActOf<T>::type>::store(reinterpret_cast<typename ActOf<T>::type*>(p.act), (size_t)m * p.H + k, v);
   }
-}
-
-// a9, first half [FLZ, "The bridge"]: rho_t = sqrt(mean(x_t^2)) (no floor)
-// and the read input x_t / (rho_t + eps) in the GEMM operand type.
-template <typename T>
-__global__ __launch_bounds__(kRowThreads) void bridge_read_kernel(const RowParams p) {
-  __shared__ float red[kRowThreads / 64];
-  const int m = blockIdx.x;
-  const float* x = p.x + (size_t)m * p.H;
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < p.H; k += kRowThreads) ss += x[k] * x[k];
-  ss = block_sum<kRowThreads>(ss, red);
-  const float rho = sqrtf(ss / p.H);
-  if (threadIdx.x == 0) p.rho[m] = rho;
-  const float inv = 1.f / (rho + p.eps);
-  using TA = typename ActOf<T>::type;
-  TA* act = reinterpret_cast<TA*>(p.act);
-  for (int k = threadIdx.x; k < p.H; k += kRowThreads) Elt<TA>::store(act, (size_t)m * p.H + k, x[k] * inv);
-}
-
-// a9, second half: c_t = sqrt(r) z_t / (||z_t||_2 + eps); the anchor row of
-// every request takes sqrt(r) C[anchor] instead [FLZ, "The bridge"].
-template <typename T>
-__global__ __launch_bounds__(kRowThreads) void bridge_code_kernel(const RowParams p) {
-  __shared__ float red[kRowThreads / 64];
-  const int m = blockIdx.x, b = m / p.W, i = m % p.W;
-  const float sr = sqrtf((float)p.r);
-  using TA = typename ActOf<T>::type;
-  TA* act = reinterpret_cast<TA*>(p.act);
-  if (i == 0) {
-    const T* cb = reinterpret_cast<const T*>(p.codebook) + (size_t)p.anchor[b] * p.r;
-    for (int k = threadIdx.x; k < p.r; k += kRowThreads)
-      Elt<TA>::store(act, (size_t)m * p.r + k, sr * Elt<T>::load(cb, k));
-    return;
-  }
-  const float* z = p.z + (size_t)m * p.r;
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < p.r; k += kRowThreads) ss += z[k] * z[k];
-  ss = block_sum<kRowThreads>(ss, red);
-  const float scale = sr / (sqrtf(ss) + p.eps);
-  for (int k = threadIdx.x; k < p.r; k += kRowThreads) Elt<TA>::store(act, (size_t)m * p.r + k, z[k] * scale);
-}
-
-// caller-supplied predecessor codes (fp32) -> GEMM operand type
-template <typename T>
-__global__ __launch_bounds__(kRowThreads) void copy_codes_kernel(const RowParams p) {
-  const int m = blockIdx.x;
-  using TA = typename ActOf<T>::type;
-  TA* act = reinterpret_cast<TA*>(p.pred_act);
-  for (int k = threadIdx.x; k < p.r; k += kRowThreads)
-    Elt<TA>::store(act, (size_t)m * p.r + k, p.pred_in[(size_t)m * p.r + k]);
 }
 
 // a2 epilogue for one draft layer [NIF, context K/V; fused context
@@ -226,8 +240,8 @@ __global__ void debug_visible_kernel(const VisibleParams p) {
     else hipLaunchKernelGGL((KERNEL<float>), __VA_ARGS__);                                \
   } while (0)
 
-hipError_t launch_embed_norm(const RowParams& p, int dtype, hipStream_t s) {
-  DSPINE_DISPATCH(dtype, embed_norm_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
+hipError_t launch_embed(const RowParams& p, int dtype, hipStream_t s) {
+  DSPINE_DISPATCH(dtype, embed_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
   return hipGetLastError();
 }
 hipError_t launch_rmsnorm(const RowParams& p, int dtype, bool f32_output, hipStream_t s) {
@@ -240,16 +254,17 @@ hipError_t launch_rmsnorm(const RowParams& p, int dtype, bool f32_output, hipStr
   }
   return hipGetLastError();
 }
-hipError_t launch_bridge_read(const RowParams& p, int dtype, hipStream_t s) {
-  DSPINE_DISPATCH(dtype, bridge_read_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
+hipError_t launch_scale_rows(const ScaleParams& p, int dtype, hipStream_t s) {
+  if (p.K % 8) return hipErrorInvalidValue;
+  DSPINE_DISPATCH(dtype, scale_rows_kernel, dim3((p.K / 8 + 255) / 256, p.M), dim3(256), 0, s, p);
   return hipGetLastError();
 }
-hipError_t launch_bridge_code(const RowParams& p, int dtype, hipStream_t s) {
-  DSPINE_DISPATCH(dtype, bridge_code_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
+hipError_t launch_bridge_msg(const ScaleParams& p, int dtype, hipStream_t s) {
+  DSPINE_DISPATCH(dtype, bridge_msg_kernel, dim3((p.K + 255) / 256, p.M), dim3(256), 0, s, p);
   return hipGetLastError();
 }
-hipError_t launch_copy_codes(const RowParams& p, int dtype, hipStream_t s) {
-  DSPINE_DISPATCH(dtype, copy_codes_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
+hipError_t launch_rowstats(const RowParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(rowstats_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
   return hipGetLastError();
 }
 hipError_t launch_kv_store(const KvStoreParams& p, int dtype, hipStream_t s) {
