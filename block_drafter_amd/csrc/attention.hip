@@ -6,13 +6,20 @@
 // [NIF, draft attention]: the mask keeps |p_key - p_query| < S on local
 // layers; block keys are all visible (bidirectional) unless block_causal.
 //
-// Layout on gfx950: one workgroup per (key split, KV head, request), one
-// wave per query head of the GQA group, so every K/V tile staged in LDS is
-// used by all heads that share it.  A wave holds the block's (<= 16) rows of
-// its head and computes S^T = K Q^T with 16x16x32 MFMAs: each lane then owns
-// one query row (lane % 16), which makes the online-softmax rescale of the
-// O^T = V^T P^T accumulators lane-local.  Splits over context keys are merged
-// with their log-sum-exp by the last wave to finish each (request, head).
+// Layout on gfx950.  A workgroup serves one (key split, KV head, request):
+// GRP waves, one per query head of the GQA group, times NSUB key
+// sub-streams.  Each sub-stream (GRP waves) takes every NSUB-th 32-key tile
+// of the split, stages it in its own LDS buffers and keeps several tiles in
+// flight in registers, so the CU always has waves with work while loads are
+// outstanding.  A wave holds the block's (<= 16) rows of its head and
+// computes S^T = K Q^T with 16x16x32 MFMAs: each lane then owns one query
+// row (lane % 16), which makes the online-softmax rescale of the
+// O^T = V^T P^T accumulators lane-local.  Sub-streams are combined through
+// LDS with their log-sum-exp; splits over context keys are merged the same
+// way by the last workgroup to finish each (request, KV head), all of its
+// waves sharing the merge.  Ring slots advance in int32 from one modulo per
+// workgroup; the window and tail masks run only on the tiles that straddle
+// an edge.
 #include "dspine_device.hpp"
 #include "dspine_internal.hpp"
 
@@ -55,88 +62,129 @@ __device__ __forceinline__ void load_vt(Frag<float>& f, const float* row, int q)
   f.v[1] = *reinterpret_cast<const u32x4*>(row + 16 + 4 * q);
 }
 
-template <typename TW, typename TQ, typename TV, int D, int GRP>
-__global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p) {
-  static_assert(sizeof(TW) == sizeof(TQ), "stored keys and key operands have one element size");
-  constexpr int EQ = (int)sizeof(TQ);
-  constexpr int EV = (int)sizeof(TV);
-  constexpr int LDQ = D + 16 / EQ;          // padded row of Q / K tiles
-  constexpr int LDV = 32 + 4;               // padded row of V^T tiles (32 keys)
-  constexpr int NT = 64 * GRP;
-  constexpr int PSZ = 64 * (D / 4) + 32;    // floats per split partial
+// Compile-time shape of one attention instantiation.
+template <typename TQ, typename TV, int D, int GRP>
+struct AttnShape {
+  static constexpr int EQ = (int)sizeof(TQ), EV = (int)sizeof(TV);
+  static constexpr int LDQ = D + 16 / EQ;               // padded row of Q / K tiles
+  static constexpr int LDV = 32 + 16 / EV;              // padded row of V^T tiles (32 keys)
+  static constexpr int K_BYTES = 32 * LDQ * EQ;
+  static constexpr int V_BYTES = D * LDV * EV;
+  static constexpr int TILE = K_BYTES + V_BYTES;        // one K tile + one V^T tile
+  static constexpr int Q_BYTES = GRP * 16 * LDQ * EQ;
+  static constexpr int PART = 64 * (D / 4 + 2) * 4;     // one wave's (o, m, l) in LDS
+  static constexpr int LIMIT = 156 * 1024;
+  static constexpr bool fits(int n) {
+    return Q_BYTES + (n + 1) * TILE <= LIMIT && GRP * (n - 1) * PART <= Q_BYTES + (n + 1) * TILE;
+  }
+  // at most 8 waves (512 threads): 256 registers per wave, two workgroups per CU
+  static constexpr int NSUB_MAX = 8 / GRP < 1 ? 1 : 8 / GRP < 4 ? 8 / GRP : 4;
+  static constexpr int NSUB = (NSUB_MAX >= 4 && fits(4)) ? 4 : (NSUB_MAX >= 2 && fits(2)) ? 2 : 1;
+  static constexpr int NT = 64 * GRP * NSUB;
+  static constexpr int SMEM = Q_BYTES + (NSUB + 1) * TILE;
+  static_assert(fits(NSUB), "attention LDS");
+  static_assert((D / 16) % NSUB == 0, "merge split of the head dimension");
+};
 
-  __shared__ __attribute__((aligned(16))) TQ sQ[GRP][16 * LDQ];
-  __shared__ __attribute__((aligned(16))) TQ sK[2][32 * LDQ];
-  __shared__ __attribute__((aligned(16))) TV sVt[2][D * LDV];
+template <typename TW, typename TQ, typename TV, int D, int GRP>
+__global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_kernel(const AttnParams p) {
+  using Sh = AttnShape<TQ, TV, D, GRP>;
+  static_assert(sizeof(TW) == sizeof(TQ), "stored keys and key operands have one element size");
+  constexpr int EQ = Sh::EQ, EV = Sh::EV, LDQ = Sh::LDQ, LDV = Sh::LDV;
+  constexpr int NSUB = Sh::NSUB;
+  constexpr int GT = 64 * GRP;                          // threads of one sub-stream
+  constexpr int PSZ = 64 * (D / 4) + 32;                // floats of one split partial in HBM
+
+  __shared__ __attribute__((aligned(16))) char smem[Sh::SMEM];
+  __shared__ uint32_t s_flag;
+  TQ* const sQ = reinterpret_cast<TQ*>(smem);           // [GRP][16][LDQ]
+  auto sK = [&](int t) { return reinterpret_cast<TQ*>(smem + Sh::Q_BYTES + t * Sh::TILE); };
+  auto sVt = [&](int t) { return reinterpret_cast<TV*>(smem + Sh::Q_BYTES + t * Sh::TILE + Sh::K_BYTES); };
 
   const int b = blockIdx.z, g = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int h = g * GRP + w;
+  const int hl = w % GRP, sub = w / GRP;                // head within the group, sub-stream
+  const int h = g * GRP + hl;
+  const int gtid = tid - sub * GT;                      // thread index within the sub-stream
   const int W = p.W, S = p.S;
   const int64_t F = p.F[b];
   const int64_t cbeg = p.lo0[b] + (int64_t)split * p.kps[b];
   const int64_t cend = (cbeg + p.kps[b] < F) ? cbeg + p.kps[b] : F;
+  const int nkeys = cend > cbeg ? (int)(cend - cbeg) : 0;
   const bool has_block = split == p.nsplit - 1;
   const int row_base = b * W;
-  const float* rope = p.rope;
 
-  // ---- context keys [cbeg, cend) in tiles of 32 ---------------------------
-  // PF tiles are in flight in registers at any time: the slot of tile i is
-  // refilled with tile i + PF as soon as tile i is in LDS, so a split's keys
-  // cost about one memory latency, not one per tile.  Loads past cend read
-  // position cend-1 (in bounds); those keys are masked and their values
-  // zeroed when the tile is written to LDS.
+  // ---- context keys [cbeg, cend) in tiles of 32 --------------------------
   const gptr<TW> kring = as_global(reinterpret_cast<const TW*>(p.kring[b]));
   const gptr<TV> vring = as_global(reinterpret_cast<const TV*>(p.vring[b]));
-  const int64_t cap = p.cap[b];
-  constexpr int KCH = D * EQ / 16, KEPC = 16 / EQ;     // 16-byte chunks per key row
+  const size_t head_base = (size_t)g * (size_t)p.cap[b];
+  const int slot0 = S > 0 ? (int)ring_slot(cbeg, S) : 0;   // slot of cbeg; later keys advance in int32
+  constexpr int KCH = D * EQ / 16, KEPC = 16 / EQ;      // 16-byte chunks per key row
   constexpr int VCH = D * EV / 16, VEPC = 16 / EV;
-  // chunks per thread; with more threads than chunks the spare threads load
-  // a duplicate chunk and store nothing
-  constexpr int KPT = (32 * KCH + NT - 1) / NT, VPT = (32 * VCH + NT - 1) / NT;
-  constexpr int PF = (16 / (KPT + VPT)) < 1 ? 1 : (16 / (KPT + VPT)) > 8 ? 8 : 16 / (KPT + VPT);
+  // chunks per thread of the sub-stream; spare threads re-load a chunk and store nothing
+  constexpr int KPT = (32 * KCH + GT - 1) / GT, VPT = (32 * VCH + GT - 1) / GT;
+  constexpr int PFR = 16 / (KPT + VPT);
+  constexpr int PF = PFR < 1 ? 1 : PFR > 4 ? 4 : PFR;   // tiles in flight per sub-stream
   u32x4 kreg[PF][KPT], vreg[PF][VPT];
-  const int n_tiles = cend > cbeg ? (int)((cend - cbeg + 31) / 32) : 0;
+  const int n_tiles = (nkeys + 31) / 32;
+  const int rounds = (n_tiles + NSUB - 1) / NSUB;       // sub-stream `sub` takes tiles r*NSUB + sub
+
+  // key row kr of tile i -> element offset of its ring row (positions past
+  // the split's end re-read its last key: in bounds, masked later)
+  auto key_row = [&](int i, int kr) -> size_t {
+    int rel = 32 * i + kr;
+    rel = rel < nkeys ? rel : nkeys - 1;
+    int64_t slot;
+    if (S > 0) {
+      const int sl = slot0 + rel;
+      slot = sl >= S ? sl - S : sl;
+    } else {
+      slot = cbeg + rel;
+    }
+    return (head_base + (size_t)slot) * D;
+  };
   auto load_tile = [&](u32x4 (&kr_)[KPT], u32x4 (&vr_)[VPT], int i) {
-    const int64_t t0 = cbeg + 32 * (int64_t)i;
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
-      const int c = (tid + q * NT) % (32 * KCH), kr = c / KCH, part = c % KCH;
-      const int64_t pos = t0 + kr < cend ? t0 + kr : cend - 1;
-      kr_[q] = gload16((gptr<void>)(kring + ((size_t)g * cap + ring_slot(pos, S)) * D + part * KEPC));
+      const int c = (gtid + q * GT) % (32 * KCH);
+      kr_[q] = gload16((gptr<void>)(kring + key_row(i, c / KCH) + (c % KCH) * KEPC));
     }
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
-      const int c = (tid + q * NT) % (32 * VCH), kr = c / VCH, part = c % VCH;
-      const int64_t pos = t0 + kr < cend ? t0 + kr : cend - 1;
-      vr_[q] = gload16((gptr<void>)(vring + ((size_t)g * cap + ring_slot(pos, S)) * D + part * VEPC));
+      const int c = (gtid + q * GT) % (32 * VCH);
+      vr_[q] = gload16((gptr<void>)(vring + key_row(i, c / VCH) + (c % VCH) * VEPC));
     }
   };
   auto store_tile = [&](const u32x4 (&kr_)[KPT], const u32x4 (&vr_)[VPT], int i) {
-    const int64_t t0 = cbeg + 32 * (int64_t)i;
+    TQ* k_t = sK(sub);
+    TV* v_t = sVt(sub);
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
-      const int c = tid + q * NT, kr = c / KCH, part = c % KCH;
+      const int c = gtid + q * GT;
       if (c < 32 * KCH)
-        *reinterpret_cast<u32x4*>(&sK[0][kr * LDQ + part * KEPC]) = key_chunk(kr_[q], (TW*)nullptr, (TQ*)nullptr);
+        *reinterpret_cast<u32x4*>(&k_t[(c / KCH) * LDQ + (c % KCH) * KEPC]) =
+            key_chunk(kr_[q], (TW*)nullptr, (TQ*)nullptr);
     }
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
-      const int c = tid + q * NT, kr = c / VCH, part = c % VCH;
+      const int c = gtid + q * GT, kr = c / VCH, part = c % VCH;
       if (c >= 32 * VCH) continue;
       alignas(16) TV val[VEPC];
-      *reinterpret_cast<u32x4*>(val) = t0 + kr < cend ? vr_[q] : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(val) = 32 * i + kr < nkeys ? vr_[q] : u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int e = 0; e < VEPC; ++e) sVt[0][(part * VEPC + e) * LDV + kr] = val[e];
+      for (int e = 0; e < VEPC; ++e) v_t[(part * VEPC + e) * LDV + kr] = val[e];
     }
   };
-  // first PF tiles in flight during the prologue below (clamped, in bounds)
+  // first PF rounds in flight during the prologue below (clamped, in bounds)
   if (n_tiles > 0) {
 #pragma unroll
-    for (int j = 0; j < PF; ++j) load_tile(kreg[j], vreg[j], j < n_tiles ? j : n_tiles - 1);
+    for (int j = 0; j < PF; ++j) {
+      const int i = j * NSUB + sub;
+      load_tile(kreg[j], vreg[j], i < n_tiles ? i : n_tiles - 1);
+    }
   }
 
-  // ---- prologue: head RMSNorm + RoPE of this wave's query head ------------
+  // ---- prologue: head RMSNorm + RoPE of the block's q (and k) rows --------
   // Every operand is loaded into registers before the first use, through
   // global-address-space pointers, so the row's loads share one latency.
   auto prep_rows = [&](int col0, const void* gain, TQ* dst) {
@@ -144,7 +192,7 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
     constexpr int NP = D / 8;               // rotation pairs per lane
     const bool live = r < W;
     const gptr<float> src = as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + col0;
-    const gptr<float> cs = as_global(rope) + (size_t)(row_base + (live ? r : 0)) * D;   // (cos, sin) x D/2
+    const gptr<float> cs = as_global(p.rope) + (size_t)(row_base + (live ? r : 0)) * D;   // (cos, sin) x D/2
     const gptr<TW> gw = as_global(reinterpret_cast<const TW*>(gain));
     float xa[NP], xb[NP], ga[NP], gb[NP], co[NP], si[NP];
 #pragma unroll
@@ -172,50 +220,60 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
       Elt<TQ>::store(dst, r * LDQ + j + D / 2, live ? c * co[jj] + a * si[jj] : 0.f);
     }
   };
-  prep_rows(h * D, p.gq, sQ[w]);
-
-  if (has_block) {
+  if (sub == 0) prep_rows(h * D, p.gq, sQ + hl * 16 * LDQ);
+  // the block's own keys and values, staged by the last sub-stream
+  if (has_block && sub == NSUB - 1) {
     const int kcol = p.nq * D + g * D;
     const int vcol = p.nq * D + p.nkv * D + g * D;
-    if (w == 0) {
-      prep_rows(kcol, p.gk, sK[1]);
-      for (int e = lane; e < 16 * D; e += 64) Elt<TQ>::store(sK[1], (16 + e / D) * LDQ + e % D, 0.f);
+    if (hl == 0) {
+      prep_rows(kcol, p.gk, sK(NSUB));
+      for (int e = lane; e < 16 * D; e += 64) Elt<TQ>::store(sK(NSUB), (16 + e / D) * LDQ + e % D, 0.f);
     }
-    if (w == (GRP > 1 ? 1 : 0)) {
+    if (hl == (GRP > 1 ? 1 : 0)) {
       const int r = lane >> 2, part = lane & 3;
       const bool live = r < W;
-      const gptr<float> src = as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + vcol + part * (D / 4);
+      const gptr<float> src =
+          as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + vcol + part * (D / 4);
       float vv[D / 4];
 #pragma unroll
       for (int d = 0; d < D / 4; ++d) vv[d] = src[d];
 #pragma unroll
-      for (int d = 0; d < D / 4; ++d) put_v(&sVt[1][(part * (D / 4) + d) * LDV + r], live ? vv[d] : 0.f);
-      for (int e = lane; e < 16 * D; e += 64) put_v(&sVt[1][(e / 16) * LDV + 16 + (e % 16)], 0.f);
+      for (int d = 0; d < D / 4; ++d) put_v(&sVt(NSUB)[(part * (D / 4) + d) * LDV + r], live ? vv[d] : 0.f);
+      for (int e = lane; e < 16 * D; e += 64) put_v(&sVt(NSUB)[(e / 16) * LDV + 16 + (e % 16)], 0.f);
     }
   }
   __syncthreads();
 
   Frag<TQ> qf[D / 32];
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c)
-    qf[c].load(&sQ[w][(lane & 15) * LDQ + c * 32 + 8 * (lane >> 4)]);
+  for (int c = 0; c < D / 32; ++c) qf[c].load(&sQ[(hl * 16 + (lane & 15)) * LDQ + c * 32 + 8 * (lane >> 4)]);
 
   const float scale_log2 = 1.4426950408889634f * rsqrtf((float)D);
   const int qrow = lane & 15;
-  const int64_t row_lo = ctx_row_lo(F, S, qrow);
+  // first visible key of a row, relative to cbeg (clamped into int range)
+  auto rel_lo = [&](int row) -> int {
+    const int64_t d = ctx_row_lo(F, S, row) - cbeg;
+    return d < -(1 << 30) ? -(1 << 30) : d > (1 << 30) ? (1 << 30) : (int)d;
+  };
+  const int lo_rel = rel_lo(qrow);
+  const int lo_rel_max = rel_lo(W - 1);      // the last row starts latest
   float m_run = -INFINITY, l_lane = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0, 0, 0, 0};
 
-  auto process = [&](int which, int64_t p0, bool is_block) {
+  // One 32-key tile from LDS tile t: context keys k0.. (relative to cbeg),
+  // with the window / tail mask only when the tile straddles an edge, or the
+  // block's keys.
+  auto process = [&](int t, int k0, bool is_block, bool mask) {
     f32x4 s[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+    const TQ* k_t = sK(t);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         Frag<TQ> kf;
-        kf.load(&sK[which][(kt * 16 + (lane & 15)) * LDQ + c * 32 + 8 * (lane >> 4)]);
+        kf.load(&k_t[(kt * 16 + (lane & 15)) * LDQ + c * 32 + 8 * (lane >> 4)]);
         mma16(s[kt], kf, qf[c]);
       }
     float sv[8];
@@ -225,12 +283,12 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int kidx = kt * 16 + 4 * (lane >> 4) + v;
-        bool vis;
-        if (!is_block) {
-          const int64_t pos = p0 + kidx;
-          vis = qrow < W && pos < cend && pos >= row_lo;
-        } else {
+        bool vis = true;
+        if (is_block) {
           vis = qrow < W && kidx < W && block_key_visible(S, p.causal, qrow, kidx);
+        } else if (mask) {
+          const int rel = k0 + kidx;
+          vis = rel < nkeys && rel >= lo_rel;
         }
         const float x = vis ? s[kt][v] * scale_log2 : -INFINITY;
         sv[kt * 4 + v] = x;
@@ -256,91 +314,140 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
     for (int e = 0; e < 8; ++e) psum += pv[e];
     l_lane = l_lane * alpha + psum;
     m_run = m_new;
+    const TV* v_t = sVt(t);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       o[dt] *= alpha;
       Frag<TV> vf;
-      load_vt(vf, &sVt[which][(dt * 16 + (lane & 15)) * LDV], lane >> 4);
+      load_vt(vf, &v_t[(dt * 16 + (lane & 15)) * LDV], lane >> 4);
       mma16(o[dt], vf, pf);
     }
   };
 
-  // Every trip issues the same loads (refills past the end re-read the last
+  // Every round issues the same loads (refills past the end re-read a valid
   // tile), so the wait before each LDS store covers exactly one slot.
-  for (int i0 = 0; i0 < n_tiles; i0 += PF) {
+  for (int r0 = 0; r0 < rounds; r0 += PF) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      const int i = i0 + j;
-      const bool live = i < n_tiles;
+      const int r = r0 + j;
+      const int i = r * NSUB + sub;
+      const bool live = r < rounds && i < n_tiles;
       if (live) store_tile(kreg[j], vreg[j], i);
       __syncthreads();
-      load_tile(kreg[j], vreg[j], i + PF < n_tiles ? i + PF : n_tiles - 1);
-      if (live) process(0, cbeg + 32 * (int64_t)i, false);
+      const int inext = (r + PF) * NSUB + sub;
+      load_tile(kreg[j], vreg[j], inext < n_tiles ? inext : n_tiles - 1);
+      if (live) {
+        const bool edge = 32 * i + 32 > nkeys || 32 * i < lo_rel_max;
+        process(sub, 32 * i, false, edge);
+      }
       __syncthreads();
     }
   }
-  if (has_block) process(1, 0, true);
+  if (has_block && sub == NSUB - 1) process(NSUB, -1, true, true);
+  __syncthreads();                                      // all tiles and Q done: LDS reused below
 
-  // ---- finish: write, or publish a partial and let the last wave merge ----
-  float lrow = l_lane + __shfl_xor(l_lane, 16, 64);
-  lrow += __shfl_xor(lrow, 32, 64);
-  TQ* out = reinterpret_cast<TQ*>(p.out);
-  auto write_row = [&](const f32x4 (&acc)[D / 16], float inv_l) {
-    if (qrow >= W) return;
-    TQ* dst = out + (size_t)(row_base + qrow) * p.ld_out + h * D + 4 * (lane >> 4);
+  // ---- combine the sub-streams of each head (lane-wise, through LDS) ------
+  float* part = reinterpret_cast<float*>(smem);
+  auto part_of = [&](int s, int head) { return part + (size_t)((s - 1) * GRP + head) * (64 * (D / 4 + 2)); };
+  if (sub > 0) {
+    float* pp = part_of(sub, hl);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Elt<TQ>::store(dst, dt * 16 + v, acc[dt][v] * inv_l);
-  };
+      for (int v = 0; v < 4; ++v) pp[(dt * 4 + v) * 64 + lane] = o[dt][v];
+    pp[(D / 4) * 64 + lane] = m_run;
+    pp[(D / 4 + 1) * 64 + lane] = l_lane;
+  }
+  __syncthreads();
+  if (sub == 0) {
+    float mstar = m_run;
+#pragma unroll
+    for (int s = 1; s < NSUB; ++s) mstar = fmaxf(mstar, part_of(s, hl)[(D / 4) * 64 + lane]);
+    if (mstar != -INFINITY) {
+      const float w0 = m_run == -INFINITY ? 0.f : exp2f(m_run - mstar);
+      l_lane *= w0;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[dt] *= w0;
+#pragma unroll
+      for (int s = 1; s < NSUB; ++s) {
+        const float* pp = part_of(s, hl);
+        const float ms = pp[(D / 4) * 64 + lane];
+        const float ws = ms == -INFINITY ? 0.f : exp2f(ms - mstar);
+        l_lane += ws * pp[(D / 4 + 1) * 64 + lane];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[dt][v] += ws * pp[(dt * 4 + v) * 64 + lane];
+      }
+    }
+    m_run = mstar;
+  }
+
+  // ---- finish: write, or publish a partial and let the last workgroup merge
+  TQ* out = reinterpret_cast<TQ*>(p.out);
+  float lrow = l_lane + __shfl_xor(l_lane, 16, 64);
+  lrow += __shfl_xor(lrow, 32, 64);
   if (p.nsplit == 1) {
-    if (lrow > 0.f) write_row(o, 1.f / lrow);
+    if (sub == 0 && qrow < W && lrow > 0.f) {
+      const float inv = 1.f / lrow;
+      TQ* dst = out + (size_t)(row_base + qrow) * p.ld_out + h * D + 4 * (lane >> 4);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Elt<TQ>::store(dst, dt * 16 + v, o[dt][v] * inv);
+    }
     return;
   }
-  float* base = p.partials + (size_t)((b * p.nq + h) * p.nsplit) * PSZ;
-  float* mine = base + (size_t)split * PSZ;
+  float* base = p.partials + (size_t)(b * p.nq + g * GRP) * p.nsplit * PSZ;   // [GRP][nsplit][PSZ]
+  if (sub == 0) {
+    float* mine = base + (size_t)(hl * p.nsplit + split) * PSZ;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) store_coherent(mine + (dt * 64 + lane) * 4, o[dt]);
-  if (lane < 16) {
-    store_coherent(mine + 64 * (D / 4) + lane, m_run);
-    store_coherent(mine + 64 * (D / 4) + 16 + lane, lrow);
+    for (int dt = 0; dt < D / 16; ++dt) store_coherent(mine + (dt * 64 + lane) * 4, o[dt]);
+    if (lane < 16) {
+      store_coherent(mine + 64 * (D / 4) + lane, m_run);
+      store_coherent(mine + 64 * (D / 4) + 16 + lane, lrow);
+    }
+    drain_own_stores();
   }
-  drain_own_stores();
-  uint32_t old = 0;
-  if (lane == 0) old = count_arrival(p.counters + b * p.nq + h);
-  old = __shfl(old, 0, 64);
-  if ((int)old != p.nsplit - 1) return;
-  // Merge: the splits' row maxima first (8 loads in flight at a time), then
-  // their partial sums four splits at a time, every load issued before use.
-  // Indexes past the last split repeat it; those copies are not added.
+  __syncthreads();
+  if (tid == 0) s_flag = count_arrival(p.counters + b * p.nkv + g);
+  __syncthreads();
+  if ((int)s_flag != p.nsplit - 1) return;
+
+  // Merge (last workgroup of this KV head): wave (head hl, part sub) merges
+  // head dims [sub*D/NSUB, (sub+1)*D/NSUB) of all splits: the maxima first
+  // (8 loads in flight), then the partials four splits at a time, in split
+  // order.  Indexes past the last split repeat it; those copies are not added.
+  constexpr int DPW = (D / 16) / NSUB;                  // 16-wide head-dim tiles per wave
+  const float* hb = base + (size_t)hl * p.nsplit * PSZ;
   float mstar = -INFINITY;
   for (int sp0 = 0; sp0 < p.nsplit; sp0 += 8) {
     float mv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int sp = sp0 + j < p.nsplit ? sp0 + j : p.nsplit - 1;
-      mv[j] = load_coherent(base + (size_t)sp * PSZ + 64 * (D / 4) + qrow);
+      mv[j] = load_coherent(hb + (size_t)sp * PSZ + 64 * (D / 4) + qrow);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) mstar = fmaxf(mstar, mv[j]);
   }
-  f32x4 acc[D / 16];
+  f32x4 acc[DPW];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
+  for (int d = 0; d < DPW; ++d) acc[d] = f32x4{0, 0, 0, 0};
   float L = 0.f;
   if (mstar != -INFINITY) {
-    constexpr int MB = 256 / D;              // splits merged per batch of loads
+    constexpr int MB = 4;
     for (int sp0 = 0; sp0 < p.nsplit; sp0 += MB) {
       float mv[MB], lv[MB];
-      f32x4 ov[MB][D / 16];
+      f32x4 ov[MB][DPW];
 #pragma unroll
       for (int j = 0; j < MB; ++j) {
         const int sp = sp0 + j < p.nsplit ? sp0 + j : p.nsplit - 1;
-        const float* part = base + (size_t)sp * PSZ;
-        mv[j] = load_coherent(part + 64 * (D / 4) + qrow);
-        lv[j] = load_coherent(part + 64 * (D / 4) + 16 + qrow);
+        const float* pt = hb + (size_t)sp * PSZ;
+        mv[j] = load_coherent(pt + 64 * (D / 4) + qrow);
+        lv[j] = load_coherent(pt + 64 * (D / 4) + 16 + qrow);
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) ov[j][dt] = load_coherent4(part + (dt * 64 + lane) * 4);
+        for (int d = 0; d < DPW; ++d) ov[j][d] = load_coherent4(pt + ((sub * DPW + d) * 64 + lane) * 4);
       }
 #pragma unroll
       for (int j = 0; j < MB; ++j) {
@@ -348,30 +455,41 @@ __global__ __launch_bounds__(64 * GRP) void attention_kernel(const AttnParams p)
         const float wgt = exp2f(mv[j] - mstar);
         L += wgt * lv[j];
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) acc[dt] += wgt * ov[j][dt];
+        for (int d = 0; d < DPW; ++d) acc[d] += wgt * ov[j][d];
       }
     }
   }
-  if (L > 0.f) write_row(acc, 1.f / L);
-  if (lane == 0) reset_counter(p.counters + b * p.nq + h);
+  if (qrow < W && L > 0.f) {
+    const float inv = 1.f / L;
+    TQ* dst = out + (size_t)(row_base + qrow) * p.ld_out + h * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int d = 0; d < DPW; ++d)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Elt<TQ>::store(dst, (sub * DPW + d) * 16 + v, acc[d][v] * inv);
+  }
+  if (tid == 0) reset_counter(p.counters + b * p.nkv + g);
 }
 
 size_t attn_partial_floats(int max_b, int nq, int head_dim) {
   return (size_t)max_b * nq * kMaxSplit * (64 * (head_dim / 4) + 32);
 }
 
+template <typename TW, typename TQ, typename TV, int D, int GRP>
+static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
+  const dim3 grid(p.nsplit, p.nkv, p.B);
+  hipLaunchKernelGGL((attention_kernel<TW, TQ, TV, D, GRP>), grid, dim3(AttnShape<TQ, TV, D, GRP>::NT), 0, s, p);
+  return hipGetLastError();
+}
+
 template <typename TW, typename TQ, typename TV, int D>
 static hipError_t launch_d(const AttnParams& p, hipStream_t s) {
-  const int grp = p.nq / p.nkv;
-  const dim3 grid(p.nsplit, p.nkv, p.B);
-  switch (grp) {
-    case 1: hipLaunchKernelGGL((attention_kernel<TW, TQ, TV, D, 1>), grid, dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((attention_kernel<TW, TQ, TV, D, 2>), grid, dim3(128), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((attention_kernel<TW, TQ, TV, D, 4>), grid, dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((attention_kernel<TW, TQ, TV, D, 8>), grid, dim3(512), 0, s, p); break;
+  switch (p.nq / p.nkv) {
+    case 1: return launch_g<TW, TQ, TV, D, 1>(p, s);
+    case 2: return launch_g<TW, TQ, TV, D, 2>(p, s);
+    case 4: return launch_g<TW, TQ, TV, D, 4>(p, s);
+    case 8: return launch_g<TW, TQ, TV, D, 8>(p, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnParams& p, int dtype, int head_dim, hipStream_t s) {

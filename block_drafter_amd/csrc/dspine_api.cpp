@@ -951,9 +951,9 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
     ap.rope = rope;
     ap.S = g.window[l];
     ap.causal = g.block_causal;
-    // Key splits: enough workgroups to spread the reads (about 256, or one
-    // split per 2048 keys on long contexts) but at least 256 keys per split,
-    // since every split adds a partial the merge has to read back.
+    // Key splits: enough workgroups to spread the reads over the CUs (about
+    // 256, or one split per 2048 keys on long contexts) but at least 128 keys
+    // per split, so that each of a workgroup's key sub-streams has a tile.
     int64_t max_ctx = 0;
     for (int b = 0; b < B; ++b) {
       ap.kring[b] = ctx[b].k_ring[l];
@@ -964,7 +964,7 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
       max_ctx = std::max(max_ctx, ap.F[b] - ap.lo0[b]);
     }
     const int64_t spread = std::max(ceil_div(256, (int64_t)B * g.n_kv_heads), ceil_div(max_ctx, 2048));
-    ap.nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({spread, ceil_div(max_ctx, 256), (int64_t)kMaxSplit}));
+    ap.nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({spread, ceil_div(max_ctx, 128), (int64_t)kMaxSplit}));
     for (int b = 0; b < B; ++b) {
       const int64_t nctx = ap.F[b] - ap.lo0[b];
       ap.kps[b] = (int32_t)(ceil_div(ceil_div(nctx, ap.nsplit), 32) * 32);
