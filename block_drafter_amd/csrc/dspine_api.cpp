@@ -677,30 +677,33 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
           HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
         }
       }
-      // per layer: head norm + RoPE + storage rounding + ring scatter
-      for (int l = 0; l < L; ++l) {
+      // every layer: head norm + RoPE + storage rounding + ring scatter
+      for (int l0 = 0; l0 < L; l0 += kKvLayers) {
         KvStoreParams kp;
         memset(&kp, 0, sizeof kp);
         kp.rows = (int)nrows;
         kp.nkv = g.n_kv_heads;
         kp.D = g.head_dim;
-        kp.S = g.window[l];
         kp.n_req = nsrc;
+        kp.n_layers = std::min(kKvLayers, L - l0);
         kp.kv = kv_raw;
         kp.ld = ldkv;
-        kp.k_col = 2 * l * kvd;
-        kp.v_col = (2 * l + 1) * kvd;
-        kp.gk = wt.layer[l].gk;
         kp.eps = g.eps;
         kp.rope_theta = g.rope_theta;
         for (int s = 0; s <= nsrc; ++s) kp.row0[s] = row0[s];
-        for (int s = 0; s < nsrc; ++s) {
-          const int b = req_of[s];
-          kp.pos0[s] = pos0[s];
-          kp.keep_lo[s] = std::max(ctx[b].frontier, live_lo(g.window[l], F1[b]));
-          kp.kring[s] = ctx[b].k_ring[l];
-          kp.vring[s] = ctx[b].v_ring[l];
-          kp.cap[s] = ctx[b].capacity[l];
+        for (int s = 0; s < nsrc; ++s) kp.pos0[s] = pos0[s];
+        for (int j = 0; j < kp.n_layers; ++j) {
+          const int l = l0 + j;
+          kp.S[j] = g.window[l];
+          kp.col[j] = 2 * l * kvd;
+          kp.gk[j] = wt.layer[l].gk;
+          for (int s = 0; s < nsrc; ++s) {
+            const int b = req_of[s];
+            kp.keep_lo[j][s] = std::max(ctx[b].frontier, live_lo(g.window[l], F1[b]));
+            kp.kring[j][s] = ctx[b].k_ring[l];
+            kp.vring[j][s] = ctx[b].v_ring[l];
+            kp.cap[j][s] = ctx[b].capacity[l];
+          }
         }
         ProfScope ps(DSPINE_PROF_CTX_STORE, stream);
         HIP_TRY(launch_kv_store(kp, g.dtype, stream));

@@ -190,18 +190,22 @@ hipError_t launch_rmsnorm(const RowParams& p, int dtype, bool f32_output, hipStr
 // sums of squares of the rows of x (one stats tile)
 hipError_t launch_rowstats(const RowParams& p, hipStream_t s);
 
+constexpr int kKvLayers = 8;       // draft layers stored by one K/V store launch
 struct KvStoreParams {
-  int32_t rows, nkv, D, S, n_req;
-  const float* kv;                // fp32 [rows, ld]: k columns at k_col, v at v_col
-  int32_t ld, k_col, v_col;
-  const void* gk;
+  int32_t rows, nkv, D, n_req, n_layers;
+  const float* kv;                // fp32 [rows, ld]: layer l's k at l*2*kvd, v at (2l+1)*kvd
+  int32_t ld;
   float eps, rope_theta;
   int32_t row0[DSPINE_MAX_BATCH + 1];
   int64_t pos0[DSPINE_MAX_BATCH];      // position of the request's first row
-  int64_t keep_lo[DSPINE_MAX_BATCH];   // rows at positions below are not stored
-  void* kring[DSPINE_MAX_BATCH];
-  void* vring[DSPINE_MAX_BATCH];
-  int64_t cap[DSPINE_MAX_BATCH];
+  // per layer of this launch
+  int32_t S[kKvLayers];
+  int32_t col[kKvLayers];              // column of the layer's k block in kv
+  const void* gk[kKvLayers];
+  int64_t keep_lo[kKvLayers][DSPINE_MAX_BATCH];   // rows at positions below are not stored
+  void* kring[kKvLayers][DSPINE_MAX_BATCH];
+  void* vring[kKvLayers][DSPINE_MAX_BATCH];
+  int64_t cap[kKvLayers][DSPINE_MAX_BATCH];
 };
 hipError_t launch_kv_store(const KvStoreParams& p, int dtype, hipStream_t s);
 

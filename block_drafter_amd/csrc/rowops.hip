@@ -135,62 +135,71 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const RowParams p)
   }
 }
 
-// a2 epilogue for one draft layer [NIF, context K/V; fused context
-// materializer]: k = rope_1d(head_rmsnorm(k_raw, gk), t) stored BF16 (no
-// rounding before the norm); v stored FP16_RNE(BF16(v_raw)).  F32 models
-// store float.  Rows at positions below keep_lo are not stored (chunk
-// truncation); position t goes to ring slot t mod S (t for a full layer).
+// a2 epilogue [NIF, context K/V; fused context materializer], for every
+// layer of the launch at once (grid: rows x layers): k =
+// rope_1d(head_rmsnorm(k_raw, gk), t) stored BF16 (no rounding before the
+// norm); v stored FP16_RNE(BF16(v_raw)).  F32 models store float.  Rows at
+// positions below keep_lo are not stored (chunk truncation); position t
+// goes to ring slot t mod S (t for a full layer).  Each thread holds 4
+// consecutive elements of a head; a head's sum of squares is reduced over
+// its D/4 threads in a fixed butterfly order.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void kv_store_kernel(const KvStoreParams p) {
-  extern __shared__ float sm[];   // D/2 (cos, sin) pairs, nkv sums, nkv*D raw keys
-  const int row = blockIdx.x;
+  extern __shared__ float sm[];   // (cos, sin) x D/2, then nkv*D raw keys
+  const int row = blockIdx.x, l = blockIdx.y;
   int b = 0;
   while (b + 1 < p.n_req && row >= p.row0[b + 1]) ++b;
   const int64_t t = p.pos0[b] + (row - p.row0[b]);
-  if (t < p.keep_lo[b]) return;
-  const int D = p.D, half = D / 2;
+  if (t < p.keep_lo[l][b]) return;
+  const int D = p.D, half = D / 2, n = p.nkv * D;
   float* cs = sm;
-  float* ssum = sm + D;
-  float* kraw = ssum + p.nkv;
-  const float* kr = p.kv + (size_t)row * p.ld + p.k_col;
-  const float* vr = p.kv + (size_t)row * p.ld + p.v_col;
+  float* kraw = sm + D;
+  const float* kr = p.kv + (size_t)row * p.ld + p.col[l];
+  const float* vr = kr + n;
   for (int j = threadIdx.x; j < half; j += kRowThreads) rope_pair(t, j, D, p.rope_theta, cs[2 * j], cs[2 * j + 1]);
-  for (int e = threadIdx.x; e < p.nkv * D; e += kRowThreads) kraw[e] = kr[e];
-  __syncthreads();
-  // per-head sum of squares in a fixed order (reproducible bits)
-  for (int hh = threadIdx.x; hh < p.nkv; hh += kRowThreads) {
-    float s = 0.f;
-    for (int d = 0; d < D; ++d) s += kraw[hh * D + d] * kraw[hh * D + d];
-    ssum[hh] = s;
+  const int S = p.S[l];
+  const size_t slot = (size_t)ring_slot(t, S);
+  const size_t cap = (size_t)p.cap[l][b];
+  const T* gk = reinterpret_cast<const T*>(p.gk[l]);
+  // the head sum needs the D/4 threads of a head inside one wave: 4 * 64 >= D
+  for (int e0 = 4 * threadIdx.x; e0 < n; e0 += 4 * kRowThreads) {
+    const float4 kv4 = *reinterpret_cast<const float4*>(kr + e0);
+    kraw[e0] = kv4.x;
+    kraw[e0 + 1] = kv4.y;
+    kraw[e0 + 2] = kv4.z;
+    kraw[e0 + 3] = kv4.w;
+    float ss = ((kv4.x * kv4.x + kv4.y * kv4.y) + kv4.z * kv4.z) + kv4.w * kv4.w;
+    for (int o = 1; o < D / 4; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    kraw[n + e0 / D] = ss;                                  // per-head sum (same in all its threads)
+    // v: FP16_RNE(BF16(v)) (or float), 4 consecutive elements
+    const float4 v4 = *reinterpret_cast<const float4*>(vr + e0);
+    const int hh = e0 / D, d = e0 % D;
+    const size_t vi = ((size_t)hh * cap + slot) * D + d;
+    const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (Elt<T>::kBytes == 2)
+        reinterpret_cast<uint16_t*>(p.vring[l][b])[vi + u] = f32_to_f16_bits(bf16_bits_to_f32(f32_to_bf16_bits(vv[u])));
+      else
+        reinterpret_cast<float*>(p.vring[l][b])[vi + u] = vv[u];
+    }
   }
   __syncthreads();
-  const int64_t slot = ring_slot(t, p.S);
-  const int64_t cap = p.cap[b];
-  const T* gk = reinterpret_cast<const T*>(p.gk);
   for (int e = threadIdx.x; e < p.nkv * half; e += kRowThreads) {
     const int hh = e / half, j = e % half;
-    const float inv = rsqrtf(ssum[hh] / D + p.eps);
+    const float inv = rsqrtf(kraw[n + hh] / D + p.eps);
     const float a = kraw[hh * D + j] * inv * Elt<T>::load(gk, j);
     const float c = kraw[hh * D + j + half] * inv * Elt<T>::load(gk, j + half);
     const float co = cs[2 * j], si = cs[2 * j + 1];
     const size_t base = ((size_t)hh * cap + slot) * D;
     if constexpr (Elt<T>::kBytes == 2) {
-      uint16_t* K = reinterpret_cast<uint16_t*>(p.kring[b]);
+      uint16_t* K = reinterpret_cast<uint16_t*>(p.kring[l][b]);
       K[base + j] = f32_to_bf16_bits(a * co - c * si);
       K[base + j + half] = f32_to_bf16_bits(c * co + a * si);
     } else {
-      float* K = reinterpret_cast<float*>(p.kring[b]);
+      float* K = reinterpret_cast<float*>(p.kring[l][b]);
       K[base + j] = a * co - c * si;
       K[base + j + half] = c * co + a * si;
-    }
-  }
-  for (int e = threadIdx.x; e < p.nkv * D; e += kRowThreads) {
-    const int hh = e / D, d = e % D;
-    const size_t idx = ((size_t)hh * cap + slot) * D + d;
-    if constexpr (Elt<T>::kBytes == 2) {
-      reinterpret_cast<uint16_t*>(p.vring[b])[idx] = f32_to_f16_bits(bf16_bits_to_f32(f32_to_bf16_bits(vr[e])));
-    } else {
-      reinterpret_cast<float*>(p.vring[b])[idx] = vr[e];
     }
   }
 }
@@ -268,8 +277,9 @@ hipError_t launch_rowstats(const RowParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_kv_store(const KvStoreParams& p, int dtype, hipStream_t s) {
-  const size_t smem = (size_t)(p.D + p.nkv + p.nkv * p.D) * sizeof(float);
-  DSPINE_DISPATCH(dtype, kv_store_kernel, dim3(p.rows), dim3(kRowThreads), smem, s, p);
+  if (p.n_layers < 1 || p.n_layers > kKvLayers || p.D % 4 || 4 * 64 < p.D) return hipErrorInvalidValue;
+  const size_t smem = (size_t)(p.D + p.nkv * p.D + p.nkv) * sizeof(float);
+  DSPINE_DISPATCH(dtype, kv_store_kernel, dim3(p.rows, p.n_layers), dim3(kRowThreads), smem, s, p);
   return hipGetLastError();
 }
 hipError_t launch_pack(const void* src, void* dst, int rows, int cols, int dtype, hipStream_t s) {
