@@ -90,6 +90,74 @@ def cpu_baseline(g, wts, seed, F, commit, W, anchor):
     return dt, threads
 
 
+MFMA_PEAK_TFLOPS = 2500.0          # MI355X dense bf16/fp16 matrix-core peak
+
+
+def prefill_measure(model, g, seed, n_req=8, chunk=32768, reps=5):
+    """One materialize call over n_req fresh rings, each given a chunk of
+    `chunk` feature rows: only a chunk's final S rows are stored (and read),
+    the frontier advances by the whole chunk.  Returns the prefill record."""
+    import torch
+    import synth
+    import block_drafter_amd as bd
+    S = max(g.windows)
+    keep = min(chunk, S) if all(w > 0 for w in g.windows) else chunk
+    width = g.n_feat_layers * g.hidden
+    chunks = []
+    for b in range(n_req):
+        t = torch.empty((chunk, width), dtype=torch.bfloat16, device="cuda")
+        t[chunk - keep:] = bd.to_device(synth.make_features(g, seed, b, keep, start=chunk - keep))
+        chunks.append(t)
+    ctxs = [model.new_context() for _ in range(n_req)]
+    ws = model.workspace(n_req, 16, n_req * keep)
+    torch.cuda.synchronize()
+
+    def call():
+        for c in ctxs:
+            c.frontier = 0
+        model.materialize(ctxs, chunks, workspace=ws)
+
+    call()                                    # warm-up
+    torch.cuda.synchronize()
+    bd.profile_enable(["ctx_gemm", "ctx_store"])
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    bd.profile_enable([])
+    ms = e0.elapsed_time(e1) / reps
+    gemm_ms, gemm_n = bd.profile_read("ctx_gemm")
+    store_ms, _ = bd.profile_read("ctx_store")
+    kvd = g.n_kv_heads * g.head_dim
+    flop = n_req * keep * 2.0 * g.hidden * (width + g.n_layers * 2 * kvd)   # a1 + a2 per call
+    gemm_avg = gemm_ms / reps
+    tflops = flop / (gemm_avg * 1e-3) / 1e12
+    del chunks
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"{n_req} requests x one {chunk}-token chunk into fresh {S}-slot rings "
+                    f"({keep} stored rows each), one materialize call",
+        "ms_per_call": round(ms, 4),
+        "chunk_tok_per_s": round(n_req * chunk / (ms * 1e-3), 1),
+        "stored_tok_per_s": round(n_req * keep / (ms * 1e-3), 1),
+        "gemm_ms_per_call": round(gemm_avg, 4),
+        "store_ms_per_call": round(store_ms / reps, 4),
+        "roofline": {
+            "kernel": "gemm_tile (feature fusion W_feat + K/V projection of every layer)",
+            "bound": "mfma",
+            "achieved": round(tflops, 1),
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+            "flop_per_call": flop,
+            "launches_per_call": gemm_n // reps,
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +168,8 @@ def main():
     ap.add_argument("--commit", type=int, default=16,
                     help="positions materialized per request per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the context-prefill measurement (27B workloads)")
     ap.add_argument("--breakdown", action="store_true",
                     help="after the timed region, time every kernel class for a few steps")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -288,6 +358,12 @@ def main():
     }
     if breakdown is not None:
         res["breakdown"] = breakdown
+    if not args.no_prefill and g.dtype == "bf16" and g.hidden == 5120:
+        del ctxs, pending, ws
+        torch.cuda.empty_cache()
+        log("context prefill: 8 requests x one 32768-token chunk ...")
+        pw = synth.WORKLOADS["prefill27b"]
+        res["prefill"] = prefill_measure(model, g, pw.seed, n_req=pw.B, chunk=pw.prefill_chunk)
     print(json.dumps(res), flush=True)
 
 

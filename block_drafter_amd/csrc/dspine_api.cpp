@@ -565,8 +565,8 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
 
       // a1: c_raw = W_feat s; a2: every layer's K and V projections of
       // c = plain_rmsnorm(c_raw, g_ctx)
-      const bool tile = g.dtype == DSPINE_BF16 && nrows > kMaxRows && H % 128 == 0 &&
-                        (g.n_feat_layers * H) % 64 == 0 && kvd % 128 == 0 && H % 64 == 0;
+      const bool tile = g.dtype == DSPINE_BF16 && nrows > kMaxRows && gemm_tile_fits(H, g.n_feat_layers * H) &&
+                        gemm_tile_fits(kvd, H);
       if (tile) {
         // long blocks: MFMA tile GEMMs with the norm between them
         TileGemmParams tp;

@@ -111,6 +111,8 @@ struct TileGemmParams {
   int32_t ldo;
 };
 hipError_t launch_gemm_tile(const TileGemmParams& p, int dtype, int num_cus, hipStream_t s);
+// true if the tile GEMM takes segments of n_seg output rows and K = k
+bool gemm_tile_fits(int n_seg, int k);
 
 // ---------------------------------------------------------------------------
 // attention over ring context + block
