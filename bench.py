@@ -117,7 +117,8 @@ def prefill_measure(model, g, seed, n_req=8, chunk=32768, reps=5):
             c.frontier = 0
         model.materialize(ctxs, chunks, workspace=ws)
 
-    call()                                    # warm-up
+    call()                                    # warm-up (twice: the first pass over
+    call()                                    # fresh chunk memory also warms translations)
     torch.cuda.synchronize()
     bd.profile_enable(["ctx_gemm", "ctx_store"])
     e0 = torch.cuda.Event(enable_timing=True)

@@ -477,7 +477,7 @@ size_t attn_partial_floats(int max_b, int nq, int head_dim) {
 template <typename TW, typename TQ, typename TV, int D, int GRP>
 static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
   const dim3 grid(p.nsplit, p.nkv, p.B);
-  hipLaunchKernelGGL((attention_kernel<TW, TQ, TV, D, GRP>), grid, dim3(AttnShape<TQ, TV, D, GRP>::NT), 0, s, p);
+  DSPINE_LAUNCH((attention_kernel<TW, TQ, TV, D, GRP>), grid, dim3(AttnShape<TQ, TV, D, GRP>::NT), 0, s, p);
   return hipGetLastError();
 }
 

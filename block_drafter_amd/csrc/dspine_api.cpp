@@ -89,26 +89,42 @@ Profiler& prof() {
   return p;
 }
 // Records a start event now and a stop event when it goes out of scope.
+// The pair of events the next launch on this thread records (see
+// DSPINE_LAUNCH); `pending` says it has not been taken yet.
+thread_local LaunchTimer t_timer;
+thread_local bool t_timer_pending = false;
+
+// Times the one kernel launched while it is alive, from the kernel's own
+// start to its end.
 class ProfScope {
  public:
-  ProfScope(int kind, hipStream_t s) : kind_(kind), s_(s) {
+  ProfScope(int kind, hipStream_t s) : kind_(kind) {
+    (void)s;
     Profiler& p = prof();
     if (!(p.mask & (1u << kind))) return;
     std::lock_guard<std::mutex> lk(p.mu);
     a_ = p.get();
     b_ = p.get();
-    if (a_ && b_) hipEventRecord(a_, s_);
+    if (a_ && b_) {
+      t_timer = LaunchTimer{a_, b_};
+      t_timer_pending = true;
+    }
   }
   ~ProfScope() {
     if (!a_ || !b_) return;
-    hipEventRecord(b_, s_);
+    const bool launched = !t_timer_pending;
+    t_timer_pending = false;
     Profiler& p = prof();
     std::lock_guard<std::mutex> lk(p.mu);
-    p.rec[kind_].emplace_back(a_, b_);
+    if (launched) {
+      p.rec[kind_].emplace_back(a_, b_);
+    } else {
+      p.pool.push_back(a_);
+      p.pool.push_back(b_);
+    }
   }
  private:
   int kind_;
-  hipStream_t s_;
   hipEvent_t a_ = nullptr, b_ = nullptr;
 };
 
@@ -374,6 +390,12 @@ int set_scaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, const f
 }
 
 }  // namespace
+
+const LaunchTimer* dspine::take_launch_timer() {
+  if (!t_timer_pending) return nullptr;
+  t_timer_pending = false;
+  return &t_timer;
+}
 
 // =============================================================================
 extern "C" {

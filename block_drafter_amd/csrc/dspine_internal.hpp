@@ -1,5 +1,6 @@
 // Internal interfaces between the C ABI (dspine_api.cpp) and the HIP kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -39,6 +40,23 @@ constexpr int kMaxRows = 128;      // B*W rows of one forward
 // ---------------------------------------------------------------------------
 // streamed (skinny) GEMM: out[m, n] (op)= sum_k A[m, k] W[n, k]
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Kernel timing: the profiler hands the next launch on this thread a pair of
+// events, which the launch records at the kernel's own start and end
+// (hipExtLaunchKernelGGL), so that a timed duration holds no queueing.
+// ---------------------------------------------------------------------------
+struct LaunchTimer {
+  hipEvent_t start, stop;
+};
+// the pending pair of this thread, cleared; NULL when none is pending
+const LaunchTimer* take_launch_timer();
+#define DSPINE_LAUNCH(kernel, grid, block, smem, stream, ...)                                       \
+  do {                                                                                              \
+    const ::dspine::LaunchTimer* lt_ = ::dspine::take_launch_timer();                               \
+    if (lt_) hipExtLaunchKernelGGL(kernel, grid, block, smem, stream, lt_->start, lt_->stop, 0, __VA_ARGS__); \
+    else hipLaunchKernelGGL(kernel, grid, block, smem, stream, __VA_ARGS__);                        \
+  } while (0)
+
 struct GemmParams {
   // weights: the virtual N space is a list of segments (or gate/up pairs)
   const void* seg_ptr[kMaxSeg];   // each [rows_s, K] row-major, model dtype

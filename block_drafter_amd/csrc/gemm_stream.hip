@@ -550,7 +550,7 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
   if (p.tiles <= grid_cap && p.tiles >= num_cus) G = p.tiles;
   else G = (int)(TI < grid_cap ? TI : grid_cap);
   p.xcd_remap = (G % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI>), dim3(G), dim3(256), 0, s, p);
+  DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI>), dim3(G), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -161,8 +161,8 @@ hipError_t launch_gemm_tile(const TileGemmParams& p, int dtype, int num_cus, hip
   for (int i = 1; i < p.nseg; ++i)
     if (p.seg_rows0[i] % kTileN != 0) return hipErrorInvalidValue;      // a tile never crosses a segment
   const int tiles = ((p.M + kTileM - 1) / kTileM) * (p.N / kTileN);
-  if (p.a_bf16) hipLaunchKernelGGL(gemm_tile_kernel<false>, dim3(tiles), dim3(512), 0, s, p);
-  else hipLaunchKernelGGL(gemm_tile_kernel<true>, dim3(tiles), dim3(512), 0, s, p);
+  if (p.a_bf16) DSPINE_LAUNCH(gemm_tile_kernel<false>, dim3(tiles), dim3(512), 0, s, p);
+  else DSPINE_LAUNCH(gemm_tile_kernel<true>, dim3(tiles), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

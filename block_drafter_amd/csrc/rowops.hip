@@ -245,8 +245,8 @@ __global__ void debug_visible_kernel(const VisibleParams p) {
 // ---------------------------------------------------------------------------
 #define DSPINE_DISPATCH(dtype, KERNEL, ...)                                               \
   do {                                                                                    \
-    if ((dtype) == DT_BF16) hipLaunchKernelGGL((KERNEL<bf16_t>), __VA_ARGS__);            \
-    else hipLaunchKernelGGL((KERNEL<float>), __VA_ARGS__);                                \
+    if ((dtype) == DT_BF16) DSPINE_LAUNCH((KERNEL<bf16_t>), __VA_ARGS__);            \
+    else DSPINE_LAUNCH((KERNEL<float>), __VA_ARGS__);                                \
   } while (0)
 
 hipError_t launch_embed(const RowParams& p, int dtype, hipStream_t s) {
@@ -255,11 +255,11 @@ hipError_t launch_embed(const RowParams& p, int dtype, hipStream_t s) {
 }
 hipError_t launch_rmsnorm(const RowParams& p, int dtype, bool f32_output, hipStream_t s) {
   if (dtype == DT_BF16) {
-    if (f32_output) hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, true>), dim3(p.M), dim3(kRowThreads), 0, s, p);
-    else hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, false>), dim3(p.M), dim3(kRowThreads), 0, s, p);
+    if (f32_output) DSPINE_LAUNCH((rmsnorm_kernel<bf16_t, true>), dim3(p.M), dim3(kRowThreads), 0, s, p);
+    else DSPINE_LAUNCH((rmsnorm_kernel<bf16_t, false>), dim3(p.M), dim3(kRowThreads), 0, s, p);
   } else {
-    if (f32_output) hipLaunchKernelGGL((rmsnorm_kernel<float, true>), dim3(p.M), dim3(kRowThreads), 0, s, p);
-    else hipLaunchKernelGGL((rmsnorm_kernel<float, false>), dim3(p.M), dim3(kRowThreads), 0, s, p);
+    if (f32_output) DSPINE_LAUNCH((rmsnorm_kernel<float, true>), dim3(p.M), dim3(kRowThreads), 0, s, p);
+    else DSPINE_LAUNCH((rmsnorm_kernel<float, false>), dim3(p.M), dim3(kRowThreads), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -273,7 +273,7 @@ hipError_t launch_bridge_msg(const ScaleParams& p, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_rowstats(const RowParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(rowstats_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
+  DSPINE_LAUNCH(rowstats_kernel, dim3(p.M), dim3(kRowThreads), 0, s, p);
   return hipGetLastError();
 }
 hipError_t launch_kv_store(const KvStoreParams& p, int dtype, hipStream_t s) {
@@ -286,17 +286,17 @@ hipError_t launch_pack(const void* src, void* dst, int rows, int cols, int dtype
   const size_t nfrag = (size_t)(rows / 16) * (cols / 32) * 64;
   const int grid = (int)std::min<size_t>((nfrag + 255) / 256, 8192);
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL((pack_kernel<uint16_t>), dim3(grid), dim3(256), 0, s,
+    DSPINE_LAUNCH((pack_kernel<uint16_t>), dim3(grid), dim3(256), 0, s,
                        static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), rows, cols);
   else
-    hipLaunchKernelGGL((pack_kernel<float>), dim3(grid), dim3(256), 0, s,
+    DSPINE_LAUNCH((pack_kernel<float>), dim3(grid), dim3(256), 0, s,
                        static_cast<const float*>(src), static_cast<float*>(dst), rows, cols);
   return hipGetLastError();
 }
 
 hipError_t launch_debug_visible(const VisibleParams& p, hipStream_t s) {
   const int n = p.B * p.W;
-  hipLaunchKernelGGL(debug_visible_kernel, dim3((n + 63) / 64), dim3(64), 0, s, p);
+  DSPINE_LAUNCH(debug_visible_kernel, dim3((n + 63) / 64), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
