@@ -175,7 +175,69 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
       for (int e = 0; e < VEPC; ++e) v_t[(part * VEPC + e) * LDV + kr] = val[e];
     }
   };
-  // first PF rounds in flight during the prologue below (clamped, in bounds)
+  // ---- prologue: head RMSNorm + RoPE of the block's q (and k) rows --------
+  // The prologue's rows are loaded first, then the first PF rounds of tiles
+  // go out (clamped, in bounds), then the prologue computes: the memory
+  // counter retires in issue order, so the rows never wait for the tiles.
+  constexpr int NP = D / 8;                   // rotation pairs per lane
+  struct PrepIn {
+    float xa[NP], xb[NP], ga[NP], gb[NP], co[NP], si[NP];
+  };
+  auto prep_load = [&](int col0, const void* gain, PrepIn& in) {
+    const int r = lane >> 2, part = lane & 3;
+    const bool live = r < W;
+    const gptr<float> src = as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + col0;
+    const gptr<float> cs = as_global(p.rope) + (size_t)(row_base + (live ? r : 0)) * D;   // (cos, sin) x D/2
+    const gptr<TW> gw = as_global(reinterpret_cast<const TW*>(gain));
+#pragma unroll
+    for (int jj = 0; jj < NP; ++jj) {
+      const int j = part * NP + jj;
+      in.xa[jj] = src[j];
+      in.xb[jj] = src[j + D / 2];
+      in.ga[jj] = Elt<TW>::gload(gw, j);
+      in.gb[jj] = Elt<TW>::gload(gw, j + D / 2);
+      in.co[jj] = cs[2 * j];
+      in.si[jj] = cs[2 * j + 1];
+    }
+  };
+  auto prep_store = [&](const PrepIn& in, TQ* dst) {
+    const int r = lane >> 2, part = lane & 3;
+    const bool live = r < W;
+    float ss = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < NP; ++jj) ss += in.xa[jj] * in.xa[jj] + in.xb[jj] * in.xb[jj];
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    const float inv = rsqrtf(ss / D + p.eps);
+#pragma unroll
+    for (int jj = 0; jj < NP; ++jj) {
+      const int j = part * NP + jj;
+      const float a = in.xa[jj] * inv * in.ga[jj];
+      const float c = in.xb[jj] * inv * in.gb[jj];
+      Elt<TQ>::store(dst, r * LDQ + j, live ? a * in.co[jj] - c * in.si[jj] : 0.f);
+      Elt<TQ>::store(dst, r * LDQ + j + D / 2, live ? c * in.co[jj] + a * in.si[jj] : 0.f);
+    }
+  };
+  // wave roles: sub-stream 0 prepares its head's q rows; in the split that
+  // owns the block, the last sub-stream's first wave its k rows and its
+  // second wave (or the first, for one head per group) its v rows
+  const bool do_q = sub == 0;
+  const bool do_k = has_block && sub == NSUB - 1 && hl == 0;
+  const bool do_v = has_block && sub == NSUB - 1 && hl == (GRP > 1 ? 1 : 0);
+  const int kcol = p.nq * D + g * D;
+  const int vcol = p.nq * D + p.nkv * D + g * D;
+  PrepIn pin;
+  if (do_q) prep_load(h * D, p.gq, pin);
+  else if (do_k) prep_load(kcol, p.gk, pin);
+  float vv[D / 4];
+  if (do_v && !do_k) {
+    const int r = lane >> 2, part = lane & 3;
+    const bool live = r < W;
+    const gptr<float> src =
+        as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + vcol + part * (D / 4);
+#pragma unroll
+    for (int d = 0; d < D / 4; ++d) vv[d] = src[d];
+  }
   if (n_tiles > 0) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
@@ -183,64 +245,24 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
       load_tile(kreg[j], vreg[j], i < n_tiles ? i : n_tiles - 1);
     }
   }
-
-  // ---- prologue: head RMSNorm + RoPE of the block's q (and k) rows --------
-  // Every operand is loaded into registers before the first use, through
-  // global-address-space pointers, so the row's loads share one latency.
-  auto prep_rows = [&](int col0, const void* gain, TQ* dst) {
+  if (do_q) prep_store(pin, sQ + hl * 16 * LDQ);
+  if (do_k) {
+    if (do_q) prep_load(kcol, p.gk, pin);        // (only with one sub-stream)
+    prep_store(pin, sK(NSUB));
+    for (int e = lane; e < 16 * D; e += 64) Elt<TQ>::store(sK(NSUB), (16 + e / D) * LDQ + e % D, 0.f);
+  }
+  if (do_v) {
     const int r = lane >> 2, part = lane & 3;
-    constexpr int NP = D / 8;               // rotation pairs per lane
     const bool live = r < W;
-    const gptr<float> src = as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + col0;
-    const gptr<float> cs = as_global(p.rope) + (size_t)(row_base + (live ? r : 0)) * D;   // (cos, sin) x D/2
-    const gptr<TW> gw = as_global(reinterpret_cast<const TW*>(gain));
-    float xa[NP], xb[NP], ga[NP], gb[NP], co[NP], si[NP];
-#pragma unroll
-    for (int jj = 0; jj < NP; ++jj) {
-      const int j = part * NP + jj;
-      xa[jj] = src[j];
-      xb[jj] = src[j + D / 2];
-      ga[jj] = Elt<TW>::gload(gw, j);
-      gb[jj] = Elt<TW>::gload(gw, j + D / 2);
-      co[jj] = cs[2 * j];
-      si[jj] = cs[2 * j + 1];
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < NP; ++jj) ss += xa[jj] * xa[jj] + xb[jj] * xb[jj];
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    const float inv = rsqrtf(ss / D + p.eps);
-#pragma unroll
-    for (int jj = 0; jj < NP; ++jj) {
-      const int j = part * NP + jj;
-      const float a = xa[jj] * inv * ga[jj];
-      const float c = xb[jj] * inv * gb[jj];
-      Elt<TQ>::store(dst, r * LDQ + j, live ? a * co[jj] - c * si[jj] : 0.f);
-      Elt<TQ>::store(dst, r * LDQ + j + D / 2, live ? c * co[jj] + a * si[jj] : 0.f);
-    }
-  };
-  if (sub == 0) prep_rows(h * D, p.gq, sQ + hl * 16 * LDQ);
-  // the block's own keys and values, staged by the last sub-stream
-  if (has_block && sub == NSUB - 1) {
-    const int kcol = p.nq * D + g * D;
-    const int vcol = p.nq * D + p.nkv * D + g * D;
-    if (hl == 0) {
-      prep_rows(kcol, p.gk, sK(NSUB));
-      for (int e = lane; e < 16 * D; e += 64) Elt<TQ>::store(sK(NSUB), (16 + e / D) * LDQ + e % D, 0.f);
-    }
-    if (hl == (GRP > 1 ? 1 : 0)) {
-      const int r = lane >> 2, part = lane & 3;
-      const bool live = r < W;
+    if (do_k) {                                   // one head per group: this wave does k and v
       const gptr<float> src =
           as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + vcol + part * (D / 4);
-      float vv[D / 4];
 #pragma unroll
       for (int d = 0; d < D / 4; ++d) vv[d] = src[d];
-#pragma unroll
-      for (int d = 0; d < D / 4; ++d) put_v(&sVt(NSUB)[(part * (D / 4) + d) * LDV + r], live ? vv[d] : 0.f);
-      for (int e = lane; e < 16 * D; e += 64) put_v(&sVt(NSUB)[(e / 16) * LDV + 16 + (e % 16)], 0.f);
     }
+#pragma unroll
+    for (int d = 0; d < D / 4; ++d) put_v(&sVt(NSUB)[(part * (D / 4) + d) * LDV + r], live ? vv[d] : 0.f);
+    for (int e = lane; e < 16 * D; e += 64) put_v(&sVt(NSUB)[(e / 16) * LDV + 16 + (e % 16)], 0.f);
   }
   __syncthreads();
 
@@ -268,14 +290,21 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
   auto process = [&](int t, int k0, bool is_block, bool mask) {
     f32x4 s[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
     const TQ* k_t = sK(t);
+    const TV* v_t = sVt(t);
+    // every fragment of the tile is read before the first multiply, so the
+    // LDS latencies overlap (the V^T reads with the softmax)
+    Frag<TQ> kf[D / 32][2];
+    Frag<TV> vf[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        Frag<TQ> kf;
-        kf.load(&k_t[(kt * 16 + (lane & 15)) * LDQ + c * 32 + 8 * (lane >> 4)]);
-        mma16(s[kt], kf, qf[c]);
-      }
+      for (int kt = 0; kt < 2; ++kt) kf[c][kt].load(&k_t[(kt * 16 + (lane & 15)) * LDQ + c * 32 + 8 * (lane >> 4)]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) load_vt(vf[dt], &v_t[(dt * 16 + (lane & 15)) * LDV], lane >> 4);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) mma16(s[kt], kf[c][kt], qf[c]);
     float sv[8];
     float tmax = -INFINITY;
 #pragma unroll
@@ -314,28 +343,29 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
     for (int e = 0; e < 8; ++e) psum += pv[e];
     l_lane = l_lane * alpha + psum;
     m_run = m_new;
-    const TV* v_t = sVt(t);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       o[dt] *= alpha;
-      Frag<TV> vf;
-      load_vt(vf, &v_t[(dt * 16 + (lane & 15)) * LDV], lane >> 4);
-      mma16(o[dt], vf, pf);
+      mma16(o[dt], vf[dt], pf);
     }
   };
 
-  // Every round issues the same loads (refills past the end re-read a valid
-  // tile), so the wait before each LDS store covers exactly one slot.
+  // Round r stages slot r % PF and refills it with round r + PF while there
+  // is one (the number of rounds is the same for every sub-stream of the
+  // workgroup, so the barriers match).
   for (int r0 = 0; r0 < rounds; r0 += PF) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int r = r0 + j;
+      if (r >= rounds) break;
       const int i = r * NSUB + sub;
-      const bool live = r < rounds && i < n_tiles;
+      const bool live = i < n_tiles;
       if (live) store_tile(kreg[j], vreg[j], i);
       __syncthreads();
-      const int inext = (r + PF) * NSUB + sub;
-      load_tile(kreg[j], vreg[j], inext < n_tiles ? inext : n_tiles - 1);
+      if (r + PF < rounds) {
+        const int inext = (r + PF) * NSUB + sub;
+        load_tile(kreg[j], vreg[j], inext < n_tiles ? inext : n_tiles - 1);
+      }
       if (live) {
         const bool edge = 32 * i + 32 > nkeys || 32 * i < lo_rel_max;
         process(sub, 32 * i, false, edge);
@@ -415,49 +445,48 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
   if ((int)s_flag != p.nsplit - 1) return;
 
   // Merge (last workgroup of this KV head): wave (head hl, part sub) merges
-  // head dims [sub*D/NSUB, (sub+1)*D/NSUB) of all splits: the maxima first
-  // (8 loads in flight), then the partials four splits at a time, in split
-  // order.  Indexes past the last split repeat it; those copies are not added.
+  // head dims [sub*D/NSUB, (sub+1)*D/NSUB) of all splits in one pass, MB
+  // splits at a time in split order, rescaling the running sum whenever the
+  // running maximum grows.  Indexes past the last split repeat it and are
+  // not added.  Plain loads suffice: each partial is written (through to
+  // memory) once per launch and read only after every split's arrival.
   constexpr int DPW = (D / 16) / NSUB;                  // 16-wide head-dim tiles per wave
+  constexpr int MB = DPW <= 4 ? 8 : 4;
   const float* hb = base + (size_t)hl * p.nsplit * PSZ;
-  float mstar = -INFINITY;
-  for (int sp0 = 0; sp0 < p.nsplit; sp0 += 8) {
-    float mv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int sp = sp0 + j < p.nsplit ? sp0 + j : p.nsplit - 1;
-      mv[j] = load_coherent(hb + (size_t)sp * PSZ + 64 * (D / 4) + qrow);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) mstar = fmaxf(mstar, mv[j]);
-  }
+  float mstar = -INFINITY, L = 0.f;
   f32x4 acc[DPW];
 #pragma unroll
   for (int d = 0; d < DPW; ++d) acc[d] = f32x4{0, 0, 0, 0};
-  float L = 0.f;
-  if (mstar != -INFINITY) {
-    constexpr int MB = 4;
-    for (int sp0 = 0; sp0 < p.nsplit; sp0 += MB) {
-      float mv[MB], lv[MB];
-      f32x4 ov[MB][DPW];
+  for (int sp0 = 0; sp0 < p.nsplit; sp0 += MB) {
+    float mv[MB], lv[MB];
+    f32x4 ov[MB][DPW];
 #pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        const int sp = sp0 + j < p.nsplit ? sp0 + j : p.nsplit - 1;
-        const float* pt = hb + (size_t)sp * PSZ;
-        mv[j] = load_coherent(pt + 64 * (D / 4) + qrow);
-        lv[j] = load_coherent(pt + 64 * (D / 4) + 16 + qrow);
+    for (int j = 0; j < MB; ++j) {
+      const int sp = sp0 + j < p.nsplit ? sp0 + j : p.nsplit - 1;
+      const gptr<float> pt = as_global(hb + (size_t)sp * PSZ);
+      mv[j] = pt[64 * (D / 4) + qrow];
+      lv[j] = pt[64 * (D / 4) + 16 + qrow];
 #pragma unroll
-        for (int d = 0; d < DPW; ++d) ov[j][d] = load_coherent4(pt + ((sub * DPW + d) * 64 + lane) * 4);
-      }
-#pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        if (sp0 + j >= p.nsplit || mv[j] == -INFINITY) continue;
-        const float wgt = exp2f(mv[j] - mstar);
-        L += wgt * lv[j];
-#pragma unroll
-        for (int d = 0; d < DPW; ++d) acc[d] += wgt * ov[j][d];
-      }
+      for (int d = 0; d < DPW; ++d) ov[j][d] = *as_global(reinterpret_cast<const f32x4*>(hb + (size_t)sp * PSZ) + (sub * DPW + d) * 64 + lane);
     }
+    float bm = mstar;
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+      if (sp0 + j < p.nsplit) bm = fmaxf(bm, mv[j]);
+    if (bm == -INFINITY) continue;
+    const float rescale = mstar == -INFINITY ? 0.f : exp2f(mstar - bm);
+    L *= rescale;
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) acc[d] *= rescale;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      if (sp0 + j >= p.nsplit || mv[j] == -INFINITY) continue;
+      const float wgt = exp2f(mv[j] - bm);
+      L += wgt * lv[j];
+#pragma unroll
+      for (int d = 0; d < DPW; ++d) acc[d] += wgt * ov[j][d];
+    }
+    mstar = bm;
   }
   if (qrow < W && L > 0.f) {
     const float inv = 1.f / L;

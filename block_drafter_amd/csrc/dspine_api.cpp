@@ -89,31 +89,35 @@ Profiler& prof() {
   return p;
 }
 // Records a start event now and a stop event when it goes out of scope.
-// The pair of events the next launch on this thread records (see
-// DSPINE_LAUNCH); `pending` says it has not been taken yet.
-thread_local LaunchTimer t_timer;
-thread_local bool t_timer_pending = false;
+// The events the launches of an open profiling scope on this thread record
+// (see DSPINE_LAUNCH): the first launch records `start` at its own start,
+// every launch records `stop` at its end (the last one counts).
+thread_local LaunchTimer t_scope{nullptr, nullptr};
+thread_local LaunchTimer t_give{nullptr, nullptr};
+thread_local bool t_scope_open = false;
+thread_local int t_scope_launches = 0;
 
-// Times the one kernel launched while it is alive, from the kernel's own
-// start to its end.
+// Times the kernels launched while it is alive, from the first one's start
+// to the last one's end.
 class ProfScope {
  public:
   ProfScope(int kind, hipStream_t s) : kind_(kind) {
     (void)s;
     Profiler& p = prof();
-    if (!(p.mask & (1u << kind))) return;
+    if (!(p.mask & (1u << kind)) || t_scope_open) return;
     std::lock_guard<std::mutex> lk(p.mu);
     a_ = p.get();
     b_ = p.get();
     if (a_ && b_) {
-      t_timer = LaunchTimer{a_, b_};
-      t_timer_pending = true;
+      t_scope = LaunchTimer{a_, b_};
+      t_scope_open = true;
+      t_scope_launches = 0;
     }
   }
   ~ProfScope() {
     if (!a_ || !b_) return;
-    const bool launched = !t_timer_pending;
-    t_timer_pending = false;
+    const bool launched = t_scope_launches > 0;
+    t_scope_open = false;
     Profiler& p = prof();
     std::lock_guard<std::mutex> lk(p.mu);
     if (launched) {
@@ -392,9 +396,10 @@ int set_scaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, const f
 }  // namespace
 
 const LaunchTimer* dspine::take_launch_timer() {
-  if (!t_timer_pending) return nullptr;
-  t_timer_pending = false;
-  return &t_timer;
+  if (!t_scope_open) return nullptr;
+  t_give = LaunchTimer{t_scope_launches == 0 ? t_scope.start : nullptr, t_scope.stop};
+  ++t_scope_launches;
+  return &t_give;
 }
 
 // =============================================================================

@@ -41,14 +41,16 @@ constexpr int kMaxRows = 128;      // B*W rows of one forward
 // streamed (skinny) GEMM: out[m, n] (op)= sum_k A[m, k] W[n, k]
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
-// Kernel timing: the profiler hands the next launch on this thread a pair of
-// events, which the launch records at the kernel's own start and end
-// (hipExtLaunchKernelGGL), so that a timed duration holds no queueing.
+// Kernel timing: while a profiling scope is open on this thread, each launch
+// takes events to record at the kernel's own start (the first launch) and
+// end (hipExtLaunchKernelGGL), so that a timed span holds no queueing before
+// its first kernel.
 // ---------------------------------------------------------------------------
 struct LaunchTimer {
   hipEvent_t start, stop;
 };
-// the pending pair of this thread, cleared; NULL when none is pending
+// the events for the next launch on this thread (either may be NULL); NULL
+// when no profiling scope is open
 const LaunchTimer* take_launch_timer();
 #define DSPINE_LAUNCH(kernel, grid, block, smem, stream, ...)                                       \
   do {                                                                                              \

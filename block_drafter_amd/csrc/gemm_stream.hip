@@ -309,7 +309,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       // result does not depend on arrival order (bit-reproducible runs).  The
       // own partial is read back like the others (the same values).  Loads go
       // out FB contributors at a time so their latencies overlap; indexes past
-      // the last contributor repeat it and are not added.
+      // the last contributor repeat it and are not added.  Plain loads are
+      // enough: each partial slot is written (through to memory) once per
+      // launch and read only after its writer's arrival, so no cache of this
+      // launch holds an older copy of it.
       constexpr int FB = NWB * MT <= 2 ? 8 : NWB * MT <= 4 ? 4 : NWB * MT <= 8 ? 2 : 1;
       f32x4 sum[NWB][MT];
 #pragma unroll
@@ -325,7 +328,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 #pragma unroll
           for (int nb = 0; nb < NWB; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < MT; ++mb) part[j][nb][mb] = load_coherent4(other + ((nb * MT + mb) * 256 + tid) * 4);
+            for (int mb = 0; mb < MT; ++mb)
+              part[j][nb][mb] = *as_global(reinterpret_cast<const f32x4*>(other + ((nb * MT + mb) * 256 + tid) * 4));
         }
 #pragma unroll
         for (int j = 0; j < FB; ++j) {
@@ -535,6 +539,8 @@ static int resident_cap(int grid_cap, int num_cus) {
   return cap < grid_cap ? cap : grid_cap;
 }
 
+constexpr int kMaxSplitWide = 6;   // contributors per tile for MT x NWB >= 8
+
 template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI>
 static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t s) {
   static_assert(NWB == 1 || NWB == 2, "tile widths");
@@ -544,11 +550,21 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
   p.tiles = (p.nblk + 4 * NWB - 1) / (4 * NWB);
   const int64_t TI = (int64_t)p.tiles * p.ipt;
   // One CU streams only about 25 GB/s, so every CU must take part: whole-K
-  // tiles only when there are at least as many tiles as CUs (and all fit at
-  // once); otherwise stream-K over the resident grid.
+  // tiles when there are at least as many tiles as CUs (and all fit at
+  // once), or when a tile's whole K fits in the register stages (its loads
+  // all go out at once and no partials have to be combined); otherwise
+  // stream-K over the resident grid.
+  // A split tile is finished by one workgroup that reads every contributor's
+  // partial tile (MT x NWB x 4 KB); for the wide tiles of large blocks that
+  // read dominates past a few contributors, so their splits are capped.
   int G;
-  if (p.tiles <= grid_cap && p.tiles >= num_cus) G = p.tiles;
-  else G = (int)(TI < grid_cap ? TI : grid_cap);
+  if (p.tiles <= grid_cap && (p.tiles >= num_cus || p.ipt <= PD + 1)) {
+    G = p.tiles;
+  } else {
+    int64_t g = TI < grid_cap ? TI : grid_cap;
+    if (MT * NWB >= 8 && g > (int64_t)p.tiles * kMaxSplitWide) g = (int64_t)p.tiles * kMaxSplitWide;
+    G = (int)g;
+  }
   p.xcd_remap = (G % 8 == 0) ? 1 : 0;
   DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI>), dim3(G), dim3(256), 0, s, p);
   return hipGetLastError();
