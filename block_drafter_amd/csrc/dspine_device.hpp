@@ -197,6 +197,17 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
+// LDS address space (the destination of direct-to-LDS loads)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt and lgkmcnt at their "no wait" maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------------------
 // Cross-workgroup handoff of partial results (last arriver finishes).
 //

@@ -100,7 +100,7 @@ constexpr int a_regs() {
 
 }  // namespace
 
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI>
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   using T = TA;                                 // LDS / MFMA operand type
   constexpr int EB = Elt<TA>::kBytes;
@@ -116,8 +116,18 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   static_assert(NST >= 1 && NST <= 4, "stages");
   constexpr int AR = a_regs<PRO, EPC>();
   constexpr bool kScaledA = PRO == PRO_NORM || PRO == PRO_SCALE;
+  // DMA: the activation chunk of a stage goes global -> LDS directly
+  // (global_load_lds_dwordx4) into a ring slot in MFMA operand order, so the
+  // register stages hold weights only; K must be a multiple of KS.
+  static_assert(!DMA || ((PRO == PRO_COPY || PRO == PRO_GATHER) && EB == 2 && (MT * KSUB) % 4 == 0 && NST >= 2),
+                "direct-to-LDS activations: 16-bit copy or gather operands");
+  constexpr int SLOT = MT * KSUB * 1024;        // DMA: one stage's chunk, 1 KB blocks [mb][ks]
+  constexpr int DBLK = MT * KSUB / 4;           // DMA: blocks per wave per stage
+  constexpr int WLD = NWB * KSUB;               // weight loads per wave per stage
+  static_assert(!DMA || (256 / MP) * MP * 4 <= SLOT, "row-scale scratch fits a ring slot");
 
-  __shared__ __attribute__((aligned(16))) T lds[2][MP * LDA];
+  __shared__ __attribute__((aligned(16))) T lds[2][DMA ? 8 : MP * LDA];
+  __shared__ __attribute__((aligned(1024))) char adma[DMA ? NST * SLOT : 16];
   __shared__ uint32_t s_flag;
   __shared__ SegTable s_seg;
   __shared__ float s_scale[MP];      // per-row scale (SCALE_* modes)
@@ -157,8 +167,19 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     else arow[q] = a_row_ptr<PRO, TA>(p, m);
   }
 
+  // DMA: lane l of block (mb, ks) fetches row mb*16 + l%16, K 8 (l/16) of
+  // the block's 32-K step; this wave takes blocks wave, wave + 4, ...
+  const TA* drow[DMA ? DBLK : 1];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int q = 0; q < DBLK; ++q) {
+      const int bi = wave + 4 * q;
+      drow[q] = a_row_ptr<PRO, TA>(p, (bi / KSUB) * 16 + (lane & 15)) + (bi % KSUB) * 32 + 8 * (lane >> 4);
+    }
+  }
+
   Frag<TW> wf[NST][NWB][KSUB];
-  u32x4 areg[NST][NCH][AR];
+  u32x4 areg[DMA ? 1 : NST][NCH][AR];
 
   // Stage j <- iteration it: activation chunk(s) first, then the weights.
   // Nothing may consume a prefetched value before it is needed: past the
@@ -167,8 +188,15 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   auto load_stage = [&](int j, int it) __attribute__((always_inline)) {
     const int tile = it / ipt;
     const int k0 = (it - tile * ipt) * KS;
+    if constexpr (DMA) {
+      char* slot = adma + j * SLOT;
 #pragma unroll
-    for (int q = 0; q < NCH; ++q) {
+      for (int q = 0; q < DBLK; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(drow[q] + k0), (lds_void*)(slot + (wave + 4 * q) * 1024), 16,
+                                         0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < (DMA ? 0 : NCH); ++q) {
       const int c = tid + q * 256;
       const int k = k0 + (c % CPR) * EPC;
       const int kc = k < p.K ? k : p.K - EPC;
@@ -214,6 +242,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   };
   // activation chunk of stage j (iteration it) -> LDS buffer buf
   auto store_a = [&](int buf, int j, int it) __attribute__((always_inline)) {
+    if constexpr (DMA) return;
     const int k0 = (it - (it / ipt) * ipt) * KS;
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
@@ -271,7 +300,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 #pragma unroll
       for (int mb = 0; mb < MT; ++mb) {
         Frag<T> af;
-        af.load(&lds[buf][(mb * 16 + (lane & 15)) * LDA + s * 32 + 8 * (lane >> 4)]);
+        if constexpr (DMA)
+          af.v = *reinterpret_cast<const u32x4*>(adma + j * SLOT + (mb * KSUB + s) * 1024 + lane * 16);
+        else
+          af.load(&lds[buf][(mb * 16 + (lane & 15)) * LDA + s * 32 + 8 * (lane >> 4)]);
 #pragma unroll
         for (int nb = 0; nb < NWB; ++nb) mma16(acc[nb][mb], wo[nb], af);
       }
@@ -444,7 +476,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     }
   }
 #pragma unroll
-  for (int j = 0; j < NST; ++j) load_stage(j, it_beg + j < it_end ? it_beg + j : it_end - 1);
+  for (int j = 0; j < (DMA ? NST - 1 : NST); ++j) load_stage(j, it_beg + j < it_end ? it_beg + j : it_end - 1);
   if (p.scale_mode == SCALE_ONE) {
     if (tid < MP) s_scale[tid] = 1.f;
     __syncthreads();
@@ -463,7 +495,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       for (int u = 0; u < LB; ++u)
         if (t0 + u * Q < p.stats_tiles) part += sv[u];
     }
-    float* s_part = reinterpret_cast<float*>(lds[1]);  // [Q][MP], free until the first step
+    // [Q][MP] scratch, free until the first step: the second activation
+    // buffer, or (direct-to-LDS) the ring slot the prologue leaves empty
+    float* s_part = DMA ? reinterpret_cast<float*>(adma + (NST - 1) * SLOT) : reinterpret_cast<float*>(lds[1]);
     s_part[sq0 * MP + sm] = part;
     __syncthreads();
     if (tid < MP) {
@@ -473,6 +507,44 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       s_scale[tid] = tid < p.M ? row_scale_of(p, tid, S) : 0.f;
     }
     __syncthreads();
+  }
+  if constexpr (DMA) {
+    // Ring of NST stages, NST - 1 in flight.  Step `it` (stage j = it % NST):
+    // wait for this wave's part of stage j (the loads issued after it are
+    // stage j's weights and the NST - 2 later stages; anything the epilogue
+    // issues only adds to that), then the barrier makes every wave's part
+    // visible and says every wave is done with stage j - 1, whose slot and
+    // registers then take iteration it + NST - 1.
+    int it = it_beg;
+    int seg_k0 = it_beg % ipt;
+    auto dstep = [&](auto J) __attribute__((always_inline)) -> bool {
+      constexpr int j = decltype(J)::value;
+      wait_vmcnt<WLD + (NST - 2) * (DBLK + WLD)>();
+      __builtin_amdgcn_s_barrier();
+      load_stage((j + NST - 1) % NST, it + NST - 1 < it_end ? it + NST - 1 : it_end - 1);
+      compute(0, j);
+      const bool has_next = it + 1 < it_end;
+      const int tile = it / ipt;
+      const int kk = it - tile * ipt;
+      if (!has_next || kk == ipt - 1) {
+        finish(tile, seg_k0, kk + 1);
+        seg_k0 = 0;
+      }
+      if (!has_next) return false;
+      ++it;
+      return true;
+    };
+    while (true) {
+      if (!dstep(std::integral_constant<int, 0>{})) break;
+      if (!dstep(std::integral_constant<int, 1 % NST>{})) break;
+      if constexpr (NST > 2) {
+        if (!dstep(std::integral_constant<int, 2 % NST>{})) break;
+      }
+      if constexpr (NST > 3) {
+        if (!dstep(std::integral_constant<int, 3 % NST>{})) break;
+      }
+    }
+    return;
   }
   store_a(0, 0, it_beg);
   __syncthreads();
@@ -524,12 +596,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 // Stream-K and whole-K tiles both assume every workgroup of the grid is
 // resident at once: the grid is capped at what the kernel's occupancy
 // allows on all CUs.
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI>
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA>
 static int resident_cap(int grid_cap, int num_cus) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA>,
                                                       256, 0) != hipSuccess ||
         n < 1)
       n = 1;
@@ -541,11 +613,11 @@ static int resident_cap(int grid_cap, int num_cus) {
 
 constexpr int kMaxSplitWide = 6;   // contributors per tile for MT x NWB >= 8
 
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI>
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA = false>
 static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t s) {
   static_assert(NWB == 1 || NWB == 2, "tile widths");
   constexpr int KS = 32 * KSUB;
-  grid_cap = resident_cap<TW, TA, MT, NWB, KSUB, PD, PRO, EPI>(grid_cap, num_cus);
+  grid_cap = resident_cap<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA>(grid_cap, num_cus);
   p.ipt = (p.K + KS - 1) / KS;
   p.tiles = (p.nblk + 4 * NWB - 1) / (4 * NWB);
   const int64_t TI = (int64_t)p.tiles * p.ipt;
@@ -566,7 +638,7 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
     G = (int)g;
   }
   p.xcd_remap = (G % 8 == 0) ? 1 : 0;
-  DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI>), dim3(G), dim3(256), 0, s, p);
+  DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA>), dim3(G), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -598,6 +670,15 @@ static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipS
     // 64 and 128 rows take pre-scaled operands (the launcher's caller forms
     // them), in 128-column tiles so that each staged activation chunk feeds
     // twice the weights
+    // 16-bit operands with K a multiple of the stage move the activation
+    // chunks global -> LDS directly, leaving the registers to four weight
+    // stages
+    if constexpr (kHalf) {
+      if (p.K % 128 == 0) {
+        if (mt <= 4) return launch_t<TW, TA, 4, 2, 4, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
+        return launch_t<TW, TA, 8, 2, 4, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
+      }
+    }
     if (mt <= 4) return launch_t<TW, TA, 4, 2, kHalf ? 4 : 2, 1, PRO, EPI>(p, grid_cap, num_cus, s);
     return launch_t<TW, TA, 8, 2, kHalf ? 4 : 1, 1, PRO, EPI>(p, grid_cap, num_cus, s);
   }

@@ -31,17 +31,6 @@
 
 namespace dspine {
 
-namespace {
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt and lgkmcnt at their "no wait" maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-}  // namespace
 
 constexpr int kGroupM = 8;          // row tiles per group of the tile order
 constexpr int kTileM = 256, kTileN = 256;
