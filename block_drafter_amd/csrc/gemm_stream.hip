@@ -612,6 +612,7 @@ static int resident_cap(int grid_cap, int num_cus) {
 }
 
 constexpr int kMaxSplitWide = 6;   // contributors per tile for MT x NWB >= 8
+constexpr int kMaxSplitSmall = 8;  // contributors per tile for MT <= 2 (one load batch of the finisher)
 
 template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA = false>
 static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t s) {
@@ -629,12 +630,20 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
   // A split tile is finished by one workgroup that reads every contributor's
   // partial tile (MT x NWB x 4 KB); for the wide tiles of large blocks that
   // read dominates past a few contributors, so their splits are capped.
+  // Small tiles take one workgroup per CU (a second one per CU only adds
+  // contributors) and at most as many contributors as the finisher loads in
+  // one batch (the 16-row bridge projection onto 1024 codes ran 15 us split
+  // 20 ways, 10 us split 8 ways).
   int G;
   if (p.tiles <= grid_cap && (p.tiles >= num_cus || p.ipt <= PD + 1)) {
     G = p.tiles;
   } else {
     int64_t g = TI < grid_cap ? TI : grid_cap;
     if (MT * NWB >= 8 && g > (int64_t)p.tiles * kMaxSplitWide) g = (int64_t)p.tiles * kMaxSplitWide;
+    if (MT <= 2) {
+      if (g > num_cus) g = num_cus;
+      if (g > (int64_t)p.tiles * kMaxSplitSmall) g = (int64_t)p.tiles * kMaxSplitSmall;
+    }
     G = (int)g;
   }
   p.xcd_remap = (G % 8 == 0) ? 1 : 0;
