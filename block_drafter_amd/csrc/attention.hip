@@ -102,7 +102,10 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
   auto sVt = [&](int t) { return reinterpret_cast<TV*>(smem + Sh::Q_BYTES + t * Sh::TILE + Sh::K_BYTES); };
 
   const int b = blockIdx.z, g = blockIdx.y, split = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform per wave: keeping it scalar keeps the role
+  // branches and the parameter loads they select (gains, columns) scalar,
+  // instead of vector loads queued behind the tile prefetch
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = w % GRP, sub = w / GRP;                // head within the group, sub-stream
   const int h = g * GRP + hl;
   const int gtid = tid - sub * GT;                      // thread index within the sub-stream
@@ -143,6 +146,25 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
     }
     return (head_base + (size_t)slot) * D;
   };
+  // V chunks: with 16-bit values and an even count per thread, a thread
+  // takes keys 2m and 2m+1 of one 8-value part (pair index pi = gtid +
+  // (q/2) GT, m = pi % 16, part = pi / 16), so that the transposed store
+  // writes both keys of a head dim as one 32-bit word; otherwise chunk c =
+  // gtid + q GT is key c / VCH, part c % VCH.
+  constexpr bool kPairV = EV == 2 && VPT % 2 == 0;
+  auto v_chunk = [&](int q, int& kr, int& part) __attribute__((always_inline)) -> bool {
+    if constexpr (kPairV) {
+      const int pi = gtid + (q >> 1) * GT;
+      kr = 2 * (pi % 16) + (q & 1);
+      part = pi / 16;
+      return pi < 16 * VCH;
+    } else {
+      const int c = gtid + q * GT;
+      kr = c / VCH;
+      part = c % VCH;
+      return c < 32 * VCH;
+    }
+  };
   auto load_tile = [&](u32x4 (&kr_)[KPT], u32x4 (&vr_)[VPT], int i) {
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
@@ -151,8 +173,9 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
     }
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
-      const int c = (gtid + q * GT) % (32 * VCH);
-      vr_[q] = gload16((gptr<void>)(vring + key_row(i, c / VCH) + (c % VCH) * VEPC));
+      int kr, part;
+      if (!v_chunk(q, kr, part)) kr = part = 0;          // spare thread: re-load chunk 0
+      vr_[q] = gload16((gptr<void>)(vring + key_row(i, kr) + part * VEPC));
     }
   };
   auto store_tile = [&](const u32x4 (&kr_)[KPT], const u32x4 (&vr_)[VPT], int i) {
@@ -165,20 +188,48 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
         *reinterpret_cast<u32x4*>(&k_t[(c / KCH) * LDQ + (c % KCH) * KEPC]) =
             key_chunk(kr_[q], (TW*)nullptr, (TQ*)nullptr);
     }
+    if constexpr (kPairV) {
+      // both keys of a head dim in one 32-bit word; lanes whose part has bit
+      // 1 set take the dims in the order 4..7, 0..3, which puts the 64 lanes
+      // of a wave on distinct banks (a V^T row is LDV/2 words)
 #pragma unroll
-    for (int q = 0; q < VPT; ++q) {
-      const int c = gtid + q * GT, kr = c / VCH, part = c % VCH;
-      if (c >= 32 * VCH) continue;
-      alignas(16) TV val[VEPC];
-      *reinterpret_cast<u32x4*>(val) = 32 * i + kr < nkeys ? vr_[q] : u32x4{0, 0, 0, 0};
+      for (int q = 0; q < VPT; q += 2) {
+        int kr, part;
+        if (!v_chunk(q, kr, part)) continue;
+        u32x4 a = 32 * i + kr < nkeys ? vr_[q] : u32x4{0, 0, 0, 0};
+        u32x4 b = 32 * i + kr + 1 < nkeys ? vr_[q + 1] : u32x4{0, 0, 0, 0};
+        const bool rot = (part >> 1) & 1;
+        if (rot) {
+          a = u32x4{a[2], a[3], a[0], a[1]};
+          b = u32x4{b[2], b[3], b[0], b[1]};
+        }
+        uint32_t* row = reinterpret_cast<uint32_t*>(v_t) + kr / 2;
 #pragma unroll
-      for (int e = 0; e < VEPC; ++e) v_t[(part * VEPC + e) * LDV + kr] = val[e];
+        for (int e = 0; e < VEPC; ++e) {
+          const int dim = part * VEPC + ((e + (rot ? 4 : 0)) & 7);
+          const uint32_t lo = e & 1 ? a[e >> 1] >> 16 : a[e >> 1] & 0xffffu;
+          const uint32_t hi = e & 1 ? b[e >> 1] >> 16 : b[e >> 1] & 0xffffu;
+          row[dim * (LDV / 2)] = lo | (hi << 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < VPT; ++q) {
+        int kr, part;
+        if (!v_chunk(q, kr, part)) continue;
+        alignas(16) TV val[VEPC];
+        *reinterpret_cast<u32x4*>(val) = 32 * i + kr < nkeys ? vr_[q] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < VEPC; ++e) v_t[(part * VEPC + e) * LDV + kr] = val[e];
+      }
     }
   };
   // ---- prologue: head RMSNorm + RoPE of the block's q (and k) rows --------
-  // The prologue's rows are loaded first, then the first PF rounds of tiles
-  // go out (clamped, in bounds), then the prologue computes: the memory
-  // counter retires in issue order, so the rows never wait for the tiles.
+  // The first PF rounds of tiles go out (clamped, in bounds), then the
+  // prologue's rows, then the prologue computes: the rows wait for the tiles
+  // (the memory counter retires in issue order), but the two latencies
+  // overlap instead of adding up (with the rows first, the compiler consumed
+  // them before issuing the tiles).
   constexpr int NP = D / 8;                   // rotation pairs per lane
   struct PrepIn {
     float xa[NP], xb[NP], ga[NP], gb[NP], co[NP], si[NP];
@@ -226,6 +277,13 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
   const bool do_v = has_block && sub == NSUB - 1 && hl == (GRP > 1 ? 1 : 0);
   const int kcol = p.nq * D + g * D;
   const int vcol = p.nq * D + p.nkv * D + g * D;
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int i = j * NSUB + sub;
+      load_tile(kreg[j], vreg[j], i < n_tiles ? i : n_tiles - 1);
+    }
+  }
   PrepIn pin;
   if (do_q) prep_load(h * D, p.gq, pin);
   else if (do_k) prep_load(kcol, p.gk, pin);
@@ -237,13 +295,6 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
         as_global(p.qkv) + (size_t)(row_base + (live ? r : 0)) * p.ld_qkv + vcol + part * (D / 4);
 #pragma unroll
     for (int d = 0; d < D / 4; ++d) vv[d] = src[d];
-  }
-  if (n_tiles > 0) {
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int i = j * NSUB + sub;
-      load_tile(kreg[j], vreg[j], i < n_tiles ? i : n_tiles - 1);
-    }
   }
   if (do_q) prep_store(pin, sQ + hl * 16 * LDQ);
   if (do_k) {
@@ -352,8 +403,30 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
 
   // Round r stages slot r % PF and refills it with round r + PF while there
   // is one (the number of rounds is the same for every sub-stream of the
-  // workgroup, so the barriers match).
-  for (int r0 = 0; r0 < rounds; r0 += PF) {
+  // workgroup, so the barriers match).  Passes whose refills are all needed
+  // run without any exit or condition around the loads: with a break or a
+  // skipped refill inside the unrolled pass, the compiler routes every slot
+  // through one set of registers, and the copy waits for the load just
+  // issued, so each round would cost a full memory round trip.
+  int r0 = 0;
+  for (; r0 + 2 * PF <= rounds; r0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int r = r0 + j;
+      const int i = r * NSUB + sub;
+      const bool live = i < n_tiles;
+      if (live) store_tile(kreg[j], vreg[j], i);
+      __syncthreads();
+      const int inext = (r + PF) * NSUB + sub;
+      load_tile(kreg[j], vreg[j], inext < n_tiles ? inext : n_tiles - 1);
+      if (live) {
+        const bool edge = 32 * i + 32 > nkeys || 32 * i < lo_rel_max;
+        process(sub, 32 * i, false, edge);
+      }
+      __syncthreads();
+    }
+  }
+  for (; r0 < rounds; r0 += PF) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int r = r0 + j;
