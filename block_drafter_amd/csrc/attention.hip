@@ -15,9 +15,8 @@
 // computes S^T = K Q^T with 16x16x32 MFMAs: each lane then owns one query
 // row (lane % 16), which makes the online-softmax rescale of the
 // O^T = V^T P^T accumulators lane-local.  Sub-streams are combined through
-// LDS with their log-sum-exp; splits over context keys are merged the same
-// way by the last workgroup to finish each (request, KV head), all of its
-// waves sharing the merge.  Ring slots advance in int32 from one modulo per
+// LDS with their log-sum-exp; splits over context keys publish partials
+// that a second, small kernel merges per (request, query head).  Ring slots advance in int32 from one modulo per
 // workgroup; the window and tail masks run only on the tiles that straddle
 // an edge.
 #include "dspine_device.hpp"
@@ -96,7 +95,6 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
   constexpr int PSZ = 64 * (D / 4) + 32;                // floats of one split partial in HBM
 
   __shared__ __attribute__((aligned(16))) char smem[Sh::SMEM];
-  __shared__ uint32_t s_flag;
   TQ* const sQ = reinterpret_cast<TQ*>(smem);           // [GRP][16][LDQ]
   auto sK = [&](int t) { return reinterpret_cast<TQ*>(smem + Sh::Q_BYTES + t * Sh::TILE); };
   auto sVt = [&](int t) { return reinterpret_cast<TV*>(smem + Sh::Q_BYTES + t * Sh::TILE + Sh::K_BYTES); };
@@ -501,31 +499,34 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
     }
     return;
   }
+  // publish this split's partial (o unnormalised, row max, row sum); the
+  // merge kernel that follows on the stream combines the splits
   float* base = p.partials + (size_t)(b * p.nq + g * GRP) * p.nsplit * PSZ;   // [GRP][nsplit][PSZ]
   if (sub == 0) {
     float* mine = base + (size_t)(hl * p.nsplit + split) * PSZ;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) store_coherent(mine + (dt * 64 + lane) * 4, o[dt]);
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(mine + (dt * 64 + lane) * 4) = o[dt];
     if (lane < 16) {
-      store_coherent(mine + 64 * (D / 4) + lane, m_run);
-      store_coherent(mine + 64 * (D / 4) + 16 + lane, lrow);
+      mine[64 * (D / 4) + lane] = m_run;
+      mine[64 * (D / 4) + 16 + lane] = lrow;
     }
-    drain_own_stores();
   }
-  __syncthreads();
-  if (tid == 0) s_flag = count_arrival(p.counters + b * p.nkv + g);
-  __syncthreads();
-  if ((int)s_flag != p.nsplit - 1) return;
+}
 
-  // Merge (last workgroup of this KV head): wave (head hl, part sub) merges
-  // head dims [sub*D/NSUB, (sub+1)*D/NSUB) of all splits in one pass, MB
-  // splits at a time in split order, rescaling the running sum whenever the
-  // running maximum grows.  Indexes past the last split repeat it and are
-  // not added.  Plain loads suffice: each partial is written (through to
-  // memory) once per launch and read only after every split's arrival.
-  constexpr int DPW = (D / 16) / NSUB;                  // 16-wide head-dim tiles per wave
+// Split merge: one workgroup per (query head, request), two waves, each
+// merging half of the head dims over every split of the head, MB splits at a
+// time in split order, rescaling the running sum whenever the running
+// maximum grows (the same order on every run: bit-reproducible).  Indexes
+// past the last split repeat it and are not added.
+template <typename TQ, int D>
+__global__ __launch_bounds__(128) void attn_merge_kernel(const AttnParams p) {
+  constexpr int PSZ = 64 * (D / 4) + 32;                // floats of one split partial
+  constexpr int DPW = (D / 16) / 2;                     // 16-wide head-dim tiles per wave
   constexpr int MB = DPW <= 4 ? 8 : 4;
-  const float* hb = base + (size_t)hl * p.nsplit * PSZ;
+  static_assert((D / 16) % 2 == 0, "two waves split the head dims");
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, qrow = lane & 15;
+  const float* hb = p.partials + (size_t)(b * p.nq + h) * p.nsplit * PSZ;
   float mstar = -INFINITY, L = 0.f;
   f32x4 acc[DPW];
 #pragma unroll
@@ -540,7 +541,8 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
       mv[j] = pt[64 * (D / 4) + qrow];
       lv[j] = pt[64 * (D / 4) + 16 + qrow];
 #pragma unroll
-      for (int d = 0; d < DPW; ++d) ov[j][d] = *as_global(reinterpret_cast<const f32x4*>(hb + (size_t)sp * PSZ) + (sub * DPW + d) * 64 + lane);
+      for (int d = 0; d < DPW; ++d)
+        ov[j][d] = *as_global(reinterpret_cast<const f32x4*>(hb + (size_t)sp * PSZ) + (wv * DPW + d) * 64 + lane);
     }
     float bm = mstar;
 #pragma unroll
@@ -561,15 +563,14 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
     }
     mstar = bm;
   }
-  if (qrow < W && L > 0.f) {
+  if (qrow < p.W && L > 0.f) {
     const float inv = 1.f / L;
-    TQ* dst = out + (size_t)(row_base + qrow) * p.ld_out + h * D + 4 * (lane >> 4);
+    TQ* dst = reinterpret_cast<TQ*>(p.out) + (size_t)(b * p.W + qrow) * p.ld_out + h * D + 4 * (lane >> 4);
 #pragma unroll
     for (int d = 0; d < DPW; ++d)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Elt<TQ>::store(dst, (sub * DPW + d) * 16 + v, acc[d][v] * inv);
+      for (int v = 0; v < 4; ++v) Elt<TQ>::store(dst, (wv * DPW + d) * 16 + v, acc[d][v] * inv);
   }
-  if (tid == 0) reset_counter(p.counters + b * p.nkv + g);
 }
 
 size_t attn_partial_floats(int max_b, int nq, int head_dim) {
@@ -580,6 +581,7 @@ template <typename TW, typename TQ, typename TV, int D, int GRP>
 static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
   const dim3 grid(p.nsplit, p.nkv, p.B);
   DSPINE_LAUNCH((attention_kernel<TW, TQ, TV, D, GRP>), grid, dim3(AttnShape<TQ, TV, D, GRP>::NT), 0, s, p);
+  if (p.nsplit > 1) DSPINE_LAUNCH((attn_merge_kernel<TQ, D>), dim3(p.nq, p.B), dim3(128), 0, s, p);
   return hipGetLastError();
 }
 

@@ -145,7 +145,7 @@ int64_t live_lo(int S, int64_t F) { return S == 0 ? 0 : std::max<int64_t>(0, F -
 // zero from call to call whatever else the calls put in the buffer.
 // ---------------------------------------------------------------------------
 struct Plan {
-  size_t gemm_cnt, attn_cnt;              // u32 counters
+  size_t gemm_cnt;                        // u32 tile counters
   size_t gemm_part, attn_part;            // f32 partials
   size_t x, act_q, act_f, qkv, z, P, P2, rope;
   size_t act_h, act_r, act_m;             // pre-scaled operands (large blocks)
@@ -168,7 +168,6 @@ Plan make_plan(const dspine_geometry& g, int64_t M, int64_t rows) {
     return o;
   };
   p.gemm_cnt = take(sizeof(uint32_t) * kMaxTiles);
-  p.attn_cnt = take(sizeof(uint32_t) * DSPINE_MAX_BATCH * g.n_q_heads);
   p.gemm_part = take(sizeof(float) * gemm_stream_partial_floats(kMaxGrid));
   p.attn_part = take(sizeof(float) * attn_partial_floats(DSPINE_MAX_BATCH, g.n_q_heads, g.head_dim));
   p.x = take(4 * Mp * g.hidden);
@@ -1002,7 +1001,6 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
     ap.out = act_q;
     ap.ld_out = qd;
     ap.partials = reinterpret_cast<float*>(ws + P.attn_part);
-    ap.counters = reinterpret_cast<uint32_t*>(ws + P.attn_cnt);
     {
       ProfScope ps(DSPINE_PROF_ATTENTION, stream);
       HIP_TRY(launch_attention(ap, g.dtype, D, stream));

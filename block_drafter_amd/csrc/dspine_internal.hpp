@@ -155,8 +155,7 @@ struct AttnParams {
   int32_t nsplit;
   void* out;                      // model dtype [M, ld_out]
   int32_t ld_out;
-  float* partials;
-  uint32_t* counters;             // [B * nq]
+  float* partials;                // [B][nq][nsplit] split partials, merged by a second kernel
 };
 hipError_t launch_attention(const AttnParams& p, int dtype, int head_dim, hipStream_t s);
 size_t attn_partial_floats(int max_b, int nq, int head_dim);
