@@ -65,6 +65,14 @@ def test_small_geometries_ragged_batch(g):
     check_run(run)
 
 
+def test_many_key_splits():
+    """Long contexts on a full-attention layer: the keys are cut into ten
+    splits (two merge batches), the last one ragged, and a second request
+    with a third of the keys (splits past its end are empty)."""
+    run = Run(Case(G_B, 81, 2, 16, [1200, 333]))
+    check_run(run)
+
+
 @pytest.mark.parametrize("W", [2, 5, 16])
 def test_block_widths(W):
     run = Run(Case(G_B, 78, 3, W, [45, 90, 12]))
