@@ -223,11 +223,10 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
     }
   };
   // ---- prologue: head RMSNorm + RoPE of the block's q (and k) rows --------
-  // The first PF rounds of tiles go out (clamped, in bounds), then the
-  // prologue's rows, then the prologue computes: the rows wait for the tiles
-  // (the memory counter retires in issue order), but the two latencies
-  // overlap instead of adding up (with the rows first, the compiler consumed
-  // them before issuing the tiles).
+  // Round 0's tile goes out first, then the prologue's rows, then the tiles
+  // of rounds 1 .. PF-1 (all clamped, in bounds): the prologue waits for its
+  // rows and the first tile only (the memory counter retires in issue
+  // order), while the later tiles stream in behind.
   constexpr int NP = D / 8;                   // rotation pairs per lane
   struct PrepIn {
     float xa[NP], xb[NP], ga[NP], gb[NP], co[NP], si[NP];
@@ -275,13 +274,7 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
   const bool do_v = has_block && sub == NSUB - 1 && hl == (GRP > 1 ? 1 : 0);
   const int kcol = p.nq * D + g * D;
   const int vcol = p.nq * D + p.nkv * D + g * D;
-  if (n_tiles > 0) {
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int i = j * NSUB + sub;
-      load_tile(kreg[j], vreg[j], i < n_tiles ? i : n_tiles - 1);
-    }
-  }
+  if (n_tiles > 0) load_tile(kreg[0], vreg[0], sub < n_tiles ? sub : n_tiles - 1);
   PrepIn pin;
   if (do_q) prep_load(h * D, p.gq, pin);
   else if (do_k) prep_load(kcol, p.gk, pin);
@@ -294,6 +287,14 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
 #pragma unroll
     for (int d = 0; d < D / 4; ++d) vv[d] = src[d];
   }
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int j = 1; j < PF; ++j) {
+      const int i = j * NSUB + sub;
+      load_tile(kreg[j], vreg[j], i < n_tiles ? i : n_tiles - 1);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   if (do_q) prep_store(pin, sQ + hl * 16 * LDQ);
   if (do_k) {
     if (do_q) prep_load(kcol, p.gk, pin);        // (only with one sub-stream)
