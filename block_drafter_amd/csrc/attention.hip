@@ -376,16 +376,15 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
+    // Branch-free: a row with nothing visible yet (m_new = -inf) shifts by 0,
+    // so its weights exp2(-inf) and its rescale exp2(-inf) are 0 (its o and
+    // l are still 0).  The hardware exp2 flushes results below 2^-126
+    // (weights that small relative to the row maximum are negligible).
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float pv[8];
-    float alpha = 1.f;
-    if (m_new == -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = exp2f(sv[e] - m_new);
-    }
+    for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
     Frag<TV> pf;
     pack_p(pf, pv);
     float psum = 0.f;
@@ -393,9 +392,11 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
     for (int e = 0; e < 8; ++e) psum += pv[e];
     l_lane = l_lane * alpha + psum;
     m_run = m_new;
+    // once the row maxima settle, most tiles change none of them
+    const bool rescale = !__all(alpha == 1.f);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      o[dt] *= alpha;
+      if (rescale) o[dt] *= alpha;
       mma16(o[dt], vf[dt], pf);
     }
   };
