@@ -16,7 +16,8 @@
 // row (lane % 16), which makes the online-softmax rescale of the
 // O^T = V^T P^T accumulators lane-local.  Sub-streams are combined through
 // LDS with their log-sum-exp; splits over context keys publish partials
-// that a second, small kernel merges per (request, query head).  Ring slots advance in int32 from one modulo per
+// that a second, small kernel merges (one wave per request, query head and
+// quarter of the head dims).  Ring slots advance in int32 from one modulo per
 // workgroup; the window and tail masks run only on the tiles that straddle
 // an edge.
 #include "dspine_device.hpp"
@@ -515,19 +516,20 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
   }
 }
 
-// Split merge: one workgroup per (query head, request), two waves, each
-// merging half of the head dims over every split of the head, MB splits at a
-// time in split order, rescaling the running sum whenever the running
-// maximum grows (the same order on every run: bit-reproducible).  Indexes
-// past the last split repeat it and are not added.
+// Split merge: one wave per (head-dim quarter, query head, request), each
+// combining its 2 x 16 head dims over every split of the head, MB splits at
+// a time in split order, rescaling the running sum whenever the running
+// maximum grows (the same order on every run: bit-reproducible).
 template <typename TQ, int D>
-__global__ __launch_bounds__(128) void attn_merge_kernel(const AttnParams p) {
+__global__ __launch_bounds__(64) void attn_merge_kernel(const AttnParams p) {
   constexpr int PSZ = 64 * (D / 4) + 32;                // floats of one split partial
-  constexpr int DPW = (D / 16) / 2;                     // 16-wide head-dim tiles per wave
-  constexpr int MB = DPW <= 4 ? 8 : 4;
-  static_assert((D / 16) % 2 == 0, "two waves split the head dims");
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, qrow = lane & 15;
+  constexpr int DPW = 2;                                // 16-wide head-dim tiles per wave
+  constexpr int NPART = (D / 16) / DPW;
+  constexpr int MB = 16;                                // splits per load batch (kMaxSplit / 2)
+  static_assert((D / 16) % DPW == 0, "head-dim parts");
+  const int part = blockIdx.x % NPART, h = blockIdx.x / NPART, b = blockIdx.y;
+  const int lane = threadIdx.x, qrow = lane & 15;
+  const int wv = part;                                  // head-dim tiles [wv DPW, (wv + 1) DPW)
   const float* hb = p.partials + (size_t)(b * p.nq + h) * p.nsplit * PSZ;
   float mstar = -INFINITY, L = 0.f;
   f32x4 acc[DPW];
@@ -538,7 +540,12 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const AttnParams p) {
     f32x4 ov[MB][DPW];
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
-      const int sp = sp0 + j < p.nsplit ? sp0 + j : p.nsplit - 1;
+      mv[j] = -INFINITY;
+      lv[j] = 0.f;
+#pragma unroll
+      for (int d = 0; d < DPW; ++d) ov[j][d] = f32x4{0, 0, 0, 0};
+      if (sp0 + j >= p.nsplit) continue;                // uniform: nothing to load past the last split
+      const int sp = sp0 + j;
       const gptr<float> pt = as_global(hb + (size_t)sp * PSZ);
       mv[j] = pt[64 * (D / 4) + qrow];
       lv[j] = pt[64 * (D / 4) + 16 + qrow];
@@ -583,7 +590,7 @@ template <typename TW, typename TQ, typename TV, int D, int GRP>
 static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
   const dim3 grid(p.nsplit, p.nkv, p.B);
   DSPINE_LAUNCH((attention_kernel<TW, TQ, TV, D, GRP>), grid, dim3(AttnShape<TQ, TV, D, GRP>::NT), 0, s, p);
-  if (p.nsplit > 1) DSPINE_LAUNCH((attn_merge_kernel<TQ, D>), dim3(p.nq, p.B), dim3(128), 0, s, p);
+  if (p.nsplit > 1) DSPINE_LAUNCH((attn_merge_kernel<TQ, D>), dim3(p.nq * (D / 32), p.B), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
