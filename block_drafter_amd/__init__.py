@@ -97,6 +97,7 @@ EXPORTS = {
                                             ctypes.c_int, ctypes.POINTER(Ctx_c), ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "dspine_profile_enable": (ctypes.c_int, [ctypes.c_uint32]),
+    "dspine_profile_stride": (ctypes.c_int, [ctypes.c_uint32]),
     "dspine_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_int64)]),
     "dspine_last_error": (ctypes.c_char_p, []),
@@ -293,6 +294,11 @@ def profile_enable(kinds: Sequence[str]):
     for k in kinds:
         mask |= 1 << PROF_KINDS.index(k)
     _check(lib().dspine_profile_enable(mask))
+
+
+def profile_stride(stride: int):
+    """Record only every `stride`-th launch scope of each enabled class."""
+    _check(lib().dspine_profile_stride(stride))
 
 
 def profile_read(kind: str):

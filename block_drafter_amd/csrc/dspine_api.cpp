@@ -71,6 +71,8 @@ int num_cus() {
 struct Profiler {
   std::mutex mu;
   uint32_t mask = 0;
+  uint32_t stride = 1;                          // time every stride-th scope of a class
+  uint64_t seen[DSPINE_PROF_KINDS] = {};        // scopes opened per class since the stride was set
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[DSPINE_PROF_KINDS];
   std::vector<hipEvent_t> pool;
   hipEvent_t get() {
@@ -106,6 +108,7 @@ class ProfScope {
     Profiler& p = prof();
     if (!(p.mask & (1u << kind)) || t_scope_open) return;
     std::lock_guard<std::mutex> lk(p.mu);
+    if (p.seen[kind]++ % p.stride != 0) return;
     a_ = p.get();
     b_ = p.get();
     if (a_ && b_) {
@@ -410,6 +413,15 @@ int dspine_profile_enable(uint32_t kind_mask) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
   p.mask = kind_mask & ((1u << DSPINE_PROF_KINDS) - 1);
+  return ok();
+}
+
+int dspine_profile_stride(uint32_t stride) {
+  if (stride == 0) return fail(DSPINE_E_ARG, "profile_stride: stride must be >= 1");
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.stride = stride;
+  for (uint64_t& n : p.seen) n = 0;
   return ok();
 }
 

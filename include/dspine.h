@@ -276,6 +276,11 @@ int dspine_debug_visible(const dspine_model* model, int layer, int B, int W,
 
 /* kind_mask: bit k enables class k; 0 disables recording.  Process-wide. */
 int dspine_profile_enable(uint32_t kind_mask);
+/* Records only every stride-th launch scope of each enabled class (counted
+ * per class from this call; 1, the default, records all), so that a
+ * measurement over many launches pays the event overhead on a sample of
+ * them.  stride 0 is DSPINE_E_ARG.  Process-wide. */
+int dspine_profile_stride(uint32_t stride);
 /* Waits for the recorded events of class `kind` (host-blocking), writes the
  * summed milliseconds and the number of launches, and clears the class. */
 int dspine_profile_read(int kind, double* total_ms, int64_t* launches);

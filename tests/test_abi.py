@@ -210,3 +210,8 @@ def test_bridge_rejections(L):
     assert L.dspine_bridge(h, 0, 1, 16, None, aid, None, FAKE, 1 << 40, None) == bd.E_ARG
     assert L.dspine_bridge(h, 0, 1, 16, FAKE, aid, FAKE + 4, FAKE, 1 << 40, None) == bd.E_ARG
     L.dspine_model_destroy(h)
+
+
+def test_profile_stride_rejects_zero(L):
+    assert L.dspine_profile_stride(0) != 0
+    assert L.dspine_profile_stride(1) == 0
