@@ -16,6 +16,14 @@
 //    stage as its weights (the vector-memory counter retires in issue order,
 //    so a load issued after the weights could not be waited for alone), and
 //    is staged through LDS for the four waves.
+//  * With 128 rows the registers cannot hold the accumulators and several
+//    weight stages at once, so both operands move global -> LDS directly
+//    (global_load_lds_dwordx4) into a ring of 64-K stages: weights as their
+//    1 KB fragment blocks, activations as full-line blocks of 8 rows x 128
+//    bytes.  The registers then hold only the accumulators and the
+//    fragments being multiplied.  All shared state lives in one array: with
+//    several __shared__ objects the compiler makes every LDS read wait for
+//    all direct-to-LDS loads in flight.
 //  * A tile (4 * NWB blocks) is either streamed over its whole K by one
 //    workgroup (no reduction at all), or, when N has fewer tiles than there
 //    are CUs (one CU alone cannot pull its share of HBM bandwidth), the
@@ -100,7 +108,7 @@ constexpr int a_regs() {
 
 }  // namespace
 
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA>
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA, bool WD>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   using T = TA;                                 // LDS / MFMA operand type
   constexpr int EB = Elt<TA>::kBytes;
@@ -112,8 +120,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   constexpr int NCH = MP * CPR / 256;           // chunks per thread
   static_assert(NCH >= 1 && (MP * CPR) % 256 == 0, "A tile must split over 256 threads");
   constexpr int WG_BLKS = 4 * NWB;              // 16-row weight blocks per tile
-  constexpr int NST = PD + 1;                   // register stages
-  static_assert(NST >= 1 && NST <= 4, "stages");
+  constexpr int NST = PD + 1;                   // register (WD: LDS) stages
+  static_assert(NST >= 1 && NST <= (WD ? 8 : 4), "stages");
   constexpr int AR = a_regs<PRO, EPC>();
   constexpr bool kScaledA = PRO == PRO_NORM || PRO == PRO_SCALE;
   // DMA: the activation chunk of a stage goes global -> LDS directly
@@ -125,13 +133,31 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   constexpr int DBLK = MT * KSUB / 4;           // DMA: blocks per wave per stage
   constexpr int WLD = NWB * KSUB;               // weight loads per wave per stage
   static_assert(!DMA || (256 / MP) * MP * 4 <= SLOT, "row-scale scratch fits a ring slot");
+  // WD: the weight blocks of a stage also go global -> LDS directly (1 KB
+  // blocks [wave][nb][ks] after the activation chunk), so the registers hold
+  // only accumulators and the fragments being multiplied, and the ring can
+  // be deeper than the register file would allow.
+  static_assert(!WD || (DMA && sizeof(TW) == 2), "weights through LDS: with direct-to-LDS activations, 16-bit weights");
+  constexpr int WSLOT = WD ? 4 * NWB * KSUB * 1024 : 0;
+  constexpr int STG = SLOT + WSLOT;             // DMA: bytes of one ring stage
 
-  __shared__ __attribute__((aligned(16))) T lds[2][DMA ? 8 : MP * LDA];
-  __shared__ __attribute__((aligned(1024))) char adma[DMA ? NST * SLOT : 16];
-  __shared__ uint32_t s_flag;
-  __shared__ SegTable s_seg;
-  __shared__ float s_scale[MP];      // per-row scale (SCALE_* modes)
-  __shared__ float s_red[4][MP];     // per-wave row sums of squares (stats_out)
+  // All shared state is carved out of one array.  With several __shared__
+  // objects the compiler tags their accesses with alias scopes, and then
+  // makes every LDS read wait for all direct-to-LDS loads in flight
+  // (vmcnt(0) before the fragment reads), which serialises the ring.
+  constexpr int kLdsA = DMA ? 8 : MP * LDA;     // activation staging, elements per buffer
+  constexpr int OFF_LDS = DMA ? NST * STG : 16;
+  constexpr int OFF_RED = OFF_LDS + ((2 * kLdsA * (int)sizeof(T) + 15) & ~15);
+  constexpr int OFF_SCALE = OFF_RED + 4 * MP * 4;
+  constexpr int OFF_SEG = OFF_SCALE + MP * 4;
+  constexpr int OFF_FLAG = OFF_SEG + (((int)sizeof(SegTable) + 15) & ~15);
+  __shared__ __attribute__((aligned(1024))) char smem[OFF_FLAG + 16];
+  char* const adma = smem;                                               // DMA ring
+  T (*const lds)[kLdsA] = reinterpret_cast<T (*)[kLdsA]>(smem + OFF_LDS);
+  float (*const s_red)[MP] = reinterpret_cast<float (*)[MP]>(smem + OFF_RED);  // per-wave row sums of squares
+  float* const s_scale = reinterpret_cast<float*>(smem + OFF_SCALE);    // per-row scale (SCALE_* modes)
+  SegTable& s_seg = *reinterpret_cast<SegTable*>(smem + OFF_SEG);
+  uint32_t& s_flag = *reinterpret_cast<uint32_t*>(smem + OFF_FLAG);
 
   const int tid = threadIdx.x;
   if (tid < p.nseg) {
@@ -169,16 +195,35 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 
   // DMA: lane l of block (mb, ks) fetches row mb*16 + l%16, K 8 (l/16) of
   // the block's 32-K step; this wave takes blocks wave, wave + 4, ...
+  // Full-line layout (WD with 64-K stages): block b holds rows 8 b .. 8 b + 7
+  // over the stage's whole 128 bytes, so every L2 request is a whole line.
+  constexpr bool kFullLine = WD && KSUB == 2;
   const TA* drow[DMA ? DBLK : 1];
   if constexpr (DMA) {
 #pragma unroll
     for (int q = 0; q < DBLK; ++q) {
       const int bi = wave + 4 * q;
-      drow[q] = a_row_ptr<PRO, TA>(p, (bi / KSUB) * 16 + (lane & 15)) + (bi % KSUB) * 32 + 8 * (lane >> 4);
+      if constexpr (kFullLine) {
+        const int r = lane >> 3;
+        drow[q] = a_row_ptr<PRO, TA>(p, bi * 8 + r) + ((lane & 7) ^ act_swz(r, bi & 1)) * 8;
+      } else {
+        drow[q] = a_row_ptr<PRO, TA>(p, (bi / KSUB) * 16 + (lane & 15)) + (bi % KSUB) * 32 + 8 * (lane >> 4);
+      }
     }
   }
+  // full-line fragment offsets in a stage's activation chunk, per 32-K half
+  int aoff[2] = {0, 0};
+  if constexpr (kFullLine) {
+    const int bb = (lane & 15) >> 3, r = lane & 7;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) aoff[h] = bb * 1024 + (r * 8 + ((4 * h + (lane >> 4)) ^ act_swz(r, bb))) * 16;
+  }
 
-  Frag<TW> wf[NST][NWB][KSUB];
+  Frag<TW> wf[WD ? 1 : NST][NWB][KSUB];
+  // WD: this wave's weight rows of the tile being loaded (looked up once
+  // per tile, not per stage)
+  int wtile = -1;
+  gptr<TW> wrow[NWB];
   u32x4 areg[DMA ? 1 : NST][NCH][AR];
 
   // Stage j <- iteration it: activation chunk(s) first, then the weights.
@@ -189,7 +234,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     const int tile = it / ipt;
     const int k0 = (it - tile * ipt) * KS;
     if constexpr (DMA) {
-      char* slot = adma + j * SLOT;
+      char* slot = adma + j * STG;
 #pragma unroll
       for (int q = 0; q < DBLK; ++q)
         __builtin_amdgcn_global_load_lds((const void*)(drow[q] + k0), (lds_void*)(slot + (wave + 4 * q) * 1024), 16,
@@ -228,15 +273,28 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
         areg[j][q][0] = gload16((gptr<void>)(as_global(reinterpret_cast<const TA*>(arow[q])) + kc));
       }
     }
+    if constexpr (WD) {
+      if (tile != wtile) {
+        wtile = tile;
+#pragma unroll
+        for (int nb = 0; nb < NWB; ++nb) wrow[nb] = seg_row_ptr<TW>(p, s_seg, tile * WG_BLKS + wave * NWB + nb) + lane * 8;
+      }
+    }
 #pragma unroll
     for (int nb = 0; nb < NWB; ++nb) {
       // fragment-ordered block: 32-K step ks of the block is 64 lanes x 8
       // elements, contiguous; a step past the end of K re-reads the last one
-      const gptr<TW> wr = seg_row_ptr<TW>(p, s_seg, tile * WG_BLKS + wave * NWB + nb) + lane * 8;
+      const gptr<TW> wr = WD ? wrow[nb] : seg_row_ptr<TW>(p, s_seg, tile * WG_BLKS + wave * NWB + nb) + lane * 8;
 #pragma unroll
       for (int s = 0; s < KSUB; ++s) {
         const int ks = k0 / 32 + s;
-        wf[j][nb][s].gload(wr + (size_t)(ks < p.K / 32 ? ks : p.K / 32 - 1) * 512);
+        const gptr<TW> src = wr + (size_t)(ks < p.K / 32 ? ks : p.K / 32 - 1) * 512;
+        if constexpr (WD)
+          __builtin_amdgcn_global_load_lds((const void*)src,
+                                           (lds_void*)(adma + j * STG + SLOT + ((wave * NWB + nb) * KSUB + s) * 1024),
+                                           16, 0, 0);
+        else
+          wf[j][nb][s].gload(src);
       }
     }
   };
@@ -296,12 +354,22 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     for (int s = 0; s < KSUB; ++s) {
       Frag<T> wo[NWB];
 #pragma unroll
-      for (int nb = 0; nb < NWB; ++nb) wo[nb] = AsOperand<T, TW>::cvt(wf[j][nb][s]);
+      for (int nb = 0; nb < NWB; ++nb) {
+        if constexpr (WD) {
+          Frag<TW> w;
+          w.v = *reinterpret_cast<const u32x4*>(adma + j * STG + SLOT + ((wave * NWB + nb) * KSUB + s) * 1024 + lane * 16);
+          wo[nb] = AsOperand<T, TW>::cvt(w);
+        } else {
+          wo[nb] = AsOperand<T, TW>::cvt(wf[j][nb][s]);
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < MT; ++mb) {
         Frag<T> af;
-        if constexpr (DMA)
-          af.v = *reinterpret_cast<const u32x4*>(adma + j * SLOT + (mb * KSUB + s) * 1024 + lane * 16);
+        if constexpr (kFullLine)
+          af.v = *reinterpret_cast<const u32x4*>(adma + j * STG + mb * 2048 + aoff[s]);
+        else if constexpr (DMA)
+          af.v = *reinterpret_cast<const u32x4*>(adma + j * STG + (mb * KSUB + s) * 1024 + lane * 16);
         else
           af.load(&lds[buf][(mb * 16 + (lane & 15)) * LDA + s * 32 + 8 * (lane >> 4)]);
 #pragma unroll
@@ -345,6 +413,38 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       // enough: each partial slot is written (through to memory) once per
       // launch and read only after its writer's arrival, so no cache of this
       // launch holds an older copy of it.
+      if constexpr (WD) {
+        // One weight block at a time, FB contributors per load batch: the
+        // registers hold the accumulators plus FB x MT partial fragments,
+        // not a second full tile (the same additions in the same order).
+        constexpr int FB = MT <= 4 ? 4 : 2;
+#pragma unroll
+        for (int nb = 0; nb < NWB; ++nb) {
+          f32x4 sum[MT];
+#pragma unroll
+          for (int mb = 0; mb < MT; ++mb) sum[mb] = f32x4{0, 0, 0, 0};
+          for (int g0 = g_first; g0 <= g_last; g0 += FB) {
+            f32x4 part[FB][MT];
+#pragma unroll
+            for (int j = 0; j < FB; ++j) {
+              const int gg = g0 + j <= g_last ? g0 + j : g_last;
+              const float* other = p.partials + (size_t)slot_of(gg) * (NWB * MT * 256 * 4);
+#pragma unroll
+              for (int mb = 0; mb < MT; ++mb)
+                part[j][mb] = *as_global(reinterpret_cast<const f32x4*>(other + ((nb * MT + mb) * 256 + tid) * 4));
+            }
+#pragma unroll
+            for (int j = 0; j < FB; ++j) {
+              if (g0 + j > g_last) break;
+#pragma unroll
+              for (int mb = 0; mb < MT; ++mb) sum[mb] += part[j][mb];
+            }
+          }
+#pragma unroll
+          for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = sum[mb];
+        }
+        if (tid == 0) reset_counter(p.counters + tile);
+      } else {
       constexpr int FB = NWB * MT <= 2 ? 8 : NWB * MT <= 4 ? 4 : NWB * MT <= 8 ? 2 : 1;
       f32x4 sum[NWB][MT];
 #pragma unroll
@@ -377,19 +477,23 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 #pragma unroll
         for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = sum[nb][mb];
       if (tid == 0) reset_counter(p.counters + tile);
+      }
     }
     // epilogue: lane holds D[n = 4*(lane/16) + v][m = lane%16] per (nb, mb)
     const int nl = 4 * (lane >> 4);
     if constexpr (EPI == EPI_SWIGLU) {
-      const int j = tile * (WG_BLKS / 2) + wave;      // gate/up row block (NWB == 2)
-      if (2 * j < p.nblk) {
+      // blocks nb = 2 i, 2 i + 1 of a wave are gate and up of row block j
+#pragma unroll
+      for (int i = 0; i < NWB / 2; ++i) {
+        const int j = (tile * WG_BLKS + wave * NWB) / 2 + i;
+        if (2 * j >= p.nblk) continue;
 #pragma unroll
         for (int mb = 0; mb < MT; ++mb) {
           const int m = mb * 16 + (lane & 15);
           if (m < p.M) {
             T* o = reinterpret_cast<T*>(p.out_act) + (size_t)m * p.ld_act + j * 16 + nl;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) Elt<T>::store(o, v, silu(acc[0][mb][v]) * acc[1][mb][v]);
+            for (int v = 0; v < 4; ++v) Elt<T>::store(o, v, silu(acc[2 * i][mb][v]) * acc[2 * i + 1][mb][v]);
           }
         }
       }
@@ -497,7 +601,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     }
     // [Q][MP] scratch, free until the first step: the second activation
     // buffer, or (direct-to-LDS) the ring slot the prologue leaves empty
-    float* s_part = DMA ? reinterpret_cast<float*>(adma + (NST - 1) * SLOT) : reinterpret_cast<float*>(lds[1]);
+    float* s_part = DMA ? reinterpret_cast<float*>(adma + (NST - 1) * STG) : reinterpret_cast<float*>(lds[1]);
     s_part[sq0 * MP + sm] = part;
     __syncthreads();
     if (tid < MP) {
@@ -508,18 +612,46 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     }
     __syncthreads();
   }
+  if constexpr (WD) {
+    // Ring of NST LDS stages, NST - 1 in flight; nothing lives in registers
+    // across steps but the accumulators, so the slot index is a plain
+    // counter and the loop runs one tile's part of the range at a time,
+    // finishing the tile after it.  Step: wait for this wave's loads of the
+    // slot (only the NST - 2 later stages may remain in flight), barrier
+    // (every wave's part landed, every wave done with the previous slot),
+    // refill the previous slot with iteration it + NST - 1, multiply.
+    int it = it_beg;
+    int j = 0;
+    while (true) {
+      const int tile = it / ipt;
+      const int kb = it - tile * ipt;
+      const int seg_end = (tile + 1) * ipt < it_end ? (tile + 1) * ipt : it_end;
+      for (; it < seg_end; ++it) {
+        wait_vmcnt<(NST - 2) * (DBLK + WLD)>();
+        __builtin_amdgcn_s_barrier();
+        load_stage(j == 0 ? NST - 1 : j - 1, it + NST - 1 < it_end ? it + NST - 1 : it_end - 1);
+        compute(0, j);
+        j = j == NST - 1 ? 0 : j + 1;
+      }
+      finish(tile, kb, it - tile * ipt);
+      if (it >= it_end) break;
+    }
+    wait_vmcnt<0>();                               // no load into LDS outlives the workgroup
+    return;
+  }
   if constexpr (DMA) {
     // Ring of NST stages, NST - 1 in flight.  Step `it` (stage j = it % NST):
     // wait for this wave's part of stage j (the loads issued after it are
-    // stage j's weights and the NST - 2 later stages; anything the epilogue
-    // issues only adds to that), then the barrier makes every wave's part
-    // visible and says every wave is done with stage j - 1, whose slot and
-    // registers then take iteration it + NST - 1.
+    // stage j's register weights, unless they too went to LDS, and the
+    // NST - 2 later stages; anything the epilogue issues only adds to
+    // that), then the barrier makes every wave's part visible and says
+    // every wave is done with stage j - 1, whose slot and registers then
+    // take iteration it + NST - 1.
     int it = it_beg;
     int seg_k0 = it_beg % ipt;
     auto dstep = [&](auto J) __attribute__((always_inline)) -> bool {
       constexpr int j = decltype(J)::value;
-      wait_vmcnt<WLD + (NST - 2) * (DBLK + WLD)>();
+      wait_vmcnt<(WD ? 0 : WLD) + (NST - 2) * (DBLK + WLD)>();
       __builtin_amdgcn_s_barrier();
       load_stage((j + NST - 1) % NST, it + NST - 1 < it_end ? it + NST - 1 : it_end - 1);
       compute(0, j);
@@ -543,7 +675,20 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       if constexpr (NST > 3) {
         if (!dstep(std::integral_constant<int, 3 % NST>{})) break;
       }
+      if constexpr (NST > 4) {
+        if (!dstep(std::integral_constant<int, 4 % NST>{})) break;
+      }
+      if constexpr (NST > 5) {
+        if (!dstep(std::integral_constant<int, 5 % NST>{})) break;
+      }
+      if constexpr (NST > 6) {
+        if (!dstep(std::integral_constant<int, 6 % NST>{})) break;
+      }
+      if constexpr (NST > 7) {
+        if (!dstep(std::integral_constant<int, 7 % NST>{})) break;
+      }
     }
+    wait_vmcnt<0>();                               // no load into LDS outlives the workgroup
     return;
   }
   store_a(0, 0, it_beg);
@@ -596,12 +741,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 // Stream-K and whole-K tiles both assume every workgroup of the grid is
 // resident at once: the grid is capped at what the kernel's occupancy
 // allows on all CUs.
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA>
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA, bool WD>
 static int resident_cap(int grid_cap, int num_cus) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>,
                                                       256, 0) != hipSuccess ||
         n < 1)
       n = 1;
@@ -614,11 +759,13 @@ static int resident_cap(int grid_cap, int num_cus) {
 constexpr int kMaxSplitWide = 6;   // contributors per tile for MT x NWB >= 8
 constexpr int kMaxSplitSmall = 8;  // contributors per tile for MT <= 2 (one load batch of the finisher)
 
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA = false>
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA = false,
+          bool WD = false>
 static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t s) {
-  static_assert(NWB == 1 || NWB == 2, "tile widths");
+  static_assert(NWB == 1 || NWB == 2 || (WD && NWB == 4), "tile widths");
+  static_assert(EPI != EPI_SWIGLU || NWB % 2 == 0, "SwiGLU pairs gate and up blocks");
   constexpr int KS = 32 * KSUB;
-  grid_cap = resident_cap<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA>(grid_cap, num_cus);
+  grid_cap = resident_cap<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>(grid_cap, num_cus);
   p.ipt = (p.K + KS - 1) / KS;
   p.tiles = (p.nblk + 4 * NWB - 1) / (4 * NWB);
   const int64_t TI = (int64_t)p.tiles * p.ipt;
@@ -646,8 +793,10 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
     }
     G = (int)g;
   }
+  // two partial slots per workgroup, each NWB * MT * 4 KB
+  if ((size_t)2 * G * (NWB * MT * 256 * 4) > gemm_stream_partial_floats(kMaxGrid)) return hipErrorInvalidValue;
   p.xcd_remap = (G % 8 == 0) ? 1 : 0;
-  DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA>), dim3(G), dim3(256), 0, s, p);
+  DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>), dim3(G), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -685,7 +834,10 @@ static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipS
     if constexpr (kHalf) {
       if (p.K % 128 == 0) {
         if (mt <= 4) return launch_t<TW, TA, 4, 2, 4, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
-        return launch_t<TW, TA, 8, 2, 4, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
+        // 128 rows: weights move global -> LDS too (a 4-stage ring of 64-K
+        // stages, full-line activation blocks); 1.2-1.3x faster than
+        // weights in registers, whose stages the allocator cannot keep
+        return launch_t<TW, TA, 8, 2, 2, 3, PRO, EPI, true, true>(p, grid_cap, num_cus, s);
       }
     }
     if (mt <= 4) return launch_t<TW, TA, 4, 2, kHalf ? 4 : 2, 1, PRO, EPI>(p, grid_cap, num_cus, s);

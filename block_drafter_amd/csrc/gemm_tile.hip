@@ -40,8 +40,6 @@ namespace dspine {
 constexpr int kGroupM = 8;          // row tiles per group of the tile order
 constexpr int kTileM = 256, kTileN = 256;
 
-// chunk swizzle of activation blocks (row r of the block, block parity bb)
-__device__ __forceinline__ int act_swz(int r, int bb) { return (((r >> 1) & 1) << 2) ^ ((r >> 2) * 3) ^ (bb << 1); }
 
 template <bool F16>
 __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(const TileGemmParams p) {
