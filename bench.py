@@ -221,9 +221,10 @@ def main():
     # the setup materializes exactly those positions from frontier F - S.
     full = any(s == 0 for s in g.windows)
     smax = max(g.windows)
+    extra_steps = min(5, total_steps) if args.breakdown else 0   # the breakdown pass below
     ctxs, pending = [], []
     for b, F in enumerate(frontiers):
-        cap = (F + args.commit * total_steps + 16) if full else 0
+        cap = (F + args.commit * (total_steps + extra_steps) + 16) if full else 0
         c = model.new_context(full_capacity=cap)
         keep = F if full else min(F, smax)
         c.frontier = F - keep
