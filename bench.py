@@ -165,7 +165,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dspine27b_b1",
-                    choices=["dspine27b_b1", "dspine27b_b8", "dflash35b_b8", "tiny_fp32"])
+                    choices=["dspine27b_b1", "dspine27b_b8", "dspine27b_causal_b8", "dflash35b_b8",
+                             "tiny_fp32"])
     ap.add_argument("--commit", type=int, default=16,
                     help="positions materialized per request per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")

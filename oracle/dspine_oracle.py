@@ -376,11 +376,19 @@ def bridge_write(g, wts, layer: int, x: np.ndarray, rho: np.ndarray, c: np.ndarr
     out = x.copy()
     for t in range(1, W):
         cp = c[t - 1] if pred_codes is None else pred_codes[t]
-        gate = sigmoid(linear(c[t][None], wts["bridge_G"])[0]
-                       + linear(cp[None], wts["bridge_Gp"])[0] + widen(wts["bridge_b"]))
-        m = gate * linear(cp[None], wts["bridge_A"])[0]
-        out[t] = x[t] + rho[t] * linear(m[None], wts[f"l{layer}.W_l"])[0]
+        out[t] = bridge_write_row(g, wts, layer, x[t], rho[t], c[t], cp)
     return out
+
+
+def bridge_write_row(g, wts, layer: int, x_t: np.ndarray, rho_t: float, c_t: np.ndarray,
+                     cp: np.ndarray) -> np.ndarray:
+    """One receiver row of the write: gate from the receiver's own code c_t
+    and the predecessor code cp, message A cp, written back scaled by the
+    receiver's RMS rho_t [FLZ, "The bridge", equations for m and x']."""
+    gate = sigmoid(linear(c_t[None], wts["bridge_G"])[0]
+                   + linear(cp[None], wts["bridge_Gp"])[0] + widen(wts["bridge_b"]))
+    m = gate * linear(cp[None], wts["bridge_A"])[0]
+    return x_t + rho_t * linear(m[None], wts[f"l{layer}.W_l"])[0]
 
 
 def bridge(g, wts, layer: int, x: np.ndarray, anchor_id: int,
@@ -428,19 +436,25 @@ def decoder_layer(g, wts, layer: int, ctxs: Sequence[RequestContext], x: np.ndar
 
 
 def draft_forward(g, wts, ctxs: Sequence[RequestContext], anchor_ids: Sequence[int], W: int,
-                  attn_fn=block_attention, return_layers: bool = False):
+                  attn_fn=block_attention, return_layers: bool = False,
+                  return_last_prewrite: bool = False):
     """a4-a12: one masked-block forward over B requests.
 
     After every decoder layer (the last one included) the bridge writes
     predecessor messages [FLZ, "The bridge"]; [PHY, 融合 kernel]; then the
     next stage normalises: the next layer's input norm, or the final plain
     RMSNorm [NIF, after the layers].  With code_dim == 0 there is no bridge
-    and this is the plain DFlash forward.  Returns [B, W, H]."""
+    and this is the plain DFlash forward.  Returns [B, W, H]; with
+    ``return_last_prewrite`` also the last layer's states before its bridge
+    write, u_L [B, W, H] (what the last-write refinement starts from)."""
     B = len(ctxs)
     x = np.concatenate([block_input(g, wts, int(anchor_ids[b]), W) for b in range(B)])
     states = []
+    prewrite = None
     for l in range(g.n_layers):
         x = decoder_layer(g, wts, l, ctxs, x, W, attn_fn)
+        if l == g.n_layers - 1:
+            prewrite = x.copy().reshape(B, W, g.hidden)
         if g.bridge:
             for b in range(B):
                 sl = slice(b * W, (b + 1) * W)
@@ -449,7 +463,151 @@ def draft_forward(g, wts, ctxs: Sequence[RequestContext], anchor_ids: Sequence[i
     out = plain_rmsnorm(x, wts["g_final"], g.eps).reshape(B, W, g.hidden)
     if return_layers:
         return out, states
+    if return_last_prewrite:
+        return out, prewrite
     return out
+
+
+# ---------------------------------------------------------------------------
+# proposal tail: candidate retrieval, last-write refinement, transition
+# table, conditional walk
+# ---------------------------------------------------------------------------
+HEAD_SLICE = 8192     # vocabulary rows widened at a time (bounds memory only)
+
+
+def head_scores(lm_head: np.ndarray, h: np.ndarray, ids: Optional[np.ndarray] = None) -> np.ndarray:
+    """Scores of the shared LM head, E_v . h, for every vocabulary row (or
+    only the rows ``ids``) [PHY, 前驱条件解码与 transition cache: the head's
+    score for token v is the dot product of its output-embedding row with the
+    final-normed state].  h is [n, H]; returns [n, V] (or [n, len(ids)]).
+    Each score is one independent dot product, so slicing the rows of the
+    head changes nothing but memory use."""
+    h = np.atleast_2d(h)
+    if ids is not None:
+        return h @ widen(lm_head[np.asarray(ids)]).T
+    V = lm_head.shape[0]
+    out = np.empty((h.shape[0], V))
+    for v0 in range(0, V, HEAD_SLICE):
+        v1 = min(V, v0 + HEAD_SLICE)
+        out[:, v0:v1] = h @ widen(lm_head[v0:v1]).T
+    return out
+
+
+def top_k(scores: np.ndarray, K: int) -> np.ndarray:
+    """The K best tokens of one score row, best first [FLZ, "The last write is
+    refined using discrete candidates": the direct path multiplies by the
+    head and retains the top 16].  Equal scores rank the smaller token id
+    first (a reading: the pages fix no tie order)."""
+    order = np.lexsort((np.arange(scores.shape[0]), -scores))
+    return order[:K].astype(np.int64)
+
+
+def transition_table(g, wts, lm_head: np.ndarray, u: np.ndarray, anchor_id: int,
+                     cand: np.ndarray) -> np.ndarray:
+    """T_t[i, j] for one request [PHY, 前驱条件解码与 transition cache, the
+    equation for T_t and the last-write refinement steps]; [FLZ, "The last
+    write is refined using discrete candidates"].
+
+    u [W, H] is the last layer's pre-write state; cand [W-1, K] holds the
+    candidates of rows 1..W-1.  For receiver row t the last layer's bridge
+    write is redone from u with the predecessor code replaced by the known
+    token's code sqrt(r) C[s]: s is the i-th candidate of row t-1, or the
+    anchor for row 1 (the first proposal is conditioned on the real anchor,
+    so all K rows of T_1 use it).  The refined state is final-normed and
+    scored by the head on row t's own candidates only.  Returns
+    [W-1, K, K], entry [t-1, i, j]."""
+    L = g.n_layers - 1
+    W, K = u.shape[0], cand.shape[1]
+    rho, c = bridge_codes(g, wts, L, u, anchor_id)
+    sr = math.sqrt(g.code_dim)
+    T = np.zeros((W - 1, K, K))
+    for t in range(1, W):
+        preds = [anchor_id] * K if t == 1 else [int(v) for v in cand[t - 2]]
+        for i, s in enumerate(preds):
+            x = bridge_write_row(g, wts, L, u[t], rho[t], c[t], sr * widen(wts["codebook"][s]))
+            h = plain_rmsnorm(x, wts["g_final"], g.eps)
+            T[t - 1, i] = head_scores(lm_head, h, cand[t - 1])[0]
+    return T
+
+
+def greedy_walk(T: np.ndarray) -> np.ndarray:
+    """Left-to-right choice [PHY, transition cache, selection stage]: row 1's
+    choice maximises T_1 on the anchor's row, each later row maximises the
+    row of T_t picked by the previous choice.  Equal scores pick the smaller
+    candidate index (the better initial rank).  Returns candidate indices
+    [W-1]."""
+    n = T.shape[0]
+    choice = np.zeros(n, dtype=np.int64)
+    i = 0
+    for t in range(n):
+        choice[t] = int(np.argmax(T[t, i]))     # first maximum
+        i = int(choice[t])
+    return choice
+
+
+def sampled_walk(T: np.ndarray, temperature: float, uniforms: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Sampled chain [FLZ, "The last write is refined using discrete
+    candidates": conditional probabilities are built, the chain is drawn and
+    the probabilities are kept for verification; the factors are computed in
+    float64].  At row t the probabilities are softmax(T_t[i*, :] / temperature)
+    over the K candidates, i* the previous choice (0 at row 1, the anchor).
+    The draw takes the given uniform u in [0, 1) and picks the first j whose
+    cumulative probability exceeds u (inverse CDF; the last j if rounding
+    leaves u above the total).  Returns (choices [W-1], q [W-1]), q the
+    probability of each chosen candidate."""
+    n, K = T.shape[0], T.shape[2]
+    choice = np.zeros(n, dtype=np.int64)
+    q = np.zeros(n)
+    i = 0
+    for t in range(n):
+        s = np.asarray(T[t, i], dtype=np.float64) / float(temperature)
+        e = np.exp(s - np.max(s))
+        p = e / np.sum(e)
+        cdf = 0.0
+        j = K - 1
+        for jj in range(K):
+            cdf += p[jj]
+            if float(uniforms[t]) < cdf:
+                j = jj
+                break
+        choice[t] = j
+        q[t] = p[j]
+        i = j
+    return choice, q
+
+
+def propose(g, wts, lm_head: np.ndarray, ctxs: Sequence[RequestContext], anchor_ids: Sequence[int],
+            W: int, K: int, walk: str = "greedy", temperature: float = 1.0,
+            uniforms: Optional[np.ndarray] = None, cand_override: Optional[np.ndarray] = None) -> dict:
+    """The proposal tail after the draft forward, per request: head scores of
+    rows 1..W-1 and their top-K candidates, the transition tables, and the
+    walk.  ``cand_override`` [B, W-1, K] replaces the candidate ids (to
+    evaluate the tables on another implementation's candidates).  Returns a
+    dict of float64/int64 arrays: out [B,W,H], scores [B,W-1,V], cand
+    [B,W-1,K], cand_scores [B,W-1,K], table [B,W-1,K,K], choice [B,W-1],
+    tokens [B,W-1], q [B,W-1] (sampled walk only)."""
+    assert g.bridge, "the refinement redoes the last bridge write"
+    out, u = draft_forward(g, wts, ctxs, anchor_ids, W, return_last_prewrite=True)
+    B = len(ctxs)
+    res = {"out": out, "scores": [], "cand": [], "cand_scores": [], "table": [], "choice": [],
+           "tokens": [], "q": []}
+    for b in range(B):
+        sc = head_scores(lm_head, out[b, 1:])
+        cand = np.stack([top_k(sc[t], K) for t in range(W - 1)]) if cand_override is None \
+            else np.asarray(cand_override[b], dtype=np.int64)
+        T = transition_table(g, wts, lm_head, u[b], int(anchor_ids[b]), cand)
+        if walk == "greedy":
+            ch, q = greedy_walk(T), np.zeros(W - 1)
+        else:
+            ch, q = sampled_walk(T, temperature, uniforms[b])
+        res["scores"].append(sc)
+        res["cand"].append(cand)
+        res["cand_scores"].append(np.take_along_axis(sc, cand, axis=1))
+        res["table"].append(T)
+        res["choice"].append(ch)
+        res["tokens"].append(cand[np.arange(W - 1), ch])
+        res["q"].append(q)
+    return {k: (v if k == "out" else np.stack(v)) for k, v in res.items()}
 
 
 # ---------------------------------------------------------------------------

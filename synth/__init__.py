@@ -109,6 +109,11 @@ G_27B = Geometry(hidden=5120, n_layers=5, n_q_heads=32, n_kv_heads=8, head_dim=1
                  ffn=17408, n_feat_layers=5, code_dim=1024, msg_dim=512, vocab=248320,
                  windows=(2048,) * 5)
 
+# The 27B checkpoint's own attention: block-causal, 8192-position windows.
+G_27B_CAUSAL = Geometry(hidden=5120, n_layers=5, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                        ffn=17408, n_feat_layers=5, code_dim=1024, msg_dim=512, vocab=248320,
+                        windows=(8192,) * 5, block_causal=True)
+
 G_35B_DFLASH = Geometry(hidden=2048, n_layers=6, n_q_heads=32, n_kv_heads=8, head_dim=128,
                         ffn=6144, n_feat_layers=8, code_dim=0, msg_dim=0, vocab=248320,
                         windows=(4096,) * 5 + (0,))
@@ -127,6 +132,10 @@ WORKLOADS: Dict[str, Workload] = {
     "dspine27b_b8": Workload("dspine27b_b8", G_27B, 1003, B=8, W=16,
                              frontiers=_uniform_frontiers(1003, 8, 1024, 16384),
                              note="27B geometry, 8 blocks, context lengths U{1024..16384}"),
+    "dspine27b_causal_b8": Workload("dspine27b_causal_b8", G_27B_CAUSAL, 1006, B=8, W=16,
+                                    frontiers=_uniform_frontiers(1006, 8, 1024, 16384),
+                                    note="27B geometry with block-causal attention and 8192-position "
+                                         "windows, 8 blocks, context lengths U{1024..16384}"),
     "dflash35b_b8": Workload("dflash35b_b8", G_35B_DFLASH, 1004, B=8, W=16,
                              frontiers=(32768,) * 8,
                              note="35B-A3B-style plain DFlash, bridge off, 5 local + 1 full layer"),
@@ -282,3 +291,19 @@ def make_anchor_ids(g: Geometry, seed: int, B: int, stream: int = 0) -> np.ndarr
 
 def with_geometry(g: Geometry, **kw) -> Geometry:
     return dataclasses.replace(g, **kw)
+
+
+LM_HEAD_INDEX = 30_000
+UNIFORM_INDEX = 40_000
+
+
+def make_lm_head(g: Geometry, seed: int) -> np.ndarray:
+    """The shared LM head [vocab, H] ~ N(0, 1/H) (the target's output
+    embedding, used by the proposal tail); drawn only when asked for."""
+    return normal(seed, LM_HEAD_INDEX, (g.vocab, g.hidden), 1.0 / math.sqrt(g.hidden), 0.0, g.dtype)
+
+
+def make_uniforms(seed: int, B: int, n: int, stream: int = 0) -> np.ndarray:
+    """Uniform draws in [0, 1) for the sampled walk, float64 [B, n]."""
+    rng = np.random.default_rng([seed, UNIFORM_INDEX + stream])
+    return rng.random((B, n))

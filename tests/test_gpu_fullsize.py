@@ -245,3 +245,37 @@ def test_prefill27b_full_size():
         for l in range(g.n_layers):
             assert bool(torch.isfinite(ctxs[b].k[l]).all()) and bool(torch.isfinite(ctxs[b].v[l]).all())
     model.close()
+
+
+def test_dspine27b_causal_b8_full_size():
+    """The 27B checkpoint's own attention: block-causal, 8192-position windows,
+    B=8 with contexts U{1024..16384} (windows both partly filled and
+    truncated).  Besides parity, causality fixes a property the GPU must
+    keep at any size: rows 0..W'-1 of a W-block equal a W'-block run with the
+    same anchors and frontiers (the bridge only sends messages forward and
+    block key j is visible to row i only when j <= i)."""
+    import block_drafter_amd as bd
+    wl = synth.WORKLOADS["dspine27b_causal_b8"]
+    g = wl.geom
+    assert g.block_causal and set(g.windows) == {8192}
+    say(f"dspine27b_causal_b8: frontiers {wl.frontiers}")
+    wts = synth.make_weights(g, wl.seed)
+    model = bd.Model.from_numpy(g, wts)
+    anchors = [int(a) for a in synth.make_anchor_ids(g, wl.seed, wl.B)]
+    ctxs = setup_windows(model, g, wl)
+    say("dspine27b_causal_b8: forward W=16")
+    gpu = to_np64(model.forward(ctxs, anchors, wl.W))
+    check_forward(g, wts, gpu, [gpu_ring_context(g, c, F) for c, F in zip(ctxs, wl.frontiers)],
+                  anchors, wl.W, "gpu rings")
+    for Wp in (5, 8):
+        say(f"dspine27b_causal_b8: forward W={Wp}, prefix of the W=16 block")
+        short = to_np64(model.forward(ctxs, anchors, Wp))
+        for i in range(wl.B):
+            err = rel_err(short[i], gpu[i, :Wp])
+            assert err <= TOL_BF16, f"W={Wp} prefix, request {i}: rel err {err:.3e}"
+    b = int(np.argmax(wl.frontiers))
+    F = wl.frontiers[b]
+    pos = sample_positions(F, 8192, 6006)
+    pos = pos[pos >= F - min(F, 8192)]
+    check_ring_positions(g, wts, wl.seed, b, ctxs[b], F, pos, f"request {b}")
+    model.close()

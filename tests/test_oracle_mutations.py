@@ -26,10 +26,10 @@ MUTATIONS = {
         "cp = c[t - 1] if pred_codes is None else pred_codes[t]",
         "cp = c[t] if pred_codes is None else pred_codes[t]"),
     "bridge drops rho scale": (
-        "out[t] = x[t] + rho[t] * linear(", "out[t] = x[t] + linear("),
+        "return x_t + rho_t * linear(", "return x_t + linear("),
     "bridge drops receiver gate term": (
-        "gate = sigmoid(linear(c[t][None], wts[\"bridge_G\"])[0]\n                       + ",
-        "gate = sigmoid(0 * linear(c[t][None], wts[\"bridge_G\"])[0]\n                       + "),
+        "gate = sigmoid(linear(c_t[None], wts[\"bridge_G\"])[0]\n                   + ",
+        "gate = sigmoid(0 * linear(c_t[None], wts[\"bridge_G\"])[0]\n                   + "),
     "bridge drops bias": (
         "[0] + widen(wts[\"bridge_b\"]))", "[0])"),
     "bridge code without sqrt(r)": (
@@ -67,6 +67,33 @@ MUTATIONS = {
         "+ 3 * msg_dim * code_dim + msg_dim", "+ 3 * msg_dim * code_dim"),
     "bf16 rounding truncates": (
         "rounded = (bits + half - np.uint64(1) + lsb) >> drop << drop", "rounded = bits >> drop << drop"),
+    "top-k ties prefer the larger id": (
+        "order = np.lexsort((np.arange(scores.shape[0]), -scores))",
+        "order = np.lexsort((-np.arange(scores.shape[0]), -scores))"),
+    "top-k keeps the smallest scores": (
+        "order = np.lexsort((np.arange(scores.shape[0]), -scores))",
+        "order = np.lexsort((np.arange(scores.shape[0]), scores))"),
+    "refinement ignores the candidate code": (
+        "sr * widen(wts[\"codebook\"][s])", "c[t - 1]"),
+    "refinement conditions row 1 on candidates": (
+        "preds = [anchor_id] * K if t == 1 else", "preds = [int(v) for v in cand[0]] if t == 1 else"),
+    "refinement predecessor from its own row": (
+        "else [int(v) for v in cand[t - 2]]", "else [int(v) for v in cand[t - 1]]"),
+    "table scores without the final norm": (
+        "h = plain_rmsnorm(x, wts[\"g_final\"], g.eps)", "h = x"),
+    "table scores the previous row's candidates": (
+        "head_scores(lm_head, h, cand[t - 1])", "head_scores(lm_head, h, cand[max(t - 2, 0)])"),
+    "greedy walk ignores the previous choice": (
+        "choice[t] = int(np.argmax(T[t, i]))", "choice[t] = int(np.argmax(T[t, 0]))"),
+    "greedy walk takes the last maximum": (
+        "choice[t] = int(np.argmax(T[t, i]))", "choice[t] = int(len(T[t, i]) - 1 - np.argmax(T[t, i][::-1]))"),
+    "sampled walk ignores temperature": (
+        "s = np.asarray(T[t, i], dtype=np.float64) / float(temperature)",
+        "s = np.asarray(T[t, i], dtype=np.float64)"),
+    "sampled walk inclusive cdf": (
+        "if float(uniforms[t]) < cdf:", "if float(uniforms[t]) <= cdf:"),
+    "sampled walk keeps the wrong probability": (
+        "q[t] = p[j]", "q[t] = p[i]"),
 }
 
 

@@ -583,3 +583,143 @@ def test_page_figures():
     for name, shape in (("l0.R", (1024, 5120)), ("l0.W_l", (5120, 512)), ("codebook", (248320, 1024)),
                         ("w_feat", (5120, 25600)), ("l0.wq", (4096, 5120))):
         assert synth.weight_shape(g27, name) == shape
+
+
+# ---------------------------------------------------------------------------
+# proposal tail: candidates, last-write refinement, transition table, walk
+# [FLZ, "The last write is refined using discrete candidates"];
+# [PHY, 前驱条件解码与 transition cache]
+# ---------------------------------------------------------------------------
+def propose_setup(overrides=None, B=1, W=5):
+    g = G_NS
+    wts = small_model(g, overrides=overrides)
+    head = synth.make_lm_head(g, 7)
+    ctxs = [build_context(g, wts, 10 + 3 * b, request=b) for b in range(B)]
+    anchors = [5 + 17 * b for b in range(B)]
+    return g, wts, head, ctxs, anchors, W
+
+
+def test_top_k_against_sorted_bruteforce():
+    rng = np.random.default_rng(3)
+    scores = rng.integers(0, 5, size=50).astype(np.float64)      # many ties
+    ranked = [i for _, i in sorted((-s, i) for i, s in enumerate(scores))]
+    for K in (1, 7, 50):
+        assert list(O.top_k(scores, K)) == ranked[:K]
+
+
+def test_head_scores_are_row_dot_products():
+    g, wts, head, ctxs, anchors, W = propose_setup()
+    h = np.random.default_rng(4).standard_normal((2, g.hidden))
+    s = O.head_scores(head, h)
+    assert s.shape == (2, g.vocab)
+    E = synth.to_float(head)
+    for n in range(2):
+        for v in (0, 13, g.vocab - 1):
+            assert abs(s[n, v] - math.fsum(E[v, k] * h[n, k] for k in range(g.hidden))) < 1e-12
+    assert np.max(np.abs(O.head_scores(head, h, [13, 2])[:, 0] - s[:, 13])) < 1e-14
+
+
+def test_anchor_conditioned_table_reproduces_forward_scores():
+    """Row 1's predecessor is the anchor, whose code the forward's own last
+    write already used: every row of T_1 equals the forward's head scores on
+    row 1's candidates (the refinement path and the forward path agree)."""
+    g, wts, head, ctxs, anchors, W = propose_setup()
+    res = O.propose(g, wts, head, ctxs, anchors, W, K=4)
+    T, cand, sc = res["table"][0], res["cand"][0], res["scores"][0]
+    assert T.shape == (W - 1, 4, 4) and cand.shape == (W - 1, 4)
+    for i in range(4):
+        assert rel_err(T[0, i], sc[0, cand[0]]) < 1e-12
+    # candidates are the forward's top-4 of each row
+    for t in range(W - 1):
+        assert list(cand[t]) == list(O.top_k(sc[t], 4))
+        assert np.all(np.diff(sc[t, cand[t]]) <= 0)
+
+
+def test_predicted_code_predecessor_reproduces_forward_row():
+    """If a predecessor candidate's codebook row equals the predicted code
+    of row t-1 (divided by sqrt(r)), refining with that candidate redoes the
+    forward's own last write, so its row of T_t equals the forward's scores."""
+    g, wts, head, ctxs, anchors, W = propose_setup()
+    res = O.propose(g, wts, head, ctxs, anchors, W, K=4)
+    cand = res["cand"][0]
+    _, u = O.draft_forward(g, wts, ctxs, anchors, W, return_last_prewrite=True)
+    rho, c = O.bridge_codes(g, wts, g.n_layers - 1, u[0], anchors[0])
+    for t in (2, 3):
+        i0 = next(i for i in range(4) if cand[t - 2][i] != anchors[0])
+        book = wts["codebook"].copy()
+        book[cand[t - 2][i0]] = (c[t - 1] / math.sqrt(g.code_dim)).astype(book.dtype)
+        res2 = O.propose(g, dict(wts, codebook=book), head, ctxs, anchors, W, K=4, cand_override=res["cand"])
+        assert rel_err(res2["table"][0][t - 1, i0], res["scores"][0][t - 1, cand[t - 1]]) < 1e-5
+
+
+@pytest.mark.parametrize("which", ["W_last_zero", "gate_closed"])
+def test_table_without_last_write_is_the_forward_scores(which):
+    """With the last layer's write off, refinement changes nothing: every
+    T_t[i, :] equals the forward's scores on row t's candidates."""
+    g = G_NS
+    L = g.n_layers - 1
+    ov = {f"l{L}.W_l": np.zeros((g.hidden, g.msg_dim), np.float32)} if which == "W_last_zero" else \
+        {"bridge_b": np.full(g.msg_dim, -1e4, np.float32)}
+    g, wts, head, ctxs, anchors, W = propose_setup(ov)
+    res = O.propose(g, wts, head, ctxs, anchors, W, K=4)
+    T, cand, sc = res["table"][0], res["cand"][0], res["scores"][0]
+    for t in range(W - 1):
+        for i in range(4):
+            assert rel_err(T[t, i], sc[t, cand[t]]) < 1e-12
+
+
+def test_table_rows_depend_on_the_predecessor():
+    g, wts, head, ctxs, anchors, W = propose_setup()
+    T = O.propose(g, wts, head, ctxs, anchors, W, K=4)["table"][0]
+    for t in range(1, W - 1):
+        assert np.max(np.abs(T[t, 0] - T[t, 1])) > 1e-6
+
+
+def test_greedy_walk_hand_example():
+    T = np.array([[[1, 3, 2], [9, 9, 9], [9, 9, 9]],        # row 1: anchor row 0 -> 1
+                  [[0, 0, 0], [5, 4, 6], [0, 9, 0]],        # row 2: given 1 -> 2
+                  [[1, 0, 0], [0, 2, 0], [0, 0, -1]]],      # row 3: given 2 -> 0 (tie, smaller index)
+                 dtype=np.float64)
+    assert list(O.greedy_walk(T)) == [1, 2, 0]
+
+
+def test_sampled_walk_definition():
+    from scipy.special import softmax
+    T = np.array([[[0.0, 0.0], [0.0, 0.0]],       # row 1 (anchor row 0): p = (1/2, 1/2)
+                  [[1.0, 2.0], [7.0, -7.0]]])     # row 2, given choice 0 or 1
+    # inverse CDF: u = 0.5 equals p_0 exactly, so the first j with cdf > u is 1
+    ch, q = O.sampled_walk(T, 1.0, np.array([0.5, 0.0]))
+    assert list(ch) == [1, 0] and q[0] == 0.5
+    assert abs(q[1] - softmax(np.array([7.0, -7.0]))[0]) < 1e-15
+    # temperature divides the scores
+    ch, q = O.sampled_walk(T, 2.0, np.array([0.49, 0.999]))
+    assert list(ch) == [0, 1]
+    assert abs(q[1] - softmax(np.array([1.0, 2.0]) / 2.0)[1]) < 1e-15
+
+
+def test_sampled_walk_frequencies_and_cold_limit():
+    rng = np.random.default_rng(5)
+    row = np.array([0.3, -1.0, 1.2, 0.0])
+    T = np.tile(row, (1, 4, 1))
+    p = np.exp(row - row.max())
+    p /= p.sum()
+    n = 20000
+    counts = np.zeros(4)
+    for u in rng.random(n):
+        counts[O.sampled_walk(T, 1.0, np.array([u]))[0][0]] += 1
+    assert np.all(np.abs(counts / n - p) <= 4 * np.sqrt(p * (1 - p) / n))
+    # a cold temperature follows the greedy chain
+    g, wts, head, ctxs, anchors, W = propose_setup()
+    Tm = O.propose(g, wts, head, ctxs, anchors, W, K=4)["table"][0]
+    cold, _ = O.sampled_walk(Tm, 1e-6, rng.random(W - 1) * 0.98 + 0.01)
+    assert list(cold) == list(O.greedy_walk(Tm))
+
+
+def test_proposals_are_per_request():
+    g, wts, head, ctxs, anchors, W = propose_setup(B=2)
+    both = O.propose(g, wts, head, ctxs, anchors, W, K=4)
+    for b in range(2):
+        one = O.propose(g, wts, head, [ctxs[b]], [anchors[b]], W, K=4)
+        assert np.array_equal(one["cand"][0], both["cand"][b])
+        assert rel_err(one["table"][0], both["table"][b]) < 1e-12
+        assert np.array_equal(one["tokens"][0], both["tokens"][b])
