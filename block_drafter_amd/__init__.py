@@ -58,12 +58,23 @@ _GLOBAL_FIELDS = ["embed", "w_feat", "g_ctx", "g_final", "codebook", "bridge_G",
                   "bridge_A", "bridge_b"]
 # matrices the library streams from its packed copy
 _PROJECTIONS = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "R", "W_l", "w_feat",
-                "bridge_G", "bridge_Gp", "bridge_A"}
+                "bridge_G", "bridge_Gp", "bridge_A", "lm_head"}
 
 
 class Weights_c(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _GLOBAL_FIELDS] + [
-        ("layer", LayerWeights_c * MAX_LAYERS)]
+        ("layer", LayerWeights_c * MAX_LAYERS), ("lm_head", ctypes.c_void_p)]
+
+
+MAX_TOPK = 16
+WALK_GREEDY, WALK_SAMPLED = 0, 1
+
+
+class Proposal_c(ctypes.Structure):
+    _fields_ = [("topk", ctypes.c_int32), ("walk", ctypes.c_int32), ("temperature", ctypes.c_double),
+                ("uniforms", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("cand", ctypes.c_void_p),
+                ("cand_scores", ctypes.c_void_p), ("table", ctypes.c_void_p),
+                ("choice", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("q", ctypes.c_void_p)]
 
 
 class Ctx_c(ctypes.Structure):
@@ -93,6 +104,13 @@ EXPORTS = {
                                      ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]),
+    "dspine_propose_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                                         ctypes.c_int]),
+    "dspine_draft_propose": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                            ctypes.POINTER(Ctx_c), ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.c_void_p, ctypes.POINTER(Proposal_c),
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]),
     "dspine_debug_visible": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, ctypes.POINTER(Ctx_c), ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -171,6 +189,8 @@ class Model:
             for n in _LAYER_FIELDS:
                 t = weights.get(f"l{l}.{n}")
                 setattr(ws.layer[l], n, t.data_ptr() if t is not None else None)
+        head = weights.get("lm_head")
+        ws.lm_head = head.data_ptr() if head is not None else None
         self._ws = ws
         h = ctypes.c_void_p()
         _check(lib().dspine_model_create(ctypes.byref(self._gs), ctypes.byref(ws), ctypes.byref(h)))
@@ -190,8 +210,11 @@ class Model:
                     del self.weights[name]
 
     @classmethod
-    def from_numpy(cls, geom, wts: Dict[str, np.ndarray], device="cuda"):
-        return cls(geom, {k: to_device(v, device) for k, v in wts.items()})
+    def from_numpy(cls, geom, wts: Dict[str, np.ndarray], device="cuda", lm_head: Optional[np.ndarray] = None):
+        t = {k: to_device(v, device) for k, v in wts.items()}
+        if lm_head is not None:
+            t["lm_head"] = to_device(lm_head, device)
+        return cls(geom, t)
 
     def close(self):
         if self.handle:
@@ -258,6 +281,55 @@ class Model:
         _check(lib().dspine_draft_forward(self.handle, B, W, arr, aid, out.data_ptr(),
                                           ws.data_ptr(), ws.numel(), st))
         return out
+
+    def propose_workspace(self, max_batch=MAX_BATCH, max_width=16, topk=MAX_TOPK):
+        """Device workspace of the proposal tail (reused while large enough)."""
+        torch = _torch()
+        need = lib().dspine_propose_workspace_bytes(self.handle, max_batch, max_width, topk)
+        if need == 0:
+            _check(E_ARG)
+        if getattr(self, "_pworkspace", None) is None or self._pworkspace.numel() < need:
+            self._pworkspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+        return self._pworkspace
+
+    def propose(self, ctxs: Sequence["Context"], anchor_ids: Sequence[int], W: int, topk: int = MAX_TOPK,
+                walk: str = "greedy", temperature: float = 1.0, uniforms=None, keep_scores: bool = False,
+                out=None, workspace=None, propose_workspace=None, stream=None, outputs=None):
+        """One draft forward plus the proposal tail.  Returns a dict of device
+        tensors: out [B,W,H], cand/cand_scores [B,W-1,K], table [B,W-1,K,K],
+        choice/tokens [B,W-1], q [B,W-1] (float64), scores [B*W,vocab] when
+        keep_scores.  ``uniforms``: device float64 [B, W-1] for the sampled
+        walk.  ``outputs`` reuses a dict returned by an earlier call."""
+        torch = _torch()
+        B, K = len(ctxs), int(topk)
+        arr = (Ctx_c * B)(*[c.struct for c in ctxs])
+        aid = (ctypes.c_int32 * B)(*[int(a) for a in anchor_ids])
+        dev = "cuda"
+        o = outputs if outputs is not None else {
+            "out": out if out is not None else torch.empty((B, W, self.geom.hidden), dtype=torch.float32, device=dev),
+            "cand": torch.empty((B, W - 1, K), dtype=torch.int32, device=dev),
+            "cand_scores": torch.empty((B, W - 1, K), dtype=torch.float32, device=dev),
+            "table": torch.empty((B, W - 1, K, K), dtype=torch.float32, device=dev),
+            "choice": torch.empty((B, W - 1), dtype=torch.int32, device=dev),
+            "tokens": torch.empty((B, W - 1), dtype=torch.int32, device=dev),
+            "q": torch.empty((B, W - 1), dtype=torch.float64, device=dev),
+        }
+        if keep_scores and "scores" not in o:
+            o["scores"] = torch.empty((B * W, self.geom.vocab), dtype=torch.float32, device=dev)
+        pr = Proposal_c()
+        pr.topk = K
+        pr.walk = WALK_GREEDY if walk == "greedy" else WALK_SAMPLED
+        pr.temperature = float(temperature)
+        pr.uniforms = uniforms.data_ptr() if uniforms is not None else None
+        pr.scores = o["scores"].data_ptr() if "scores" in o else None
+        for n in ("cand", "cand_scores", "table", "choice", "tokens", "q"):
+            setattr(pr, n, o[n].data_ptr())
+        ws = workspace if workspace is not None else self.workspace()
+        pws = propose_workspace if propose_workspace is not None else self.propose_workspace(B, W, K)
+        st = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        _check(lib().dspine_draft_propose(self.handle, B, W, arr, aid, o["out"].data_ptr(), ctypes.byref(pr),
+                                          ws.data_ptr(), ws.numel(), pws.data_ptr(), pws.numel(), st))
+        return o
 
     def bridge(self, layer: int, x, anchor_ids: Sequence[int], pred_codes=None,
                workspace=None, stream=None):

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -272,6 +273,10 @@ int check_weights(const dspine_geometry& g, const dspine_weights& w) {
     }
   }
 #undef NEED
+  if (w.lm_head) {
+    if (!aligned16(w.lm_head)) return fail(DSPINE_E_ARG, "weight lm_head not 16-byte aligned");
+    if (g.vocab % 16) return fail(DSPINE_E_UNSUPPORTED, "lm_head needs vocab %d to be a multiple of 16", g.vocab);
+  }
   return DSPINE_OK;
 }
 
@@ -319,12 +324,14 @@ std::vector<Proj> projections(const dspine_geometry& g) {
   }
   return v;
 }
-size_t packed_bytes(const dspine_geometry& g) {
+// bytes of the fragment-ordered copy (the shared LM head too when given)
+size_t packed_bytes(const dspine_geometry& g, bool head) {
   size_t total = 0;
   for (const Proj& pr : projections(g)) {
     const size_t one = align256((size_t)pr.rows * pr.cols * elt_bytes(g));
     total += pr.layer ? one * g.n_layers : one;
   }
+  if (head) total += align256((size_t)g.vocab * g.hidden * elt_bytes(g));
   return total;
 }
 
@@ -476,13 +483,13 @@ size_t dspine_packed_bytes(const dspine_model* model) {
     fail(DSPINE_E_ARG, "packed_bytes: NULL model");
     return 0;
   }
-  return packed_bytes(model->g);
+  return packed_bytes(model->g, model->w.lm_head != nullptr);
 }
 
 int dspine_pack_weights(dspine_model* model, void* dst, size_t dst_bytes, dspine_stream_t stream) {
   if (!model || !dst) return fail(DSPINE_E_ARG, "pack_weights: NULL argument");
   if (((uintptr_t)dst & 255u) != 0) return fail(DSPINE_E_ARG, "pack_weights: dst not 256-byte aligned");
-  const size_t need = packed_bytes(model->g);
+  const size_t need = packed_bytes(model->g, model->w.lm_head != nullptr);
   if (dst_bytes < need) return fail(DSPINE_E_WORKSPACE, "pack_weights: %zu bytes < %zu needed", dst_bytes, need);
   const dspine_geometry& g = model->g;
   dspine_weights pw = model->w;
@@ -501,6 +508,10 @@ int dspine_pack_weights(dspine_model* model, void* dst, size_t dst_bytes, dspine
       pw.*pr.global = out;
       out += one;
     }
+  }
+  if (model->w.lm_head) {
+    HIP_TRY(launch_pack(model->w.lm_head, out, g.vocab, g.hidden, g.dtype, s));
+    pw.lm_head = out;
   }
   model->pw = pw;
   model->packed = true;
@@ -906,8 +917,9 @@ int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x, 
 // -----------------------------------------------------------------------------
 // a4-a12
 // -----------------------------------------------------------------------------
-int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_ctx* ctx, const int32_t* anchor_ids,
-                         float* out, void* workspace, size_t workspace_bytes, dspine_stream_t stream_) {
+// checks shared by the forward and the propose call
+static int check_forward(const dspine_model* model, int B, int W, const dspine_ctx* ctx, const int32_t* anchor_ids,
+                         const float* out, void* workspace, size_t workspace_bytes) {
   size_t need = 0;
   int rc = check_call(model, B, W, anchor_ids, workspace, workspace_bytes, &need);
   if (rc) return rc;
@@ -915,11 +927,16 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
   if (!out || !aligned16(out)) return fail(DSPINE_E_ARG, "forward: out NULL or unaligned");
   for (int b = 0; b < B; ++b)
     if ((rc = check_ctx_rings(*model, ctx[b], b, ctx[b].frontier))) return rc;
-  if ((rc = check_packed(model))) return rc;
+  return DSPINE_OK;
+}
 
+// The forward's launches (arguments already checked).  save_u, when given,
+// receives the last layer's state before its bridge write [B*W, H].
+static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx* ctx, const int32_t* anchor_ids,
+                       float* out, void* workspace, hipStream_t stream, float* save_u) {
+  int rc = DSPINE_OK;
   const dspine_geometry& g = model->g;
   const dspine_weights& wt = model->w;
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   char* ws = static_cast<char*>(workspace);
   const int M = B * W, H = g.hidden, D = g.head_dim;
   const int qd = g.n_q_heads * D, kvd = g.n_kv_heads * D;
@@ -1068,6 +1085,8 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
     xst = st1;
     xst_tiles = tH;
 
+    if (save_u && l == g.n_layers - 1)
+      HIP_TRY(hipMemcpyAsync(save_u, x, sizeof(float) * (size_t)M * H, hipMemcpyDeviceToDevice, stream));
     // a9-a11 (statistics of the written rows go to st0)
     if (g.code_dim > 0) {
       ProfScope ps(DSPINE_PROF_BRIDGE, stream);
@@ -1089,6 +1108,222 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
     ProfScope ps(DSPINE_PROF_NORM, stream);
     HIP_TRY(launch_rmsnorm(fp, g.dtype, true, stream));
   }
+  return DSPINE_OK;
+}
+
+int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_ctx* ctx, const int32_t* anchor_ids,
+                         float* out, void* workspace, size_t workspace_bytes, dspine_stream_t stream) {
+  int rc = check_forward(model, B, W, ctx, anchor_ids, out, workspace, workspace_bytes);
+  if (rc) return rc;
+  if ((rc = check_packed(model))) return rc;
+  rc = run_forward(model, B, W, ctx, anchor_ids, out, workspace, reinterpret_cast<hipStream_t>(stream), nullptr);
+  return rc ? rc : ok();
+}
+
+// -----------------------------------------------------------------------------
+// proposal tail
+// -----------------------------------------------------------------------------
+namespace {
+struct ProposePlan {
+  size_t u, scores, part_v, part_i, codes, Pc, msg, Y, total;
+};
+ProposePlan make_propose_plan(const dspine_geometry& g, int B, int W, int K) {
+  ProposePlan p{};
+  const size_t eb = act_bytes(g);
+  const int64_t M = (int64_t)B * W, Mp = (int64_t)B * (W - 1);
+  const int64_t Mc = Mp * K + kMaxRows;      // the GEMMs may read a padded last row block
+  const int r = std::max(g.code_dim, 1), a = std::max(g.msg_dim, 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  p.u = take(4 * (size_t)M * g.hidden);
+  p.scores = take(4 * (size_t)M * g.vocab);
+  p.part_v = take(4 * topk_partial_entries((int)Mp));
+  p.part_i = take(4 * topk_partial_entries((int)Mp));
+  p.codes = take(eb * Mc * r);
+  p.Pc = take(4 * Mc * 2 * a);
+  p.msg = take(eb * Mc * a);
+  p.Y = take(4 * Mc * g.hidden);
+  p.total = off;
+  return p;
+}
+// tiles of the head GEMM must fit its tile counters
+bool head_fits(const dspine_geometry& g) { return (int64_t)g.vocab / 16 <= 4LL * kMaxTiles; }
+}  // namespace
+
+size_t dspine_propose_workspace_bytes(const dspine_model* model, int max_batch, int max_width, int topk) {
+  if (!model || max_batch < 1 || max_batch > DSPINE_MAX_BATCH || max_width < DSPINE_MIN_WIDTH ||
+      max_width > DSPINE_MAX_WIDTH || topk < 1 || topk > DSPINE_MAX_TOPK || !model->w.lm_head) {
+    fail(DSPINE_E_ARG, "propose_workspace_bytes: bad argument or no lm_head");
+    return 0;
+  }
+  return make_propose_plan(model->g, max_batch, max_width, topk).total;
+}
+
+int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_ctx* ctx, const int32_t* anchor_ids,
+                         float* out, const dspine_proposal* prop, void* workspace, size_t workspace_bytes,
+                         void* propose_ws, size_t propose_ws_bytes, dspine_stream_t stream_) {
+  int rc = check_forward(model, B, W, ctx, anchor_ids, out, workspace, workspace_bytes);
+  if (rc) return rc;
+  const dspine_geometry& g = model->g;
+  if (g.code_dim == 0) return fail(DSPINE_E_UNSUPPORTED, "propose: the refinement needs the bridge (code_dim 0)");
+  if (!model->w.lm_head) return fail(DSPINE_E_UNSUPPORTED, "propose: the model has no lm_head");
+  if (g.hidden > propose_max_hidden())
+    return fail(DSPINE_E_UNSUPPORTED, "propose: hidden %d > %d", g.hidden, propose_max_hidden());
+  if (!head_fits(g)) return fail(DSPINE_E_UNSUPPORTED, "propose: vocab %d too large for the head GEMM", g.vocab);
+  if (!prop) return fail(DSPINE_E_ARG, "propose: prop NULL");
+  const int K = prop->topk;
+  if (K < 1 || K > DSPINE_MAX_TOPK || K > g.vocab)
+    return fail(DSPINE_E_ARG, "propose: topk %d not in 1..%d (and <= vocab)", K, DSPINE_MAX_TOPK);
+  if (prop->walk != DSPINE_WALK_GREEDY && prop->walk != DSPINE_WALK_SAMPLED)
+    return fail(DSPINE_E_ARG, "propose: walk %d", prop->walk);
+  if (prop->walk == DSPINE_WALK_SAMPLED) {
+    if (!(prop->temperature > 0.0) || !std::isfinite(prop->temperature))
+      return fail(DSPINE_E_ARG, "propose: temperature must be finite and > 0");
+    if (!prop->uniforms || ((uintptr_t)prop->uniforms & 7u)) return fail(DSPINE_E_ARG, "propose: uniforms NULL or unaligned");
+  }
+  if (!prop->cand || !prop->cand_scores || !prop->table || !prop->choice || !prop->tokens)
+    return fail(DSPINE_E_ARG, "propose: an output pointer is NULL");
+  if ((prop->scores && !aligned16(prop->scores)) || ((uintptr_t)prop->q & 7u))
+    return fail(DSPINE_E_ARG, "propose: scores or q unaligned");
+  const ProposePlan PP = make_propose_plan(g, B, W, K);
+  if (!propose_ws || !aligned16(propose_ws)) return fail(DSPINE_E_ARG, "propose: propose workspace NULL or unaligned");
+  if (propose_ws_bytes < PP.total)
+    return fail(DSPINE_E_WORKSPACE, "propose: propose workspace %zu bytes < %zu needed", propose_ws_bytes, PP.total);
+  if ((rc = check_packed(model))) return rc;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  char* pws = static_cast<char*>(propose_ws);
+  char* ws = static_cast<char*>(workspace);
+  const int M = B * W, H = g.hidden, V = g.vocab, r = g.code_dim, a = g.msg_dim, L = g.n_layers;
+  const int Mc = B * (W - 1) * K;
+  const size_t eb = act_bytes(g);
+  const int cus = num_cus();
+  const Plan P = make_plan(g, M, 0);
+  float* u = reinterpret_cast<float*>(pws + PP.u);
+  float* scores = prop->scores ? prop->scores : reinterpret_cast<float*>(pws + PP.scores);
+
+  if ((rc = run_forward(model, B, W, ctx, anchor_ids, out, workspace, stream, u))) return rc;
+
+  // head scores E h of every row (h = the forward's final-normed output)
+  GemmParams gp = gemm_base(P, ws, H, M);
+  set_segments(gp, {{model->pw.lm_head, V}});
+  if ((rc = set_scaled_a(gp, g, M, W, out, H, H, SCALE_ONE, nullptr, 0, (float)H, nullptr, ws + P.act_h, stream)))
+    return rc;
+  gp.epi = EPI_STORE;
+  gp.out = scores;
+  gp.ldo = V;
+  HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+
+  ProposeParams pp;
+  memset(&pp, 0, sizeof pp);
+  pp.B = B;
+  pp.W = W;
+  pp.K = K;
+  pp.vocab = V;
+  pp.H = H;
+  pp.r = r;
+  pp.a = a;
+  pp.walk = prop->walk;
+  pp.temperature = prop->temperature;
+  pp.eps = g.eps;
+  pp.code_scale = sqrtf((float)r);
+  for (int b = 0; b < B; ++b) pp.anchor[b] = anchor_ids[b];
+  pp.scores = scores;
+  pp.part_v = reinterpret_cast<float*>(pws + PP.part_v);
+  pp.part_i = reinterpret_cast<int32_t*>(pws + PP.part_i);
+  pp.cand = prop->cand;
+  pp.cand_scores = prop->cand_scores;
+  pp.codebook = model->w.codebook;
+  pp.codes = pws + PP.codes;
+  pp.P_own = reinterpret_cast<const float*>(ws + P.P);
+  pp.P_cand = reinterpret_cast<const float*>(pws + PP.Pc);
+  pp.bias = model->w.bridge_b;
+  pp.msg = pws + PP.msg;
+  pp.u = u;
+  pp.Y = reinterpret_cast<const float*>(pws + PP.Y);
+  pp.g_final = model->w.g_final;
+  pp.head_packed = model->pw.lm_head;
+  pp.table = prop->table;
+  pp.uniforms = prop->uniforms;
+  pp.choice = prop->choice;
+  pp.tokens = prop->tokens;
+  pp.q = prop->q;
+  HIP_TRY(launch_topk(pp, stream));
+  HIP_TRY(launch_cand_codes(pp, g.dtype, stream));
+
+  // [G_p; A] of the candidate codes, then W_l of their messages
+  float* Pc = reinterpret_cast<float*>(pws + PP.Pc);
+  float* Y = reinterpret_cast<float*>(pws + PP.Y);
+  const bool tile = g.dtype == DSPINE_BF16 && gemm_tile_fits(a, r) && gemm_tile_fits(H, a);
+  if (tile) {
+    TileGemmParams tp;
+    memset(&tp, 0, sizeof tp);
+    tp.seg_ptr[0] = model->pw.bridge_Gp;
+    tp.seg_ptr[1] = model->pw.bridge_A;
+    tp.seg_rows0[0] = 0;
+    tp.seg_rows0[1] = a;
+    tp.seg_rows0[2] = 2 * a;
+    tp.nseg = 2;
+    tp.N = 2 * a;
+    tp.K = r;
+    tp.M = Mc;
+    tp.pro = PRO_COPY;
+    tp.a = pws + PP.codes;
+    tp.lda = r;
+    tp.out = Pc;
+    tp.ldo = 2 * a;
+    HIP_TRY(launch_gemm_tile(tp, g.dtype, cus, stream));
+  } else {
+    for (int r0 = 0; r0 < Mc; r0 += kMaxRows) {
+      const int mr = std::min(kMaxRows, Mc - r0);
+      gp = gemm_base(P, ws, r, mr);
+      set_segments(gp, {{model->pw.bridge_Gp, a}, {model->pw.bridge_A, a}});
+      gp.pro = PRO_COPY;
+      gp.a = pws + PP.codes + (size_t)r0 * r * eb;
+      gp.lda = r;
+      gp.epi = EPI_STORE;
+      gp.out = Pc + (size_t)r0 * 2 * a;
+      gp.ldo = 2 * a;
+      HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+    }
+  }
+  HIP_TRY(launch_cand_msg(pp, g.dtype, stream));
+  if (tile) {
+    TileGemmParams tp;
+    memset(&tp, 0, sizeof tp);
+    tp.seg_ptr[0] = model->pw.layer[L - 1].W_l;
+    tp.seg_rows0[0] = 0;
+    tp.seg_rows0[1] = H;
+    tp.nseg = 1;
+    tp.N = H;
+    tp.K = a;
+    tp.M = Mc;
+    tp.pro = PRO_COPY;
+    tp.a = pws + PP.msg;
+    tp.lda = a;
+    tp.out = Y;
+    tp.ldo = H;
+    HIP_TRY(launch_gemm_tile(tp, g.dtype, cus, stream));
+  } else {
+    for (int r0 = 0; r0 < Mc; r0 += kMaxRows) {
+      const int mr = std::min(kMaxRows, Mc - r0);
+      gp = gemm_base(P, ws, a, mr);
+      set_segments(gp, {{model->pw.layer[L - 1].W_l, H}});
+      gp.pro = PRO_COPY;
+      gp.a = pws + PP.msg + (size_t)r0 * a * eb;
+      gp.lda = a;
+      gp.epi = EPI_STORE;
+      gp.out = Y + (size_t)r0 * H;
+      gp.ldo = H;
+      HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+    }
+  }
+  HIP_TRY(launch_cand_score(pp, g.dtype, stream));
+  HIP_TRY(launch_walk(pp, stream));
   return ok();
 }
 

@@ -6,7 +6,9 @@
  *     features and store every draft layer's context K/V in per-request rings;
  *   - dspine_draft_forward:   one masked-block forward (anchor + masks) over
  *     B requests, with the DSpine gated predecessor bridge after every layer;
- *   - dspine_bridge:          the bridge alone on one layer's block states.
+ *   - dspine_bridge:          the bridge alone on one layer's block states;
+ *   - dspine_draft_propose:   the forward, then candidates from the shared LM
+ *     head, the transition table of the last-write refinement and the walk.
  *
  * Sources, cited by tag in the comments below:
  *   [FLZ] "DSpine for Qwen3.8-27B: Causal Features Through Depth" (flozi.net guide)
@@ -120,6 +122,8 @@ typedef struct {
     const void* bridge_A;      /* [a, r]  predecessor value map, shared */
     const void* bridge_b;      /* [a]     gate bias, shared */
     dspine_layer_weights layer[DSPINE_MAX_LAYERS];
+    const void* lm_head;       /* [vocab, H]  shared LM head for dspine_draft_propose (vocab a
+                                  multiple of 16); NULL when proposals are not used */
 } dspine_weights;
 
 /*
@@ -155,7 +159,7 @@ void dspine_model_destroy(dspine_model* model);
 /*
  * Projection weights in fragment order.  The GEMMs stream every projection
  * matrix (wq, wk, wv, wo, w_gate, w_up, w_down, R, W_l per layer; w_feat,
- * bridge_G, bridge_Gp, bridge_A) in the order their MFMA fragments are
+ * bridge_G, bridge_Gp, bridge_A; lm_head when given) in the order their MFMA fragments are
  * loaded: inside each block of 16 rows, 32-wide column step ks holds the 64
  * lane fragments (row 16b + l%16, columns 32ks + 8(l/16) .. +8) in
  * consecutive memory.  dspine_pack_weights writes that copy into `dst`
@@ -241,6 +245,62 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
 int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x,
                   const int32_t* anchor_ids, const float* pred_codes,
                   void* workspace, size_t workspace_bytes, dspine_stream_t stream);
+
+/*
+ * Proposal tail after the draft forward.  [FLZ, "The last write is refined
+ * using discrete candidates"]; [PHY, 前驱条件解码与 transition cache]:
+ *   - candidates: the K best tokens of the shared LM head's scores E_v . h_t
+ *     of every proposal row t = 1..W-1 (h = the forward's final-normed
+ *     state), best first, equal scores by smaller token id (direct BF16 path);
+ *   - transition table T_t[i, j]: the last layer's bridge write is redone
+ *     from its pre-write state u_t with the predecessor code replaced by
+ *     sqrt(r) C[s], s = candidate i of row t-1 (the anchor for t = 1, so the
+ *     K rows of T_1 are equal); the result is final-normed and scored by the
+ *     head on row t's candidates j;
+ *   - walk: row 1 picks from T_1's row 0, row t from the row of T_t chosen at
+ *     t-1.  Greedy: the largest score (smaller index on ties).  Sampled:
+ *     p = softmax(T_t[i*, :] / temperature) in float64, the first j whose
+ *     cumulative probability exceeds the given uniform u (the last j if
+ *     rounding leaves u above the total); q = p[j] is kept.
+ */
+#define DSPINE_MAX_TOPK 16
+#define DSPINE_WALK_GREEDY 0
+#define DSPINE_WALK_SAMPLED 1
+
+typedef struct {
+    int32_t topk;              /* K, 1..DSPINE_MAX_TOPK */
+    int32_t walk;              /* DSPINE_WALK_GREEDY or DSPINE_WALK_SAMPLED */
+    double temperature;        /* sampled walk: > 0 */
+    const double* uniforms;    /* sampled walk: device float64 [B, W-1], each in [0, 1) */
+    /* outputs, device */
+    float* scores;             /* optional (NULL: kept in the workspace): float32 [B*W, vocab]
+                                  head scores of every row (anchor rows included) */
+    int32_t* cand;             /* int32 [B, W-1, K] candidate token ids of rows 1..W-1 */
+    float* cand_scores;        /* float32 [B, W-1, K] their head scores */
+    float* table;              /* float32 [B, W-1, K, K]: entry [b, t-1, i, j] = T_t[i, j] */
+    int32_t* choice;           /* int32 [B, W-1] chosen candidate index of each row */
+    int32_t* tokens;           /* int32 [B, W-1] chosen token ids */
+    double* q;                 /* float64 [B, W-1] probability of each choice (sampled); may be
+                                  NULL for the greedy walk (otherwise written as 1) */
+} dspine_proposal;
+
+/* Bytes of the second workspace dspine_draft_propose needs for up to
+ * max_batch requests of width up to max_width and top-k up to topk.  It needs
+ * no zero fill.  0 on error (or when the model has no lm_head). */
+size_t dspine_propose_workspace_bytes(const dspine_model* model, int max_batch, int max_width, int topk);
+
+/*
+ * One draft forward (exactly dspine_draft_forward: same arguments, same
+ * `out`) followed by the proposal tail above.  Needs a bridge (code_dim > 0)
+ * and lm_head.  `workspace` is the forward's; `propose_ws` the tail's.
+ * Errors: those of dspine_draft_forward, E_ARG (NULL output, K or walk out
+ * of range, temperature <= 0 or uniforms NULL for the sampled walk),
+ * E_UNSUPPORTED (no bridge or no lm_head), E_WORKSPACE.
+ */
+int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_ctx* ctx,
+                         const int32_t* anchor_ids, float* out, const dspine_proposal* prop,
+                         void* workspace, size_t workspace_bytes,
+                         void* propose_ws, size_t propose_ws_bytes, dspine_stream_t stream);
 
 /*
  * a3 as the attention kernel evaluates it, for exact comparison: for every

@@ -553,8 +553,9 @@ def sampled_walk(T: np.ndarray, temperature: float, uniforms: np.ndarray) -> Tup
     over the K candidates, i* the previous choice (0 at row 1, the anchor).
     The draw takes the given uniform u in [0, 1) and picks the first j whose
     cumulative probability exceeds u (inverse CDF; the last j if rounding
-    leaves u above the total).  Returns (choices [W-1], q [W-1]), q the
-    probability of each chosen candidate."""
+    leaves u above the total).  The normaliser and the cumulative sum are
+    taken left to right over the candidates.  Returns (choices [W-1], q
+    [W-1]), q the probability of each chosen candidate."""
     n, K = T.shape[0], T.shape[2]
     choice = np.zeros(n, dtype=np.int64)
     q = np.zeros(n)
@@ -562,7 +563,10 @@ def sampled_walk(T: np.ndarray, temperature: float, uniforms: np.ndarray) -> Tup
     for t in range(n):
         s = np.asarray(T[t, i], dtype=np.float64) / float(temperature)
         e = np.exp(s - np.max(s))
-        p = e / np.sum(e)
+        total = 0.0
+        for v in e:                 # left to right (the pages fix no order)
+            total += v
+        p = e / total
         cdf = 0.0
         j = K - 1
         for jj in range(K):

@@ -215,3 +215,75 @@ def test_bridge_rejections(L):
 def test_profile_stride_rejects_zero(L):
     assert L.dspine_profile_stride(0) != 0
     assert L.dspine_profile_stride(1) == 0
+
+
+def call_propose(L, h, B, W, ctxs, anchors, prop, pws=FAKE, pws_bytes=1 << 40, out=FAKE):
+    arr = (bd.Ctx_c * len(ctxs))(*ctxs)
+    aid = (ctypes.c_int32 * len(anchors))(*anchors)
+    return L.dspine_draft_propose(h, B, W, arr, aid, out, ctypes.byref(prop) if prop is not None else None,
+                                  FAKE, 1 << 40, pws, pws_bytes, None)
+
+
+def good_proposal(K=16, walk=bd.WALK_GREEDY):
+    p = bd.Proposal_c()
+    p.topk = K
+    p.walk = walk
+    p.temperature = 1.0
+    p.uniforms = FAKE if walk == bd.WALK_SAMPLED else None
+    for n in ("cand", "cand_scores", "table", "choice", "tokens", "q"):
+        setattr(p, n, FAKE + 0x4000)
+    return p
+
+
+def test_propose_rejections_before_any_launch(L):
+    g = synth.G_27B
+    h = make_model(L, g)                           # no lm_head
+    c = fake_ctx(g, 4096)
+    assert L.dspine_propose_workspace_bytes(h, 1, 16, 16) == 0
+    assert call_propose(L, h, 1, 16, [c], [5], good_proposal()) == bd.E_UNSUPPORTED
+    assert b"lm_head" in L.dspine_last_error()
+    L.dspine_model_destroy(h)
+
+    ws = fake_weights(g)
+    ws.lm_head = FAKE + 0x100000
+    gs = bd.geometry_struct(g)
+    h = ctypes.c_void_p()
+    assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == 0
+    head_bytes = g.vocab * g.hidden * 2
+    assert L.dspine_packed_bytes(h) == head_bytes + sum(
+        int(np.prod(synth.weight_shape(g, n))) * 2
+        for n in synth.weight_names(g) if n.split(".")[-1] in bd._PROJECTIONS)
+    need = L.dspine_propose_workspace_bytes(h, 8, 16, 16)
+    assert need >= 8 * 16 * g.vocab * 4                    # every row's head scores
+    assert L.dspine_propose_workspace_bytes(h, 8, 16, 17) == 0
+    assert L.dspine_propose_workspace_bytes(h, 8, 16, 0) == 0
+    assert call_propose(L, h, 1, 16, [c], [5], None) == bd.E_ARG
+    assert call_propose(L, h, 1, 16, [c], [5], good_proposal(K=0)) == bd.E_ARG
+    assert call_propose(L, h, 1, 16, [c], [5], good_proposal(K=17)) == bd.E_ARG
+    p = good_proposal()
+    p.walk = 2
+    assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG
+    p = good_proposal(walk=bd.WALK_SAMPLED)
+    p.temperature = 0.0
+    assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG
+    p = good_proposal(walk=bd.WALK_SAMPLED)
+    p.uniforms = None
+    assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG
+    p = good_proposal()
+    p.table = None
+    assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG
+    assert call_propose(L, h, 1, 16, [c], [5], good_proposal(), pws_bytes=1024) == bd.E_WORKSPACE
+    assert call_propose(L, h, 1, 16, [c], [g.vocab], good_proposal()) == bd.E_ARG
+    assert call_propose(L, h, 1, 17, [c], [5], good_proposal()) == bd.E_UNSUPPORTED
+    # valid arguments: the model is not packed yet
+    assert call_propose(L, h, 1, 16, [c], [5], good_proposal()) == bd.E_STATE
+    L.dspine_model_destroy(h)
+
+    g = synth.G_35B_DFLASH                         # no bridge to refine
+    ws = fake_weights(g)
+    ws.lm_head = FAKE + 0x100000
+    gs = bd.geometry_struct(g)
+    h = ctypes.c_void_p()
+    assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == 0
+    assert call_propose(L, h, 1, 16, [fake_ctx(g, 100, full_cap=200)], [5], good_proposal()) == bd.E_UNSUPPORTED
+    L.dspine_model_destroy(h)

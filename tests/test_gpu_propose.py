@@ -1,0 +1,177 @@
+"""GPU parity of the proposal tail (dspine_draft_propose) against the oracle.
+
+Floating-point values (head scores, the transition table) compare with
+max |gpu - oracle| / rms(oracle) <= 2e-2 (bf16) or 1e-4 (float32).  Where a
+float decides an integer (the top-K ranking, the walk's argmax or draw),
+both sides take the decision on the same numbers: the oracle's ranking and
+walk run on the GPU's own scores and table and must agree bit for bit.  The
+table is evaluated by the oracle on the GPU's candidates, so a near-tie at
+the K-th rank cannot make the two tables index different tokens.  The
+candidates themselves are also checked in the oracle's exact arithmetic:
+each rank's oracle score is within tolerance of the oracle's own top-K."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import dspine_oracle as O
+from tests.gpu_cases import Case, Run, TOL_BF16, rel_err, tol_for, to_np64
+
+pytestmark = pytest.mark.gpu
+
+# small geometries whose vocabularies are multiples of 16 (the head's packed blocks)
+G_A = synth.Geometry(hidden=256, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=512,
+                     n_feat_layers=3, code_dim=64, msg_dim=32, vocab=512, windows=(24, 0))
+# code and message widths of 256: the refinement GEMMs take the MFMA tile path
+G_T = synth.Geometry(hidden=512, n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1024,
+                     n_feat_layers=2, code_dim=256, msg_dim=256, vocab=2048, windows=(32, 0),
+                     block_causal=True)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_drafter_amd as bd
+    bd.lib()
+
+
+def say(msg):
+    print(f"[propose] {msg}", flush=True)
+
+
+def gpu_propose(model, ctxs, anchors, W, K, walk, temperature, uniforms):
+    import torch
+    u = torch.from_numpy(uniforms).cuda() if uniforms is not None else None
+    res = model.propose(ctxs, anchors, W, K, walk=walk, temperature=temperature, uniforms=u,
+                        keep_scores=True)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in res.items()}
+    out["out"] = out["out"].astype(np.float64)
+    return out
+
+
+def check_proposal(g, wts, head, gp, octxs, anchors, W, K, walk, temperature, uniforms, label,
+                   requests=None):
+    """gp: the GPU's results for all B requests; the oracle runs on
+    `requests` (default all) with the contexts octxs (one per listed request)."""
+    tol = tol_for(g)
+    B = gp["cand"].shape[0]
+    req = list(range(B)) if requests is None else list(requests)
+    V = g.vocab
+    scores = gp["scores"].reshape(B, W, V).astype(np.float64)
+    # integer decisions on the GPU's own numbers: bit-exact
+    for b in range(B):
+        for t in range(W - 1):
+            ref = O.top_k(scores[b, t + 1], K)
+            assert np.array_equal(gp["cand"][b, t], ref), f"{label} request {b} row {t + 1}: top-{K}"
+            assert np.array_equal(gp["cand_scores"][b, t].astype(np.float64), scores[b, t + 1, ref])
+        T = gp["table"][b].astype(np.float64)
+        if walk == "greedy":
+            ch = O.greedy_walk(T)
+        else:
+            ch, q = O.sampled_walk(T, temperature, uniforms[b])
+            assert np.max(np.abs(gp["q"][b] - q)) <= 1e-12, f"{label} request {b}: q"
+        assert np.array_equal(gp["choice"][b], ch), f"{label} request {b}: walk"
+        assert np.array_equal(gp["tokens"][b], gp["cand"][b, np.arange(W - 1), ch])
+    # float values against the oracle, on the GPU's candidates
+    orc = O.propose(g, wts, head, octxs, [anchors[b] for b in req], W, K, walk, temperature,
+                    None if uniforms is None else uniforms[req], cand_override=gp["cand"][req])
+    for i, b in enumerate(req):
+        e_out = rel_err(gp["out"][b], orc["out"][i])
+        e_sc = rel_err(scores[b, 1:], orc["scores"][i])
+        e_tab = rel_err(gp["table"][b].astype(np.float64), orc["table"][i])
+        say(f"{label} request {b}: out {e_out:.2e} scores {e_sc:.2e} table {e_tab:.2e}")
+        assert e_out <= tol and e_sc <= tol and e_tab <= tol, label
+        # the GPU's candidates are (near-)best in the oracle's arithmetic too:
+        # with every score within e of the oracle's, the oracle score of the
+        # GPU's k-th pick is within 2e of the oracle's k-th best
+        e = np.max(np.abs(scores[b, 1:] - orc["scores"][i]))
+        for t in range(W - 1):
+            best = np.sort(orc["scores"][i][t])[::-1][:K]
+            got = orc["scores"][i][t][gp["cand"][b, t]]
+            assert np.max(np.abs(got - best)) <= 2 * e + 1e-12, f"{label} request {b} row {t + 1}: ranks"
+    return orc
+
+
+@pytest.mark.parametrize("which,walk", [("tiny_fp32", "greedy"), ("A", "sampled"), ("T", "greedy"),
+                                        ("T", "sampled")])
+def test_propose_small(which, walk):
+    import block_drafter_amd as bd
+    if which == "tiny_fp32":
+        wl = synth.WORKLOADS["tiny_fp32"]
+        case = Case(wl.geom, wl.seed, 1, wl.W, wl.frontiers)
+        K = 16
+    elif which == "A":
+        case = Case(G_A, 71, 3, 9, (40, 7, 25))
+        K = 5
+    else:
+        case = Case(G_T, 72, 3, 16, (50, 33, 9))
+        K = 16
+    g = case.g
+    wts = synth.make_weights(g, case.seed)
+    head = synth.make_lm_head(g, case.seed)
+    model = bd.Model.from_numpy(g, wts, lm_head=head)
+    run = Run(case, model=model, wts=wts)
+    uni = synth.make_uniforms(case.seed, case.B, case.W - 1) if walk == "sampled" else None
+    say(f"{which} {walk}: B={case.B} W={case.W} K={K}")
+    gp = gpu_propose(model, run.ctxs, run.anchors, case.W, K, walk, 0.7, uni)
+    check_proposal(g, wts, head, gp, [run.oracle_ctx(b) for b in range(case.B)], run.anchors, case.W, K,
+                   walk, 0.7, uni, which)
+    # the forward inside the call is the forward
+    fwd = run.gpu_forward()
+    assert np.array_equal(fwd, gp["out"])
+    model.close()
+
+
+def test_propose_rows_are_per_request():
+    """Changing another request's anchor and frontier leaves a request's
+    proposal bit-identical (the longest context, which sets the attention
+    splits, is unchanged)."""
+    import block_drafter_amd as bd
+    case = Case(G_T, 73, 2, 12, (45, 30))
+    g = case.g
+    wts = synth.make_weights(g, case.seed)
+    head = synth.make_lm_head(g, case.seed)
+    model = bd.Model.from_numpy(g, wts, lm_head=head)
+    run = Run(case, model=model, wts=wts)
+    a = gpu_propose(model, run.ctxs, run.anchors, case.W, 16, "greedy", 1.0, None)
+    run.anchors[1] = (run.anchors[1] + 17) % g.vocab
+    run.ctxs[1].frontier = 20
+    b = gpu_propose(model, run.ctxs, run.anchors, case.W, 16, "greedy", 1.0, None)
+    for k in ("cand", "table", "tokens", "out"):
+        assert np.array_equal(a[k][0], b[k][0]), k
+    assert not np.array_equal(a["out"][1], b["out"][1])
+    c = gpu_propose(model, run.ctxs, run.anchors, case.W, 16, "greedy", 1.0, None)
+    for k in ("cand", "table", "tokens", "out"):
+        assert np.array_equal(b[k], c[k]), k          # and runs are reproducible
+    model.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,walk,requests", [("dspine27b_b1", "greedy", None),
+                                                ("dspine27b_b8", "sampled", (0, 5))])
+def test_propose_full_size(name, walk, requests):
+    """The 27B geometry with a 248320-row head, K = 16: B=1 (greedy walk) and
+    B=8 (sampled walk, oracle on two requests over the GPU's rings)."""
+    import torch
+    import block_drafter_amd as bd
+    from tests.test_gpu_fullsize import gpu_ring_context, setup_windows
+    wl = synth.WORKLOADS[name]
+    g = wl.geom
+    say(f"{name}: weights and head")
+    wts = synth.make_weights(g, wl.seed)
+    head = synth.make_lm_head(g, wl.seed)
+    model = bd.Model.from_numpy(g, wts, lm_head=head)
+    anchors = [int(a) for a in synth.make_anchor_ids(g, wl.seed, wl.B)]
+    ctxs = setup_windows(model, g, wl)
+    uni = synth.make_uniforms(wl.seed, wl.B, wl.W - 1) if walk == "sampled" else None
+    say(f"{name}: propose ({walk})")
+    gp = gpu_propose(model, ctxs, anchors, wl.W, 16, walk, 1.0, uni)
+    req = list(range(wl.B)) if requests is None else list(requests)
+    say(f"{name}: oracle on requests {req}")
+    check_proposal(g, wts, head, gp, [gpu_ring_context(g, ctxs[b], wl.frontiers[b]) for b in req],
+                   anchors, wl.W, 16, walk, 1.0, uni, name, requests=req)
+    model.close()
+    del model
+    torch.cuda.empty_cache()
