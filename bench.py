@@ -159,6 +159,58 @@ def prefill_measure(model, g, seed, n_req=8, chunk=32768, reps=5):
     }
 
 
+def propose_measure(model, g, ctxs, anchors, W, ws, steps, fwd_ms, K=16):
+    """One dspine_draft_propose call per step (the forward, then head scores,
+    top-16, the refinement table and the greedy walk), timed over `steps`
+    calls; the LM head's score GEMM is timed by its own event pairs.  Its
+    roofline is HBM: the bf16 head is read once per call."""
+    import torch
+    import block_drafter_amd as bd
+    B = len(ctxs)
+    pws = model.propose_workspace(B, W, K)
+    o = model.propose(ctxs, anchors, W, K, workspace=ws, propose_workspace=pws)
+    for _ in range(3):
+        model.propose(ctxs, anchors, W, K, workspace=ws, propose_workspace=pws, outputs=o)
+    torch.cuda.synchronize()
+    bd.profile_enable(["head", "tail"])
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        model.propose(ctxs, anchors, W, K, workspace=ws, propose_workspace=pws, outputs=o)
+    e1.record()
+    torch.cuda.synchronize()
+    bd.profile_enable([])
+    ms = e0.elapsed_time(e1) / steps
+    head_ms, head_n = bd.profile_read("head")
+    tail_ms, _ = bd.profile_read("tail")
+    elt = 2 if g.dtype == "bf16" else 4
+    M = B * W
+    head_bytes = g.vocab * g.hidden * elt + M * g.hidden * 4 + M * g.vocab * 4
+    head_avg = head_ms / max(1, head_n)
+    achieved = head_bytes / (head_avg * 1e-3) / 1e9
+    return {
+        "workload": f"one draft forward + proposal tail, B={B}, W={W}, top-{K}, greedy walk, "
+                    f"{g.vocab}-row bf16 LM head",
+        "ms_per_call": round(ms, 4),
+        "proposals_per_s": round(1000.0 / ms, 3),
+        "tail_ms": round(ms - fwd_ms, 4),
+        "head_ms": round(head_avg, 4),
+        "refine_walk_ms": round(tail_ms / steps, 4),
+        "roofline": {
+            "kernel": "gemm_stream (LM head scores of every row)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "bytes_per_launch": head_bytes,
+            "avg_launch_us": round(head_avg * 1000, 2),
+            "launches": head_n,
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +224,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the context-prefill measurement (27B workloads)")
+    ap.add_argument("--no-propose", action="store_true",
+                    help="skip the proposal-tail measurement (workloads with a bridge)")
     ap.add_argument("--breakdown", action="store_true",
                     help="after the timed region, time every kernel class for a few steps")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -211,8 +265,12 @@ def main():
     t = time.time()
     wts = synth.make_weights(g, wl.seed)
     log(f"weights generated in {time.time() - t:.1f}s")
+    # the shared LM head of the proposal tail (packed with the projections)
+    with_propose = bool(g.bridge) and not args.no_propose
+    head = synth.make_lm_head(g, wl.seed) if with_propose else None
     t = time.time()
-    model = bd.Model.from_numpy(g, wts)
+    model = bd.Model.from_numpy(g, wts, lm_head=head)
+    del head
     torch.cuda.synchronize()
     log(f"weights uploaded in {time.time() - t:.1f}s")
     anchors = [int(a) for a in synth.make_anchor_ids(g, wl.seed, B)]
@@ -288,6 +346,10 @@ def main():
     fwd_ev1.record()
     torch.cuda.synchronize()
     fwd_ms = fwd_ev0.elapsed_time(fwd_ev1) / args.steps
+
+    propose = None
+    if with_propose:
+        propose = propose_measure(model, g, ctxs, anchors, W, ws, args.steps, fwd_ms)
 
     # HBM traffic of the same kernel from the PMC runs summarised under
     # profiles/ (null unless they were taken on this workload with the
@@ -366,6 +428,8 @@ def main():
     }
     if breakdown is not None:
         res["breakdown"] = breakdown
+    if propose is not None:
+        res["propose"] = propose
     if not args.no_prefill and g.dtype == "bf16" and g.hidden == 5120:
         del ctxs, pending, ws
         torch.cuda.empty_cache()

@@ -358,7 +358,7 @@ class Model:
 
 
 PROF_KINDS = ["gemm_qkv", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "bridge", "norm",
-              "ctx_gemm", "ctx_store"]
+              "ctx_gemm", "ctx_store", "head", "tail"]
 
 
 def profile_enable(kinds: Sequence[str]):

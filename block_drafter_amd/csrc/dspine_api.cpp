@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "dspine_internal.hpp"
+#include "propose_internal.hpp"
 
 struct dspine_model {
   dspine_geometry g;
@@ -1141,8 +1142,8 @@ ProposePlan make_propose_plan(const dspine_geometry& g, int B, int W, int K) {
   };
   p.u = take(4 * (size_t)M * g.hidden);
   p.scores = take(4 * (size_t)M * g.vocab);
-  p.part_v = take(4 * topk_partial_entries((int)Mp));
-  p.part_i = take(4 * topk_partial_entries((int)Mp));
+  p.part_v = take(4 * topk_partial_entries((int)Mp, g.vocab));
+  p.part_i = take(4 * topk_partial_entries((int)Mp, g.vocab));
   p.codes = take(eb * Mc * r);
   p.Pc = take(4 * Mc * 2 * a);
   p.msg = take(eb * Mc * a);
@@ -1151,7 +1152,9 @@ ProposePlan make_propose_plan(const dspine_geometry& g, int B, int W, int K) {
   return p;
 }
 // tiles of the head GEMM must fit its tile counters
-bool head_fits(const dspine_geometry& g) { return (int64_t)g.vocab / 16 <= 4LL * kMaxTiles; }
+bool head_fits(const dspine_geometry& g) {
+  return (int64_t)g.vocab / 16 <= 4LL * kMaxTiles && g.vocab <= topk_max_vocab();
+}
 }  // namespace
 
 size_t dspine_propose_workspace_bytes(const dspine_model* model, int max_batch, int max_width, int topk) {
@@ -1216,7 +1219,11 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
   gp.epi = EPI_STORE;
   gp.out = scores;
   gp.ldo = V;
-  HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+  {
+    ProfScope ps(DSPINE_PROF_HEAD, stream);
+    HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+  }
+  ProfScope tail_scope(DSPINE_PROF_TAIL, stream);
 
   ProposeParams pp;
   memset(&pp, 0, sizeof pp);

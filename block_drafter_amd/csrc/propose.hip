@@ -11,11 +11,11 @@
 
 #include "dspine_device.hpp"
 #include "dspine_internal.hpp"
+#include "propose_internal.hpp"
 
 namespace dspine {
 
 constexpr int kTopkThreads = 256;
-constexpr int kTopkChunks = 64;        // vocabulary slices of one row's partial top-K
 constexpr int kScoreThreads = 256;
 constexpr int kMaxHidden = 8192;       // refined state kept in LDS
 
@@ -25,119 +25,183 @@ __device__ __forceinline__ bool ranks_before(float av, int ai, float bv, int bi)
   return av > bv || (av == bv && ai < bi);
 }
 
-// A sorted list of the best kMaxTopK (score, token) pairs in registers.
-struct TopList {
-  float v[kMaxTopK];
-  int i[kMaxTopK];
-  __device__ __forceinline__ void clear() {
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-      v[s] = -INFINITY;
-      i[s] = INT_MAX;
-    }
-  }
-  __device__ __forceinline__ void insert(float nv, int ni) {
-    if (!ranks_before(nv, ni, v[kMaxTopK - 1], i[kMaxTopK - 1])) return;
-    // walk up from the last slot: entries the new pair beats move down one
-    bool placed = false;
-#pragma unroll
-    for (int s = kMaxTopK - 1; s >= 1; --s) {
-      const bool up = !placed && ranks_before(nv, ni, v[s - 1], i[s - 1]);
-      const float wv = up ? v[s - 1] : (placed ? v[s] : nv);
-      const int wi = up ? i[s - 1] : (placed ? i[s] : ni);
-      placed = placed || !up;
-      v[s] = wv;
-      i[s] = wi;
-    }
-    if (!placed) {
-      v[0] = nv;
-      i[0] = ni;
-    }
-  }
-};
+// logits row of proposal row r (rows 1..W-1 of every request)
+__device__ __forceinline__ int score_row(int r, int W) { return (r / (W - 1)) * W + 1 + r % (W - 1); }
 
-// Tree merge of n sorted lists held in LDS (list t at sv/si[t*kMaxTopK ..]):
-// at each level thread t < half merges lists t and t + half into list t.
-// Leaves the best kMaxTopK pairs in list 0.  Every thread of the block calls.
-__device__ void merge_lists(float* sv, int* si, int n) {
-  for (int half = n / 2; half >= 1; half /= 2) {
-    __syncthreads();
-    const int t = threadIdx.x;
-    float ov[kMaxTopK];
-    int oi[kMaxTopK];
-    if (t < half) {
-      const float* av = sv + t * kMaxTopK;
-      const int* ai = si + t * kMaxTopK;
-      const float* bv = sv + (t + half) * kMaxTopK;
-      const int* bi = si + (t + half) * kMaxTopK;
-      // both lists hold kMaxTopK entries and kMaxTopK are taken, so neither
-      // runs out before the last step; the read indices stay clamped anyway
-      int ia = 0, ib = 0;
+// Rank of pair (v, i) among the n4 pairs (cv, ci) in LDS: how many rank
+// before it.  n4 is a multiple of 4 and the arrays are 16-byte aligned (read
+// four pairs at a time, several reads in flight); padding pairs (-inf,
+// INT_MAX) rank before nothing.
+__device__ __forceinline__ int rank_among(float v, int i, const float* cv, const int* ci, int n4) {
+  int r = 0;
+#pragma unroll 4
+  for (int u = 0; u < n4; u += 4) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(cv + u);
+    const int4 b = *reinterpret_cast<const int4*>(ci + u);
+    r += (ranks_before(a[0], b.x, v, i) ? 1 : 0) + (ranks_before(a[1], b.y, v, i) ? 1 : 0) +
+         (ranks_before(a[2], b.z, v, i) ? 1 : 0) + (ranks_before(a[3], b.w, v, i) ? 1 : 0);
+  }
+  return r;
+}
+
+// Partial top-K: block (c, r) ranks slice c (kSliceValues scores, kVpt per
+// thread, held in registers) of proposal row r's scores and writes the
+// slice's best kMaxTopK pairs in order.  A NaN score ranks as -inf.
+//
+// Selection by threshold: tau = the kMaxTopK-th best of the 256 per-thread
+// best pairs.  Those are kMaxTopK distinct slice pairs ranking at or before
+// tau, so every pair of the slice's top kMaxTopK ranks at or before tau too.
+// The pairs at or before tau (usually a few dozen) are gathered in LDS and
+// placed by counting how many of them rank before each.  A pair qualifies
+// only if its thread's best pair does, i.e. only from the kMaxTopK threads
+// whose best pairs rank at or before tau, and tau's own thread adds only tau:
+// at most (kMaxTopK - 1) * kVpt + 1 pairs.  (With fewer than kMaxTopK
+// threads holding a score, tau is (-inf, INT_MAX) and every score of the
+// slice qualifies: fewer than kMaxTopK * kVpt.)
+constexpr int kVpt = 32;
+constexpr int kSliceValues = kVpt * kTopkThreads;
+constexpr int kGather = kMaxTopK * kVpt;
+__global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(const ProposeParams p) {
+  __shared__ __align__(16) float sv[kGather + 4];    // the gathered pairs (+ padding)
+  __shared__ __align__(16) int si[kGather + 4];
+  __shared__ __align__(16) float mv[kTopkThreads];
+  __shared__ __align__(16) int mi[kTopkThreads];
+  __shared__ float tau_v;
+  __shared__ int tau_i, count;
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int lo = c * kSliceValues, hi = min(p.vocab, lo + kSliceValues);
+  const gptr<float> row = as_global(p.scores) + (size_t)score_row(r, p.W) * p.vocab;
+  float x[kVpt];
 #pragma unroll
-      for (int s = 0; s < kMaxTopK; ++s) {
-        const bool take_a = ranks_before(av[ia], ai[ia], bv[ib], bi[ib]);
-        ov[s] = take_a ? av[ia] : bv[ib];
-        oi[s] = take_a ? ai[ia] : bi[ib];
-        ia = min(ia + (take_a ? 1 : 0), kMaxTopK - 1);
-        ib = min(ib + (take_a ? 0 : 1), kMaxTopK - 1);
-      }
+  for (int u = 0; u < kVpt; ++u) {
+    const int v = lo + tid + u * kTopkThreads;
+    const float s = v < hi ? row[v] : -INFINITY;
+    x[u] = s == s ? s : -INFINITY;
+  }
+  // this thread's best pair
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+#pragma unroll
+  for (int u = 0; u < kVpt; ++u) {
+    const int v = lo + tid + u * kTopkThreads;
+    if (v < hi && ranks_before(x[u], v, bv, bi)) {
+      bv = x[u];
+      bi = v;
     }
-    __syncthreads();
-    if (t < half) {
+  }
+  mv[tid] = bv;
+  mi[tid] = bi;
+  if (tid == 0) {
+    count = 0;
+    tau_v = -INFINITY;      // kept when fewer than kMaxTopK threads hold a score
+    tau_i = INT_MAX;
+  }
+  __syncthreads();
+  if (rank_among(bv, bi, mv, mi, kTopkThreads) == kMaxTopK - 1) {
+    tau_v = bv;
+    tau_i = bi;
+  }
+  __syncthreads();
+  const float tv = tau_v;
+  const int ti = tau_i;
 #pragma unroll
-      for (int s = 0; s < kMaxTopK; ++s) {
-        sv[t * kMaxTopK + s] = ov[s];
-        si[t * kMaxTopK + s] = oi[s];
+  for (int u = 0; u < kVpt; ++u) {
+    const int v = lo + tid + u * kTopkThreads;
+    if (v < hi && !ranks_before(tv, ti, x[u], v)) {   // at or before tau
+      const int slot = atomicAdd(&count, 1);
+      if (slot < kGather) {                             // always (bound above)
+        sv[slot] = x[u];
+        si[slot] = v;
       }
     }
   }
   __syncthreads();
-}
-
-// logits row of proposal row r (rows 1..W-1 of every request)
-__device__ __forceinline__ int score_row(int r, int W) { return (r / (W - 1)) * W + 1 + r % (W - 1); }
-
-// Partial top-K: block (c, r) ranks slice c of the vocabulary of proposal row r.
-__global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(const ProposeParams p) {
-  __shared__ float sv[kTopkThreads * kMaxTopK];
-  __shared__ int si[kTopkThreads * kMaxTopK];
-  const int c = blockIdx.x, r = blockIdx.y;
-  const int slice = (p.vocab + kTopkChunks - 1) / kTopkChunks;
-  const int lo = c * slice, hi = min(p.vocab, lo + slice);
-  const gptr<float> row = as_global(p.scores) + (size_t)score_row(r, p.W) * p.vocab;
-  TopList L;
-  L.clear();
-  for (int v = lo + threadIdx.x; v < hi; v += kTopkThreads) L.insert(row[v], v);
-#pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) {
-    sv[threadIdx.x * kMaxTopK + s] = L.v[s];
-    si[threadIdx.x * kMaxTopK + s] = L.i[s];
+  const int n = count;                                // <= kGather (see above)
+  const int n4 = (n + 3) & ~3;
+  const size_t out0 = ((size_t)r * gridDim.x + c) * kMaxTopK;
+  if (tid < kMaxTopK) {
+    p.part_v[out0 + tid] = -INFINITY;                  // slots no pair fills
+    p.part_i[out0 + tid] = INT_MAX;
   }
-  merge_lists(sv, si, kTopkThreads);
-  if (threadIdx.x < kMaxTopK) {
-    const size_t o = ((size_t)r * kTopkChunks + c) * kMaxTopK + threadIdx.x;
-    p.part_v[o] = sv[threadIdx.x];
-    p.part_i[o] = si[threadIdx.x];
+  if (tid < n4 - n) {
+    sv[n + tid] = -INFINITY;
+    si[n + tid] = INT_MAX;
+  }
+  __syncthreads();
+  for (int e = tid; e < n; e += kTopkThreads) {
+    const int rk = rank_among(sv[e], si[e], sv, si, n4);
+    if (rk < kMaxTopK) {
+      p.part_v[out0 + rk] = sv[e];
+      p.part_i[out0 + rk] = si[e];
+    }
   }
 }
 
-// Final top-K of proposal row r from its kTopkChunks partial lists.  Slots
-// that no finite score filled (fewer than K ranked tokens) get token -1.
-__global__ __launch_bounds__(kTopkChunks) void topk_merge_kernel(const ProposeParams p) {
-  __shared__ float sv[kTopkChunks * kMaxTopK];
-  __shared__ int si[kTopkChunks * kMaxTopK];
-  const int r = blockIdx.x;
-#pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) {
-    const size_t o = ((size_t)r * kTopkChunks + threadIdx.x) * kMaxTopK + s;
-    sv[threadIdx.x * kMaxTopK + s] = p.part_v[o];
-    si[threadIdx.x * kMaxTopK + s] = p.part_i[o];
+// Final top-K of proposal row r from its partial lists (one sorted list of
+// kMaxTopK pairs per slice, at most kMaxSlices).  Same selection as above
+// with the lists' heads as the groups: tau = the kMaxTopK-th best head; only
+// lists whose head ranks at or before tau contribute, tau's list only its
+// head, so at most (kMaxTopK - 1) * kMaxTopK + 1 pairs are gathered and
+// ranked.  Slots that no ranked pair fills (fewer than K finite scores) get
+// token -1.
+constexpr int kMaxSlices = 32;
+__global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(const ProposeParams p, int slices) {
+  __shared__ __align__(16) float sv[kMaxSlices * kMaxTopK];
+  __shared__ __align__(16) int si[kMaxSlices * kMaxTopK];
+  __shared__ __align__(16) float gv[kMaxTopK * kMaxTopK + 4];
+  __shared__ __align__(16) int gi[kMaxTopK * kMaxTopK + 4];
+  __shared__ __align__(16) float hv[kMaxSlices];
+  __shared__ __align__(16) int hi_[kMaxSlices];
+  __shared__ float tau_v;
+  __shared__ int tau_i, count;
+  const int r = blockIdx.x, n = slices * kMaxTopK, tid = threadIdx.x;
+  for (int e = tid; e < n; e += kTopkThreads) {
+    sv[e] = p.part_v[(size_t)r * n + e];
+    si[e] = p.part_i[(size_t)r * n + e];
   }
-  merge_lists(sv, si, kTopkChunks);
-  if (threadIdx.x < p.K) {
-    const int tok = si[threadIdx.x];
-    p.cand[r * p.K + threadIdx.x] = tok == INT_MAX ? -1 : tok;
-    p.cand_scores[r * p.K + threadIdx.x] = sv[threadIdx.x];
+  if (tid < kMaxSlices) {                 // heads (padding lists rank last)
+    hv[tid] = tid < slices ? p.part_v[(size_t)r * n + tid * kMaxTopK] : -INFINITY;
+    hi_[tid] = tid < slices ? p.part_i[(size_t)r * n + tid * kMaxTopK] : INT_MAX;
+  }
+  if (tid < p.K) {
+    p.cand[r * p.K + tid] = -1;
+    p.cand_scores[r * p.K + tid] = -INFINITY;
+  }
+  if (tid == 0) {
+    count = 0;
+    tau_v = -INFINITY;                    // kept with fewer than kMaxTopK real heads
+    tau_i = INT_MAX;
+  }
+  __syncthreads();
+  if (tid < slices && hi_[tid] != INT_MAX && rank_among(hv[tid], hi_[tid], hv, hi_, kMaxSlices) == kMaxTopK - 1) {
+    tau_v = hv[tid];
+    tau_i = hi_[tid];
+  }
+  __syncthreads();
+  const float tv = tau_v;
+  const int ti = tau_i;
+  for (int e = tid; e < n; e += kTopkThreads) {
+    if (si[e] != INT_MAX && !ranks_before(tv, ti, sv[e], si[e])) {   // at or before tau
+      const int slot = atomicAdd(&count, 1);
+      if (slot < kMaxTopK * kMaxTopK) {                              // always (bound above)
+        gv[slot] = sv[e];
+        gi[slot] = si[e];
+      }
+    }
+  }
+  __syncthreads();
+  const int m = count, m4 = (m + 3) & ~3;
+  if (tid < m4 - m) {
+    gv[m + tid] = -INFINITY;
+    gi[m + tid] = INT_MAX;
+  }
+  __syncthreads();
+  for (int e = tid; e < m; e += kTopkThreads) {
+    const int rk = rank_among(gv[e], gi[e], gv, gi, m4);
+    if (rk < p.K) {
+      p.cand[r * p.K + rk] = gi[e];
+      p.cand_scores[r * p.K + rk] = gv[e];
+    }
   }
 }
 
@@ -182,6 +246,22 @@ __global__ __launch_bounds__(128) void cand_msg_kernel(const ProposeParams p) {
   }
 }
 
+// the 8 elements of a lane fragment as floats
+__device__ __forceinline__ void frag_to_float(const Frag<bf16_t>& f, float* w) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    w[2 * d] = __uint_as_float(f.v[d] << 16);
+    w[2 * d + 1] = __uint_as_float(f.v[d] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void frag_to_float(const Frag<float>& f, float* w) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    w[d] = __uint_as_float(f.v[0][d]);
+    w[4 + d] = __uint_as_float(f.v[1][d]);
+  }
+}
+
 // Row (b, t, i) of the transition table: x' = u_t + rho_t Y, h = g_final x' /
 // rms(x'), T[b, t-1, i, j] = E[cand_j] . h for the K candidates j of row t.
 // Head rows are read from the fragment-ordered copy: element (v, k) sits at
@@ -195,39 +275,64 @@ __global__ __launch_bounds__(kScoreThreads) void cand_score_kernel(const Propose
   const int H = p.H;
   const float* u = p.u + (size_t)(c.b * p.W + c.t) * H;
   const float* y = p.Y + (size_t)blockIdx.x * H;
+  // u, Y and the gain in one batch of loads (H <= kMaxHidden: 32 per thread),
+  // then x' = u + rho Y and h = g_final x' / rms(x') from registers
+  constexpr int kBatch = kMaxHidden / kScoreThreads;
+  const TW* gain = reinterpret_cast<const TW*>(p.g_final);
+  float uu[kBatch], yy[kBatch], gg[kBatch];
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q) {
+    const int k = threadIdx.x + q * kScoreThreads;
+    uu[q] = k < H ? u[k] : 0.f;
+    yy[q] = k < H ? y[k] : 0.f;
+    gg[q] = k < H ? Elt<TW>::load(gain, k) : 0.f;
+  }
   float ss = 0.f;
-  for (int k = threadIdx.x; k < H; k += kScoreThreads) ss += u[k] * u[k];
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q) ss += uu[q] * uu[q];
   const float rho = sqrtf(block_sum<kScoreThreads>(ss, red) / H);
   float sx = 0.f;
-  for (int k = threadIdx.x; k < H; k += kScoreThreads) {
-    const float x = u[k] + rho * y[k];
-    h[k] = x;
-    sx += x * x;
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q) {
+    uu[q] += rho * yy[q];                // x'
+    sx += uu[q] * uu[q];
   }
   const float inv = rsqrtf(block_sum<kScoreThreads>(sx, red) / H + p.eps);
-  const TW* gain = reinterpret_cast<const TW*>(p.g_final);
-  for (int k = threadIdx.x; k < H; k += kScoreThreads) h[k] = h[k] * inv * Elt<TW>::load(gain, k);
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q) {
+    const int k = threadIdx.x + q * kScoreThreads;
+    if (k < H) h[k] = uu[q] * inv * gg[q];
+  }
   __syncthreads();
 
   const int* cj = p.cand + (size_t)(c.b * (p.W - 1) + c.t - 1) * p.K;
-  const gptr<TW> E = as_global(reinterpret_cast<const TW*>(p.head_packed));
+  const TW* E = reinterpret_cast<const TW*>(p.head_packed);
+  size_t rowbase[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    const int v = clamp_token(j < p.K ? cj[j] : cj[0], p.vocab);
+    rowbase[j] = (size_t)(v / 16) * (H / 32) * 512 + 8 * (v % 16);
+  }
   float acc[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) acc[j] = 0.f;
   const int nchunk = H / 8;              // 8 consecutive columns of one lane fragment
+  for (int ch = threadIdx.x; ch < nchunk; ch += kScoreThreads) {
+    const size_t off = (size_t)(ch / 4) * 512 + 128 * (ch % 4);
+    Frag<TW> f[kMaxTopK];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j < p.K) {
-      const int v = clamp_token(cj[j], p.vocab);
-      const size_t rowbase = (size_t)(v / 16) * (H / 32) * 512 + 8 * (v % 16);
-      for (int ch = threadIdx.x; ch < nchunk; ch += kScoreThreads) {
-        const size_t o = rowbase + (size_t)(ch / 4) * 512 + 128 * (ch % 4);
-        const float* hk = h + 8 * ch;
-        float s = 0.f;
+    for (int j = 0; j < kMaxTopK; ++j) f[j].gload(as_global(E + rowbase[j] + off));
+    float hk[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += Elt<TW>::gload(E, o + e) * hk[e];
-        acc[j] += s;
-      }
+    for (int e = 0; e < 8; ++e) hk[e] = h[8 * ch + e];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      float w[8];
+      frag_to_float(f[j], w);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += w[e] * hk[e];
+      acc[j] += s;
     }
   }
   const int w = threadIdx.x >> 6;
@@ -245,46 +350,73 @@ __global__ __launch_bounds__(kScoreThreads) void cand_score_kernel(const Propose
   }
 }
 
-// The walk of request b, serial over its rows (one thread): row 1 uses table
-// row 0 (the anchor), row t the row chosen at t-1.  Greedy: the first
-// maximum.  Sampled: float64 p = softmax(T / temperature) with the normaliser
-// and the cumulative sum taken left to right, the first j whose cumulative
+// The walk of request b: one wave; the request's tables go to LDS in one
+// pass, then the rows are taken in order.  Row 1 uses table row 0 (the
+// anchor), row t the row chosen at t-1.  Lane j holds candidate j's score.
+// Greedy: the first maximum.  Sampled: float64 p = softmax(T / temperature);
+// the normaliser and the cumulative sum are taken left to right (every lane
+// forms the same sums), and the choice is the first j whose cumulative
 // probability exceeds the uniform (the last j if none does).
 __global__ __launch_bounds__(64) void walk_kernel(const ProposeParams p) {
-  if (threadIdx.x != 0) return;
-  const int b = blockIdx.x, n = p.W - 1, K = p.K;
+  __shared__ float tab[(DSPINE_MAX_WIDTH - 1) * kMaxTopK * kMaxTopK];
+  const int b = blockIdx.x, n = p.W - 1, K = p.K, lane = threadIdx.x;
+  const gptr<float> src = as_global(p.table) + (size_t)b * n * K * K;
+  constexpr int kBatch = 16;
+  for (int e0 = lane; e0 < n * K * K; e0 += 64 * kBatch) {
+    float x[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) x[u] = e0 + 64 * u < n * K * K ? src[e0 + 64 * u] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (e0 + 64 * u < n * K * K) tab[e0 + 64 * u] = x[u];
+  }
+  __syncthreads();
+  const bool on = lane < K;
   int i = 0;
   for (int t = 0; t < n; ++t) {
-    const float* row = p.table + ((size_t)(b * n + t) * K + i) * K;
+    const float v = on ? tab[(t * K + i) * K + lane] : -INFINITY;
     int j = 0;
     double q = 1.0;
     if (p.walk == DSPINE_WALK_GREEDY) {
-      float best = row[0];
-      for (int jj = 1; jj < K; ++jj)
-        if (row[jj] > best) {
-          best = row[jj];
-          j = jj;
+      // first maximum: larger score, then smaller index
+      float bv = v;
+      int bj = on ? lane : INT_MAX;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oj = __shfl_xor(bj, o, 64);
+        if (ov > bv || (ov == bv && oj < bj)) {
+          bv = ov;
+          bj = oj;
         }
+      }
+      j = bj;
     } else {
-      double mx = (double)row[0] / p.temperature;
-      for (int jj = 1; jj < K; ++jj) mx = fmax(mx, (double)row[jj] / p.temperature);
+      const double sv = (double)v / p.temperature;
+      double mx = sv;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+      const double e = on ? exp(sv - mx) : 0.0;
       double total = 0.0;
-      for (int jj = 0; jj < K; ++jj) total += exp((double)row[jj] / p.temperature - mx);
+      for (int jj = 0; jj < K; ++jj) total += __shfl(e, jj, 64);
+      const double pj = e / total;
       const double u = p.uniforms[b * n + t];
       double cdf = 0.0;
       j = K - 1;
       for (int jj = 0; jj < K; ++jj) {
-        cdf += exp((double)row[jj] / p.temperature - mx) / total;
+        cdf += __shfl(pj, jj, 64);
         if (u < cdf) {
           j = jj;
           break;
         }
       }
-      q = exp((double)row[j] / p.temperature - mx) / total;
+      q = __shfl(pj, j, 64);
     }
-    p.choice[b * n + t] = j;
-    p.tokens[b * n + t] = p.cand[(b * n + t) * K + j];
-    if (p.q) p.q[b * n + t] = q;
+    if (lane == 0) {
+      p.choice[b * n + t] = j;
+      p.tokens[b * n + t] = p.cand[(b * n + t) * K + j];
+      if (p.q) p.q[b * n + t] = q;
+    }
     i = j;
   }
 }
@@ -292,13 +424,16 @@ __global__ __launch_bounds__(64) void walk_kernel(const ProposeParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+int topk_slices(int vocab) { return (vocab + kSliceValues - 1) / kSliceValues; }
 hipError_t launch_topk(const ProposeParams& p, hipStream_t s) {
-  const int rows = p.B * (p.W - 1);
-  DSPINE_LAUNCH(topk_partial_kernel, dim3(kTopkChunks, rows), dim3(kTopkThreads), 0, s, p);
-  DSPINE_LAUNCH(topk_merge_kernel, dim3(rows), dim3(kTopkChunks), 0, s, p);
+  const int rows = p.B * (p.W - 1), slices = topk_slices(p.vocab);
+  if (slices > kMaxSlices) return hipErrorInvalidValue;
+  DSPINE_LAUNCH(topk_partial_kernel, dim3(slices, rows), dim3(kTopkThreads), 0, s, p);
+  DSPINE_LAUNCH(topk_merge_kernel, dim3(rows), dim3(kTopkThreads), 0, s, p, slices);
   return hipGetLastError();
 }
-size_t topk_partial_entries(int rows) { return (size_t)rows * kTopkChunks * kMaxTopK; }
+size_t topk_partial_entries(int rows, int vocab) { return (size_t)rows * topk_slices(vocab) * kMaxTopK; }
+int topk_max_vocab() { return kMaxSlices * kSliceValues; }
 int propose_max_hidden() { return kMaxHidden; }
 
 hipError_t launch_cand_codes(const ProposeParams& p, int dtype, hipStream_t s) {

@@ -1,0 +1,46 @@
+// Internal interface of the proposal tail kernels (propose.hip) for the C ABI.
+#pragma once
+#include "dspine_internal.hpp"
+
+namespace dspine {
+
+// ---------------------------------------------------------------------------
+// proposal tail (candidates, refinement rows, walk)
+// ---------------------------------------------------------------------------
+constexpr int kMaxTopK = DSPINE_MAX_TOPK;
+struct ProposeParams {
+  int32_t B, W, K, vocab, H, r, a, walk;
+  double temperature;
+  float eps, code_scale;
+  int32_t anchor[DSPINE_MAX_BATCH];
+  const float* scores;            // [B*W, vocab] head scores
+  float* part_v;                  // partial top-K lists [rows][chunks][kMaxTopK]
+  int32_t* part_i;
+  int32_t* cand;                  // [B, W-1, K]
+  float* cand_scores;
+  const void* codebook;           // [vocab, r] model dtype
+  void* codes;                    // [B*(W-1)*K, r] operand type
+  const float* P_own;             // [B*W, 3a]: the forward's last [G; G_p; A] c
+  const float* P_cand;            // [B*(W-1)*K, 2a]: [G_p; A] of the candidate codes
+  const void* bias;               // [a] model dtype
+  void* msg;                      // [B*(W-1)*K, a] operand type
+  const float* u;                 // [B*W, H] last layer's pre-write state
+  const float* Y;                 // [B*(W-1)*K, H] W_l msg
+  const void* g_final;            // [H] model dtype
+  const void* head_packed;        // [vocab, H] in fragment order
+  float* table;                   // [B, W-1, K, K]
+  const double* uniforms;         // [B, W-1]
+  int32_t* choice;                // [B, W-1]
+  int32_t* tokens;                // [B, W-1]
+  double* q;                      // [B, W-1] or NULL
+};
+hipError_t launch_topk(const ProposeParams& p, hipStream_t s);
+size_t topk_partial_entries(int rows, int vocab);
+int topk_max_vocab();
+int propose_max_hidden();
+hipError_t launch_cand_codes(const ProposeParams& p, int dtype, hipStream_t s);
+hipError_t launch_cand_msg(const ProposeParams& p, int dtype, hipStream_t s);
+hipError_t launch_cand_score(const ProposeParams& p, int dtype, hipStream_t s);
+hipError_t launch_walk(const ProposeParams& p, hipStream_t s);
+
+}  // namespace dspine

@@ -332,7 +332,9 @@ int dspine_debug_visible(const dspine_model* model, int layer, int B, int W,
 #define DSPINE_PROF_NORM 6          /* input/post/final norms and the embedding gather */
 #define DSPINE_PROF_CTX_GEMM 7      /* a1-a2 feature and K/V projections */
 #define DSPINE_PROF_CTX_STORE 8     /* a1 norm, a2 head norm + RoPE + ring scatter */
-#define DSPINE_PROF_KINDS 9
+#define DSPINE_PROF_HEAD 9          /* proposal: the LM head's scores of every row */
+#define DSPINE_PROF_TAIL 10         /* proposal: top-K, refinement table and walk */
+#define DSPINE_PROF_KINDS 11
 
 /* kind_mask: bit k enables class k; 0 disables recording.  Process-wide. */
 int dspine_profile_enable(uint32_t kind_mask);
