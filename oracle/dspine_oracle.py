@@ -409,16 +409,52 @@ def block_input(g, wts, anchor_id: int, W: int) -> np.ndarray:
     return widen(emb[rows])
 
 
+# ---------------------------------------------------------------------------
+# DFlash2 dynamic grouped convolution [NIF, DFlash2 layer equations]
+# ---------------------------------------------------------------------------
+def conv_delta(g, wts, layer: int, branch: str, X: np.ndarray) -> np.ndarray:
+    """delta = W_delta X reshaped to [W, 2 sides, 2 taps, H/16 groups] for one
+    request block X [W, H] (the branch's normalised input)."""
+    d = linear(X, wts[f"l{layer}.{branch}_conv_w"])
+    return d.reshape(X.shape[0], 2, 2, g.conv_groups)
+
+
+def conv_apply(g, wts, layer: int, branch: str, side: int, X: np.ndarray, delta: np.ndarray) -> np.ndarray:
+    """Conv_side(X)[i, g, j] = (base[side,0,g,j] + delta[i,side,0,g]) X[i,g,j]
+    + [i >= 1] (base[side,1,g,j] + delta[i,side,1,g]) X[i-1,g,j]: per-channel
+    base coefficients, increments shared by the channels of a group, no tap
+    before row 0 and no history across requests [NIF, DFlash2 layer
+    equations].  X [W, H] is one request's block."""
+    W, G, gw = X.shape[0], g.conv_groups, g.conv_group
+    base = widen(wts[f"l{layer}.{branch}_conv_base"]).reshape(2, 2, G, gw)
+    Xg = X.reshape(W, G, gw)
+    out = (base[side, 0][None] + delta[:, side, 0, :, None]) * Xg
+    out[1:] += (base[side, 1][None] + delta[1:, side, 1, :, None]) * Xg[:-1]
+    return out.reshape(W, g.hidden)
+
+
+def conv_blocks(g, wts, layer: int, branch: str, side: int, X: np.ndarray, deltas, W: int) -> np.ndarray:
+    """conv_apply on each request's rows of stacked X [B*W, H]."""
+    return np.concatenate([conv_apply(g, wts, layer, branch, side, X[b * W:(b + 1) * W], deltas[b])
+                           for b in range(len(deltas))])
+
+
 def decoder_layer(g, wts, layer: int, ctxs: Sequence[RequestContext], x: np.ndarray, W: int,
                   attn_fn=block_attention) -> np.ndarray:
     """a5-a8 [NIF, layer equations]: n = plain_rmsnorm(x, input_norm); q and k
     are head-RMSNormed and rotated; attention over context plus block; y = x +
     W_o a; m = plain_rmsnorm(y, post_attention_norm); x_next = y +
-    W_down(SiLU(W_gate m) * W_up m).  x is [B*W, H]: rows of all requests are
+    W_down(SiLU(W_gate m) * W_up m).  With conv_group > 0 (DFlash2) each
+    branch's normalised input goes through the prepare side of its
+    convolution and the branch output through the finish side, with the
+    delta projected from that normalised input.  x is [B*W, H]: rows of all requests are
     stacked for the row-wise linear maps; attention runs per request."""
     p = f"l{layer}."
     B = len(ctxs)
     n = plain_rmsnorm(x, wts[p + "g_in"], g.eps)
+    if g.conv:      # DFlash2: prepare the attention branch's input
+        d_a = [conv_delta(g, wts, layer, "attn", n[b * W:(b + 1) * W]) for b in range(B)]
+        n = conv_blocks(g, wts, layer, "attn", 0, n, d_a, W)
     pos = np.concatenate([np.arange(c.frontier, c.frontier + W) for c in ctxs])
     q = rope_1d(head_rmsnorm(linear(n, wts[p + "wq"]), wts[p + "gq"], g.eps, g.head_dim),
                 pos, g.rope_theta, g.head_dim)
@@ -429,10 +465,18 @@ def decoder_layer(g, wts, layer: int, ctxs: Sequence[RequestContext], x: np.ndar
     for b in range(B):
         sl = slice(b * W, (b + 1) * W)
         a[sl] = attn_fn(g, layer, ctxs[b], q[sl], k[sl], v[sl])
-    y = x + linear(a, wts[p + "wo"])
+    o = linear(a, wts[p + "wo"])
+    if g.conv:      # finish: the output side, with the prepare's delta
+        o = conv_blocks(g, wts, layer, "attn", 1, o, d_a, W)
+    y = x + o
     m = plain_rmsnorm(y, wts[p + "g_post"], g.eps)
-    return y + linear(silu(linear(m, wts[p + "w_gate"])) * linear(m, wts[p + "w_up"]),
-                      wts[p + "w_down"])
+    if g.conv:
+        d_m = [conv_delta(g, wts, layer, "mlp", m[b * W:(b + 1) * W]) for b in range(B)]
+        m = conv_blocks(g, wts, layer, "mlp", 0, m, d_m, W)
+    z = linear(silu(linear(m, wts[p + "w_gate"])) * linear(m, wts[p + "w_up"]), wts[p + "w_down"])
+    if g.conv:
+        z = conv_blocks(g, wts, layer, "mlp", 1, z, d_m, W)
+    return y + z
 
 
 def draft_forward(g, wts, ctxs: Sequence[RequestContext], anchor_ids: Sequence[int], W: int,

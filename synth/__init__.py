@@ -71,6 +71,15 @@ class Geometry:
     rope_theta: float = 1e7
     dtype: str = "bf16"    # "bf16" or "f32"
     block_causal: bool = False
+    conv_group: int = 0    # DFlash2 dynamic grouped convolution group width; 0 = none
+
+    @property
+    def conv(self) -> bool:
+        return self.conv_group > 0
+
+    @property
+    def conv_groups(self) -> int:
+        return self.hidden // self.conv_group if self.conv_group else 0
 
     @property
     def mask_token_id(self) -> int:
@@ -114,6 +123,11 @@ G_27B_CAUSAL = Geometry(hidden=5120, n_layers=5, n_q_heads=32, n_kv_heads=8, hea
                         ffn=17408, n_feat_layers=5, code_dim=1024, msg_dim=512, vocab=248320,
                         windows=(8192,) * 5, block_causal=True)
 
+# DFlash2 27B: five local layers, dynamic grouped convolution of group width 16, no bridge
+G_27B_DFLASH2 = Geometry(hidden=5120, n_layers=5, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         ffn=17408, n_feat_layers=5, code_dim=0, msg_dim=0, vocab=248320,
+                         windows=(2048,) * 5, conv_group=16)
+
 G_35B_DFLASH = Geometry(hidden=2048, n_layers=6, n_q_heads=32, n_kv_heads=8, head_dim=128,
                         ffn=6144, n_feat_layers=8, code_dim=0, msg_dim=0, vocab=248320,
                         windows=(4096,) * 5 + (0,))
@@ -136,6 +150,10 @@ WORKLOADS: Dict[str, Workload] = {
                                     frontiers=_uniform_frontiers(1006, 8, 1024, 16384),
                                     note="27B geometry with block-causal attention and 8192-position "
                                          "windows, 8 blocks, context lengths U{1024..16384}"),
+    "dflash2_27b_b8": Workload("dflash2_27b_b8", G_27B_DFLASH2, 1007, B=8, W=16,
+                               frontiers=_uniform_frontiers(1007, 8, 1024, 16384),
+                               note="DFlash2 27B geometry: dynamic grouped convolution (two taps, "
+                                    "group width 16) around attention and MLP, no bridge"),
     "dflash35b_b8": Workload("dflash35b_b8", G_35B_DFLASH, 1004, B=8, W=16,
                              frontiers=(32768,) * 8,
                              note="35B-A3B-style plain DFlash, bridge off, 5 local + 1 full layer"),
@@ -225,6 +243,9 @@ def weight_names(g: Geometry) -> List[str]:
     if g.bridge:
         names += ["bridge_G", "bridge_Gp", "bridge_A", "bridge_b", "codebook"]
     names += ["g_final", "embed"]
+    if g.conv:      # appended last: the other tensors keep their draw indices
+        for l in range(g.n_layers):
+            names += [f"l{l}.attn_conv_w", f"l{l}.attn_conv_base", f"l{l}.mlp_conv_w", f"l{l}.mlp_conv_base"]
     return names
 
 
@@ -240,6 +261,8 @@ def weight_shape(g: Geometry, name: str) -> tuple:
         "bridge_G": (g.msg_dim, g.code_dim), "bridge_Gp": (g.msg_dim, g.code_dim),
         "bridge_A": (g.msg_dim, g.code_dim), "bridge_b": (g.msg_dim,),
         "codebook": (g.vocab, g.code_dim), "embed": (g.vocab, H),
+        "attn_conv_w": (4 * g.conv_groups, H), "mlp_conv_w": (4 * g.conv_groups, H),
+        "attn_conv_base": (4, H), "mlp_conv_base": (4, H),
     }
     return table[base]
 
@@ -262,6 +285,14 @@ def make_weights(g: Geometry, seed: int, overrides: Optional[dict] = None) -> Di
             out[name] = unit_rows(seed, idx, shape[0], shape[1], g.dtype)
         elif base == "embed":
             out[name] = normal(seed, idx, shape, 1.0, 0.0, g.dtype)
+        elif base.endswith("_conv_base"):
+            # rows (side, tap): the current-row taps near 1, the previous-row taps near 0
+            b = normal(seed, idx, shape, 0.1, 0.0, "f32")
+            b[0] += 1.0
+            b[2] += 1.0
+            out[name] = f32_to_bf16_bits(b) if g.dtype == "bf16" else b
+        elif base.endswith("_conv_w"):
+            out[name] = normal(seed, idx, shape, 0.1 / math.sqrt(shape[1]), 0.0, g.dtype)
         else:
             out[name] = normal(seed, idx, shape, 1.0 / math.sqrt(shape[1]), 0.0, g.dtype)
     return out

@@ -42,7 +42,7 @@ MUTATIONS = {
         "silu(linear(m, wts[p + \"w_gate\"])) * linear(m, wts[p + \"w_up\"])",
         "silu(linear(m, wts[p + \"w_up\"])) * linear(m, wts[p + \"w_gate\"])"),
     "attention residual dropped": (
-        "y = x + linear(a, wts[p + \"wo\"])", "y = linear(a, wts[p + \"wo\"])"),
+        "    y = x + o\n", "    y = o\n"),
     "post norm uses input gain": (
         "m = plain_rmsnorm(y, wts[p + \"g_post\"], g.eps)", "m = plain_rmsnorm(y, wts[p + \"g_in\"], g.eps)"),
     "window off by one": (
@@ -94,6 +94,21 @@ MUTATIONS = {
         "if float(uniforms[t]) < cdf:", "if float(uniforms[t]) <= cdf:"),
     "sampled walk keeps the wrong probability": (
         "q[t] = p[j]", "q[t] = p[i]"),
+    "conv tap before row zero": (
+        "    out[1:] += (base[side, 1][None] + delta[1:, side, 1, :, None]) * Xg[:-1]\n",
+        "    out += (base[side, 1][None] + delta[:, side, 1, :, None]) * np.roll(Xg, 1, axis=0)\n"),
+    "conv delta rows in the wrong order": (
+        "return d.reshape(X.shape[0], 2, 2, g.conv_groups)",
+        "return d.reshape(X.shape[0], g.conv_groups, 2, 2).transpose(0, 2, 3, 1)"),
+    "conv finish projects its own delta": (
+        "o = conv_blocks(g, wts, layer, \"attn\", 1, o, d_a, W)",
+        "o = conv_blocks(g, wts, layer, \"attn\", 1, o, [conv_delta(g, wts, layer, \"attn\", o[b * W:(b + 1) * W]) for b in range(B)], W)"),
+    "conv sides swapped": (
+        "n = conv_blocks(g, wts, layer, \"attn\", 0, n, d_a, W)",
+        "n = conv_blocks(g, wts, layer, \"attn\", 1, n, d_a, W)"),
+    "mlp conv prepares from the pre-norm state": (
+        "d_m = [conv_delta(g, wts, layer, \"mlp\", m[b * W:(b + 1) * W]) for b in range(B)]",
+        "d_m = [conv_delta(g, wts, layer, \"mlp\", y[b * W:(b + 1) * W]) for b in range(B)]"),
 }
 
 

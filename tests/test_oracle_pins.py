@@ -723,3 +723,142 @@ def test_proposals_are_per_request():
         assert np.array_equal(one["cand"][0], both["cand"][b])
         assert rel_err(one["table"][0], both["table"][b]) < 1e-12
         assert np.array_equal(one["tokens"][0], both["tokens"][b])
+
+
+# ---------------------------------------------------------------------------
+# DFlash2 dynamic grouped convolution [NIF, DFlash2 layer equations]
+# ---------------------------------------------------------------------------
+G_CONV = synth.Geometry(hidden=96, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=16, ffn=160,
+                        n_feat_layers=2, code_dim=0, msg_dim=0, vocab=64, windows=(12, 0),
+                        dtype="f32", conv_group=16)
+
+
+def test_conv_hand_worked():
+    """H = 32 (two groups of 16), W = 2; rows of ones and twos.  delta rows
+    are ordered (side, tap, group): row 0 = (0,0,0) reads 0.5 x channel 0,
+    row 3 = (0,1,1) reads 0.1 x channel 16.  Base: side 0 taps (1, 0.25),
+    side 1 taps (2, 0).  Worked by hand:
+      side 0, row 0: group 0 (1 + 0.5*1) * 1 = 1.5; group 1: 1 * 1 = 1
+      side 0, row 1: group 0 (1 + 0.5*2) * 2 + 0.25 * 1 = 4.25;
+                     group 1 1 * 2 + (0.25 + 0.1*2) * 1 = 2.45
+      side 1: 2 x the input everywhere."""
+    g = synth.Geometry(hidden=32, n_layers=1, n_q_heads=1, n_kv_heads=1, head_dim=64, ffn=64,
+                       n_feat_layers=1, code_dim=0, msg_dim=0, vocab=16, windows=(0,), dtype="f32",
+                       conv_group=16)
+    Wd = np.zeros((8, 32), np.float32)
+    Wd[0, 0] = 0.5
+    Wd[3, 16] = 0.1
+    base = np.zeros((4, 32), np.float32)
+    base[0], base[1], base[2], base[3] = 1.0, 0.25, 2.0, 0.0
+    wts = {"l0.attn_conv_w": Wd, "l0.attn_conv_base": base}
+    X = np.stack([np.ones(32), 2 * np.ones(32)])
+    d = O.conv_delta(g, wts, 0, "attn", X)
+    out0 = O.conv_apply(g, wts, 0, "attn", 0, X, d)
+    assert np.allclose(out0[0, :16], 1.5) and np.allclose(out0[0, 16:], 1.0)
+    assert np.allclose(out0[1, :16], 4.25) and np.allclose(out0[1, 16:], 2.45)
+    out1 = O.conv_apply(g, wts, 0, "attn", 1, X, d)
+    assert np.allclose(out1, 2 * X)
+
+
+def test_conv_rows_look_back_one():
+    g = G_CONV
+    wts = small_model(g)
+    X = np.random.default_rng(8).standard_normal((6, g.hidden))
+    d = O.conv_delta(g, wts, 0, "mlp", X)
+    a = O.conv_apply(g, wts, 0, "mlp", 0, X, d)
+    X2 = X.copy()
+    X2[2] += 1.0
+    b = O.conv_apply(g, wts, 0, "mlp", 0, X2, O.conv_delta(g, wts, 0, "mlp", X2))
+    changed = np.any(a != b, axis=1)
+    assert list(changed) == [False, False, True, True, False, False]
+
+
+def test_conv_identity_reduces_to_dflash():
+    """Zero delta projections, current-row taps 1 and previous-row taps 0 on
+    both sides: the DFlash2 forward is the DFlash forward."""
+    g = G_CONV
+    plain = dataclasses_replace(g, conv_group=0)
+    wts = small_model(g)
+    ov = dict(wts)
+    for l in range(g.n_layers):
+        for br in ("attn", "mlp"):
+            ov[f"l{l}.{br}_conv_w"] = np.zeros_like(wts[f"l{l}.{br}_conv_w"])
+            ov[f"l{l}.{br}_conv_base"] = np.array([[1.0], [0.0], [1.0], [0.0]], np.float32) * \
+                np.ones((1, g.hidden), np.float32)
+    ctx = build_context(g, ov, 20)
+    a = O.draft_forward(g, ov, [ctx], [3], 7)
+    b = O.draft_forward(plain, ov, [ctx], [3], 7)
+    assert np.array_equal(a, b)
+    assert rel_err(O.draft_forward(g, wts, [ctx], [3], 7), b) > 1e-3   # the live conv changes it
+
+
+@pytest.mark.parametrize("branch", ["attn", "mlp"])
+def test_conv_finish_is_linear_in_the_branch_output(branch):
+    """The finish side applies the delta of the branch's normalised input to
+    the branch output, so scaling the branch output map by 2 scales the
+    branch's contribution x_next - x by exactly 2 (the other branch off)."""
+    g = G_CONV
+    wts = small_model(g)
+    ctx = build_context(g, wts, 15)
+    x = np.random.default_rng(9).standard_normal((7, g.hidden))
+    off, scale = ("l0.w_down", "l0.wo") if branch == "attn" else ("l0.wo", "l0.w_down")
+    w1 = dict(wts)
+    w1[off] = np.zeros_like(wts[off])
+    w2 = dict(w1)
+    w2[scale] = (2 * wts[scale]).astype(wts[scale].dtype)
+    d1 = O.decoder_layer(g, w1, 0, [ctx], x, 7) - x
+    d2 = O.decoder_layer(g, w2, 0, [ctx], x, 7) - x
+    assert np.max(np.abs(d2 - 2 * d1)) < 1e-12 * np.max(np.abs(d1))
+    assert np.max(np.abs(d1)) > 1e-3
+
+
+def test_conv_has_no_history_across_requests():
+    g = G_CONV
+    wts = small_model(g)
+    ctxs = [build_context(g, wts, 15, request=b) for b in range(2)]
+    both = O.draft_forward(g, wts, ctxs, [3, 9], 6)
+    for b in range(2):
+        one = O.draft_forward(g, wts, [ctxs[b]], [[3, 9][b]], 6)
+        assert rel_err(one[0], both[b]) < 1e-12
+
+
+def dataclasses_replace(g, **kw):
+    return synth.with_geometry(g, **kw)
+
+
+def test_conv_prepare_and_finish_sides():
+    """Prepare side = identity, finish side = 2 x identity (zero deltas): the
+    DFlash2 forward equals the plain forward with W_o and W_down doubled."""
+    g = G_CONV
+    plain = dataclasses_replace(g, conv_group=0)
+    wts = small_model(g)
+    ov = dict(wts)
+    doubled = dict(wts)
+    for l in range(g.n_layers):
+        for br in ("attn", "mlp"):
+            ov[f"l{l}.{br}_conv_w"] = np.zeros_like(wts[f"l{l}.{br}_conv_w"])
+            ov[f"l{l}.{br}_conv_base"] = np.array([[1.0], [0.0], [2.0], [0.0]], np.float32) * \
+                np.ones((1, g.hidden), np.float32)
+        for n in ("wo", "w_down"):
+            doubled[f"l{l}.{n}"] = 2 * wts[f"l{l}.{n}"]
+    ctx = build_context(g, ov, 20)
+    a = O.draft_forward(g, ov, [ctx], [3], 7)
+    b = O.draft_forward(plain, doubled, [ctx], [3], 7)
+    assert rel_err(a, b) < 1e-12
+
+
+@pytest.mark.parametrize("branch", ["attn", "mlp"])
+def test_conv_branch_ignores_the_residual_scale(branch):
+    """Each branch's delta comes from its normalised input, so a branch's
+    contribution x_next - x (the other branch off) does not change when the
+    residual is scaled (up to the norm's epsilon)."""
+    g = G_CONV
+    wts = small_model(g)
+    ctx = build_context(g, wts, 15)
+    off = "l0.w_down" if branch == "attn" else "l0.wo"
+    w1 = dict(wts)
+    w1[off] = np.zeros_like(wts[off])
+    x = np.random.default_rng(10).standard_normal((7, g.hidden))
+    d1 = O.decoder_layer(g, w1, 0, [ctx], x, 7) - x
+    d2 = O.decoder_layer(g, w1, 0, [ctx], 3.0 * x, 7) - 3.0 * x
+    assert rel_err(d2, d1) < 1e-5
