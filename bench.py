@@ -45,6 +45,8 @@ def step_algorithmic_bytes(g, wts, B, W, frontiers, commit):
     per_layer = ["g_in", "wq", "wk", "wv", "gq", "gk", "wo", "g_post", "w_gate", "w_up", "w_down"]
     if g.bridge:
         per_layer += ["R", "W_l"]
+    if getattr(g, "conv", False):
+        per_layer += ["attn_conv_w", "attn_conv_base", "mlp_conv_w", "mlp_conv_base"]
     fwd = sum(weight_bytes(wts, [f"l{l}.{n}" for n in per_layer]) for l in range(L))
     fwd += weight_bytes(wts, ["g_final"])
     elt = 2 if g.dtype == "bf16" else 4
@@ -218,7 +220,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dspine27b_b1",
                     choices=["dspine27b_b1", "dspine27b_b8", "dspine27b_causal_b8", "dflash35b_b8",
-                             "tiny_fp32"])
+                             "dflash2_27b_b8", "tiny_fp32"])
     ap.add_argument("--commit", type=int, default=16,
                     help="positions materialized per request per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")

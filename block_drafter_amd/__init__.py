@@ -43,11 +43,12 @@ class Geometry_c(ctypes.Structure):
                 ("msg_dim", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("mask_token_id", ctypes.c_int32), ("block_causal", ctypes.c_int32),
                 ("window", ctypes.c_int32 * MAX_LAYERS), ("eps", ctypes.c_float),
-                ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("conv_group", ctypes.c_int32)]
 
 
 _LAYER_FIELDS = ["g_in", "wq", "wk", "wv", "gq", "gk", "wo", "g_post", "w_gate", "w_up",
-                 "w_down", "R", "W_l"]
+                 "w_down", "R", "W_l", "attn_conv_w", "attn_conv_base", "mlp_conv_w", "mlp_conv_base"]
 
 
 class LayerWeights_c(ctypes.Structure):
@@ -58,7 +59,7 @@ _GLOBAL_FIELDS = ["embed", "w_feat", "g_ctx", "g_final", "codebook", "bridge_G",
                   "bridge_A", "bridge_b"]
 # matrices the library streams from its packed copy
 _PROJECTIONS = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "R", "W_l", "w_feat",
-                "bridge_G", "bridge_Gp", "bridge_A", "lm_head"}
+                "bridge_G", "bridge_Gp", "bridge_A", "lm_head", "attn_conv_w", "mlp_conv_w"}
 
 
 class Weights_c(ctypes.Structure):
@@ -157,6 +158,7 @@ def geometry_struct(g) -> Geometry_c:
     gs.eps = float(g.eps)
     gs.rope_theta = float(g.rope_theta)
     gs.dtype = BF16 if g.dtype == "bf16" else F32
+    gs.conv_group = int(getattr(g, "conv_group", 0))
     return gs
 
 
@@ -358,7 +360,7 @@ class Model:
 
 
 PROF_KINDS = ["gemm_qkv", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "bridge", "norm",
-              "ctx_gemm", "ctx_store", "head", "tail"]
+              "ctx_gemm", "ctx_store", "head", "tail", "conv"]
 
 
 def profile_enable(kinds: Sequence[str]):

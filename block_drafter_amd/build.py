@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdspine.so")
-SOURCES = ["dspine_api.cpp", "gemm_stream.hip", "gemm_tile.hip", "attention.hip", "rowops.hip", "propose.hip"]
+SOURCES = ["dspine_api.cpp", "gemm_stream.hip", "gemm_tile.hip", "attention.hip", "rowops.hip", "propose.hip",
+           "conv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -14,6 +14,7 @@
 
 #include "dspine_internal.hpp"
 #include "propose_internal.hpp"
+#include "conv_internal.hpp"
 
 struct dspine_model {
   dspine_geometry g;
@@ -156,6 +157,7 @@ struct Plan {
   size_t act_h, act_r, act_m;             // pre-scaled operands (large blocks)
   size_t st0, st1, stz, stc;              // row statistics [lists][kMaxRows]
   size_t c_raw, c_act, kv_raw;            // materialize, per row block
+  size_t conv_da, conv_dm, o_tmp;         // DFlash2 convolution deltas and branch output
   size_t total;
 };
 // row-statistics lists a GEMM writes for `width` output columns (one per 64)
@@ -191,6 +193,10 @@ Plan make_plan(const dspine_geometry& g, int64_t M, int64_t rows) {
   p.st1 = take(4 * (size_t)kMaxRows * stat_tiles(g.hidden));
   p.stz = take(4 * (size_t)kMaxRows * stat_tiles(r));
   p.stc = take(4 * (size_t)kMaxRows * stat_tiles(g.hidden));
+  const size_t cg = g.conv_group > 0 ? (size_t)g.hidden / g.conv_group : 0;
+  p.conv_da = take(4 * Mp * 4 * cg);
+  p.conv_dm = take(4 * Mp * 4 * cg);
+  p.o_tmp = take(cg ? 4 * Mp * g.hidden : 0);
   const int64_t R = std::max<int64_t>(rows, 0);
   p.c_raw = take(4 * R * g.hidden);
   p.c_act = take(eb * R * g.hidden);
@@ -233,6 +239,10 @@ int check_geometry(const dspine_geometry& g) {
   for (int l = 0; l < g.n_layers; ++l)
     if (g.window[l] < 0) return fail(DSPINE_E_UNSUPPORTED, "window[%d] = %d", l, g.window[l]);
   if (!(g.eps >= 0.f) || !(g.rope_theta > 0.f)) return fail(DSPINE_E_UNSUPPORTED, "eps / rope_theta");
+  if (g.conv_group < 0 || (g.conv_group > 0 && (g.conv_group % 4 || g.hidden % g.conv_group ||
+                                                (g.hidden / g.conv_group) % 16 || g.hidden > 8192)))
+    return fail(DSPINE_E_UNSUPPORTED, "conv_group %d: a multiple of 4 dividing hidden into a multiple of 16 groups "
+                "(hidden <= 8192)", g.conv_group);
   return DSPINE_OK;
 }
 
@@ -271,6 +281,12 @@ int check_weights(const dspine_geometry& g, const dspine_weights& w) {
     if (g.code_dim > 0) {
       NEED(L.R, "R", l);
       NEED(L.W_l, "W_l", l);
+    }
+    if (g.conv_group > 0) {
+      NEED(L.attn_conv_w, "attn_conv_w", l);
+      NEED(L.attn_conv_base, "attn_conv_base", l);
+      NEED(L.mlp_conv_w, "mlp_conv_w", l);
+      NEED(L.mlp_conv_base, "mlp_conv_base", l);
     }
   }
 #undef NEED
@@ -316,6 +332,10 @@ std::vector<Proj> projections(const dspine_geometry& g) {
   if (g.code_dim > 0) {
     v.push_back({nullptr, &dspine_layer_weights::R, g.code_dim, H});
     v.push_back({nullptr, &dspine_layer_weights::W_l, H, g.msg_dim});
+  }
+  if (g.conv_group > 0) {
+    v.push_back({nullptr, &dspine_layer_weights::attn_conv_w, 4 * (H / g.conv_group), H});
+    v.push_back({nullptr, &dspine_layer_weights::mlp_conv_w, 4 * (H / g.conv_group), H});
   }
   v.push_back({&dspine_weights::w_feat, nullptr, H, g.n_feat_layers * H});
   if (g.code_dim > 0) {
@@ -931,6 +951,21 @@ static int check_forward(const dspine_model* model, int B, int W, const dspine_c
   return DSPINE_OK;
 }
 
+// DFlash2 convolution of one branch (side 0 "prepare" or side 1 "finish")
+static ConvParams conv_params(const dspine_geometry& g, int M, int W, const float* delta, const void* base) {
+  ConvParams cp;
+  memset(&cp, 0, sizeof cp);
+  cp.M = M;
+  cp.W = W;
+  cp.H = g.hidden;
+  cp.cg = g.conv_group;
+  cp.G = g.hidden / g.conv_group;
+  cp.delta = delta;
+  cp.base = base;
+  cp.eps = g.eps;
+  return cp;
+}
+
 // The forward's launches (arguments already checked).  save_u, when given,
 // receives the last layer's state before its bridge write [B*W, H].
 static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx* ctx, const int32_t* anchor_ids,
@@ -951,6 +986,11 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
   float* st0 = reinterpret_cast<float*>(ws + P.st0);
   float* st1 = reinterpret_cast<float*>(ws + P.st1);
   const int tH = stat_tiles(H);
+  const bool conv = g.conv_group > 0;
+  const int G4 = conv ? 4 * (H / g.conv_group) : 0;
+  float* conv_da = reinterpret_cast<float*>(ws + P.conv_da);
+  float* conv_dm = reinterpret_cast<float*>(ws + P.conv_dm);
+  float* o_tmp = reinterpret_cast<float*>(ws + P.o_tmp);
 
   // a4: x, its row statistics (one list) and the rotation table of F_b + i
   RowParams rp;
@@ -982,10 +1022,37 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     const dspine_layer_weights& Pw = model->pw.layer[l];
     // a5: q | k | v projections of n = input_norm(x) (norm formed in the GEMM)
     GemmParams gp = gemm_base(P, ws, H, M);
+    if (conv) {
+      // DFlash2: delta of the attention branch from n = input_norm(x), then
+      // the prepared input Conv_0(n) as the projections' operand
+      GemmParams dg = gemm_base(P, ws, H, M);
+      set_segments(dg, {{Pw.attn_conv_w, G4}});
+      if ((rc = set_scaled_a(dg, g, M, W, x, H, H, SCALE_RMSNORM, xst, xst_tiles, (float)H, Lw.g_in, ws + P.act_h,
+                             stream)))
+        return rc;
+      dg.epi = EPI_STORE;
+      dg.out = conv_da;
+      dg.ldo = G4;
+      ProfScope ps(DSPINE_PROF_CONV, stream);
+      HIP_TRY(launch_gemm_stream(dg, g.dtype, cus, stream));
+      ConvParams cp = conv_params(g, M, W, conv_da, Lw.attn_conv_base);
+      cp.x = x;
+      cp.stats = xst;
+      cp.lists = xst_tiles;
+      cp.ld = kMaxRows;
+      cp.gain = Lw.g_in;
+      cp.act = ws + P.act_h;
+      HIP_TRY(launch_conv_prepare(cp, g.dtype, stream));
+    }
     set_segments(gp, {{Pw.wq, qd}, {Pw.wk, kvd}, {Pw.wv, kvd}});
-    if ((rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RMSNORM, xst, xst_tiles, (float)H, Lw.g_in, ws + P.act_h,
-                           stream)))
+    if (conv) {
+      gp.pro = PRO_COPY;
+      gp.a = ws + P.act_h;
+      gp.lda = H;
+    } else if ((rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RMSNORM, xst, xst_tiles, (float)H, Lw.g_in,
+                                  ws + P.act_h, stream))) {
       return rc;
+    }
     gp.epi = EPI_STORE;
     gp.out = qkv;
     gp.ldo = qd + 2 * kvd;
@@ -1042,14 +1109,25 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     gp.pro = PRO_COPY;
     gp.a = act_q;
     gp.lda = qd;
-    gp.epi = EPI_ADD;
-    gp.out = x;
+    gp.epi = conv ? EPI_STORE : EPI_ADD;
+    gp.out = conv ? o_tmp : x;
     gp.ldo = H;
-    gp.stats_out = st0;
+    gp.stats_out = conv ? nullptr : st0;
     gp.stats_out_ld = kMaxRows;
     {
       ProfScope ps(DSPINE_PROF_GEMM_O, stream);
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
+    }
+    int yst_tiles = tH;                   // statistics lists of y in st0
+    if (conv) {
+      // y = x + Conv_1(W_o a) with the prepare's delta; one statistics list
+      ConvParams cp = conv_params(g, M, W, conv_da, Lw.attn_conv_base);
+      cp.o = o_tmp;
+      cp.x_out = x;
+      cp.stats_out = st0;
+      ProfScope ps(DSPINE_PROF_CONV, stream);
+      HIP_TRY(launch_conv_finish(cp, g.dtype, stream));
+      yst_tiles = 1;
     }
 
     // a8: x = y + W_down(SiLU(W_gate m) * W_up m), m = post_norm(y) formed
@@ -1060,8 +1138,33 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     gp.nseg = 2;
     gp.interleave = 1;
     gp.nblk = 2 * (g.ffn / 16);
-    if ((rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RMSNORM, st0, tH, (float)H, Lw.g_post, ws + P.act_h, stream)))
+    if (conv) {
+      // DFlash2: delta of the MLP branch from m = post_norm(y), then Conv_0(m)
+      GemmParams dg = gemm_base(P, ws, H, M);
+      set_segments(dg, {{Pw.mlp_conv_w, G4}});
+      if ((rc = set_scaled_a(dg, g, M, W, x, H, H, SCALE_RMSNORM, st0, yst_tiles, (float)H, Lw.g_post,
+                             ws + P.act_h, stream)))
+        return rc;
+      dg.epi = EPI_STORE;
+      dg.out = conv_dm;
+      dg.ldo = G4;
+      ProfScope ps(DSPINE_PROF_CONV, stream);
+      HIP_TRY(launch_gemm_stream(dg, g.dtype, cus, stream));
+      ConvParams cp = conv_params(g, M, W, conv_dm, Lw.mlp_conv_base);
+      cp.x = x;
+      cp.stats = st0;
+      cp.lists = yst_tiles;
+      cp.ld = kMaxRows;
+      cp.gain = Lw.g_post;
+      cp.act = ws + P.act_h;
+      HIP_TRY(launch_conv_prepare(cp, g.dtype, stream));
+      gp.pro = PRO_COPY;
+      gp.a = ws + P.act_h;
+      gp.lda = H;
+    } else if ((rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RMSNORM, st0, tH, (float)H, Lw.g_post, ws + P.act_h,
+                                  stream))) {
       return rc;
+    }
     gp.epi = EPI_SWIGLU;
     gp.out_act = act_f;
     gp.ld_act = g.ffn;
@@ -1074,10 +1177,10 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     gp.pro = PRO_COPY;
     gp.a = act_f;
     gp.lda = g.ffn;
-    gp.epi = EPI_ADD;
-    gp.out = x;
+    gp.epi = conv ? EPI_STORE : EPI_ADD;
+    gp.out = conv ? o_tmp : x;
     gp.ldo = H;
-    gp.stats_out = st1;
+    gp.stats_out = conv ? nullptr : st1;
     gp.stats_out_ld = kMaxRows;
     {
       ProfScope ps(DSPINE_PROF_GEMM_DOWN, stream);
@@ -1085,15 +1188,26 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     }
     xst = st1;
     xst_tiles = tH;
+    if (conv) {
+      // x_next = y + Conv_1(z) with the MLP prepare's delta
+      ConvParams cp = conv_params(g, M, W, conv_dm, Lw.mlp_conv_base);
+      cp.o = o_tmp;
+      cp.x_out = x;
+      cp.stats_out = st1;
+      ProfScope ps(DSPINE_PROF_CONV, stream);
+      HIP_TRY(launch_conv_finish(cp, g.dtype, stream));
+      xst_tiles = 1;
+    }
 
     if (save_u && l == g.n_layers - 1)
       HIP_TRY(hipMemcpyAsync(save_u, x, sizeof(float) * (size_t)M * H, hipMemcpyDeviceToDevice, stream));
     // a9-a11 (statistics of the written rows go to st0)
     if (g.code_dim > 0) {
       ProfScope ps(DSPINE_PROF_BRIDGE, stream);
-      rc = run_bridge(*model, l, B, W, x, st1, tH, st0, anchor_ids, nullptr, ws, P, cus, stream);
+      rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream);
       if (rc) return rc;
-      xst = st0;
+      xst = st0;                          // the write GEMM's lists, one per 64 columns
+      xst_tiles = tH;
     }
   }
   // a12

@@ -90,6 +90,9 @@ typedef struct {
     float eps;                 /* RMSNorm epsilon, also the bridge floor */
     float rope_theta;
     int32_t dtype;             /* DSPINE_F32 or DSPINE_BF16 */
+    int32_t conv_group;        /* DFlash2 dynamic grouped convolution [NIF, DFlash2 layer
+                                  equations]: group width (16), 0 = none; hidden/conv_group
+                                  must be a multiple of 16 */
 } dspine_geometry;
 
 /* Per-layer weights (device, borrowed; element type = geometry.dtype). */
@@ -107,6 +110,16 @@ typedef struct {
     const void* w_down;        /* [H, ffn] */
     const void* R;             /* [r, H]  bridge read [FLZ]; NULL when r == 0 */
     const void* W_l;           /* [H, a]  bridge write;     NULL when r == 0 */
+    /* DFlash2 convolutions (NULL when conv_group == 0), G = H / conv_group groups:
+     * W_delta [4G, H], output row (side*2 + tap)*G + g; base [4, H], row side*2 + tap.
+     * Conv_side(X)[i] = (base[side,0] + delta[i,side,0,g]) X[i]
+     *                 + [i >= 1] (base[side,1] + delta[i,side,1,g]) X[i-1]
+     * on the branch's normalised input X (side 0, "prepare") and on the branch
+     * output with the same delta (side 1, "finish"). */
+    const void* attn_conv_w;
+    const void* attn_conv_base;
+    const void* mlp_conv_w;
+    const void* mlp_conv_base;
 } dspine_layer_weights;
 
 /* All model weights (device, borrowed, element type = geometry.dtype).  They
@@ -158,7 +171,7 @@ void dspine_model_destroy(dspine_model* model);
 
 /*
  * Projection weights in fragment order.  The GEMMs stream every projection
- * matrix (wq, wk, wv, wo, w_gate, w_up, w_down, R, W_l per layer; w_feat,
+ * matrix (wq, wk, wv, wo, w_gate, w_up, w_down, R, W_l, attn/mlp_conv_w per layer; w_feat,
  * bridge_G, bridge_Gp, bridge_A; lm_head when given) in the order their MFMA fragments are
  * loaded: inside each block of 16 rows, 32-wide column step ks holds the 64
  * lane fragments (row 16b + l%16, columns 32ks + 8(l/16) .. +8) in
@@ -210,8 +223,10 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
  * a4-a12: one masked-block draft forward for B requests of width W.
  * [NIF, draft input]: row i of request b is the embedding of the anchor
  * (i = 0) or of the mask token (i > 0), at position F_b + i.
- * [NIF, layer equations] per layer, then the bridge [FLZ, "The bridge"]
- * after every layer when code_dim > 0, then the final plain RMSNorm.
+ * [NIF, layer equations] per layer (with conv_group > 0, DFlash2's dynamic
+ * grouped convolution around attention and MLP [NIF, DFlash2 layer
+ * equations]), then the bridge [FLZ, "The bridge"] after every layer when
+ * code_dim > 0, then the final plain RMSNorm.
  * Attention [NIF, draft attention]: key at position p is visible to the
  * row at q iff |p - q| < S (local) plus, with block_causal, block key j <=
  * row i; context keys are the ring positions [max(0, q-S+1), F).
@@ -334,7 +349,8 @@ int dspine_debug_visible(const dspine_model* model, int layer, int B, int W,
 #define DSPINE_PROF_CTX_STORE 8     /* a1 norm, a2 head norm + RoPE + ring scatter */
 #define DSPINE_PROF_HEAD 9          /* proposal: the LM head's scores of every row */
 #define DSPINE_PROF_TAIL 10         /* proposal: top-K, refinement table and walk */
-#define DSPINE_PROF_KINDS 11
+#define DSPINE_PROF_CONV 11         /* DFlash2 convolution deltas, prepare and finish */
+#define DSPINE_PROF_KINDS 12
 
 /* kind_mask: bit k enables class k; 0 disables recording.  Process-wide. */
 int dspine_profile_enable(uint32_t kind_mask);

@@ -279,3 +279,21 @@ def test_dspine27b_causal_b8_full_size():
     pos = pos[pos >= F - min(F, 8192)]
     check_ring_positions(g, wts, wl.seed, b, ctxs[b], F, pos, f"request {b}")
     model.close()
+
+
+def test_dflash2_27b_b8_full_size():
+    """DFlash2 27B geometry: dynamic grouped convolution (group width 16)
+    around attention and MLP, five local layers, B=8, contexts U{1024..16384}."""
+    import block_drafter_amd as bd
+    wl = synth.WORKLOADS["dflash2_27b_b8"]
+    g = wl.geom
+    say(f"dflash2_27b_b8: frontiers {wl.frontiers}")
+    wts = synth.make_weights(g, wl.seed)
+    model = bd.Model.from_numpy(g, wts)
+    anchors = [int(a) for a in synth.make_anchor_ids(g, wl.seed, wl.B)]
+    ctxs = setup_windows(model, g, wl)
+    say("dflash2_27b_b8: forward")
+    gpu = to_np64(model.forward(ctxs, anchors, wl.W))
+    check_forward(g, wts, gpu, [gpu_ring_context(g, c, F) for c, F in zip(ctxs, wl.frontiers)],
+                  anchors, wl.W, "gpu rings")
+    model.close()

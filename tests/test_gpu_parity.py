@@ -26,6 +26,15 @@ G_D = synth.Geometry(hidden=256, n_layers=2, n_q_heads=2, n_kv_heads=2, head_dim
                      block_causal=True)
 
 
+# DFlash2's dynamic grouped convolution (group width 16), with and without a bridge
+G_E = synth.Geometry(hidden=256, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=512,
+                     n_feat_layers=2, code_dim=0, msg_dim=0, vocab=512, windows=(24, 0), conv_group=16)
+G_F = synth.Geometry(hidden=512, n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1024,
+                     n_feat_layers=2, code_dim=64, msg_dim=32, vocab=512, windows=(40, 33), conv_group=16,
+                     block_causal=True)
+G_E32 = synth.with_geometry(G_E, dtype="f32")
+
+
 @pytest.fixture(autouse=True)
 def _gpu():
     import torch
@@ -201,3 +210,15 @@ def test_bridge_identity_gives_plain_dflash_on_gpu():
     m_off = bd.Model.from_numpy(g_off, {k: v for k, v in wts.items()})
     b = Run(Case(g_off, 85, 2, 16, [30, 5]), model=m_off, wts=wts).gpu_forward()
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("g", [G_E, G_F, G_E32], ids=["E", "F", "E-fp32"])
+@pytest.mark.parametrize("B,W", [(1, 16), (3, 7), (8, 16)])
+def test_dflash2_convolution(g, B, W):
+    """DFlash2's convolution around attention and MLP: ragged frontiers, a
+    block row 0 per request (no tap before it), both operand paths (B*W up
+    to 32 rows fused, more pre-scaled), with and without the bridge."""
+    rng = np.random.default_rng(90 + B)
+    fr = [int(v) for v in rng.integers(5, 70, size=B)]
+    run = Run(Case(g, 91 + B, B, W, fr))
+    check_run(run)
