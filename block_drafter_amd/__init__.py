@@ -62,6 +62,10 @@ _PROJECTIONS = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "R", "W_l", 
                 "bridge_G", "bridge_Gp", "bridge_A", "lm_head", "attn_conv_w", "mlp_conv_w"}
 
 
+# packed, but also read row-major by the library (kept after packing)
+_READ_ROW_MAJOR = {"lm_head"}
+
+
 class Weights_c(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _GLOBAL_FIELDS] + [
         ("layer", LayerWeights_c * MAX_LAYERS), ("lm_head", ctypes.c_void_p)]
@@ -208,7 +212,7 @@ class Model:
         if drop_row_major:
             torch.cuda.current_stream().synchronize()
             for name in list(self.weights):
-                if name.split(".")[-1] in _PROJECTIONS:
+                if name.split(".")[-1] in _PROJECTIONS and name not in _READ_ROW_MAJOR:
                     del self.weights[name]
 
     @classmethod

@@ -1367,7 +1367,7 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
   pp.u = u;
   pp.Y = reinterpret_cast<const float*>(pws + PP.Y);
   pp.g_final = model->w.g_final;
-  pp.head_packed = model->pw.lm_head;
+  pp.head = model->w.lm_head;             // row-major: the candidates' rows are gathered
   pp.table = prop->table;
   pp.uniforms = prop->uniforms;
   pp.choice = prop->choice;

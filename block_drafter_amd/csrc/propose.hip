@@ -264,8 +264,9 @@ __device__ __forceinline__ void frag_to_float(const Frag<float>& f, float* w) {
 
 // Row (b, t, i) of the transition table: x' = u_t + rho_t Y, h = g_final x' /
 // rms(x'), T[b, t-1, i, j] = E[cand_j] . h for the K candidates j of row t.
-// Head rows are read from the fragment-ordered copy: element (v, k) sits at
-// ((v/16)*(H/32) + k/32)*512 + 8*((v%16) + 16*((k%32)/8)) + k%8.
+// Head rows are read from the row-major head (each row one contiguous read;
+// in the fragment-ordered copy a row's pieces share cache lines with seven
+// other rows).
 template <typename TW>
 __global__ __launch_bounds__(kScoreThreads) void cand_score_kernel(const ProposeParams p) {
   __shared__ float h[kMaxHidden];
@@ -306,19 +307,16 @@ __global__ __launch_bounds__(kScoreThreads) void cand_score_kernel(const Propose
   __syncthreads();
 
   const int* cj = p.cand + (size_t)(c.b * (p.W - 1) + c.t - 1) * p.K;
-  const TW* E = reinterpret_cast<const TW*>(p.head_packed);
+  const TW* E = reinterpret_cast<const TW*>(p.head);
   size_t rowbase[kMaxTopK];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    const int v = clamp_token(j < p.K ? cj[j] : cj[0], p.vocab);
-    rowbase[j] = (size_t)(v / 16) * (H / 32) * 512 + 8 * (v % 16);
-  }
+  for (int j = 0; j < kMaxTopK; ++j) rowbase[j] = (size_t)clamp_token(j < p.K ? cj[j] : cj[0], p.vocab) * H;
   float acc[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) acc[j] = 0.f;
   const int nchunk = H / 8;              // 8 consecutive columns of one lane fragment
   for (int ch = threadIdx.x; ch < nchunk; ch += kScoreThreads) {
-    const size_t off = (size_t)(ch / 4) * 512 + 128 * (ch % 4);
+    const size_t off = (size_t)8 * ch;
     Frag<TW> f[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) f[j].gload(as_global(E + rowbase[j] + off));

@@ -27,7 +27,7 @@ struct ProposeParams {
   const float* u;                 // [B*W, H] last layer's pre-write state
   const float* Y;                 // [B*(W-1)*K, H] W_l msg
   const void* g_final;            // [H] model dtype
-  const void* head_packed;        // [vocab, H] in fragment order
+  const void* head;               // [vocab, H] row-major
   float* table;                   // [B, W-1, K, K]
   const double* uniforms;         // [B, W-1]
   int32_t* choice;                // [B, W-1]

@@ -136,7 +136,10 @@ typedef struct {
     const void* bridge_b;      /* [a]     gate bias, shared */
     dspine_layer_weights layer[DSPINE_MAX_LAYERS];
     const void* lm_head;       /* [vocab, H]  shared LM head for dspine_draft_propose (vocab a
-                                  multiple of 16); NULL when proposals are not used */
+                                  multiple of 16); NULL when proposals are not used.  Packed
+                                  like the projections for the score GEMM, and also read
+                                  row-major (candidate rows): unlike the projections it must
+                                  stay valid while the model is used */
 } dspine_weights;
 
 /*
