@@ -352,6 +352,12 @@ def main():
     propose = None
     if with_propose:
         propose = propose_measure(model, g, ctxs, anchors, W, ws, args.steps, fwd_ms)
+        propose["roofline"]["traffic"] = None
+        if wl.name == "dspine27b_b1":
+            from block_drafter_amd import profsum
+            rec = profsum.read_traffic(os.path.join(ROOT, "profiles", "traffic_gemm_stream_lm_head_dspine27b_b1.md"))
+            if rec is not None and rec[1] == profsum.source_hash():
+                propose["roofline"]["traffic"] = rec[0]
 
     # HBM traffic of the same kernel from the PMC runs summarised under
     # profiles/ (null unless they were taken on this workload with the

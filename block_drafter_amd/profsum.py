@@ -5,7 +5,9 @@
 
   python -m block_drafter_amd.profsum traffic --fetch CSV --write CSV
         --fetch-copy CSV --write-copy CSV --kernel REGEX --algorithmic BYTES
-      HBM traffic per launch of the kernels whose name matches REGEX, from two
+      [--min-fetch-kib KIB]
+      HBM traffic per launch of the kernels whose name matches REGEX (and,
+      with --min-fetch-kib, whose fetch reaches KIB), from two
       ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs (KiB per dispatch).
       Each counter is scaled by the factor that turns its reading on a plain
       device copy of known size into the copy's true bytes (the copy runs
@@ -70,13 +72,25 @@ def traffic(args) -> str:
     write = _counter(args.write, args.kernel)
     if not fetch or not write:
         raise SystemExit("kernel regex matched no dispatch")
+    if args.min_fetch_kib > 0:
+        # one instantiation can serve several GEMMs: keep the dispatches whose
+        # fetch reaches the given size, and the same ordinals of the write run
+        # (both runs launch the same kernels in the same order)
+        if len(fetch) != len(write):
+            raise SystemExit("the two runs dispatched the kernel a different number of times")
+        keep = [i for i, v in enumerate(fetch) if v >= args.min_fetch_kib]
+        if not keep:
+            raise SystemExit("no dispatch reaches --min-fetch-kib")
+        fetch = [fetch[i] for i in keep]
+        write = [write[i] for i in keep]
     ff = copy_factor(args.fetch_copy, args.copy_bytes)
     wf = copy_factor(args.write_copy, args.copy_bytes)
     fb = statistics.median(fetch) * 1024.0 * ff
     wb = statistics.median(write) * 1024.0 * wf
     t = fb + wb
     lines = [
-        f"kernel regex: `{args.kernel}`",
+        f"kernel regex: `{args.kernel}`" + (f", dispatches fetching >= {args.min_fetch_kib:.0f} KiB"
+                                            if args.min_fetch_kib > 0 else ""),
         f"dispatches: {len(fetch)} (FETCH_SIZE run), {len(write)} (WRITE_SIZE run)",
         f"copy calibration: FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {wf:.4f} (plain copy of {args.copy_bytes} bytes)",
         f"fetched bytes per launch: {fb:.0f}",
@@ -116,6 +130,7 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, default=1 << 30)
     t.add_argument("--kernel", required=True)
     t.add_argument("--algorithmic", type=int, required=True)
+    t.add_argument("--min-fetch-kib", type=float, default=0.0)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv, a.top))
