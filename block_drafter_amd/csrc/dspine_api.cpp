@@ -670,6 +670,7 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
         rp.H = H;
         rp.x = c_raw;
         rp.act = c_act;
+        rp.act_bf16 = 1;                  // the K/V tile GEMM multiplies bf16 x bf16
         rp.gain = wt.g_ctx;
         rp.eps = g.eps;
         {
@@ -689,6 +690,7 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
         tp.K = H;
         tp.M = (int)nrows;
         tp.pro = PRO_COPY;
+        tp.a_bf16 = 1;
         tp.a = c_act;
         tp.lda = H;
         tp.out = kv_raw;

@@ -181,6 +181,7 @@ struct RowParams {
   int32_t head_dim;
   float rope_theta;
   float* stats;                   // [M] sum of squares of each row (one stats tile)
+  int32_t act_bf16;               // rmsnorm: act is bfloat16 (the tile GEMM's bf16 x bf16 path)
 };
 // Operand pre-scale for large blocks: act[m, k] = x[m, k] * s[m] (* gain[k]),
 // s[m] from the row's statistics lists; or the bridge message

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(256) void bridge_msg_kernel(const ScaleParams p) {
 }
 
 // plain_rmsnorm [NIF]: out = g * x / sqrt(mean(x^2) + eps); out in the model
-// dtype (GEMM operand) or fp32 (final hidden states).
+// dtype (GEMM operand), bf16 (operand of the tile GEMM's bf16 x bf16 path)
+// or fp32 (final hidden states).
 template <typename T, bool F32OUT>
 __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const RowParams p) {
   __shared__ float red[kRowThreads / 64];
@@ -131,6 +132,7 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const RowParams p)
   for (int k = threadIdx.x; k < p.H; k += kRowThreads) {
     const float v = x[k] * inv * Elt<T>::gload(gw, k);
     if (F32OUT) p.f32_out[(size_t)m * p.H + k] = v;
+    else if (p.act_bf16) Elt<bf16_t>::store(reinterpret_cast<bf16_t*>(p.act), (size_t)m * p.H + k, v);
     else Elt<typename ActOf<T>::type>::store(reinterpret_cast<typename ActOf<T>::type*>(p.act), (size_t)m * p.H + k, v);
   }
 }
