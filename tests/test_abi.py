@@ -287,3 +287,26 @@ def test_propose_rejections_before_any_launch(L):
     assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == 0
     assert call_propose(L, h, 1, 16, [fake_ctx(g, 100, full_cap=200)], [5], good_proposal()) == bd.E_UNSUPPORTED
     L.dspine_model_destroy(h)
+
+
+def test_conv_geometry_checks(L):
+    """DFlash2's convolution: the group width must be a multiple of 4 that
+    splits hidden into a multiple of 16 groups, and each layer needs its
+    four convolution tensors."""
+    g = synth.G_27B_DFLASH2
+    ws = fake_weights(g)
+    gs = bd.geometry_struct(g)
+    h = ctypes.c_void_p()
+    assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == 0
+    two = sum(int(np.prod(synth.weight_shape(g, n))) * 2 for n in synth.weight_names(g)
+              if n.split(".")[-1] in bd._PROJECTIONS)
+    assert L.dspine_packed_bytes(h) == two                     # W_delta of both branches packed too
+    assert L.dspine_workspace_bytes(h, 8, 16, 0) > 0
+    L.dspine_model_destroy(h)
+    for bad in (6, 7, 640, -16):                               # not a multiple of 4; 8 groups; negative
+        gs = bd.geometry_struct(synth.with_geometry(g, conv_group=bad))
+        assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == bd.E_UNSUPPORTED, bad
+    ws.layer[3].mlp_conv_base = None
+    gs = bd.geometry_struct(g)
+    assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == bd.E_ARG
+    assert b"mlp_conv_base" in L.dspine_last_error()
