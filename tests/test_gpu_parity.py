@@ -213,7 +213,7 @@ def test_bridge_identity_gives_plain_dflash_on_gpu():
 
 
 @pytest.mark.parametrize("g", [G_E, G_F, G_E32], ids=["E", "F", "E-fp32"])
-@pytest.mark.parametrize("B,W", [(1, 16), (3, 7), (8, 16)])
+@pytest.mark.parametrize("B,W", [(1, 16), (3, 7), (8, 16), (5, 2)])
 def test_dflash2_convolution(g, B, W):
     """DFlash2's convolution around attention and MLP: ragged frontiers, a
     block row 0 per request (no tap before it), both operand paths (B*W up

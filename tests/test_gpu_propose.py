@@ -95,8 +95,11 @@ def check_proposal(g, wts, head, gp, octxs, anchors, W, K, walk, temperature, un
 
 
 @pytest.mark.parametrize("which,walk", [("tiny_fp32", "greedy"), ("A", "sampled"), ("T", "greedy"),
-                                        ("T", "sampled")])
+                                        ("T", "sampled"), ("A-W2-K1", "sampled"), ("T-W2", "greedy"),
+                                        ("A-B8", "sampled")])
 def test_propose_small(which, walk):
+    """Edge cases too: W = 2 (one proposal row, conditioned only on the
+    anchor), K = 1 (the walk has one choice), and the largest batch."""
     import block_drafter_amd as bd
     if which == "tiny_fp32":
         wl = synth.WORKLOADS["tiny_fp32"]
@@ -105,6 +108,15 @@ def test_propose_small(which, walk):
     elif which == "A":
         case = Case(G_A, 71, 3, 9, (40, 7, 25))
         K = 5
+    elif which == "A-W2-K1":
+        case = Case(G_A, 74, 2, 2, (30, 3))
+        K = 1
+    elif which == "T-W2":
+        case = Case(G_T, 75, 4, 2, (12, 40, 1, 25))
+        K = 16
+    elif which == "A-B8":
+        case = Case(G_A, 76, 8, 16, (5, 60, 33, 18, 70, 2, 44, 29))
+        K = 16
     else:
         case = Case(G_T, 72, 3, 16, (50, 33, 9))
         K = 16
