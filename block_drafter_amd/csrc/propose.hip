@@ -61,6 +61,7 @@ __device__ __forceinline__ int rank_among(float v, int i, const float* cv, const
 constexpr int kVpt = 32;
 constexpr int kSliceValues = kVpt * kTopkThreads;
 constexpr int kGather = kMaxTopK * kVpt;
+static_assert((kMaxTopK - 1) * kVpt + 1 <= kGather, "gather buffer below the bound on qualifying pairs");
 __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(const ProposeParams p) {
   __shared__ __align__(16) float sv[kGather + 4];    // the gathered pairs (+ padding)
   __shared__ __align__(16) int si[kGather + 4];

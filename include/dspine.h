@@ -293,7 +293,8 @@ typedef struct {
     /* outputs, device */
     float* scores;             /* optional (NULL: kept in the workspace): float32 [B*W, vocab]
                                   head scores of every row (anchor rows included) */
-    int32_t* cand;             /* int32 [B, W-1, K] candidate token ids of rows 1..W-1 */
+    int32_t* cand;             /* int32 [B, W-1, K] candidate token ids of rows 1..W-1 (-1 in
+                                  slots beyond the number of finite scores; NaN ranks as -inf) */
     float* cand_scores;        /* float32 [B, W-1, K] their head scores */
     float* table;              /* float32 [B, W-1, K, K]: entry [b, t-1, i, j] = T_t[i, j] */
     int32_t* choice;           /* int32 [B, W-1] chosen candidate index of each row */
