@@ -1303,6 +1303,7 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
     if (!(prop->temperature > 0.0) || !std::isfinite(prop->temperature))
       return fail(DSPINE_E_ARG, "propose: temperature must be finite and > 0");
     if (!prop->uniforms || ((uintptr_t)prop->uniforms & 7u)) return fail(DSPINE_E_ARG, "propose: uniforms NULL or unaligned");
+    if (!prop->q) return fail(DSPINE_E_ARG, "propose: the sampled walk needs q (the choices' probabilities)");
   }
   if (!prop->cand || !prop->cand_scores || !prop->table || !prop->choice || !prop->tokens)
     return fail(DSPINE_E_ARG, "propose: an output pointer is NULL");

@@ -299,8 +299,9 @@ typedef struct {
     float* table;              /* float32 [B, W-1, K, K]: entry [b, t-1, i, j] = T_t[i, j] */
     int32_t* choice;           /* int32 [B, W-1] chosen candidate index of each row */
     int32_t* tokens;           /* int32 [B, W-1] chosen token ids */
-    double* q;                 /* float64 [B, W-1] probability of each choice (sampled); may be
-                                  NULL for the greedy walk (otherwise written as 1) */
+    double* q;                 /* float64 [B, W-1] probability of each choice: required for the
+                                  sampled walk (it is kept for verification); for the greedy
+                                  walk NULL or written as 1 */
 } dspine_proposal;
 
 /* Bytes of the second workspace dspine_draft_propose needs for up to
@@ -313,7 +314,7 @@ size_t dspine_propose_workspace_bytes(const dspine_model* model, int max_batch, 
  * `out`) followed by the proposal tail above.  Needs a bridge (code_dim > 0)
  * and lm_head.  `workspace` is the forward's; `propose_ws` the tail's.
  * Errors: those of dspine_draft_forward, E_ARG (NULL output, K or walk out
- * of range, temperature <= 0 or uniforms NULL for the sampled walk),
+ * of range, temperature <= 0, uniforms or q NULL for the sampled walk),
  * E_UNSUPPORTED (no bridge or no lm_head), E_WORKSPACE.
  */
 int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_ctx* ctx,

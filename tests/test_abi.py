@@ -269,6 +269,10 @@ def test_propose_rejections_before_any_launch(L):
     p = good_proposal(walk=bd.WALK_SAMPLED)
     p.uniforms = None
     assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG
+    p = good_proposal(walk=bd.WALK_SAMPLED)
+    p.q = None
+    assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG
+    assert b"q" in L.dspine_last_error()
     p = good_proposal()
     p.table = None
     assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG
