@@ -67,6 +67,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(const Propos
   __shared__ __align__(16) int si[kGather + 4];
   __shared__ __align__(16) float mv[kTopkThreads];
   __shared__ __align__(16) int mi[kTopkThreads];
+  __shared__ __align__(16) float wv[kTopkThreads / 64 * kMaxTopK];   // each wave's best maxima
+  __shared__ __align__(16) int wi[kTopkThreads / 64 * kMaxTopK];
   __shared__ float tau_v;
   __shared__ int tau_i, count;
   const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
@@ -92,15 +94,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(const Propos
   }
   mv[tid] = bv;
   mi[tid] = bi;
+  if (tid < kTopkThreads / 64 * kMaxTopK) {
+    wv[tid] = -INFINITY;
+    wi[tid] = INT_MAX;
+  }
   if (tid == 0) {
     count = 0;
     tau_v = -INFINITY;      // kept when fewer than kMaxTopK threads hold a score
     tau_i = INT_MAX;
   }
   __syncthreads();
-  if (rank_among(bv, bi, mv, mi, kTopkThreads) == kMaxTopK - 1) {
-    tau_v = bv;
-    tau_i = bi;
+  // tau in two steps: each wave keeps its kMaxTopK best maxima (the
+  // kMaxTopK best of all 256 are among them), then tau is the kMaxTopK-th
+  // best of those.  Real pairs have distinct ranks; empty threads' pairs
+  // (-inf, INT_MAX) all rank after them and write identical values.
+  const int wave = tid >> 6;
+  const int rw = rank_among(bv, bi, mv + 64 * wave, mi + 64 * wave, 64);
+  if (rw < kMaxTopK) {
+    wv[wave * kMaxTopK + rw] = bv;
+    wi[wave * kMaxTopK + rw] = bi;
+  }
+  __syncthreads();
+  if (tid < kTopkThreads / 64 * kMaxTopK && wi[tid] != INT_MAX &&
+      rank_among(wv[tid], wi[tid], wv, wi, kTopkThreads / 64 * kMaxTopK) == kMaxTopK - 1) {
+    tau_v = wv[tid];
+    tau_i = wi[tid];
   }
   __syncthreads();
   const float tv = tau_v;
