@@ -376,9 +376,19 @@ __global__ __launch_bounds__(kScoreThreads) void cand_score_kernel(const Propose
 // probability exceeds the uniform (the last j if none does).
 __global__ __launch_bounds__(64) void walk_kernel(const ProposeParams p) {
   __shared__ float tab[(DSPINE_MAX_WIDTH - 1) * kMaxTopK * kMaxTopK];
+  __shared__ int cand[(DSPINE_MAX_WIDTH - 1) * kMaxTopK];
+  __shared__ double uni[DSPINE_MAX_WIDTH - 1];
   const int b = blockIdx.x, n = p.W - 1, K = p.K, lane = threadIdx.x;
+  // the request's candidates and uniforms come in with the tables, so the
+  // serial walk below touches only LDS
+#pragma unroll
+  for (int q = 0; q < ((DSPINE_MAX_WIDTH - 1) * kMaxTopK + 63) / 64; ++q) {
+    const int e = lane + 64 * q;
+    if (e < n * K) cand[e] = p.cand[(size_t)b * n * K + e];
+  }
+  if (p.walk != DSPINE_WALK_GREEDY && lane < n) uni[lane] = p.uniforms[b * n + lane];
   const gptr<float> src = as_global(p.table) + (size_t)b * n * K * K;
-  constexpr int kBatch = 16;
+  constexpr int kBatch = ((DSPINE_MAX_WIDTH - 1) * kMaxTopK * kMaxTopK + 63) / 64;   // the largest table in one batch
   for (int e0 = lane; e0 < n * K * K; e0 += 64 * kBatch) {
     float x[kBatch];
 #pragma unroll
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(64) void walk_kernel(const ProposeParams p) {
       double total = 0.0;
       for (int jj = 0; jj < K; ++jj) total += __shfl(e, jj, 64);
       const double pj = e / total;
-      const double u = p.uniforms[b * n + t];
+      const double u = uni[t];
       double cdf = 0.0;
       j = K - 1;
       for (int jj = 0; jj < K; ++jj) {
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(64) void walk_kernel(const ProposeParams p) {
     }
     if (lane == 0) {
       p.choice[b * n + t] = j;
-      p.tokens[b * n + t] = p.cand[(b * n + t) * K + j];
+      p.tokens[b * n + t] = cand[t * K + j];
       if (p.q) p.q[b * n + t] = q;
     }
     i = j;
