@@ -18,6 +18,17 @@ Sources (cited by tag):
 Tensor conventions: uint16 arrays hold bfloat16 bit patterns; matrices are
 ``[out, in]`` (y = W x).  A model is the dict made by ``synth.make_weights``
 plus its ``synth.Geometry``.
+
+Pins (tests/test_oracle_pins.py): every function below is tied to something
+other than this code: closed forms (RMSNorm, window counts), hand-worked
+examples (context, bridge, decoder layer, the DFlash2 convolution, the
+walks), brute force (attention, top-K), special cases that reduce to a
+simpler computation (bridge or convolution switched off gives plain DFlash;
+the anchor-conditioned or predicted-code refinement gives the forward's own
+scores), invariants (RoPE shift, request independence, one-row look-back)
+and the figures the pages print.  Parity unpinned: the absolute output values
+at the 27B and 35B geometries, for which the pages print no worked example;
+there the GPU is compared with this oracle on identical inputs.
 """
 from __future__ import annotations
 
