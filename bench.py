@@ -9,10 +9,16 @@ attention + SwiGLU + bridge, final norm).  Inputs are seeded synthetic
 tensors of the workload's geometry, resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` is draft forwards per second (each forward
-covers B blocks).  ``roofline`` reports the dominant kernel (the gate/up
-projection, about half of all bytes a step reads) against MI355X's HBM
-bandwidth, timed with HIP events on the library's stream inside the timed
-region.  ``cpu_baseline`` times the CPU oracle on a bounded sample.
+covers B blocks) of the headline workload (27B geometry, B=1).  ``roofline``
+reports the dominant kernel (the gate/up projection, about half of all bytes
+a step reads) against MI355X's HBM bandwidth, timed with HIP events on the
+library's stream inside the timed region.  ``cpu_baseline`` times the CPU
+oracle on a bounded sample.  With the default workload the same line also
+carries ``b8`` (the 27B geometry at B=8, the other half of the metric) and
+``dflash35b_b8`` (the 35B-style plain DFlash drafter at B=8), each with the
+same step, forward-only and gate/up roofline fields, ``propose`` (forward
+plus proposal tail) and ``prefill`` (context materialization of 8 x 32768
+positions).
 """
 from __future__ import annotations
 
@@ -68,28 +74,46 @@ def step_algorithmic_bytes(g, wts, B, W, frontiers, commit):
     return fwd + ctx + mat + out, fwd, ctx, mat
 
 
-def cpu_baseline(g, wts, seed, F, commit, W, anchor):
-    """The oracle, as it stands, on one request: the context is set up untimed
-    (its live window), then one step (materialize `commit` positions + one
-    B=1 forward) is timed once."""
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if info:
+            return max(d.get("num_threads", 1) for d in info), info[0].get("internal_api", "blas")
+    except Exception:
+        pass
+    return os.cpu_count() or 1, "unknown"
+
+
+def cpu_baseline(g, wts, seed, frontiers, commit, W, anchors, repeats=3, warmup=1):
+    """The oracle, as it stands, on the workload's step: every request's
+    context is set up untimed (its live window), then one step (materialize
+    `commit` positions of every request + one forward over all of them) is
+    run `warmup` times untimed and `repeats` times timed; the median is
+    returned with the individual times."""
     import numpy as np
     import synth
     from oracle import dspine_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()
-                       if d.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    keep = min(F, max(s for s in g.windows)) if all(s > 0 for s in g.windows) else F
-    ctx = O.materialize(g, wts, O.empty_context(g, F - keep),
-                        synth.make_features(g, seed, 0, keep, start=F - keep))
-    feats = synth.make_features(g, seed, 0, commit, start=F)
-    t0 = time.perf_counter()
-    ctx = O.materialize(g, wts, ctx, feats)
-    O.draft_forward(g, wts, [ctx], [anchor], W)
-    dt = time.perf_counter() - t0
-    return dt, threads
+    threads, api = _blas_threads()
+    ctxs0 = []
+    for b, F in enumerate(frontiers):
+        keep = min(F, max(s for s in g.windows)) if all(s > 0 for s in g.windows) else F
+        ctxs0.append(O.materialize(g, wts, O.empty_context(g, F - keep),
+                                   synth.make_features(g, seed, b, keep, start=F - keep)))
+    feats = [synth.make_features(g, seed, b, commit, start=F) for b, F in enumerate(frontiers)]
+
+    def step():
+        ctxs = [O.materialize(g, wts, c, f) for c, f in zip(ctxs0, feats)]
+        O.draft_forward(g, wts, ctxs, list(anchors), W)
+
+    for _ in range(warmup):
+        step()
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        step()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), times, threads, api
 
 
 MFMA_PEAK_TFLOPS = 2500.0          # MI355X dense bf16/fp16 matrix-core peak
@@ -140,22 +164,31 @@ def prefill_measure(model, g, seed, n_req=8, chunk=32768, reps=5):
     tflops = flop / (gemm_avg * 1e-3) / 1e12
     del chunks
     torch.cuda.empty_cache()
+    call_tflops = flop / (ms * 1e-3) / 1e12
     return {
         "workload": f"{n_req} requests x one {chunk}-token chunk into fresh {S}-slot rings "
                     f"({keep} stored rows each), one materialize call",
         "ms_per_call": round(ms, 4),
-        "chunk_tok_per_s": round(n_req * chunk / (ms * 1e-3), 1),
-        "stored_tok_per_s": round(n_req * keep / (ms * 1e-3), 1),
+        "computed_tok_per_s": round(n_req * keep / (ms * 1e-3), 1),
+        "computed_tok_note": f"positions fused, projected and stored per second: the final {keep} of "
+                             f"each chunk, the only ones any layer's window keeps",
+        "chunk_advance_tok_per_s": round(n_req * chunk / (ms * 1e-3), 1),
         "gemm_ms_per_call": round(gemm_avg, 4),
         "store_ms_per_call": round(store_ms / reps, 4),
         "roofline": {
-            "kernel": "gemm_tile (feature fusion W_feat + K/V projection of every layer)",
+            "kernel": "whole materialize call (feature fusion W_feat + K/V projection tile GEMMs, "
+                      "context norm, head norm + RoPE + ring store)",
             "bound": "mfma",
-            "achieved": round(tflops, 1),
+            "achieved": round(call_tflops, 1),
             "peak": MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+            "frac": round(call_tflops / MFMA_PEAK_TFLOPS, 4),
             "flop_per_call": flop,
+        },
+        "gemm_only": {
+            "kernel": "gemm_tile (W_feat + K/V projection of every layer), HIP events around its launches",
+            "achieved": round(tflops, 1),
+            "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
             "launches_per_call": gemm_n // reps,
         },
     }
@@ -266,52 +299,16 @@ def propose_measure(model, g, ctxs, anchors, W, ws, steps, fwd_ms, K=16):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dspine27b_b1",
-                    choices=["dspine27b_b1", "dspine27b_b8", "dspine27b_causal_b8", "dflash35b_b8",
-                             "dflash2_27b_b8", "tiny_fp32"])
-    ap.add_argument("--commit", type=int, default=16,
-                    help="positions materialized per request per step")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the context-prefill measurement (27B workloads)")
-    ap.add_argument("--no-propose", action="store_true",
-                    help="skip the proposal-tail measurement (workloads with a bridge)")
-    ap.add_argument("--breakdown", action="store_true",
-                    help="after the timed region, time every kernel class for a few steps")
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES bytes 5 times and exit (calibrates "
-                         "hardware byte counters against a known traffic)")
-    args = ap.parse_args()
-
-    if args.copy_probe:
-        import torch
-        n = args.copy_probe // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}), flush=True)
-        return
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the draft round is "
-              "data-parallel over requests with no exchange, so N GPUs would run N independent "
-              "copies.", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def measure_workload(name, args, with_propose, gate_up_traffic_md=None):
+    """Times one forward workload: `args.warmup` untimed steps, then
+    `args.steps` timed steps (materialize the committed positions of every
+    request + one draft forward), the gate/up GEMM timed live on a sample of
+    its launches, then the forward alone and (with a bridge) the proposal
+    call.  Returns (record, state) where state keeps what later legs reuse."""
     import torch
     import synth
     import block_drafter_amd as bd
-
-    bd.lib()                                  # fails loudly without the built library
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[name]
     g, B, W = wl.geom, wl.B, wl.W
     frontiers = list(wl.frontiers)
     total_steps = args.warmup + args.steps
@@ -320,8 +317,7 @@ def main():
     t = time.time()
     wts = synth.make_weights(g, wl.seed)
     log(f"weights generated in {time.time() - t:.1f}s")
-    # the shared LM head of the proposal tail (packed with the projections)
-    with_propose = bool(g.bridge) and not args.no_propose
+    with_propose = with_propose and bool(g.bridge)
     head = synth.make_lm_head(g, wl.seed) if with_propose else None
     t = time.time()
     model = bd.Model.from_numpy(g, wts, lm_head=head)
@@ -332,19 +328,25 @@ def main():
 
     # contexts: the live window of every local layer holds the last S positions
     # before F (a chunk longer than the ring stores only its final window), so
-    # the setup materializes exactly those positions from frontier F - S.
+    # the setup materializes exactly those positions from frontier F - S.  A
+    # full-attention layer needs every position: those contexts are
+    # materialized in full.
     full = any(s == 0 for s in g.windows)
     smax = max(g.windows)
     extra_steps = min(5, total_steps) if args.breakdown else 0   # the breakdown pass below
     ctxs, pending = [], []
+    setup_ws = None
     for b, F in enumerate(frontiers):
         cap = (F + args.commit * (total_steps + extra_steps) + 16) if full else 0
         c = model.new_context(full_capacity=cap)
         keep = F if full else min(F, smax)
         c.frontier = F - keep
-        feats = bd.to_device(synth.make_features(g, wl.seed, b, keep, start=F - keep))
-        model.materialize([c], [feats], workspace=model.workspace(B, W, max(keep, 256)))
-        del feats
+        for s0 in range(0, keep, 16384):
+            n = min(16384, keep - s0)
+            feats = bd.to_device(synth.make_features(g, wl.seed, b, n, start=F - keep + s0))
+            setup_ws = model.workspace(B, W, max(n, 256))
+            model.materialize([c], [feats], workspace=setup_ws)
+            del feats
         pending.append(bd.to_device(synth.make_features(g, wl.seed, b, args.commit * total_steps, start=F)))
         ctxs.append(c)
     torch.cuda.synchronize()
@@ -401,6 +403,8 @@ def main():
     fwd_ev1.record()
     torch.cuda.synchronize()
     fwd_ms = fwd_ev0.elapsed_time(fwd_ev1) / args.steps
+    fwd_total_bytes = fwd_bytes + ctx_bytes + B * W * g.hidden * 4
+    fwd_gbps = fwd_total_bytes / (fwd_ms * 1e-3) / 1e9
 
     propose = None
     if with_propose:
@@ -416,9 +420,9 @@ def main():
     # profiles/ (null unless they were taken on this workload with the
     # current kernel sources)
     traffic = None
-    if wl.name == "dspine27b_b1":
+    if gate_up_traffic_md is not None:
         from block_drafter_amd import profsum
-        rec = profsum.read_traffic(os.path.join(ROOT, "profiles", "traffic_gemm_stream_gate_up_dspine27b_b1.md"))
+        rec = profsum.read_traffic(os.path.join(ROOT, "profiles", gate_up_traffic_md))
         if rec is not None and rec[1] == profsum.source_hash():
             traffic = rec[0]
 
@@ -432,48 +436,29 @@ def main():
         breakdown = {}
         for k in bd.PROF_KINDS:
             ms, n = bd.profile_read(k)
-            breakdown[k] = {"ms_per_step": round(ms / min(5, total_steps), 4), "launches_per_step": n // min(5, total_steps)}
+            breakdown[k] = {"ms_per_step": round(ms / min(5, total_steps), 4),
+                            "launches_per_step": n // min(5, total_steps)}
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on one request's step ...")
-        dt, threads = cpu_baseline(g, wts, wl.seed, frontiers[0], args.commit, W, anchors[0])
-        cpu = {"value": round(1.0 / (dt * B), 6), "unit": "forwards/s", "cores": int(threads),
-               "kind": "oracle",
-               "sample": f"one step of request 0 (materialize {args.commit} positions + one "
-                         f"B=1 forward, float64 numpy), timed once; forwards/s = 1 / ({B} x "
-                         f"{dt:.2f} s)"}
-
-    res = {
-        "metric": "draft-block forwards/s at 27B geometry (B=1,8); ctx-prefill tok/s; % roofline",
-        "value": round(value, 3),
-        "unit": "forwards/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    rec = {
+        "workload": wl.name, "B": B, "W": W, "context": frontiers, "layers": g.n_layers,
+        "hidden": g.hidden, "windows": list(g.windows), "bridge": bool(g.bridge),
+        "block_causal": bool(g.block_causal),
+        "step": f"materialize {args.commit} committed positions per request + one draft forward",
+        "steps_per_s": round(value, 3),
         "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": g.dtype,
-        "data": "synthetic",
-        "config": {
-            "workload": wl.name, "B": B, "W": W, "context": frontiers, "layers": g.n_layers,
-            "hidden": g.hidden, "windows": list(g.windows), "bridge": bool(g.bridge),
-            "step": f"materialize {args.commit} committed positions per request + one draft forward",
-            "blocks_per_s": round(value * B, 3),
-            "step_algorithmic_bytes": step_bytes,
-            "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-            "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "bytes_forward_weights": fwd_bytes, "bytes_context_kv": ctx_bytes,
-            "bytes_materialize": mat_bytes, "wall_s": round(wall, 3),
-            "forward_only_ms": round(fwd_ms, 4),
-            "forward_only_per_s": round(1000.0 / fwd_ms, 3),
-            "forward_only_GBps": round((fwd_bytes + ctx_bytes + B * W * g.hidden * 4) / (fwd_ms * 1e-3) / 1e9, 1),
-            "operands": "bf16 weights widened to fp16 in registers x fp16 activations, fp32 accumulate",
-        },
+        "blocks_per_s": round(value * B, 3),
+        "step_algorithmic_bytes": step_bytes,
+        "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "bytes_forward_weights": fwd_bytes, "bytes_context_kv": ctx_bytes,
+        "bytes_materialize": mat_bytes, "wall_s": round(wall, 3),
+        "forward_only_ms": round(fwd_ms, 4),
+        "forward_only_per_s": round(1000.0 / fwd_ms, 3),
+        "forward_only_bytes": fwd_total_bytes,
+        "forward_only_GBps": round(fwd_gbps, 1),
+        "forward_only_hbm_frac": round(fwd_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {
-            "kernel": "gemm_stream (gate/up projection + SwiGLU)",
+            "kernel": f"gemm_stream (gate/up projection + SwiGLU, M={M})",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -485,20 +470,134 @@ def main():
             "avg_launch_us": round(gu_avg_ms * 1000, 2),
             "launches": gu_n,
         },
-        "cpu_baseline": cpu,
     }
     if breakdown is not None:
-        res["breakdown"] = breakdown
+        rec["breakdown"] = breakdown
     if propose is not None:
-        res["propose"] = propose
+        rec["propose"] = propose
+    state = {"wl": wl, "g": g, "wts": wts, "model": model, "anchors": anchors, "frontiers": frontiers}
+    del ctxs, pending, ws, out, setup_ws
+    return rec, state
+
+
+def release(state):
+    import torch
+    state["model"].close()
+    state.clear()
+    torch.cuda.empty_cache()
+
+
+def oracle_record(g, wts, wl, args, anchors, note, repeats=3, warmup=1):
+    log(f"timing the CPU oracle on the {wl.name} step ...")
+    med, times, threads, api = cpu_baseline(g, wts, wl.seed, list(wl.frontiers), args.commit, wl.W, anchors,
+                                            repeats=repeats, warmup=warmup)
+    how = (f"{warmup} warm-up run(s) then {repeats} timed, median {med:.2f} s "
+           f"({', '.join(f'{t:.2f}' for t in times)})" if repeats > 1 else
+           f"timed once ({med:.2f} s), in the same process after the headline oracle's warm-up")
+    return {"value": round(1.0 / med, 6), "unit": "forwards/s", "cores": int(threads), "kind": "oracle",
+            "blas": api,
+            "sample": f"{note}: one step of the {wl.name} workload (materialize {args.commit} positions "
+                      f"of each of its {wl.B} requests + one B={wl.B} forward, float64 numpy), {how}; "
+                      f"forwards/s = 1 / that time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dspine27b_b1",
+                    choices=["dspine27b_b1", "dspine27b_b8", "dspine27b_causal_b8", "dflash35b_b8",
+                             "dflash2_27b_b8", "tiny_fp32"])
+    ap.add_argument("--commit", type=int, default=16,
+                    help="positions materialized per request per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the context-prefill measurement (27B workloads)")
+    ap.add_argument("--no-propose", action="store_true",
+                    help="skip the proposal-tail measurement (workloads with a bridge)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="with the default workload: skip the 27B B=8 and 35B B=8 records")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="after the timed region, time every kernel class for a few steps")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times and exit (calibrates "
+                         "hardware byte counters against a known traffic)")
+    args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}), flush=True)
+        return
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the draft round is "
+              "data-parallel over requests with no exchange, so N GPUs would run N independent "
+              "copies.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import block_drafter_amd as bd
+
+    bd.lib()                                  # fails loudly without the built library
+    headline = args.workload
+    traffic_md = "traffic_gemm_stream_gate_up_dspine27b_b1.md" if headline == "dspine27b_b1" else None
+    rec, st = measure_workload(headline, args, not args.no_propose, traffic_md)
+    g, wl = st["g"], st["wl"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = oracle_record(g, st["wts"], wl, args, st["anchors"], "headline workload")
+
+    res = {
+        "metric": "draft-block forwards/s at 27B geometry (B=1,8); ctx-prefill tok/s; % roofline",
+        "value": rec["steps_per_s"],
+        "unit": "forwards/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": g.dtype,
+        "data": "synthetic",
+        "config": {k: v for k, v in rec.items() if k not in ("roofline", "propose", "breakdown")},
+        "roofline": rec["roofline"],
+        "cpu_baseline": cpu,
+    }
+    res["config"]["operands"] = ("bf16 weights widened to fp16 in registers x fp16 activations, "
+                                 "fp32 accumulate")
+    if "breakdown" in rec:
+        res["breakdown"] = rec["breakdown"]
+    if "propose" in rec:
+        res["propose"] = rec["propose"]
     if not args.no_prefill and g.dtype == "bf16" and g.hidden == 5120:
-        del ctxs, pending, ws
-        torch.cuda.empty_cache()
         log("context prefill: 8 requests x one 32768-token chunk ...")
         pw = synth.WORKLOADS["prefill27b"]
-        res["prefill"] = prefill_measure(model, g, pw.seed, n_req=pw.B, chunk=pw.prefill_chunk)
+        res["prefill"] = prefill_measure(st["model"], g, pw.seed, n_req=pw.B, chunk=pw.prefill_chunk)
         log("context prefill without the window skip ...")
-        res["prefill"]["no_skip"] = prefill_noskip_measure(g, wts, pw.seed, n_req=pw.B, chunk=pw.prefill_chunk)
+        res["prefill"]["no_skip"] = prefill_noskip_measure(g, st["wts"], pw.seed, n_req=pw.B,
+                                                           chunk=pw.prefill_chunk)
+    release(st)
+
+    # the other half of the metric (27B at B=8) and the 35B plain-DFlash
+    # workload, each as its own record of the same fields
+    if headline == "dspine27b_b1" and not args.no_extra:
+        for name, key in (("dspine27b_b8", "b8"), ("dflash35b_b8", "dflash35b_b8")):
+            r, st = measure_workload(name, args, not args.no_propose and name == "dspine27b_b8")
+            if name == "dspine27b_b8" and not args.no_cpu_baseline:
+                r["cpu_baseline"] = oracle_record(st["g"], st["wts"], st["wl"], args, st["anchors"],
+                                                  "B=8 record", repeats=1, warmup=0)
+            res[key] = r
+            release(st)
     print(json.dumps(res), flush=True)
 
 

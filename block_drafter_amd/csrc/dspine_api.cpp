@@ -383,7 +383,8 @@ void set_segments(GemmParams& gp, std::initializer_list<std::pair<const void*, i
 // times `gain` when given.  Small blocks form it in the GEMM prologue; large
 // ones through the pre-scale kernel into `act` (stride K).
 int set_scaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, const float* x, int ldx, int K, int mode,
-                 const float* st, int lists, float n, const void* gain, void* act, hipStream_t stream) {
+                 const float* st, int lists, float n, const void* gain, void* act, hipStream_t stream,
+                 bool round_bf16 = false) {
   gp.scale_n = n;
   gp.eps = g.eps;
   gp.code_scale = sqrtf((float)std::max(g.code_dim, 1));
@@ -397,6 +398,7 @@ int set_scaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, const f
     gp.stats_in = st;
     gp.stats_tiles = lists;
     gp.stats_ld = kMaxRows;
+    gp.act_round_bf16 = round_bf16 ? 1 : 0;
     return DSPINE_OK;
   }
   ScaleParams sp;
@@ -414,6 +416,7 @@ int set_scaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, const f
   sp.x = x;
   sp.ldx = ldx;
   sp.gain = gain;
+  sp.round_bf16 = round_bf16 ? 1 : 0;
   sp.act = act;
   sp.ld_act = K;
   HIP_TRY(launch_scale_rows(sp, g.dtype, stream));
@@ -739,8 +742,10 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
           }
           gp.nseg = 2 * L;
           gp.nblk = blk;
+          // c passes through bf16, as the long-block path stores it, so that
+          // both paths project the same operand values
           int rc2 = set_scaled_a(gp, g, mr, 1, c_raw + r0 * H, H, H, SCALE_RMSNORM, stc, stat_tiles(H), (float)H,
-                                 wt.g_ctx, c_act, stream);
+                                 wt.g_ctx, c_act, stream, g.dtype == DSPINE_BF16);
           if (rc2) return rc2;
           gp.epi = EPI_STORE;
           gp.out = kv_raw + r0 * ldkv;

@@ -35,6 +35,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
+// float -> the nearest bfloat16 value (RNE), as a float
+__device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
 // float -> IEEE half bits, round to nearest even (hardware conversion).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   _Float16 h = (_Float16)f;

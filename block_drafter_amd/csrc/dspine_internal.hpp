@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/dspine.h"
+#include "/root/repo/include/dspine.h"
 
 namespace dspine {
 
@@ -83,6 +83,8 @@ struct GemmParams {
   int32_t a_dim, W, pred_shift;
   const float* xa;                // PRO_NORM / PRO_SCALE: fp32 rows, stride lda
   const void* gain;               // PRO_NORM: [K] model dtype
+  int32_t act_round_bf16;         // PRO_NORM / PRO_SCALE: operand values pass through bfloat16
+                                  //   (RNE) before the fp16 store, as the tile GEMM's bf16 operands do
   // per-row scale (prologue of PRO_NORM / PRO_SCALE, or EPI_ADD_ROWSCALE)
   int32_t scale_mode;
   const float* stats_in;          // [stats_tiles][stats_ld] per-64-column sums of squares
@@ -196,6 +198,7 @@ struct ScaleParams {
   const float* x;                 // fp32 [M, ldx]
   int32_t ldx;
   const void* gain;               // [K] model dtype, or NULL
+  int32_t round_bf16;             // scale_rows: values pass through bfloat16 (RNE) first
   const float* P;                 // bridge_msg: [M, 3a]
   const float* Ppred;
   const void* bias;               // [a] model dtype

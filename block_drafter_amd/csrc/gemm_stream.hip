@@ -320,7 +320,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 #pragma unroll
           for (int e = 0; e < EPC; ++e) {
             const float gn = (PRO == PRO_NORM) ? Elt<TW>::load(gv, e) : 1.f;
-            Elt<T>::store(tv, e, xv[e] * sc * gn);
+            const float av = xv[e] * sc * gn;
+            Elt<T>::store(tv, e, p.act_round_bf16 ? round_bf16(av) : av);
           }
           v = *reinterpret_cast<const u32x4*>(tv);
         }
@@ -409,10 +410,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       // result does not depend on arrival order (bit-reproducible runs).  The
       // own partial is read back like the others (the same values).  Loads go
       // out FB contributors at a time so their latencies overlap; indexes past
-      // the last contributor repeat it and are not added.  Plain loads are
-      // enough: each partial slot is written (through to memory) once per
-      // launch and read only after its writer's arrival, so no cache of this
-      // launch holds an older copy of it.
+      // the last contributor repeat it and are not added.  The partials are
+      // read with agent-scope loads, from the device coherence point the
+      // writers stored them to: this workgroup's L2 may still hold a line of
+      // the same slot from an earlier launch that reused the workspace, and
+      // the loads are issued only after the arrival count (whose value they
+      // depend on) has returned.
       if constexpr (WD) {
         // One weight block at a time, FB contributors per load batch: the
         // registers hold the accumulators plus FB x MT partial fragments,
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
               const float* other = p.partials + (size_t)slot_of(gg) * (NWB * MT * 256 * 4);
 #pragma unroll
               for (int mb = 0; mb < MT; ++mb)
-                part[j][mb] = *as_global(reinterpret_cast<const f32x4*>(other + ((nb * MT + mb) * 256 + tid) * 4));
+                part[j][mb] = load_coherent4(other + ((nb * MT + mb) * 256 + tid) * 4);
             }
 #pragma unroll
             for (int j = 0; j < FB; ++j) {
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
           for (int nb = 0; nb < NWB; ++nb)
 #pragma unroll
             for (int mb = 0; mb < MT; ++mb)
-              part[j][nb][mb] = *as_global(reinterpret_cast<const f32x4*>(other + ((nb * MT + mb) * 256 + tid) * 4));
+              part[j][nb][mb] = load_coherent4(other + ((nb * MT + mb) * 256 + tid) * 4);
         }
 #pragma unroll
         for (int j = 0; j < FB; ++j) {

@@ -89,7 +89,8 @@ __global__ __launch_bounds__(256) void scale_rows_kernel(const ScaleParams p) {
 #pragma unroll
   for (int e = 0; e < EPC; ++e) {
     const float g = p.gain ? Elt<T>::gload(gn, e) : 1.f;
-    Elt<TA>::store(out, e, x[e] * sc * g);
+    const float v = x[e] * sc * g;
+    Elt<TA>::store(out, e, p.round_bf16 ? round_bf16(v) : v);
   }
 }
 

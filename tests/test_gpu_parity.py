@@ -10,7 +10,7 @@ import pytest
 
 import synth
 from oracle import dspine_oracle as O
-from tests.gpu_cases import Case, Run, rel_err, storage_err, tol_for, to_np64
+from tests.gpu_cases import Case, Run, bf16_ulp, rel_err, storage_err, tol_for, to_np64
 
 pytestmark = pytest.mark.gpu
 
@@ -95,12 +95,16 @@ def test_chunked_and_truncated_materialization():
     run = Run(Case(G_B, 79, 3, 16, [100, 100, 100], chunks=chunks, shared_features=True))
     gpu, _ = check_run(run)
     # the three ways of reaching frontier 100 agree with each other on the GPU
-    # too.  The first call (143 rows) runs the tile GEMMs, whose K/V
-    # projection multiplies bf16 operands; the later short calls run the
-    # streamed GEMM on fp16 operands.  A stored element may therefore sit one
-    # bf16 step away, and beyond that differ by the bf16 rounding of the
-    # normalised context features (about 2^-9 of the row's rms per operand,
-    # measured 5.5e-3 relative to rms), well inside the oracle bound of 2e-2
+    # too.  The first call (143 rows) runs the tile GEMMs (bf16 x bf16); the
+    # later calls run the streamed GEMM, whose prologue (fused at <= 32 rows,
+    # the pre-scale kernel above) passes the normalised context features
+    # through bf16 as well, so both paths project the same operand values up
+    # to the fp32 summation order of the feature projection: about one
+    # context-feature element per call lands on the other side of a bf16
+    # rounding boundary, which moves every K/V element of that row by about
+    # 2^-8 |c_i w_i|.  So almost every stored element is identical, and each
+    # difference is within one bf16 step at the layer's rms (one ulp of the
+    # element itself can be smaller than that for elements near zero)
     for l in range(G_B.n_layers):
         for ring in ("k", "v"):
             a = to_np64(getattr(run.ctxs[0], ring)[l])
@@ -108,7 +112,13 @@ def test_chunked_and_truncated_materialization():
                 c = to_np64(getattr(run.ctxs[b], ring)[l])
                 assert np.array_equal(np.isnan(a), np.isnan(c))
                 m = ~np.isnan(a)
-                assert storage_err(c[m], a[m], True) <= 1e-2, (l, ring, b)
+                d = np.abs(a[m] - c[m])
+                step = np.maximum(bf16_ulp(a[m]), 2.0 ** -8 * np.sqrt(np.mean(a[m] ** 2)))
+                same = float(np.mean(d == 0))
+                print(f"layer {l} {ring} request {b}: identical {same:.5f}, beyond one ulp "
+                      f"{int(np.sum(d > bf16_ulp(a[m])))}, max / step {float(np.max(d / step)):.3f}")
+                assert same > 0.99, (l, ring, b, same)
+                assert np.all(d <= step), (l, ring, b, float(np.max(d / step)))
 
 
 def test_debug_visible_bit_exact():
