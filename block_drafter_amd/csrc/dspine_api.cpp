@@ -158,15 +158,23 @@ struct Plan {
   size_t st0, st1, stz, stc;              // row statistics [lists][kMaxRows]
   size_t c_raw, c_act, kv_raw;            // materialize, per row block
   size_t conv_da, conv_dm, o_tmp;         // DFlash2 convolution deltas and branch output
+  size_t gemm_part_floats;                // capacity of gemm_part
   size_t total;
 };
 // row-statistics lists a GEMM writes for `width` output columns (one per 64)
 int stat_tiles(int width) { return gemm_stream_stat_lists(width); }
 
-Plan make_plan(const dspine_geometry& g, int64_t M, int64_t rows) {
+// Workspace of a call over B requests of width W (forward, bridge, propose)
+// or of a materialize call whose row blocks hold up to `rows` positions:
+// the streamed GEMMs' split partials are sized for the most rows one of
+// them multiplies (B*W, or a materialize chunk of at most kMaxRows), the
+// attention's for B requests.
+Plan make_plan(const dspine_geometry& g, int64_t B, int64_t W, int64_t rows) {
   Plan p{};
   const size_t eb = elt_bytes(g);
+  const int64_t M = B * W;
   const int64_t Mp = ((std::max<int64_t>(M, 1) + 15) / 16) * 16;
+  const int gemm_rows = (int)std::max<int64_t>(M, std::min<int64_t>(rows, kMaxRows));
   const int qd = g.n_q_heads * g.head_dim, kvd = g.n_kv_heads * g.head_dim;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -175,8 +183,9 @@ Plan make_plan(const dspine_geometry& g, int64_t M, int64_t rows) {
     return o;
   };
   p.gemm_cnt = take(sizeof(uint32_t) * kMaxTiles);
-  p.gemm_part = take(sizeof(float) * gemm_stream_partial_floats(kMaxGrid));
-  p.attn_part = take(sizeof(float) * attn_partial_floats(DSPINE_MAX_BATCH, g.n_q_heads, g.head_dim));
+  p.gemm_part_floats = gemm_stream_partial_floats(gemm_rows);
+  p.gemm_part = take(sizeof(float) * p.gemm_part_floats);
+  p.attn_part = take(sizeof(float) * attn_partial_floats((int)std::max<int64_t>(B, 1), g.n_q_heads, g.head_dim));
   p.x = take(4 * Mp * g.hidden);
   p.act_q = take(eb * Mp * qd);
   p.act_f = take(eb * Mp * g.ffn);
@@ -204,15 +213,18 @@ Plan make_plan(const dspine_geometry& g, int64_t M, int64_t rows) {
   p.total = off;
   return p;
 }
-// materialize row-block capacity of a workspace of `bytes`
+// materialize row-block capacity of a workspace of `bytes`: the most rows
+// whose plan fits (the plan grows with the rows)
 int64_t rows_capacity(const dspine_geometry& g, size_t bytes) {
-  const Plan base = make_plan(g, 1, 0);
-  if (bytes <= base.total) return 0;
-  const size_t per_row = 4 * (size_t)g.hidden + elt_bytes(g) * (size_t)g.hidden +
-                         4 * (size_t)g.n_layers * 2 * g.n_kv_heads * g.head_dim;
-  int64_t r = (int64_t)((bytes - base.total) / per_row);
-  while (r > 0 && make_plan(g, 1, r).total > bytes) --r;   // alignment slack
-  return r;
+  if (make_plan(g, 1, 1, 1).total > bytes) return 0;
+  int64_t lo = 1, hi = 1;
+  while (hi < (int64_t(1) << 40) && make_plan(g, 1, 1, 2 * hi).total <= bytes) hi *= 2;
+  hi *= 2;                                             // plan(lo) fits, plan(hi) does not
+  while (hi - lo > 1) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    (make_plan(g, 1, 1, mid).total <= bytes ? lo : hi) = mid;
+  }
+  return lo;
 }
 
 int check_geometry(const dspine_geometry& g) {
@@ -363,6 +375,7 @@ GemmParams gemm_base(const Plan& P, char* ws, int K, int M) {
   gp.K = K;
   gp.M = M;
   gp.partials = reinterpret_cast<float*>(ws + P.gemm_part);
+  gp.partial_floats = P.gemm_part_floats;
   gp.counters = reinterpret_cast<uint32_t*>(ws + P.gemm_cnt);
   return gp;
 }
@@ -561,7 +574,7 @@ size_t dspine_workspace_bytes(const dspine_model* model, int max_batch, int max_
     fail(DSPINE_E_ARG, "workspace_bytes: bad argument");
     return 0;
   }
-  return make_plan(model->g, (int64_t)max_batch * max_width, max_rows).total;
+  return make_plan(model->g, max_batch, max_width, max_rows).total;
 }
 
 // -----------------------------------------------------------------------------
@@ -602,7 +615,7 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
     char* ws = static_cast<char*>(workspace);
     const int cus = num_cus();
     const int64_t blk_rows = std::min<int64_t>(cap_rows, total_rows);
-    const Plan P = make_plan(g, 1, blk_rows);
+    const Plan P = make_plan(g, 1, 1, blk_rows);
     float* c_raw = reinterpret_cast<float*>(ws + P.c_raw);
     void* c_act = ws + P.c_act;
     float* kv_raw = reinterpret_cast<float*>(ws + P.kv_raw);
@@ -904,7 +917,7 @@ int check_call(const dspine_model* model, int B, int W, const int32_t* anchor_id
   for (int b = 0; b < B; ++b)
     if (anchor_ids[b] < 0 || anchor_ids[b] >= model->g.vocab)
       return fail(DSPINE_E_ARG, "anchor_ids[%d] = %d outside [0, %d)", b, anchor_ids[b], model->g.vocab);
-  *need = make_plan(model->g, (int64_t)B * W, 0).total;
+  *need = make_plan(model->g, B, W, 0).total;
   if (!ws || !aligned16(ws)) return fail(DSPINE_E_ARG, "workspace NULL or not 16-byte aligned");
   if (ws_bytes < *need) return fail(DSPINE_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, *need);
   return DSPINE_OK;
@@ -926,7 +939,7 @@ int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x, 
   if (!x || !aligned16(x)) return fail(DSPINE_E_ARG, "bridge: x NULL or unaligned");
   if (pred_codes && !aligned16(pred_codes)) return fail(DSPINE_E_ARG, "bridge: pred_codes unaligned");
   if ((rc = check_packed(model))) return rc;
-  const Plan P = make_plan(model->g, (int64_t)B * W, 0);
+  const Plan P = make_plan(model->g, B, W, 0);
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* st1 = reinterpret_cast<float*>(ws + P.st1);
@@ -983,7 +996,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
   char* ws = static_cast<char*>(workspace);
   const int M = B * W, H = g.hidden, D = g.head_dim;
   const int qd = g.n_q_heads * D, kvd = g.n_kv_heads * D;
-  const Plan P = make_plan(g, M, 0);
+  const Plan P = make_plan(g, B, W, 0);
   const int cus = num_cus();
   float* x = reinterpret_cast<float*>(ws + P.x);
   void* act_q = ws + P.act_q;
@@ -1327,7 +1340,7 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
   const int Mc = B * (W - 1) * K;
   const size_t eb = act_bytes(g);
   const int cus = num_cus();
-  const Plan P = make_plan(g, M, 0);
+  const Plan P = make_plan(g, B, W, 0);
   float* u = reinterpret_cast<float*>(pws + PP.u);
   float* scores = prop->scores ? prop->scores : reinterpret_cast<float*>(pws + PP.scores);
 
@@ -1388,6 +1401,7 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
   float* Pc = reinterpret_cast<float*>(pws + PP.Pc);
   float* Y = reinterpret_cast<float*>(pws + PP.Y);
   const bool tile = g.dtype == DSPINE_BF16 && gemm_tile_fits(a, r) && gemm_tile_fits(H, a);
+  const int chunk = gemm_stream_row_tile(M);
   if (tile) {
     TileGemmParams tp;
     memset(&tp, 0, sizeof tp);
@@ -1407,8 +1421,10 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
     tp.ldo = 2 * a;
     HIP_TRY(launch_gemm_tile(tp, g.dtype, cus, stream));
   } else {
-    for (int r0 = 0; r0 < Mc; r0 += kMaxRows) {
-      const int mr = std::min(kMaxRows, Mc - r0);
+    // chunks of at most the rows whose split partials the forward's
+    // workspace holds (the streamed GEMM's row tile of M = B*W)
+    for (int r0 = 0; r0 < Mc; r0 += chunk) {
+      const int mr = std::min(chunk, Mc - r0);
       gp = gemm_base(P, ws, r, mr);
       set_segments(gp, {{model->pw.bridge_Gp, a}, {model->pw.bridge_A, a}});
       gp.pro = PRO_COPY;
@@ -1438,8 +1454,8 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
     tp.ldo = H;
     HIP_TRY(launch_gemm_tile(tp, g.dtype, cus, stream));
   } else {
-    for (int r0 = 0; r0 < Mc; r0 += kMaxRows) {
-      const int mr = std::min(kMaxRows, Mc - r0);
+    for (int r0 = 0; r0 < Mc; r0 += chunk) {
+      const int mr = std::min(chunk, Mc - r0);
       gp = gemm_base(P, ws, a, mr);
       set_segments(gp, {{model->pw.layer[L - 1].W_l, H}});
       gp.pro = PRO_COPY;

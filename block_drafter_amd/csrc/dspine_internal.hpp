@@ -105,10 +105,14 @@ struct GemmParams {
   // filled by the launcher
   int32_t tiles, ipt, xcd_remap;
   float* partials;
+  size_t partial_floats;          // capacity of `partials` (gemm_stream_partial_floats of the rows)
   uint32_t* counters;
 };
 hipError_t launch_gemm_stream(const GemmParams& p, int dtype, int num_cus, hipStream_t s);
-size_t gemm_stream_partial_floats(int grid_cap);
+// split partials (floats) of streamed GEMMs of up to `rows` rows
+size_t gemm_stream_partial_floats(int rows);
+// rows of the row tile a streamed GEMM of M rows runs (16, 32, 64 or 128)
+int gemm_stream_row_tile(int M);
 int gemm_stream_grid_cap(int num_cus);
 int gemm_stream_stat_lists(int n_columns);
 int gemm_stream_fused_rows();

@@ -797,7 +797,7 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
     G = (int)g;
   }
   // two partial slots per workgroup, each NWB * MT * 4 KB
-  if ((size_t)2 * G * (NWB * MT * 256 * 4) > gemm_stream_partial_floats(kMaxGrid)) return hipErrorInvalidValue;
+  if ((size_t)2 * G * (NWB * MT * 256 * 4) > p.partial_floats) return hipErrorInvalidValue;
   p.xcd_remap = (G % 8 == 0) ? 1 : 0;
   DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>), dim3(G), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -805,9 +805,16 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
 
 int gemm_stream_grid_cap(int num_cus) { return 2 * num_cus < kMaxGrid ? 2 * num_cus : kMaxGrid; }
 
-size_t gemm_stream_partial_floats(int grid_cap) {
-  // 2 slots per workgroup, each NWB*MT*256*4 floats at most (NWB = 2, MT = 8)
-  return (size_t)2 * grid_cap * (2 * 8 * 256 * 4);
+int gemm_stream_row_tile(int M) {
+  const int mt = (M + 15) / 16;
+  return 16 * (mt <= 1 ? 1 : mt <= 2 ? 2 : mt <= 4 ? 4 : 8);
+}
+
+size_t gemm_stream_partial_floats(int rows) {
+  // 2 slots per workgroup of a grid of at most kMaxGrid, each NWB*MT*256*4
+  // floats with NWB <= 2 and MT the row tile of `rows` (see launch_mt)
+  const int mt = gemm_stream_row_tile(rows < 1 ? 1 : rows > kMaxRows ? kMaxRows : rows) / 16;
+  return (size_t)2 * kMaxGrid * (2 * mt * 256 * 4);
 }
 
 // statistics lists a GEMM of N output columns writes (one per 64 columns)
