@@ -105,6 +105,9 @@ EXPORTS = {
                                             ctypes.POINTER(Ctx_c), ctypes.POINTER(ctypes.c_int32),
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                             ctypes.c_void_p]),
+    "dspine_draft_forward_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.POINTER(Ctx_c), ctypes.POINTER(ctypes.c_int32),
+                                                    ctypes.c_void_p, ctypes.c_void_p]),
     "dspine_bridge": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -286,6 +289,18 @@ class Model:
         st = stream if stream is not None else torch.cuda.current_stream().cuda_stream
         _check(lib().dspine_draft_forward(self.handle, B, W, arr, aid, out.data_ptr(),
                                           ws.data_ptr(), ws.numel(), st))
+        return out
+
+    def forward_noalloc(self, ctxs: Sequence["Context"], anchor_ids: Sequence[int], W: int, out=None, stream=None):
+        """dspine_draft_forward_noalloc: the forward on the library's static scratch (no workspace)."""
+        torch = _torch()
+        B = len(ctxs)
+        arr = (Ctx_c * B)(*[c.struct for c in ctxs])
+        aid = (ctypes.c_int32 * B)(*[int(a) for a in anchor_ids])
+        if out is None:
+            out = torch.empty((B, W, self.geom.hidden), dtype=torch.float32, device="cuda")
+        st = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        _check(lib().dspine_draft_forward_noalloc(self.handle, B, W, arr, aid, out.data_ptr(), st))
         return out
 
     def propose_workspace(self, max_batch=MAX_BATCH, max_width=16, topk=MAX_TOPK):

@@ -908,8 +908,8 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
   return DSPINE_OK;
 }
 
-int check_call(const dspine_model* model, int B, int W, const int32_t* anchor_ids, const void* ws,
-               size_t ws_bytes, size_t* need) {
+// checks of a call over B requests of width W, workspace aside
+int check_call_args(const dspine_model* model, int B, int W, const int32_t* anchor_ids) {
   if (!model || !anchor_ids) return fail(DSPINE_E_ARG, "NULL argument");
   if (B < 1 || B > DSPINE_MAX_BATCH) return fail(DSPINE_E_UNSUPPORTED, "B = %d not in 1..%d", B, DSPINE_MAX_BATCH);
   if (W < DSPINE_MIN_WIDTH || W > DSPINE_MAX_WIDTH)
@@ -917,6 +917,12 @@ int check_call(const dspine_model* model, int B, int W, const int32_t* anchor_id
   for (int b = 0; b < B; ++b)
     if (anchor_ids[b] < 0 || anchor_ids[b] >= model->g.vocab)
       return fail(DSPINE_E_ARG, "anchor_ids[%d] = %d outside [0, %d)", b, anchor_ids[b], model->g.vocab);
+  return DSPINE_OK;
+}
+int check_call(const dspine_model* model, int B, int W, const int32_t* anchor_ids, const void* ws,
+               size_t ws_bytes, size_t* need) {
+  int rc = check_call_args(model, B, W, anchor_ids);
+  if (rc) return rc;
   *need = make_plan(model->g, B, W, 0).total;
   if (!ws || !aligned16(ws)) return fail(DSPINE_E_ARG, "workspace NULL or not 16-byte aligned");
   if (ws_bytes < *need) return fail(DSPINE_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, *need);
@@ -958,7 +964,17 @@ int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x, 
 // -----------------------------------------------------------------------------
 // a4-a12
 // -----------------------------------------------------------------------------
-// checks shared by the forward and the propose call
+// checks shared by the forward calls and the propose call, workspace aside
+static int check_forward_args(const dspine_model* model, int B, int W, const dspine_ctx* ctx,
+                              const int32_t* anchor_ids, const float* out) {
+  int rc = check_call_args(model, B, W, anchor_ids);
+  if (rc) return rc;
+  if (!ctx) return fail(DSPINE_E_ARG, "forward: ctx NULL");
+  if (!out || !aligned16(out)) return fail(DSPINE_E_ARG, "forward: out NULL or unaligned");
+  for (int b = 0; b < B; ++b)
+    if ((rc = check_ctx_rings(*model, ctx[b], b, ctx[b].frontier))) return rc;
+  return DSPINE_OK;
+}
 static int check_forward(const dspine_model* model, int B, int W, const dspine_ctx* ctx, const int32_t* anchor_ids,
                          const float* out, void* workspace, size_t workspace_bytes) {
   size_t need = 0;
@@ -1252,6 +1268,56 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
   if (rc) return rc;
   if ((rc = check_packed(model))) return rc;
   rc = run_forward(model, B, W, ctx, anchor_ids, out, workspace, reinterpret_cast<hipStream_t>(stream), nullptr);
+  return rc ? rc : ok();
+}
+
+// -----------------------------------------------------------------------------
+// allocation-free forward: the workspace is a static device array
+// -----------------------------------------------------------------------------
+// One copy of the array lives on every device the library runs on, until the
+// process ends.  On the host, `scratch` only names the symbol: its device
+// address on the current device comes from hipGetSymbolAddress, and only that
+// address is ever handed to a kernel.
+static __device__ __align__(256) char scratch[DSPINE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.  The first call
+// on a device looks it up and clears the stream-K tile counters (at the start
+// of every plan) on `stream`; every forward leaves them at zero again.
+int scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSPINE_E_UNSUPPORTED, "device index %d not below %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || ((uintptr_t)p & 255u)) return fail(DSPINE_E_HIP, "static scratch: bad device address");
+    HIP_TRY(launch_zero_words(p, kMaxTiles, stream));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSPINE_OK;
+}
+}  // namespace
+
+int dspine_draft_forward_noalloc(const dspine_model* model, int B, int W, const dspine_ctx* ctx,
+                                 const int32_t* anchor_ids, float* out, dspine_stream_t stream) {
+  int rc = check_forward_args(model, B, W, ctx, anchor_ids, out);
+  if (rc) return rc;
+  const size_t need = make_plan(model->g, B, W, 0).total;
+  if (need > DSPINE_NOALLOC_SCRATCH_BYTES)
+    return fail(DSPINE_E_WORKSPACE, "forward_noalloc: B = %d, W = %d needs %zu bytes of scratch, more than the "
+                "static %zu", B, W, need, (size_t)DSPINE_NOALLOC_SCRATCH_BYTES);
+  if ((rc = check_packed(model))) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((rc = scratch_for_current_device(s, &ws))) return rc;
+  rc = run_forward(model, B, W, ctx, anchor_ids, out, ws, s, nullptr);
   return rc ? rc : ok();
 }
 

@@ -247,6 +247,9 @@ struct VisibleParams {
 };
 hipError_t launch_debug_visible(const VisibleParams& p, hipStream_t s);
 
+// words [0, n_words) of p <- 0 with a kernel
+hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);
+
 // projection matrix [rows, cols] row-major -> fragment order (see pack_kernel)
 hipError_t launch_pack(const void* src, void* dst, int rows, int cols, int dtype, hipStream_t s);
 

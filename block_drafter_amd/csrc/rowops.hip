@@ -213,6 +213,20 @@ __global__ __launch_bounds__(kRowThreads) void kv_store_kernel(const KvStorePara
 // .. +8, at element offset (b*(K/32) + ks)*512 + 8*l.  This is the order in
 // which a wave's MFMA fragments are loaded, so each load reads 1 KB
 // (bf16; 2 KB for float) of consecutive memory.
+// words [0, n) of p <- 0 (a plain kernel, not a memset node, so that it can
+// sit in a captured graph)
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s) {
+  if (n_words == 0) return hipSuccess;
+  const size_t blocks = (n_words + 255) / 256;
+  DSPINE_LAUNCH(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s,
+                static_cast<uint32_t*>(p), n_words);
+  return hipGetLastError();
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void pack_kernel(const T* src, T* dst, int R, int K) {
   const size_t nfrag = (size_t)(R / 16) * (K / 32) * 64;

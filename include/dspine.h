@@ -246,6 +246,27 @@ int dspine_draft_forward(const dspine_model* model, int B, int W, const dspine_c
                          void* workspace, size_t workspace_bytes, dspine_stream_t stream);
 
 /*
+ * dspine_draft_forward for callers that cannot allocate (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * forward and the same kernels, with the workspace replaced by a static
+ * device array of DSPINE_NOALLOC_SCRATCH_BYTES held by the library on every
+ * GPU it runs on until the process ends.  The call allocates nothing.
+ *
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents: calls that overlap on one GPU (other streams, other
+ *     threads) race and must be ordered by the caller.
+ *   - The first call on a device looks the array up and clears its tile
+ *     counters on `stream` before the forward.
+ *   - B * W and the geometry must fit the array: the 27B geometry takes up to
+ *     B * W = 32 rows (B = 2 at W = 16).  Larger calls fail with
+ *     DSPINE_E_WORKSPACE before any launch.
+ * Arguments and errors otherwise as dspine_draft_forward.
+ */
+#define DSPINE_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+int dspine_draft_forward_noalloc(const dspine_model* model, int B, int W, const dspine_ctx* ctx,
+                                 const int32_t* anchor_ids, float* out, dspine_stream_t stream);
+
+/*
  * a9-a11 alone on one layer's block states.  [FLZ, "The bridge"]:
  *   rho_t = rms(x_t), z_t = R_l x_t / (rho_t + eps),
  *   c_t = sqrt(r) z_t / (||z_t|| + eps), anchor row: c_0 = sqrt(r) C[a_b];

@@ -144,6 +144,34 @@ def test_forward_rejections_before_any_launch(L):
     L.dspine_model_destroy(h)
 
 
+def test_forward_noalloc_rejections_before_any_launch(L):
+    """The allocation-free forward checks its arguments like the forward and
+    refuses calls whose workspace plan exceeds its static scratch, before it
+    touches the GPU."""
+    g = synth.G_27B
+    h = make_model(L, g)
+    c = fake_ctx(g, 4096)
+
+    def call(B, W, ctxs, anchors, out=FAKE):
+        arr = (bd.Ctx_c * len(ctxs))(*ctxs)
+        aid = (ctypes.c_int32 * len(anchors))(*anchors)
+        return L.dspine_draft_forward_noalloc(h, B, W, arr, aid, out, None)
+
+    assert call(0, 16, [c], [1]) == bd.E_UNSUPPORTED
+    assert call(1, 17, [c], [1]) == bd.E_UNSUPPORTED
+    assert call(1, 16, [c], [g.vocab]) == bd.E_ARG
+    assert call(1, 16, [c], [5], out=FAKE + 4) == bd.E_ARG
+    assert call(1, 16, [fake_ctx(g, -1)], [5]) == bd.E_STATE
+    # B * W = 128 rows at 27B needs about 144 MB of workspace: more than the scratch
+    assert call(8, 16, [c] * 8, [5] * 8) == bd.E_WORKSPACE
+    assert b"scratch" in L.dspine_last_error()
+    # 32 rows fit; the unpacked model is refused next
+    assert L.dspine_workspace_bytes(h, 2, 16, 0) <= 40 << 20 < L.dspine_workspace_bytes(h, 4, 16, 0)
+    assert call(2, 16, [c] * 2, [5] * 2) == bd.E_STATE
+    assert b"pack" in L.dspine_last_error()
+    L.dspine_model_destroy(h)
+
+
 def test_full_layer_capacity_checks(L):
     g = synth.G_35B_DFLASH
     h = make_model(L, g)
