@@ -22,11 +22,14 @@ plus its ``synth.Geometry``.
 Pins (tests/test_oracle_pins.py): every function below is tied to something
 other than this code: closed forms (RMSNorm, window counts), hand-worked
 examples (context, bridge, decoder layer, the DFlash2 convolution, the
-walks), brute force (attention, top-K), special cases that reduce to a
-simpler computation (bridge or convolution switched off gives plain DFlash;
-the anchor-conditioned or predicted-code refinement gives the forward's own
-scores), invariants (RoPE shift, request independence, one-row look-back)
-and the figures the pages print.  Parity unpinned: the absolute output values
+walks, the FP8 rounding and a retrieval that misses the BF16 best), brute
+force (attention, top-K), a library routine (torch's float8_e4m3fn cast for
+the FP8 rounding), special cases that reduce to a simpler computation
+(bridge or convolution switched off gives plain DFlash; the
+anchor-conditioned or predicted-code refinement gives the forward's own
+scores; an FP8-representable head scores exactly; retrieving the whole
+vocabulary is the direct path), invariants (RoPE shift, request
+independence, one-row look-back) and the figures the pages print.  Parity unpinned: the absolute output values
 at the 27B and 35B geometries, for which the pages print no worked example;
 there the GPU is compared with this oracle on identical inputs.
 """
@@ -557,6 +560,70 @@ def top_k(scores: np.ndarray, K: int) -> np.ndarray:
     return order[:K].astype(np.int64)
 
 
+# ---------------------------------------------------------------------------
+# FP8 row-scaled candidate retrieval [FLZ, "The last write is refined using
+# discrete candidates": the optimized path scores the whole vocabulary
+# approximately with a row-scaled FP8 head, keeps 128 candidates, rescores
+# them with the original BF16 head and keeps the best 16]
+# ---------------------------------------------------------------------------
+FP8_E4M3_MAX = 448.0      # largest finite OCP E4M3 value, 1.75 x 2^8
+RETRIEVE = 128            # candidates the FP8 scores keep per row
+
+
+def round_fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """Nearest OCP FP8 E4M3 value, ties to even, as float64.  E4M3 keeps 3
+    fraction bits with exponent bias 7: normal binades 2^-6 .. 2^8 (step
+    2^(e-3) in binade 2^e) and subnormals in steps of 2^-9 below 2^-6.
+    Inputs must be finite with |x| <= 448 (the row scale below keeps the
+    head's values there), so nothing saturates."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    mant, ex = np.frexp(a)                  # a = mant * 2^ex, mant in [0.5, 1)
+    e = np.maximum(ex - 1, -6)              # binade exponent, floored at the subnormal range
+    step = np.ldexp(1.0, e - 3)
+    return np.copysign(np.round(a / step) * step, x)   # numpy rounds halves to even
+
+
+def quantize_head_fp8(lm_head: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """The row-scaled FP8 copy of the head.  Reading (the pages fix only
+    "row-scaled FP8"): row v's scale s_v is the smallest power of two with
+    max_k |E_v[k]| / s_v <= 448 (1 for an all-zero row), and its codes are
+    E_v / s_v rounded to E4M3, ties to even.  Dividing by a power of two is
+    exact, so each code is one rounding of the BF16 value.  Returns the codes
+    (as float64 values) [V, H] and the scales [V]."""
+    E = widen(lm_head)
+    m = np.max(np.abs(E), axis=1)
+    s = np.ones_like(m)
+    nz = m > 0
+    mant, ex = np.frexp(m[nz] / FP8_E4M3_MAX)        # m / 448 = mant * 2^ex
+    s[nz] = np.where(mant == 0.5, np.ldexp(1.0, ex - 1), np.ldexp(1.0, ex))
+    return round_fp8_e4m3(E / s[:, None]), s
+
+
+def head_scores_fp8(codes: np.ndarray, scales: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """Approximate head scores s_v * (q_v . h) of every vocabulary row for the
+    rows of h [n, H]; returns [n, V]."""
+    h = np.atleast_2d(h)
+    V = codes.shape[0]
+    out = np.empty((h.shape[0], V))
+    for v0 in range(0, V, HEAD_SLICE):
+        v1 = min(V, v0 + HEAD_SLICE)
+        out[:, v0:v1] = (h @ codes[v0:v1].T) * scales[None, v0:v1]
+    return out
+
+
+def retrieve_and_rescore(approx: np.ndarray, lm_head: np.ndarray, h: np.ndarray, R: int,
+                         K: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """One proposal row: the R best approximate scores (ties: smaller token
+    first), their exact BF16 head scores E_v . h, and the K best of those
+    (same order rule).  Returns (retrieved ids [R], their exact scores [R],
+    the K kept ids, their exact scores)."""
+    ids = top_k(approx, R)
+    exact = head_scores(lm_head, h, ids)[0]
+    keep = np.lexsort((ids, -exact))[:K]
+    return ids, exact, ids[keep], exact[keep]
+
+
 def transition_table(g, wts, lm_head: np.ndarray, u: np.ndarray, anchor_id: int,
                      cand: np.ndarray) -> np.ndarray:
     """T_t[i, j] for one request [PHY, 前驱条件解码与 transition cache, the
@@ -637,23 +704,41 @@ def sampled_walk(T: np.ndarray, temperature: float, uniforms: np.ndarray) -> Tup
 
 def propose(g, wts, lm_head: np.ndarray, ctxs: Sequence[RequestContext], anchor_ids: Sequence[int],
             W: int, K: int, walk: str = "greedy", temperature: float = 1.0,
-            uniforms: Optional[np.ndarray] = None, cand_override: Optional[np.ndarray] = None) -> dict:
+            uniforms: Optional[np.ndarray] = None, cand_override: Optional[np.ndarray] = None,
+            retrieve: int = 0, fp8_head: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> dict:
     """The proposal tail after the draft forward, per request: head scores of
     rows 1..W-1 and their top-K candidates, the transition tables, and the
-    walk.  ``cand_override`` [B, W-1, K] replaces the candidate ids (to
-    evaluate the tables on another implementation's candidates).  Returns a
-    dict of float64/int64 arrays: out [B,W,H], scores [B,W-1,V], cand
-    [B,W-1,K], cand_scores [B,W-1,K], table [B,W-1,K,K], choice [B,W-1],
-    tokens [B,W-1], q [B,W-1] (sampled walk only)."""
+    walk.  With ``retrieve`` = R > 0 the candidates come from the FP8
+    retrieval instead: the R best FP8 scores, rescored with the BF16 head,
+    the best K kept (``fp8_head`` = quantize_head_fp8(lm_head), computed
+    here when not given); ``scores`` then holds the FP8 scores and
+    ``retrieved`` / ``rescored`` [B,W-1,R] the R ids and their BF16 scores.
+    ``cand_override`` [B, W-1, K] replaces the candidate ids (to evaluate the
+    tables on another implementation's candidates).  Returns a dict of
+    float64/int64 arrays: out [B,W,H], scores [B,W-1,V], cand [B,W-1,K],
+    cand_scores [B,W-1,K] (BF16 head scores), table [B,W-1,K,K], choice
+    [B,W-1], tokens [B,W-1], q [B,W-1] (sampled walk only)."""
     assert g.bridge, "the refinement redoes the last bridge write"
     out, u = draft_forward(g, wts, ctxs, anchor_ids, W, return_last_prewrite=True)
     B = len(ctxs)
     res = {"out": out, "scores": [], "cand": [], "cand_scores": [], "table": [], "choice": [],
            "tokens": [], "q": []}
+    if retrieve:
+        res["retrieved"], res["rescored"] = [], []
+        if fp8_head is None:
+            fp8_head = quantize_head_fp8(lm_head)
     for b in range(B):
-        sc = head_scores(lm_head, out[b, 1:])
-        cand = np.stack([top_k(sc[t], K) for t in range(W - 1)]) if cand_override is None \
-            else np.asarray(cand_override[b], dtype=np.int64)
+        if retrieve:
+            sc = head_scores_fp8(fp8_head[0], fp8_head[1], out[b, 1:])
+            rows = [retrieve_and_rescore(sc[t], lm_head, out[b, 1 + t], retrieve, K) for t in range(W - 1)]
+            res["retrieved"].append(np.stack([r[0] for r in rows]))
+            res["rescored"].append(np.stack([r[1] for r in rows]))
+            cand = np.stack([r[2] for r in rows])
+        else:
+            sc = head_scores(lm_head, out[b, 1:])
+            cand = np.stack([top_k(sc[t], K) for t in range(W - 1)])
+        if cand_override is not None:
+            cand = np.asarray(cand_override[b], dtype=np.int64)
         T = transition_table(g, wts, lm_head, u[b], int(anchor_ids[b]), cand)
         if walk == "greedy":
             ch, q = greedy_walk(T), np.zeros(W - 1)
@@ -661,7 +746,9 @@ def propose(g, wts, lm_head: np.ndarray, ctxs: Sequence[RequestContext], anchor_
             ch, q = sampled_walk(T, temperature, uniforms[b])
         res["scores"].append(sc)
         res["cand"].append(cand)
-        res["cand_scores"].append(np.take_along_axis(sc, cand, axis=1))
+        res["cand_scores"].append(np.stack([head_scores(lm_head, out[b, 1 + t], cand[t])[0]
+                                            for t in range(W - 1)]) if retrieve
+                                  else np.take_along_axis(sc, cand, axis=1))
         res["table"].append(T)
         res["choice"].append(ch)
         res["tokens"].append(cand[np.arange(W - 1), ch])

@@ -94,6 +94,23 @@ MUTATIONS = {
         "if float(uniforms[t]) < cdf:", "if float(uniforms[t]) <= cdf:"),
     "sampled walk keeps the wrong probability": (
         "q[t] = p[j]", "q[t] = p[i]"),
+    "fp8 rounding truncates": (
+        "return np.copysign(np.round(a / step) * step, x)", "return np.copysign(np.floor(a / step) * step, x)"),
+    "fp8 subnormal step halved": (
+        "e = np.maximum(ex - 1, -6)", "e = np.maximum(ex - 1, -7)"),
+    "fp8 scale one power of two too small": (
+        "s[nz] = np.where(mant == 0.5, np.ldexp(1.0, ex - 1), np.ldexp(1.0, ex))",
+        "s[nz] = np.ldexp(1.0, ex - 1)"),
+    "fp8 scale from the wrong maximum": (
+        "mant, ex = np.frexp(m[nz] / FP8_E4M3_MAX)", "mant, ex = np.frexp(m[nz] / 240.0)"),
+    "fp8 scores drop the row scale": (
+        "out[:, v0:v1] = (h @ codes[v0:v1].T) * scales[None, v0:v1]", "out[:, v0:v1] = h @ codes[v0:v1].T"),
+    "retrieval keeps the fp8 order": (
+        "keep = np.lexsort((ids, -exact))[:K]", "keep = np.arange(K)"),
+    "rescoring ties prefer the larger id": (
+        "keep = np.lexsort((ids, -exact))[:K]", "keep = np.lexsort((-ids, -exact))[:K]"),
+    "retrieval keeps one candidate fewer": (
+        "ids = top_k(approx, R)", "ids = top_k(approx, R - 1)"),
     "conv tap before row zero": (
         "    out[1:] += (base[side, 1][None] + delta[1:, side, 1, :, None]) * Xg[:-1]\n",
         "    out += (base[side, 1][None] + delta[:, side, 1, :, None]) * np.roll(Xg, 1, axis=0)\n"),

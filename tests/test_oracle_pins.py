@@ -619,6 +619,173 @@ def test_head_scores_are_row_dot_products():
     assert np.max(np.abs(O.head_scores(head, h, [13, 2])[:, 0] - s[:, 13])) < 1e-14
 
 
+# ---------------------------------------------------------------------------
+# FP8 row-scaled retrieval
+# ---------------------------------------------------------------------------
+def e4m3_values():
+    """Every finite non-negative OCP E4M3 value, from the format's definition:
+    bits eeee.mmm, bias 7; exponent field 0 is subnormal (m/8 * 2^-6); field
+    15 with mantissa 7 is NaN (no infinities)."""
+    out = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            out.append(m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(sorted(set(out)))
+
+
+def test_fp8_e4m3_hand_values():
+    r = O.round_fp8_e4m3
+    assert r(448.0) == 448.0 and r(-448.0) == -448.0
+    assert r(440.0) == 448.0 and r(415.0) == 416.0           # steps of 32 in [256, 512)
+    assert r(1.0625) == 1.0                                   # tie: even mantissa 0
+    assert r(1.1875) == 1.25                                  # tie: 1.125 (m=1) vs 1.25 (m=2)
+    assert r(0.3) == 0.3125                                   # 9.6 steps of 2^-5
+    assert r(2.0 ** -10) == 0.0                               # tie between 0 and 2^-9
+    assert r(3 * 2.0 ** -10) == 2.0 ** -8                     # tie between 2^-9 and 2^-8
+    assert r(2.0 ** -9) == 2.0 ** -9 and r(2.0 ** -6) == 2.0 ** -6
+    assert r(-0.0) == 0.0 and r(7.4) == 7.5
+
+
+def test_fp8_e4m3_fixed_points_and_midpoints():
+    vals = e4m3_values()
+    assert len(vals) == 127 and vals[-1] == 448.0 and vals[1] == 2.0 ** -9
+    assert np.array_equal(O.round_fp8_e4m3(vals), vals)
+    assert np.array_equal(O.round_fp8_e4m3(-vals), -vals)
+    mids = (vals[:-1] + vals[1:]) / 2
+    got = O.round_fp8_e4m3(mids)
+    # ties go to the neighbour whose mantissa is even (its step count is even)
+    lo, hi = vals[:-1], vals[1:]
+    mant_lo = np.array([round((v / 2.0 ** max(math.frexp(v)[1] - 1, -6)) * 8) % 2 if v > 0 else 0 for v in lo])
+    want = np.where(mant_lo == 0, lo, hi)
+    assert np.array_equal(got, want)
+    # just off the midpoints the nearest value wins
+    assert np.array_equal(O.round_fp8_e4m3(mids * (1 - 1e-9)), lo)
+    assert np.array_equal(O.round_fp8_e4m3(mids * (1 + 1e-9)), hi)
+
+
+def test_fp8_e4m3_matches_torch_cast():
+    """torch's float8_e4m3fn cast (ties to even) on float32 inputs of every
+    magnitude the head codes take, subnormals included."""
+    import torch
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal(20000) * np.exp2(rng.uniform(-12, 8.7, 20000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    x = np.concatenate([x, (e4m3_values()[:-1] + e4m3_values()[1:]).astype(np.float32) / 2])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(O.round_fp8_e4m3(x.astype(np.float64)), want)
+
+
+def test_fp8_head_scales_and_codes():
+    rng = np.random.default_rng(13)
+    E = rng.standard_normal((40, 64)) * np.exp2(rng.uniform(-20, 10, (40, 1)))
+    E[3] = 0.0
+    E[5, :] = 0.25
+    E[5, 7] = 448.0 * 2.0 ** -3              # max exactly 448 x a power of two
+    head = synth.f32_to_bf16_bits(E.astype(np.float32))
+    Ew = synth.to_float(head)
+    codes, sc = O.quantize_head_fp8(head)
+    mant, _ = np.frexp(sc)
+    assert np.all(mant == 0.5)                                   # powers of two
+    nz = np.arange(40) != 3
+    top = np.max(np.abs(Ew), axis=1)[nz] / sc[nz]
+    assert np.all(top <= 448) and np.all(top > 224)              # the smallest such power of two
+    m = np.max(np.abs(codes), axis=1)
+    assert np.all(m[nz] <= 448) and np.all(m[nz] >= 224)
+    assert sc[3] == 1.0 and np.all(codes[3] == 0)
+    assert sc[5] == 2.0 ** -3 and codes[5, 7] == 448.0 and codes[5, 0] == 2.0
+    assert np.array_equal(O.round_fp8_e4m3(codes), codes)       # codes are E4M3 values
+    # one rounding of E / s: within half a step of the E4M3 grid
+    x = Ew / sc[:, None]
+    assert np.all(np.abs(codes - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10) + 1e-300)
+
+
+def test_fp8_scores_exact_for_representable_head():
+    """A head whose rows are E4M3 values times a power of two (max at 448 x
+    2^k) is held exactly by the FP8 copy: its approximate scores equal the
+    BF16 scores, and the retrieval keeps the direct path's top-K."""
+    rng = np.random.default_rng(14)
+    vals = e4m3_values()
+    V, H = 300, 32
+    k = np.exp2(rng.integers(-12, -4, (V, 1)))
+    E = rng.choice(np.concatenate([vals, -vals]), size=(V, H)) * k
+    E[:, 0] = 448.0 * k[:, 0]
+    head = synth.f32_to_bf16_bits(E.astype(np.float32))
+    assert np.array_equal(synth.to_float(head), E)
+    codes, sc = O.quantize_head_fp8(head)
+    h = rng.standard_normal((3, H))
+    approx = O.head_scores_fp8(codes, sc, h)
+    exact = O.head_scores(head, h)
+    assert np.max(np.abs(approx - exact)) <= 1e-12 * np.max(np.abs(exact))
+    for n in range(3):
+        ids, ex, keep, kept = O.retrieve_and_rescore(approx[n], head, h[n], 20, 5)
+        assert list(keep) == list(O.top_k(exact[n], 5))
+
+
+def test_retrieval_covering_the_vocabulary_is_the_direct_path():
+    """R >= V: every token is rescored with the BF16 head, so the K kept are
+    the direct path's top-K, best first, ties by the smaller id."""
+    g, wts, head, ctxs, anchors, W = propose_setup()
+    rng = np.random.default_rng(15)
+    h = rng.standard_normal((4, g.hidden))
+    codes, sc = O.quantize_head_fp8(head)
+    approx = O.head_scores_fp8(codes, sc, h)
+    exact = O.head_scores(head, h)
+    for n in range(4):
+        ids, ex, keep, kept = O.retrieve_and_rescore(approx[n], head, h[n], g.vocab, 6)
+        assert sorted(ids) == list(range(g.vocab))
+        assert list(keep) == list(O.top_k(exact[n], 6))
+        assert np.max(np.abs(kept - exact[n, keep])) <= 1e-12 * np.max(np.abs(kept))
+        # the approximation is close but not exact (the FP8 codes round)
+        assert 0 < np.max(np.abs(approx[n] - exact[n])) < 0.1 * np.sqrt(np.mean(exact[n] ** 2))
+
+
+def test_retrieval_keeps_the_fp8_best_and_can_miss_the_bf16_best():
+    """The kept tokens are the R best FP8 scores re-sorted by their BF16
+    scores, so a token whose FP8 score falls outside the R best is lost even
+    when its BF16 score is the best [FLZ: rescoring does not prove that the
+    retrieval held the global BF16 top-16].  Hand case, H = 1, h = 1: token 0
+    has E = 1 (exact in FP8), token 1 has E = 1 + 2^-7 whose FP8 code rounds
+    to 1 (scale 2^-8: 258 -> 256), token 2 has E = 0.5; with R = 1 the FP8
+    tie goes to token 0 and token 1, the BF16 best, is missed."""
+    head = synth.f32_to_bf16_bits(np.array([[1.0], [1.0 + 2.0 ** -7], [0.5]], dtype=np.float32))
+    codes, sc = O.quantize_head_fp8(head)
+    assert list(sc) == [2.0 ** -8, 2.0 ** -8, 2.0 ** -9] and list(codes[:, 0]) == [256.0, 256.0, 256.0]
+    h = np.array([1.0])
+    approx = O.head_scores_fp8(codes, sc, h[None])[0]
+    assert list(approx) == [1.0, 1.0, 0.5]
+    ids, ex, keep, kept = O.retrieve_and_rescore(approx, head, h, 1, 1)
+    assert list(ids) == [0] and list(keep) == [0]
+    ids, ex, keep, kept = O.retrieve_and_rescore(approx, head, h, 2, 2)
+    assert list(ids) == [0, 1] and list(keep) == [1, 0] and list(kept) == [1.0 + 2.0 ** -7, 1.0]
+    # ties in the BF16 rescoring keep the smaller token first
+    head2 = synth.f32_to_bf16_bits(np.array([[0.75], [0.75], [0.25]], dtype=np.float32))
+    c2, s2 = O.quantize_head_fp8(head2)
+    a2 = O.head_scores_fp8(c2, s2, h[None])[0]
+    ids, ex, keep, kept = O.retrieve_and_rescore(a2, head2, h, 3, 2)
+    assert list(keep) == [0, 1]
+
+
+def test_propose_with_retrieval_uses_rescored_candidates():
+    """The proposal with FP8 retrieval: candidates are the rescored best K of
+    the R retrieved, their scores are BF16 head scores, and with R = V the
+    whole proposal equals the direct path's."""
+    g, wts, head, ctxs, anchors, W = propose_setup()
+    direct = O.propose(g, wts, head, ctxs, anchors, W, K=4)
+    full = O.propose(g, wts, head, ctxs, anchors, W, K=4, retrieve=g.vocab)
+    for k in ("cand", "cand_scores", "table", "choice", "tokens"):
+        assert np.array_equal(direct[k], full[k]) or np.max(np.abs(direct[k] - full[k])) < 1e-12, k
+    part = O.propose(g, wts, head, ctxs, anchors, W, K=4, retrieve=8)
+    assert part["retrieved"].shape == (len(ctxs), W - 1, 8)
+    for b in range(len(ctxs)):
+        for t in range(W - 1):
+            ids = part["retrieved"][b, t]
+            assert list(ids) == list(O.top_k(part["scores"][b, t], 8))
+            assert set(part["cand"][b, t]) <= set(ids)
+            assert np.all(np.diff(part["cand_scores"][b, t]) <= 0)
+
+
 def test_anchor_conditioned_table_reproduces_forward_scores():
     """Row 1's predecessor is the anchor, whose code the forward's own last
     write already used: every row of T_1 equals the forward's head scores on
