@@ -247,25 +247,27 @@ def prefill_noskip_measure(g, wts, seed, n_req=8, chunk=32768, reps=2):
     }
 
 
-def propose_measure(model, g, ctxs, anchors, W, ws, steps, fwd_ms, K=16):
+def propose_measure(model, g, ctxs, anchors, W, ws, steps, fwd_ms, K=16, retrieve=0):
     """One dspine_draft_propose call per step (the forward, then head scores,
     top-16, the refinement table and the greedy walk), timed over `steps`
     calls; the LM head's score GEMM is timed by its own event pairs.  Its
-    roofline is HBM: the bf16 head is read once per call."""
+    roofline is HBM: the head is read once per call (bf16, or with
+    ``retrieve`` its FP8 copy and row scales, then the retrieval of
+    ``retrieve`` candidates per row and their BF16 rescoring)."""
     import torch
     import block_drafter_amd as bd
     B = len(ctxs)
     pws = model.propose_workspace(B, W, K)
-    o = model.propose(ctxs, anchors, W, K, workspace=ws, propose_workspace=pws)
+    o = model.propose(ctxs, anchors, W, K, workspace=ws, propose_workspace=pws, retrieve=retrieve)
     for _ in range(3):
-        model.propose(ctxs, anchors, W, K, workspace=ws, propose_workspace=pws, outputs=o)
+        model.propose(ctxs, anchors, W, K, workspace=ws, propose_workspace=pws, outputs=o, retrieve=retrieve)
     torch.cuda.synchronize()
     bd.profile_enable(["head", "tail"])
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        model.propose(ctxs, anchors, W, K, workspace=ws, propose_workspace=pws, outputs=o)
+        model.propose(ctxs, anchors, W, K, workspace=ws, propose_workspace=pws, outputs=o, retrieve=retrieve)
     e1.record()
     torch.cuda.synchronize()
     bd.profile_enable([])
@@ -274,19 +276,25 @@ def propose_measure(model, g, ctxs, anchors, W, ws, steps, fwd_ms, K=16):
     tail_ms, _ = bd.profile_read("tail")
     elt = 2 if g.dtype == "bf16" else 4
     M = B * W
-    head_bytes = g.vocab * g.hidden * elt + M * g.hidden * 4 + M * g.vocab * 4
+    if retrieve:
+        head_bytes = g.vocab * g.hidden + 4 * g.vocab + M * g.hidden * 4 + M * g.vocab * 4
+    else:
+        head_bytes = g.vocab * g.hidden * elt + M * g.hidden * 4 + M * g.vocab * 4
     head_avg = head_ms / max(1, head_n)
     achieved = head_bytes / (head_avg * 1e-3) / 1e9
+    how = (f"FP8 row-scaled retrieval of {retrieve} candidates per row, BF16 rescoring" if retrieve
+           else "direct bf16 LM head")
     return {
         "workload": f"one draft forward + proposal tail, B={B}, W={W}, top-{K}, greedy walk, "
-                    f"{g.vocab}-row bf16 LM head",
+                    f"{g.vocab}-row LM head: {how}",
         "ms_per_call": round(ms, 4),
         "proposals_per_s": round(1000.0 / ms, 3),
         "tail_ms": round(ms - fwd_ms, 4),
         "head_ms": round(head_avg, 4),
         "refine_walk_ms": round(tail_ms / steps, 4),
         "roofline": {
-            "kernel": "gemm_stream (LM head scores of every row)",
+            "kernel": ("gemm_stream (FP8 LM head scores of every row)" if retrieve
+                       else "gemm_stream (LM head scores of every row)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -409,6 +417,10 @@ def measure_workload(name, args, with_propose, gate_up_traffic_md=None):
     propose = None
     if with_propose:
         propose = propose_measure(model, g, ctxs, anchors, W, ws, args.steps, fwd_ms)
+        if g.dtype == "bf16":
+            propose["fp8_retrieval"] = propose_measure(model, g, ctxs, anchors, W, ws, args.steps, fwd_ms,
+                                                       retrieve=128)
+            propose["fp8_retrieval"]["roofline"]["traffic"] = None
         propose["roofline"]["traffic"] = None
         if wl.name == "dspine27b_b1":
             from block_drafter_amd import profsum

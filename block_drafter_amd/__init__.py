@@ -75,9 +75,14 @@ MAX_TOPK = 16
 WALK_GREEDY, WALK_SAMPLED = 0, 1
 
 
+MAX_RETRIEVE = 128
+
+
 class Proposal_c(ctypes.Structure):
-    _fields_ = [("topk", ctypes.c_int32), ("walk", ctypes.c_int32), ("temperature", ctypes.c_double),
-                ("uniforms", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("cand", ctypes.c_void_p),
+    _fields_ = [("topk", ctypes.c_int32), ("walk", ctypes.c_int32), ("retrieve", ctypes.c_int32),
+                ("temperature", ctypes.c_double),
+                ("uniforms", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("retrieved", ctypes.c_void_p),
+                ("rescored", ctypes.c_void_p), ("cand", ctypes.c_void_p),
                 ("cand_scores", ctypes.c_void_p), ("table", ctypes.c_void_p),
                 ("choice", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("q", ctypes.c_void_p)]
 
@@ -315,12 +320,16 @@ class Model:
 
     def propose(self, ctxs: Sequence["Context"], anchor_ids: Sequence[int], W: int, topk: int = MAX_TOPK,
                 walk: str = "greedy", temperature: float = 1.0, uniforms=None, keep_scores: bool = False,
-                out=None, workspace=None, propose_workspace=None, stream=None, outputs=None):
+                out=None, workspace=None, propose_workspace=None, stream=None, outputs=None,
+                retrieve: int = 0):
         """One draft forward plus the proposal tail.  Returns a dict of device
         tensors: out [B,W,H], cand/cand_scores [B,W-1,K], table [B,W-1,K,K],
         choice/tokens [B,W-1], q [B,W-1] (float64), scores [B*W,vocab] when
         keep_scores.  ``uniforms``: device float64 [B, W-1] for the sampled
-        walk.  ``outputs`` reuses a dict returned by an earlier call."""
+        walk.  ``retrieve`` = R > 0: FP8 retrieval of R candidates per row,
+        rescored with the BF16 head (``scores`` then holds the FP8 scores,
+        and with keep_scores ``retrieved`` / ``rescored`` [B,W-1,R] are
+        returned too).  ``outputs`` reuses a dict returned by an earlier call."""
         torch = _torch()
         B, K = len(ctxs), int(topk)
         arr = (Ctx_c * B)(*[c.struct for c in ctxs])
@@ -337,9 +346,15 @@ class Model:
         }
         if keep_scores and "scores" not in o:
             o["scores"] = torch.empty((B * W, self.geom.vocab), dtype=torch.float32, device=dev)
+        if keep_scores and retrieve and "retrieved" not in o:
+            o["retrieved"] = torch.empty((B, W - 1, retrieve), dtype=torch.int32, device=dev)
+            o["rescored"] = torch.empty((B, W - 1, retrieve), dtype=torch.float32, device=dev)
         pr = Proposal_c()
         pr.topk = K
         pr.walk = WALK_GREEDY if walk == "greedy" else WALK_SAMPLED
+        pr.retrieve = int(retrieve)
+        pr.retrieved = o["retrieved"].data_ptr() if retrieve and "retrieved" in o else None
+        pr.rescored = o["rescored"].data_ptr() if retrieve and "rescored" in o else None
         pr.temperature = float(temperature)
         pr.uniforms = uniforms.data_ptr() if uniforms is not None else None
         pr.scores = o["scores"].data_ptr() if "scores" in o else None

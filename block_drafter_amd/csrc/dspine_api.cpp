@@ -20,6 +20,8 @@ struct dspine_model {
   dspine_geometry g;
   dspine_weights w;    // as given: projection matrices row-major [out, in]
   dspine_weights pw;   // the same with projection matrices in fragment order
+  const void* head_fp8 = nullptr;        // the LM head's E4M3 codes in fragment order (BF16 models)
+  const float* head_fp8_scale = nullptr; // 256 x its power-of-two row scales
   bool packed = false;
 };
 
@@ -365,6 +367,8 @@ size_t packed_bytes(const dspine_geometry& g, bool head) {
     total += pr.layer ? one * g.n_layers : one;
   }
   if (head) total += align256((size_t)g.vocab * g.hidden * elt_bytes(g));
+  if (head && g.dtype == DSPINE_BF16)          // the head's FP8 copy and its row scales
+    total += align256((size_t)g.vocab * g.hidden) + align256(sizeof(float) * (size_t)g.vocab);
   return total;
 }
 
@@ -549,6 +553,13 @@ int dspine_pack_weights(dspine_model* model, void* dst, size_t dst_bytes, dspine
   if (model->w.lm_head) {
     HIP_TRY(launch_pack(model->w.lm_head, out, g.vocab, g.hidden, g.dtype, s));
     pw.lm_head = out;
+    out += align256((size_t)g.vocab * g.hidden * elt_bytes(g));
+    if (g.dtype == DSPINE_BF16) {
+      float* scale = reinterpret_cast<float*>(out + align256((size_t)g.vocab * g.hidden));
+      HIP_TRY(launch_quant_head_fp8(model->w.lm_head, out, scale, g.vocab, g.hidden, s));
+      model->head_fp8 = out;
+      model->head_fp8_scale = scale;
+    }
   }
   model->pw = pw;
   model->packed = true;
@@ -1326,7 +1337,7 @@ int dspine_draft_forward_noalloc(const dspine_model* model, int B, int W, const 
 // -----------------------------------------------------------------------------
 namespace {
 struct ProposePlan {
-  size_t u, scores, part_v, part_i, codes, Pc, msg, Y, total;
+  size_t u, scores, part_v, part_i, codes, Pc, msg, Y, retr, resc, total;
 };
 ProposePlan make_propose_plan(const dspine_geometry& g, int B, int W, int K) {
   ProposePlan p{};
@@ -1342,8 +1353,11 @@ ProposePlan make_propose_plan(const dspine_geometry& g, int B, int W, int K) {
   };
   p.u = take(4 * (size_t)M * g.hidden);
   p.scores = take(4 * (size_t)M * g.vocab);
-  p.part_v = take(4 * topk_partial_entries((int)Mp, g.vocab));
-  p.part_i = take(4 * topk_partial_entries((int)Mp, g.vocab));
+  const size_t parts = std::max(topk_partial_entries((int)Mp, g.vocab), retrieve_partial_entries((int)Mp, g.vocab));
+  p.part_v = take(4 * parts);
+  p.part_i = take(4 * parts);
+  p.retr = take(4 * (size_t)Mp * kMaxRetrieve);
+  p.resc = take(4 * (size_t)Mp * kMaxRetrieve);
   p.codes = take(eb * Mc * r);
   p.Pc = take(4 * Mc * 2 * a);
   p.msg = take(eb * Mc * a);
@@ -1383,6 +1397,15 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
     return fail(DSPINE_E_ARG, "propose: topk %d not in 1..%d (and <= vocab)", K, DSPINE_MAX_TOPK);
   if (prop->walk != DSPINE_WALK_GREEDY && prop->walk != DSPINE_WALK_SAMPLED)
     return fail(DSPINE_E_ARG, "propose: walk %d", prop->walk);
+  const int R = prop->retrieve;
+  if (R != 0) {
+    if (R < K || R > DSPINE_MAX_RETRIEVE || R > g.vocab)
+      return fail(DSPINE_E_ARG, "propose: retrieve %d not in K = %d..%d (and <= vocab)", R, K, DSPINE_MAX_RETRIEVE);
+    if (g.dtype != DSPINE_BF16)
+      return fail(DSPINE_E_UNSUPPORTED, "propose: the FP8 retrieval needs a BF16 model (its head's FP8 copy)");
+    if ((prop->retrieved && !aligned16(prop->retrieved)) || (prop->rescored && !aligned16(prop->rescored)))
+      return fail(DSPINE_E_ARG, "propose: retrieved or rescored unaligned");
+  }
   if (prop->walk == DSPINE_WALK_SAMPLED) {
     if (!(prop->temperature > 0.0) || !std::isfinite(prop->temperature))
       return fail(DSPINE_E_ARG, "propose: temperature must be finite and > 0");
@@ -1398,6 +1421,7 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
   if (propose_ws_bytes < PP.total)
     return fail(DSPINE_E_WORKSPACE, "propose: propose workspace %zu bytes < %zu needed", propose_ws_bytes, PP.total);
   if ((rc = check_packed(model))) return rc;
+  if (R != 0 && !model->head_fp8) return fail(DSPINE_E_STATE, "propose: the model has no FP8 head copy");
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   char* pws = static_cast<char*>(propose_ws);
@@ -1412,11 +1436,37 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
 
   if ((rc = run_forward(model, B, W, ctx, anchor_ids, out, workspace, stream, u))) return rc;
 
-  // head scores E h of every row (h = the forward's final-normed output)
+  // head scores E h of every row (h = the forward's final-normed output), or
+  // their FP8 approximation s_v (q_v . h)
   GemmParams gp = gemm_base(P, ws, H, M);
-  set_segments(gp, {{model->pw.lm_head, V}});
-  if ((rc = set_scaled_a(gp, g, M, W, out, H, H, SCALE_ONE, nullptr, 0, (float)H, nullptr, ws + P.act_h, stream)))
-    return rc;
+  if (R != 0) {
+    set_segments(gp, {{model->head_fp8, V}});
+    gp.w_fp8 = 1;
+    gp.col_scale = model->head_fp8_scale;
+    // the FP8 GEMM reads fp16 rows (copy prologue): h converted once
+    ScaleParams sp;
+    memset(&sp, 0, sizeof sp);
+    sp.M = M;
+    sp.K = H;
+    sp.W = W;
+    sp.mode = SCALE_ONE;
+    sp.x = out;
+    sp.ldx = H;
+    sp.act = ws + P.act_h;
+    sp.ld_act = H;
+    {
+      ProfScope ps(DSPINE_PROF_HEAD, stream);
+      HIP_TRY(launch_scale_rows(sp, g.dtype, stream));
+    }
+    gp.pro = PRO_COPY;
+    gp.a = ws + P.act_h;
+    gp.lda = H;
+  } else {
+    set_segments(gp, {{model->pw.lm_head, V}});
+    if ((rc = set_scaled_a(gp, g, M, W, out, H, H, SCALE_ONE, nullptr, 0, (float)H, nullptr, ws + P.act_h,
+                           stream)))
+      return rc;
+  }
   gp.epi = EPI_STORE;
   gp.out = scores;
   gp.ldo = V;
@@ -1460,7 +1510,15 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
   pp.choice = prop->choice;
   pp.tokens = prop->tokens;
   pp.q = prop->q;
-  HIP_TRY(launch_topk(pp, stream));
+  if (R != 0) {
+    pp.R = R;
+    pp.retrieved = prop->retrieved ? prop->retrieved : reinterpret_cast<int32_t*>(pws + PP.retr);
+    pp.rescored = prop->rescored ? prop->rescored : reinterpret_cast<float*>(pws + PP.resc);
+    pp.h = out;
+    HIP_TRY(launch_retrieve(pp, stream));
+  } else {
+    HIP_TRY(launch_topk(pp, stream));
+  }
   HIP_TRY(launch_cand_codes(pp, g.dtype, stream));
 
   // [G_p; A] of the candidate codes, then W_l of their messages

@@ -24,6 +24,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 struct bf16_t { uint16_t bits; };
 struct f16_t { uint16_t bits; };
+struct fp8_t { uint8_t bits; };      // OCP FP8 E4M3 code (the row-scaled LM head copy)
 
 // float -> bfloat16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
@@ -77,6 +78,11 @@ template <> struct Elt<f16_t> {
   __device__ static __forceinline__ float gload(gptr<f16_t> p, size_t i) { return f16_bits_to_f32(p[i].bits); }
   __device__ static __forceinline__ void store(f16_t* p, size_t i, float v) { p[i].bits = f32_to_f16_bits(v); }
 };
+template <> struct Elt<fp8_t> {    // (the FP8 head has no gain, bias or codebook operand)
+  static constexpr int kBytes = 1;
+  __device__ static __forceinline__ float load(const fp8_t*, size_t) { return 0.f; }
+  __device__ static __forceinline__ float gload(gptr<fp8_t>, size_t) { return 0.f; }
+};
 template <> struct Elt<bf16_t> {
   static constexpr int kBytes = 2;
   __device__ static __forceinline__ float load(const bf16_t* p, size_t i) {
@@ -117,6 +123,16 @@ template <> struct Frag<f16_t> {
   __device__ __forceinline__ void load(const f16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
   __device__ __forceinline__ void zero() { v = u32x4{0, 0, 0, 0}; }
 };
+// 8 E4M3 codes (8 bytes) of one lane's fragment
+template <> struct Frag<fp8_t> {
+  uint32_t v[2];
+  __device__ __forceinline__ void gload(gptr<fp8_t> p) {
+    const uint64_t q = *(gptr<uint64_t>)(p);
+    v[0] = (uint32_t)q;
+    v[1] = (uint32_t)(q >> 32);
+  }
+  __device__ __forceinline__ void zero() { v[0] = v[1] = 0u; }
+};
 template <> struct ActOf<bf16_t> { using type = f16_t; };
 template <> struct ActOf<float> { using type = float; };
 
@@ -139,10 +155,31 @@ __device__ __forceinline__ int act_swz(int r, int bb) { return (((r >> 1) & 1) <
 __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
   return u32x4{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]), bf16x2_to_f16x2(v[3])};
 }
+// Two E4M3 codes (bytes 0 and 1 of d) -> two fp16 whose values are the codes'
+// values / 256, exactly: the sign moves to bit 15 and the 4 exponent + 3
+// fraction bits to bits 13..7, so exponent field e (bias 7) reads as e with
+// bias 15 (a factor 2^-8) and a subnormal code m (m/8 x 2^-6) as the fp16
+// subnormal m x 2^-17.  The 256 goes into the row scale.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2_div256(uint32_t d) {
+  const uint32_t t = (d & 0xffu) | ((d & 0xff00u) << 8);      // byte 0 -> bits 0..7, byte 1 -> 16..23
+  return ((t << 7) & 0x3f803f80u) | ((t << 8) & 0x80008000u);
+}
+__device__ __forceinline__ u32x4 e4m3x8_to_f16x8_div256(const uint32_t v[2]) {
+  return u32x4{e4m3x2_to_f16x2_div256(v[0]), e4m3x2_to_f16x2_div256(v[0] >> 16),
+               e4m3x2_to_f16x2_div256(v[1]), e4m3x2_to_f16x2_div256(v[1] >> 16)};
+}
+
 // weight fragment in the MFMA operand type
 template <typename TA, typename TW> struct AsOperand;
 template <typename T> struct AsOperand<T, T> {
   __device__ static __forceinline__ Frag<T> cvt(const Frag<T>& w) { return w; }
+};
+template <> struct AsOperand<f16_t, fp8_t> {
+  __device__ static __forceinline__ Frag<f16_t> cvt(const Frag<fp8_t>& w) {
+    Frag<f16_t> r;
+    r.v = e4m3x8_to_f16x8_div256(w.v);
+    return r;
+  }
 };
 template <> struct AsOperand<f16_t, bf16_t> {
   __device__ static __forceinline__ Frag<f16_t> cvt(const Frag<bf16_t>& w) {

@@ -98,6 +98,10 @@ struct GemmParams {
   int32_t ld_act;
   float* stats_out;               // or NULL: [n / 64][stats_out_ld] sums of squares of the stored rows
   int32_t stats_out_ld;
+  // FP8 weights (w_fp8): E4M3 codes in fragment order, read as value / 256;
+  // EPI_STORE multiplies output column n by col_scale[n]
+  int32_t w_fp8;
+  const float* col_scale;
   // EPI_STORE: rows m % W == 0 store code_scale * codebook[anchor[m / W]] instead
   int32_t code_anchor;
   const void* codebook;           // [vocab, N] model dtype

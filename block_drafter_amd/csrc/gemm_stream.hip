@@ -520,6 +520,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
             val = *o + s_scale[m] * acc[nb][mb];
           } else {
             val = acc[nb][mb];
+            if constexpr (sizeof(TW) == 1) {          // FP8 rows: codes read as value / 256
+              const f32x4 cs = *as_global(reinterpret_cast<const f32x4*>(p.col_scale + vb * 16 + nl));
+              val = f32x4{val[0] * cs[0], val[1] * cs[1], val[2] * cs[2], val[3] * cs[3]};
+            }
             if (p.code_anchor && m % p.W == 0) {      // anchor code: sqrt(r) C[anchor]
               const gptr<TW> cb = as_global(reinterpret_cast<const TW*>(p.codebook)) +
                                   (size_t)p.anchor[m / p.W] * p.ldo + vb * 16 + nl;
@@ -830,6 +834,16 @@ template <typename TW, typename TA, int PRO, int EPI>
 static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipStream_t s) {
   const int mt = (p.M + 15) / 16;
   constexpr bool kHalf = Elt<TA>::kBytes == 2;
+  if constexpr (sizeof(TW) == 1 && PRO == PRO_COPY) {
+    // One-byte FP8 weights: 512-K stages (16 fragments of 8 bytes per
+    // lane, as many bytes in flight as 16-bit weights in 256-K stages) with
+    // the activation chunks going global -> LDS directly, so that the
+    // registers hold only weight stages and two workgroups fit on a CU
+    if (p.K % 512 == 0) {
+      if (mt <= 1) return launch_t<TW, TA, 1, 1, 16, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
+      if (mt <= 2) return launch_t<TW, TA, 2, 1, 16, 2, PRO, EPI, true>(p, grid_cap, num_cus, s);
+    }
+  }
   constexpr int NWB1 = EPI == EPI_SWIGLU ? 2 : 1;   // narrow tiles: more of them
   constexpr int PD_SMALL = PRO == PRO_BRIDGE_MSG ? 1 : (NWB1 == 2 ? 2 : 3);
   if (mt <= 1) return launch_t<TW, TA, 1, NWB1, kHalf ? 8 : 4, PD_SMALL, PRO, EPI>(p, grid_cap, num_cus, s);
@@ -846,8 +860,10 @@ static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipS
         if (mt <= 4) return launch_t<TW, TA, 4, 2, 4, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
         // 128 rows: weights move global -> LDS too (a 4-stage ring of 64-K
         // stages, full-line activation blocks); 1.2-1.3x faster than
-        // weights in registers, whose stages the allocator cannot keep
-        return launch_t<TW, TA, 8, 2, 2, 3, PRO, EPI, true, true>(p, grid_cap, num_cus, s);
+        // weights in registers, whose stages the allocator cannot keep.
+        // One-byte FP8 weights keep their (half as large) stages in registers.
+        if constexpr (sizeof(TW) == 2) return launch_t<TW, TA, 8, 2, 2, 3, PRO, EPI, true, true>(p, grid_cap, num_cus, s);
+        else return launch_t<TW, TA, 8, 2, 2, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
       }
     }
     if (mt <= 4) return launch_t<TW, TA, 4, 2, kHalf ? 4 : 2, 1, PRO, EPI>(p, grid_cap, num_cus, s);
@@ -885,6 +901,11 @@ static hipError_t launch_kind(const GemmParams& p, int grid_cap, int num_cus, hi
 
 hipError_t launch_gemm_stream(const GemmParams& p, int dtype, int num_cus, hipStream_t s) {
   const int grid_cap = gemm_stream_grid_cap(num_cus);
+  if (p.w_fp8) {                      // the LM head's FP8 copy: scores of fp16 rows only
+    if (dtype != DT_BF16 || p.epi != EPI_STORE || !p.col_scale || p.code_anchor || p.pro != PRO_COPY)
+      return hipErrorInvalidValue;
+    return launch_mt<fp8_t, f16_t, PRO_COPY, EPI_STORE>(p, grid_cap, num_cus, s);
+  }
   if (p.pro == PRO_GATHER) {          // target features, stored output only
     if (p.epi != EPI_STORE) return hipErrorInvalidValue;
     if (dtype == DT_BF16) return launch_mt<bf16_t, bf16_t, PRO_GATHER, EPI_STORE>(p, grid_cap, num_cus, s);

@@ -449,8 +449,315 @@ __global__ __launch_bounds__(64) void walk_kernel(const ProposeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// FP8 row-scaled retrieval [FLZ, "The last write is refined using discrete
+// candidates": the optimized path scores the vocabulary approximately with a
+// row-scaled FP8 head, keeps 128 candidates, rescores them with the BF16 head
+// and retains 16]
+// ---------------------------------------------------------------------------
+// E4M3 code of x (finite, |x| <= 448), round to nearest, ties to even.  At or
+// above 2^-6 the float's exponent and top 3 fraction bits are the code's
+// (rebiased from 127 to 7) after rounding away the 20 lower bits; below it
+// the code is the number of 2^-9 steps.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a >= 0.015625f) {
+    const uint32_t b = __float_as_uint(a);
+    code = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+  } else {
+    code = (uint32_t)rintf(a * 512.0f);
+  }
+  return sign | code;
+}
+
+// One workgroup per block of 16 head rows: each row's absolute maximum m
+// (16 threads per row), its scale exponent k (2^k the smallest power of two
+// >= m / 448; 0 for a zero row), then the codes of E / 2^k written in the
+// fragment order of the packed projections (lane l of 32-column step ks: row
+// l % 16, columns 32 ks + 8 (l / 16) .. + 8, at byte (blk K/32 + ks) 512 + 8 l).
+__global__ __launch_bounds__(256) void quant_head_fp8_kernel(const bf16_t* head, uint8_t* codes, float* col_scale,
+                                                             int H) {
+  __shared__ int s_k[16];
+  const int blk = blockIdx.x, tid = threadIdx.x;
+  const int r = tid >> 4, j = tid & 15;
+  const gptr<bf16_t> row = as_global(head) + (size_t)(16 * blk + r) * H;
+  float m = 0.f;
+  for (int c = j; c < H / 8; c += 16) {
+    const u32x4 v = gload16((gptr<void>)(row + 8 * c));
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      m = fmaxf(m, fmaxf(fabsf(__uint_as_float(v[d] << 16)), fabsf(__uint_as_float(v[d] & 0xffff0000u))));
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (j == 0) {
+    int k = 0;
+    if (m > 0.f) {
+      int ex = 0;
+      const float mant = frexpf(m / 448.0f, &ex);      // m / 448 = mant 2^ex, mant in [0.5, 1)
+      k = mant == 0.5f ? ex - 1 : ex;
+    }
+    s_k[r] = k;
+    col_scale[16 * blk + r] = ldexpf(1.0f, k + 8);
+  }
+  __syncthreads();
+  const int steps = H / 32;
+  for (int f = tid; f < steps * 64; f += 256) {
+    const int ks = f >> 6, lane = f & 63;
+    const int rr = lane & 15;
+    const int k = s_k[rr];
+    const u32x4 v = gload16((gptr<void>)(as_global(head) + (size_t)(16 * blk + rr) * H + 32 * ks + 8 * (lane >> 4)));
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = e4m3_code(ldexpf(__uint_as_float(v[d] << 16), -k));
+      const uint32_t hi = e4m3_code(ldexpf(__uint_as_float(v[d] & 0xffff0000u), -k));
+      w[d >> 1] |= (lo | (hi << 8)) << (16 * (d & 1));
+    }
+    *reinterpret_cast<uint64_t*>(codes + ((size_t)blk * steps + ks) * 512 + 8 * lane) =
+        (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+  }
+}
+
+// Partial top-R of the FP8 scores: block (c, r) keeps the R best pairs of
+// slice c of proposal row r, in order.  Same threshold selection as
+// topk_partial_kernel with kMaxRetrieve for kMaxTopK and tau taken in one
+// step (the kMaxRetrieve-th best of the 256 per-thread best pairs): at most
+// (kMaxRetrieve - 1) * kVpt + 1 pairs are gathered.
+constexpr int kRGather = kMaxRetrieve * kVpt;
+static_assert((kMaxRetrieve - 1) * kVpt + 1 <= kRGather, "gather buffer below the bound on qualifying pairs");
+__global__ __launch_bounds__(kTopkThreads) void retrieve_partial_kernel(const ProposeParams p) {
+  __shared__ __align__(16) float sv[kRGather + 4];
+  __shared__ __align__(16) int si[kRGather + 4];
+  __shared__ __align__(16) float mv[kTopkThreads];
+  __shared__ __align__(16) int mi[kTopkThreads];
+  __shared__ float tau_v;
+  __shared__ int tau_i, count;
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int lo = c * kSliceValues, hi = min(p.vocab, lo + kSliceValues);
+  const gptr<float> row = as_global(p.scores) + (size_t)score_row(r, p.W) * p.vocab;
+  float x[kVpt];
+#pragma unroll
+  for (int u = 0; u < kVpt; ++u) {
+    const int v = lo + tid + u * kTopkThreads;
+    const float sc = v < hi ? row[v] : -INFINITY;
+    x[u] = sc == sc ? sc : -INFINITY;
+  }
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+#pragma unroll
+  for (int u = 0; u < kVpt; ++u) {
+    const int v = lo + tid + u * kTopkThreads;
+    if (v < hi && ranks_before(x[u], v, bv, bi)) {
+      bv = x[u];
+      bi = v;
+    }
+  }
+  mv[tid] = bv;
+  mi[tid] = bi;
+  if (tid == 0) {
+    count = 0;
+    tau_v = -INFINITY;        // kept when fewer than kMaxRetrieve threads hold a score
+    tau_i = INT_MAX;
+  }
+  __syncthreads();
+  if (bi != INT_MAX && rank_among(bv, bi, mv, mi, kTopkThreads) == kMaxRetrieve - 1) {
+    tau_v = bv;
+    tau_i = bi;
+  }
+  __syncthreads();
+  const float tv = tau_v;
+  const int ti = tau_i;
+#pragma unroll
+  for (int u = 0; u < kVpt; ++u) {
+    const int v = lo + tid + u * kTopkThreads;
+    if (v < hi && !ranks_before(tv, ti, x[u], v)) {
+      const int slot = atomicAdd(&count, 1);
+      if (slot < kRGather) {                            // always (bound above)
+        sv[slot] = x[u];
+        si[slot] = v;
+      }
+    }
+  }
+  __syncthreads();
+  const int n = count;
+  const int n4 = (n + 3) & ~3;
+  const size_t out0 = ((size_t)r * gridDim.x + c) * kMaxRetrieve;
+  if (tid < kMaxRetrieve) {
+    p.part_v[out0 + tid] = -INFINITY;
+    p.part_i[out0 + tid] = INT_MAX;
+  }
+  if (tid < n4 - n) {
+    sv[n + tid] = -INFINITY;
+    si[n + tid] = INT_MAX;
+  }
+  __syncthreads();
+  for (int e = tid; e < n; e += kTopkThreads) {
+    const int rk = rank_among(sv[e], si[e], sv, si, n4);
+    if (rk < kMaxRetrieve) {
+      p.part_v[out0 + rk] = sv[e];
+      p.part_i[out0 + rk] = si[e];
+    }
+  }
+}
+
+// Final top-R of proposal row r from its slice lists (sorted, kMaxRetrieve
+// each).  tau = the kMaxRetrieve-th best of the lists' first J = ceil(R /
+// slices) pairs: those are distinct pairs of the row, so the row's R best all
+// rank at or before tau; every pair at or before tau is gathered and placed by
+// counting.  (With fewer than kMaxRetrieve real pairs among them, tau is
+// (-inf, INT_MAX) and every pair qualifies.)  Ids beyond the real pairs are -1.
+__global__ __launch_bounds__(kTopkThreads) void retrieve_merge_kernel(const ProposeParams p, int slices) {
+  __shared__ __align__(16) float sv[kMaxSlices * kMaxRetrieve];
+  __shared__ __align__(16) int si[kMaxSlices * kMaxRetrieve];
+  __shared__ __align__(16) float gv[kMaxSlices * kMaxRetrieve + 4];
+  __shared__ __align__(16) int gi[kMaxSlices * kMaxRetrieve + 4];
+  __shared__ float tau_v;
+  __shared__ int tau_i, count;
+  const int r = blockIdx.x, n = slices * kMaxRetrieve, tid = threadIdx.x;
+  for (int e = tid; e < n; e += kTopkThreads) {
+    sv[e] = p.part_v[(size_t)r * n + e];
+    si[e] = p.part_i[(size_t)r * n + e];
+  }
+  if (tid == 0) {
+    tau_v = -INFINITY;
+    tau_i = INT_MAX;
+    count = 0;
+  }
+  __syncthreads();
+  // the subset: the first J pairs of every list, compacted into gv/gi
+  const int J = (kMaxRetrieve + slices - 1) / slices;
+  const int ns = J * slices, ns4 = (ns + 3) & ~3;
+  for (int e = tid; e < ns4; e += kTopkThreads) {
+    const bool in = e < ns;
+    gv[e] = in ? sv[(e / J) * kMaxRetrieve + e % J] : -INFINITY;
+    gi[e] = in ? si[(e / J) * kMaxRetrieve + e % J] : INT_MAX;
+  }
+  __syncthreads();
+  for (int e = tid; e < ns; e += kTopkThreads)
+    if (gi[e] != INT_MAX && rank_among(gv[e], gi[e], gv, gi, ns4) == kMaxRetrieve - 1) {
+      tau_v = gv[e];
+      tau_i = gi[e];
+    }
+  __syncthreads();
+  const float tv = tau_v;
+  const int ti = tau_i;
+  for (int e = tid; e < n; e += kTopkThreads) {
+    if (si[e] != INT_MAX && !ranks_before(tv, ti, sv[e], si[e])) {
+      const int slot = atomicAdd(&count, 1);
+      gv[slot] = sv[e];                        // slot < n: at most every pair
+      gi[slot] = si[e];
+    }
+  }
+  __syncthreads();
+  const int m = count, m4 = (m + 3) & ~3;
+  if (tid < m4 - m) {
+    gv[m + tid] = -INFINITY;
+    gi[m + tid] = INT_MAX;
+  }
+  if (tid < p.R) p.retrieved[(size_t)r * p.R + tid] = -1;
+  __syncthreads();
+  for (int e = tid; e < m; e += kTopkThreads) {
+    const int rk = rank_among(gv[e], gi[e], gv, gi, m4);
+    if (rk < p.R) p.retrieved[(size_t)r * p.R + rk] = gi[e];
+  }
+}
+
+// BF16 rescoring: grid (R / 16, rows); wave w scores candidates 16 x + 4 w ..
+// + 3 of proposal row r: E_v . h with h the forward's final-normed row (in
+// LDS), each lane's 8-column pieces summed in order, then a wave sum.
+// Empty retrieval slots (-1) score -inf.
+__global__ __launch_bounds__(256) void rescore_kernel(const ProposeParams p) {
+  __shared__ __align__(16) float h[kMaxHidden];
+  const int r = blockIdx.y, H = p.H;
+  const float* hr = p.h + (size_t)score_row(r, p.W) * H;
+  for (int k = threadIdx.x; k < H; k += 256) h[k] = hr[k];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i0 = blockIdx.x * 16 + 4 * w;
+  int id[4];
+  gptr<bf16_t> e[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = i0 + j;
+    id[j] = i < p.R ? p.retrieved[(size_t)r * p.R + i] : -1;
+    e[j] = as_global(reinterpret_cast<const bf16_t*>(p.head)) + (size_t)clamp_token(id[j], p.vocab) * H;
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int ch = lane; ch < H / 8; ch += 64) {
+    u32x4 f[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = gload16((gptr<void>)(e[j] + 8 * ch));
+    const f32x4 h0 = *reinterpret_cast<const f32x4*>(&h[8 * ch]);
+    const f32x4 h1 = *reinterpret_cast<const f32x4*>(&h[8 * ch + 4]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float hl = d < 2 ? h0[2 * d] : h1[2 * d - 4];
+        const float hh = d < 2 ? h0[2 * d + 1] : h1[2 * d - 3];
+        s += __uint_as_float(f[j][d] << 16) * hl;
+        s += __uint_as_float(f[j][d] & 0xffff0000u) * hh;
+      }
+      acc[j] += s;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float sc = wave_sum(acc[j]);
+    const int i = i0 + j;
+    if (lane == 0 && i < p.R) p.rescored[(size_t)r * p.R + i] = id[j] < 0 ? -INFINITY : sc;
+  }
+}
+
+// The K best rescored candidates of proposal row r, best first (equal scores:
+// the smaller token first; NaN ranks last); slots no candidate fills get -1.
+__global__ __launch_bounds__(kMaxRetrieve) void retrieve_keep_kernel(const ProposeParams p) {
+  __shared__ __align__(16) float v[kMaxRetrieve];
+  __shared__ __align__(16) int id[kMaxRetrieve];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int t = tid < p.R ? p.retrieved[(size_t)r * p.R + tid] : -1;
+  const float x = tid < p.R ? p.rescored[(size_t)r * p.R + tid] : -INFINITY;
+  v[tid] = (t < 0 || x != x) ? -INFINITY : x;
+  id[tid] = t < 0 ? INT_MAX : t;
+  if (tid < p.K) {
+    p.cand[(size_t)r * p.K + tid] = -1;
+    p.cand_scores[(size_t)r * p.K + tid] = -INFINITY;
+  }
+  __syncthreads();
+  if (id[tid] != INT_MAX) {
+    const int rk = rank_among(v[tid], id[tid], v, id, kMaxRetrieve);
+    if (rk < p.K) {
+      p.cand[(size_t)r * p.K + rk] = id[tid];
+      p.cand_scores[(size_t)r * p.K + rk] = v[tid];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_quant_head_fp8(const void* head, void* codes, float* col_scale, int V, int H, hipStream_t s) {
+  if (V % 16 || H % 32) return hipErrorInvalidValue;
+  DSPINE_LAUNCH(quant_head_fp8_kernel, dim3(V / 16), dim3(256), 0, s, static_cast<const bf16_t*>(head),
+                static_cast<uint8_t*>(codes), col_scale, H);
+  return hipGetLastError();
+}
+size_t retrieve_partial_entries(int rows, int vocab) {
+  return (size_t)rows * ((vocab + kSliceValues - 1) / kSliceValues) * kMaxRetrieve;
+}
+hipError_t launch_retrieve(const ProposeParams& p, hipStream_t s) {
+  const int rows = p.B * (p.W - 1), slices = (p.vocab + kSliceValues - 1) / kSliceValues;
+  if (slices > kMaxSlices || p.R < p.K || p.R > kMaxRetrieve || p.H > kMaxHidden || p.H % 8)
+    return hipErrorInvalidValue;
+  DSPINE_LAUNCH(retrieve_partial_kernel, dim3(slices, rows), dim3(kTopkThreads), 0, s, p);
+  DSPINE_LAUNCH(retrieve_merge_kernel, dim3(rows), dim3(kTopkThreads), 0, s, p, slices);
+  DSPINE_LAUNCH(rescore_kernel, dim3((p.R + 15) / 16, rows), dim3(256), 0, s, p);
+  DSPINE_LAUNCH(retrieve_keep_kernel, dim3(rows), dim3(kMaxRetrieve), 0, s, p);
+  return hipGetLastError();
+}
 int topk_slices(int vocab) { return (vocab + kSliceValues - 1) / kSliceValues; }
 hipError_t launch_topk(const ProposeParams& p, hipStream_t s) {
   const int rows = p.B * (p.W - 1), slices = topk_slices(p.vocab);

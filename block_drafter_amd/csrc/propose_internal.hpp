@@ -33,6 +33,12 @@ struct ProposeParams {
   int32_t* choice;                // [B, W-1]
   int32_t* tokens;                // [B, W-1]
   double* q;                      // [B, W-1] or NULL
+  // FP8 row-scaled retrieval (R > 0): the R best of the FP8 scores (in
+  // `scores`), rescored with the BF16 head, the best K kept
+  int32_t R;
+  int32_t* retrieved;             // [B*(W-1), R] ids, best FP8 score first
+  float* rescored;                // [B*(W-1), R] their BF16 head scores
+  const float* h;                 // [B*W, H] the forward's final-normed output
 };
 hipError_t launch_topk(const ProposeParams& p, hipStream_t s);
 size_t topk_partial_entries(int rows, int vocab);
@@ -42,5 +48,15 @@ hipError_t launch_cand_codes(const ProposeParams& p, int dtype, hipStream_t s);
 hipError_t launch_cand_msg(const ProposeParams& p, int dtype, hipStream_t s);
 hipError_t launch_cand_score(const ProposeParams& p, int dtype, hipStream_t s);
 hipError_t launch_walk(const ProposeParams& p, hipStream_t s);
+
+// FP8 retrieval: candidates kept by the FP8 scores of one row (at most)
+constexpr int kMaxRetrieve = DSPINE_MAX_RETRIEVE;
+hipError_t launch_retrieve(const ProposeParams& p, hipStream_t s);
+size_t retrieve_partial_entries(int rows, int vocab);
+// Row-scaled FP8 copy of a bf16 head [V, H] (V a multiple of 16): E4M3 codes
+// in the fragment order of the packed projections (one byte per element) and
+// col_scale[v] = 256 s_v, s_v the smallest power of two with max|E_v| / s_v
+// <= 448 (256: the GEMM reads each code as its value / 256).
+hipError_t launch_quant_head_fp8(const void* head, void* codes, float* col_scale, int V, int H, hipStream_t s);
 
 }  // namespace dspine

@@ -182,8 +182,12 @@ void dspine_model_destroy(dspine_model* model);
  * (device, 256-byte aligned, dspine_packed_bytes bytes, caller-owned) with
  * kernels on `stream`; from then on the model reads projections only from
  * `dst`, which must outlive the model (the row-major matrices may be freed
- * once those kernels have run).  Every other call returns DSPINE_E_STATE
- * until the model is packed.  Errors: E_ARG, E_WORKSPACE (dst too small).
+ * once those kernels have run).  With an lm_head on a BF16 model, `dst` also
+ * receives the head's row-scaled FP8 copy for the retrieval of
+ * dspine_draft_propose (one E4M3 code per element in the same fragment order,
+ * and a float32 scale per row: vocab * (hidden + 4) bytes more).  Every other
+ * call returns DSPINE_E_STATE until the model is packed.  Errors: E_ARG,
+ * E_WORKSPACE (dst too small).
  */
 size_t dspine_packed_bytes(const dspine_model* model);
 int dspine_pack_weights(dspine_model* model, void* dst, size_t dst_bytes, dspine_stream_t stream);
@@ -291,6 +295,12 @@ int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x,
  *   - candidates: the K best tokens of the shared LM head's scores E_v . h_t
  *     of every proposal row t = 1..W-1 (h = the forward's final-normed
  *     state), best first, equal scores by smaller token id (direct BF16 path);
+ *     or, with retrieve = R > 0 (BF16 models), by FP8 row-scaled retrieval:
+ *     the vocabulary is scored with the head's FP8 copy, s_v (q_v . h_t), the
+ *     R best of those (same order rule) are rescored with the BF16 head and
+ *     the K best rescored kept.  The FP8 copy (made by dspine_pack_weights):
+ *     q_v = E4M3 codes (OCP, round to nearest even) of E_v / s_v, s_v the
+ *     smallest power of two with max_k |E_v[k]| / s_v <= 448;
  *   - transition table T_t[i, j]: the last layer's bridge write is redone
  *     from its pre-write state u_t with the predecessor code replaced by
  *     sqrt(r) C[s], s = candidate i of row t-1 (the anchor for t = 1, so the
@@ -303,20 +313,27 @@ int dspine_bridge(const dspine_model* model, int layer, int B, int W, float* x,
  *     rounding leaves u above the total); q = p[j] is kept.
  */
 #define DSPINE_MAX_TOPK 16
+#define DSPINE_MAX_RETRIEVE 128
 #define DSPINE_WALK_GREEDY 0
 #define DSPINE_WALK_SAMPLED 1
 
 typedef struct {
     int32_t topk;              /* K, 1..DSPINE_MAX_TOPK */
     int32_t walk;              /* DSPINE_WALK_GREEDY or DSPINE_WALK_SAMPLED */
+    int32_t retrieve;          /* 0: direct BF16 head scores; R in K..DSPINE_MAX_RETRIEVE (and <=
+                                  vocab): FP8 retrieval of R candidates per row, BF16 rescoring */
     double temperature;        /* sampled walk: > 0 */
     const double* uniforms;    /* sampled walk: device float64 [B, W-1], each in [0, 1) */
     /* outputs, device */
     float* scores;             /* optional (NULL: kept in the workspace): float32 [B*W, vocab]
-                                  head scores of every row (anchor rows included) */
+                                  head scores of every row (anchor rows included); the FP8
+                                  scores when retrieve > 0 */
+    int32_t* retrieved;        /* optional, retrieve > 0: int32 [B, W-1, R] the retrieved ids,
+                                  best FP8 score first (-1 beyond the finite scores) */
+    float* rescored;           /* optional, retrieve > 0: float32 [B, W-1, R] their BF16 scores */
     int32_t* cand;             /* int32 [B, W-1, K] candidate token ids of rows 1..W-1 (-1 in
                                   slots beyond the number of finite scores; NaN ranks as -inf) */
-    float* cand_scores;        /* float32 [B, W-1, K] their head scores */
+    float* cand_scores;        /* float32 [B, W-1, K] their BF16 head scores */
     float* table;              /* float32 [B, W-1, K, K]: entry [b, t-1, i, j] = T_t[i, j] */
     int32_t* choice;           /* int32 [B, W-1] chosen candidate index of each row */
     int32_t* tokens;           /* int32 [B, W-1] chosen token ids */
@@ -334,9 +351,10 @@ size_t dspine_propose_workspace_bytes(const dspine_model* model, int max_batch, 
  * One draft forward (exactly dspine_draft_forward: same arguments, same
  * `out`) followed by the proposal tail above.  Needs a bridge (code_dim > 0)
  * and lm_head.  `workspace` is the forward's; `propose_ws` the tail's.
- * Errors: those of dspine_draft_forward, E_ARG (NULL output, K or walk out
- * of range, temperature <= 0, uniforms or q NULL for the sampled walk),
- * E_UNSUPPORTED (no bridge or no lm_head), E_WORKSPACE.
+ * Errors: those of dspine_draft_forward, E_ARG (NULL output, K, R or walk
+ * out of range, temperature <= 0, uniforms or q NULL for the sampled walk),
+ * E_UNSUPPORTED (no bridge or no lm_head; retrieval on a float32 model),
+ * E_WORKSPACE.
  */
 int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_ctx* ctx,
                          const int32_t* anchor_ids, float* out, const dspine_proposal* prop,

@@ -590,14 +590,22 @@ def quantize_head_fp8(lm_head: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     max_k |E_v[k]| / s_v <= 448 (1 for an all-zero row), and its codes are
     E_v / s_v rounded to E4M3, ties to even.  Dividing by a power of two is
     exact, so each code is one rounding of the BF16 value.  Returns the codes
-    (as float64 values) [V, H] and the scales [V]."""
-    E = widen(lm_head)
-    m = np.max(np.abs(E), axis=1)
-    s = np.ones_like(m)
-    nz = m > 0
-    mant, ex = np.frexp(m[nz] / FP8_E4M3_MAX)        # m / 448 = mant * 2^ex
-    s[nz] = np.where(mant == 0.5, np.ldexp(1.0, ex - 1), np.ldexp(1.0, ex))
-    return round_fp8_e4m3(E / s[:, None]), s
+    [V, H] (float32, which holds every E4M3 value exactly) and the scales [V]
+    (float64).  Rows are processed in slices (bounds memory only)."""
+    V = lm_head.shape[0]
+    codes = np.empty(lm_head.shape, dtype=np.float32)
+    s = np.ones(V)
+    for v0 in range(0, V, HEAD_SLICE):
+        v1 = min(V, v0 + HEAD_SLICE)
+        E = widen(lm_head[v0:v1])
+        m = np.max(np.abs(E), axis=1)
+        nz = m > 0
+        mant, ex = np.frexp(m[nz] / FP8_E4M3_MAX)    # m / 448 = mant * 2^ex
+        sv = np.ones_like(m)
+        sv[nz] = np.where(mant == 0.5, np.ldexp(1.0, ex - 1), np.ldexp(1.0, ex))
+        s[v0:v1] = sv
+        codes[v0:v1] = round_fp8_e4m3(E / sv[:, None])
+    return codes, s
 
 
 def head_scores_fp8(codes: np.ndarray, scales: np.ndarray, h: np.ndarray) -> np.ndarray:
@@ -608,7 +616,7 @@ def head_scores_fp8(codes: np.ndarray, scales: np.ndarray, h: np.ndarray) -> np.
     out = np.empty((h.shape[0], V))
     for v0 in range(0, V, HEAD_SLICE):
         v1 = min(V, v0 + HEAD_SLICE)
-        out[:, v0:v1] = (h @ codes[v0:v1].T) * scales[None, v0:v1]
+        out[:, v0:v1] = (h @ codes[v0:v1].astype(np.float64).T) * scales[None, v0:v1]
     return out
 
 

@@ -278,7 +278,8 @@ def test_propose_rejections_before_any_launch(L):
     h = ctypes.c_void_p()
     assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == 0
     head_bytes = g.vocab * g.hidden * 2
-    assert L.dspine_packed_bytes(h) == head_bytes + sum(
+    fp8_bytes = g.vocab * g.hidden + 4 * g.vocab          # the FP8 copy and its row scales
+    assert L.dspine_packed_bytes(h) == head_bytes + fp8_bytes + sum(
         int(np.prod(synth.weight_shape(g, n))) * 2
         for n in synth.weight_names(g) if n.split(".")[-1] in bd._PROJECTIONS)
     need = L.dspine_propose_workspace_bytes(h, 8, 16, 16)
@@ -304,11 +305,39 @@ def test_propose_rejections_before_any_launch(L):
     p = good_proposal()
     p.table = None
     assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG
+    # FP8 retrieval: R in K..128
+    for R in (8, 129, -1):
+        p = good_proposal()
+        p.retrieve = R
+        assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG, R
+    p = good_proposal()
+    p.retrieve = 128
+    p.retrieved = FAKE + 4
+    assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_ARG
     assert call_propose(L, h, 1, 16, [c], [5], good_proposal(), pws_bytes=1024) == bd.E_WORKSPACE
     assert call_propose(L, h, 1, 16, [c], [g.vocab], good_proposal()) == bd.E_ARG
     assert call_propose(L, h, 1, 17, [c], [5], good_proposal()) == bd.E_UNSUPPORTED
     # valid arguments: the model is not packed yet
     assert call_propose(L, h, 1, 16, [c], [5], good_proposal()) == bd.E_STATE
+    p = good_proposal()
+    p.retrieve = 128
+    assert call_propose(L, h, 1, 16, [c], [5], p) == bd.E_STATE
+    L.dspine_model_destroy(h)
+
+    g = synth.G_TINY                               # float32: no FP8 copy of the head
+    ws = fake_weights(g)
+    ws.lm_head = FAKE + 0x100000
+    gs = bd.geometry_struct(g)
+    h = ctypes.c_void_p()
+    assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == 0
+    assert L.dspine_packed_bytes(h) == g.vocab * g.hidden * 4 + sum(
+        int(np.prod(synth.weight_shape(g, n))) * 4
+        for n in synth.weight_names(g) if n.split(".")[-1] in bd._PROJECTIONS)
+    p = good_proposal()
+    p.retrieve = 128
+    cf = fake_ctx(g, 100, full_cap=200)
+    assert call_propose(L, h, 1, 16, [cf], [5], p) == bd.E_UNSUPPORTED
+    assert b"BF16" in L.dspine_last_error()
     L.dspine_model_destroy(h)
 
     g = synth.G_35B_DFLASH                         # no bridge to refine

@@ -40,11 +40,11 @@ def say(msg):
     print(f"[propose] {msg}", flush=True)
 
 
-def gpu_propose(model, ctxs, anchors, W, K, walk, temperature, uniforms):
+def gpu_propose(model, ctxs, anchors, W, K, walk, temperature, uniforms, retrieve=0):
     import torch
     u = torch.from_numpy(uniforms).cuda() if uniforms is not None else None
     res = model.propose(ctxs, anchors, W, K, walk=walk, temperature=temperature, uniforms=u,
-                        keep_scores=True)
+                        keep_scores=True, retrieve=retrieve)
     torch.cuda.synchronize()
     out = {k: v.cpu().numpy() for k, v in res.items()}
     out["out"] = out["out"].astype(np.float64)
@@ -92,6 +92,110 @@ def check_proposal(g, wts, head, gp, octxs, anchors, W, K, walk, temperature, un
             got = orc["scores"][i][t][gp["cand"][b, t]]
             assert np.max(np.abs(got - best)) <= 2 * e + 1e-12, f"{label} request {b} row {t + 1}: ranks"
     return orc
+
+
+def check_walk_on_gpu_table(gp, W, walk, temperature, uniforms, label):
+    B = gp["cand"].shape[0]
+    for b in range(B):
+        T = gp["table"][b].astype(np.float64)
+        if walk == "greedy":
+            ch = O.greedy_walk(T)
+        else:
+            ch, q = O.sampled_walk(T, temperature, uniforms[b])
+            assert np.max(np.abs(gp["q"][b] - q)) <= 1e-12, f"{label} request {b}: q"
+        assert np.array_equal(gp["choice"][b], ch), f"{label} request {b}: walk"
+        assert np.array_equal(gp["tokens"][b], gp["cand"][b, np.arange(W - 1), ch])
+
+
+def check_retrieval(g, wts, head, fp8, gp, octxs, anchors, W, K, R, walk, temperature, uniforms, label,
+                    requests=None):
+    """FP8 retrieval on the GPU against the oracle.  Decisions are checked
+    on the GPU's own numbers, bit for bit: the R retrieved are the oracle's
+    top-R of the GPU's FP8 scores, and the K kept are the oracle's order of
+    the GPU's rescored values.  The FP8 scores themselves equal the oracle's
+    FP8 head applied to the GPU's fp16 operand rows up to fp32 summation
+    (2e-5 of rms: a single code differing from the oracle's would move a
+    score by about 1e-3 of rms), and the rescoring equals E . h on the
+    GPU's fp32 rows to 1e-5.  The table, the walk and the forward follow
+    check_proposal's rules."""
+    codes, scales = fp8
+    B = gp["cand"].shape[0]
+    req = list(range(B)) if requests is None else list(requests)
+    V = g.vocab
+    approx = gp["scores"].reshape(B, W, V).astype(np.float64)
+    h = gp["out"]
+    h16 = h.astype(np.float16).astype(np.float64)
+    for b in range(B):
+        ref = O.head_scores_fp8(codes, scales, h16[b, 1:])
+        e = rel_err(approx[b, 1:], ref)
+        assert e <= 2e-5, f"{label} request {b}: FP8 scores {e:.2e}"
+        for t in range(W - 1):
+            ids = gp["retrieved"][b, t]
+            assert np.array_equal(ids, O.top_k(approx[b, t + 1], R)), f"{label} request {b} row {t + 1}: retrieval"
+            resc = gp["rescored"][b, t].astype(np.float64)
+            ex = O.head_scores(head, h[b, t + 1], ids)[0]
+            assert np.max(np.abs(resc - ex)) <= 1e-5 * np.sqrt(np.mean(ex * ex)), f"{label}: rescoring"
+            keep = np.lexsort((ids, -resc))[:K]
+            assert np.array_equal(gp["cand"][b, t], ids[keep]), f"{label} request {b} row {t + 1}: kept"
+            assert np.array_equal(gp["cand_scores"][b, t].astype(np.float64), resc[keep])
+    check_walk_on_gpu_table(gp, W, walk, temperature, uniforms, label)
+    orc = O.propose(g, wts, head, octxs, [anchors[b] for b in req], W, K, walk, temperature,
+                    None if uniforms is None else uniforms[req], cand_override=gp["cand"][req],
+                    retrieve=R, fp8_head=fp8)
+    tol = tol_for(g)
+    for i, b in enumerate(req):
+        e_out = rel_err(gp["out"][b], orc["out"][i])
+        e_sc = rel_err(approx[b, 1:], orc["scores"][i])
+        e_tab = rel_err(gp["table"][b].astype(np.float64), orc["table"][i])
+        e_cs = rel_err(gp["cand_scores"][b].astype(np.float64), orc["cand_scores"][i])
+        say(f"{label} request {b}: out {e_out:.2e} fp8 scores {e_sc:.2e} kept scores {e_cs:.2e} table {e_tab:.2e}")
+        assert e_out <= tol and e_sc <= tol and e_tab <= tol and e_cs <= tol, label
+        # near-best in the oracle's arithmetic: the oracle's own retrieval on
+        # its own rows keeps K tokens whose BF16 scores match the GPU's
+        # picks rank by rank, within twice the largest score difference.
+        # (Only with R well above K: with R close to K the retrieval boundary
+        # itself decides, where the two sides' FP8 scores legitimately
+        # differ by the forward's tolerance.)
+        if R < 4 * K:
+            continue
+        for t in range(W - 1):
+            ids_o, ex_o, keep_o, kept_o = O.retrieve_and_rescore(orc["scores"][i][t], head, orc["out"][i][t + 1], R, K)
+            union = np.union1d(ids_o, gp["retrieved"][b, t])
+            d = np.max(np.abs(O.head_scores(head, orc["out"][i][t + 1], union)[0] -
+                              O.head_scores(head, h[b, t + 1], union)[0]))
+            got = O.head_scores(head, orc["out"][i][t + 1], gp["cand"][b, t])[0]
+            assert np.max(np.abs(np.sort(got)[::-1] - kept_o)) <= 2 * d + 1e-12, f"{label} request {b} row {t + 1}"
+    return orc
+
+
+@pytest.mark.parametrize("which,walk,R", [("A", "sampled", 128), ("T", "greedy", 128), ("T-R16", "sampled", 16),
+                                          ("A-B8", "greedy", 128)])
+def test_propose_fp8_retrieval_small(which, walk, R):
+    """FP8 row-scaled retrieval: one slice (vocab 512) and several slices
+    with the refinement's tile path (vocab 2048), R = K, and 128 rows (the
+    FP8 GEMM's large-block path)."""
+    import block_drafter_amd as bd
+    if which == "A":
+        case, K = Case(G_A, 171, 3, 9, (40, 7, 25)), 5
+    elif which == "A-B8":
+        case, K = Case(G_A, 176, 8, 16, (5, 60, 33, 18, 70, 2, 44, 29)), 16
+    elif which == "T-R16":
+        case, K = Case(G_T, 173, 2, 16, (21, 50)), 16
+    else:
+        case, K = Case(G_T, 172, 3, 16, (50, 33, 9)), 16
+    g = case.g
+    wts = synth.make_weights(g, case.seed)
+    head = synth.make_lm_head(g, case.seed)
+    model = bd.Model.from_numpy(g, wts, lm_head=head)
+    run = Run(case, model=model, wts=wts)
+    uni = synth.make_uniforms(case.seed, case.B, case.W - 1) if walk == "sampled" else None
+    say(f"fp8 {which} {walk}: B={case.B} W={case.W} K={K} R={R}")
+    gp = gpu_propose(model, run.ctxs, run.anchors, case.W, K, walk, 0.7, uni, retrieve=R)
+    check_retrieval(g, wts, head, O.quantize_head_fp8(head), gp, [run.oracle_ctx(b) for b in range(case.B)],
+                    run.anchors, case.W, K, R, walk, 0.7, uni, which)
+    # the forward inside the call is the forward, and the direct path is unchanged
+    assert np.array_equal(run.gpu_forward(), gp["out"])
+    model.close()
 
 
 @pytest.mark.parametrize("which,walk", [("tiny_fp32", "greedy"), ("A", "sampled"), ("T", "greedy"),
@@ -182,8 +286,16 @@ def test_propose_full_size(name, walk, requests):
     gp = gpu_propose(model, ctxs, anchors, wl.W, 16, walk, 1.0, uni)
     req = list(range(wl.B)) if requests is None else list(requests)
     say(f"{name}: oracle on requests {req}")
-    check_proposal(g, wts, head, gp, [gpu_ring_context(g, ctxs[b], wl.frontiers[b]) for b in req],
-                   anchors, wl.W, 16, walk, 1.0, uni, name, requests=req)
+    octxs = [gpu_ring_context(g, ctxs[b], wl.frontiers[b]) for b in req]
+    check_proposal(g, wts, head, gp, octxs, anchors, wl.W, 16, walk, 1.0, uni, name, requests=req)
+    # the same call with FP8 row-scaled retrieval of 128 candidates per row
+    say(f"{name}: propose with FP8 retrieval ({walk})")
+    gp8 = gpu_propose(model, ctxs, anchors, wl.W, 16, walk, 1.0, uni, retrieve=128)
+    assert np.array_equal(gp8["out"], gp["out"])
+    say(f"{name}: oracle FP8 head")
+    fp8 = O.quantize_head_fp8(head)
+    check_retrieval(g, wts, head, fp8, gp8, octxs, anchors, wl.W, 16, 128, walk, 1.0, uni, name + " fp8",
+                    requests=req)
     model.close()
     del model
     torch.cuda.empty_cache()

@@ -99,12 +99,13 @@ MUTATIONS = {
     "fp8 subnormal step halved": (
         "e = np.maximum(ex - 1, -6)", "e = np.maximum(ex - 1, -7)"),
     "fp8 scale one power of two too small": (
-        "s[nz] = np.where(mant == 0.5, np.ldexp(1.0, ex - 1), np.ldexp(1.0, ex))",
-        "s[nz] = np.ldexp(1.0, ex - 1)"),
+        "sv[nz] = np.where(mant == 0.5, np.ldexp(1.0, ex - 1), np.ldexp(1.0, ex))",
+        "sv[nz] = np.ldexp(1.0, ex - 1)"),
     "fp8 scale from the wrong maximum": (
         "mant, ex = np.frexp(m[nz] / FP8_E4M3_MAX)", "mant, ex = np.frexp(m[nz] / 240.0)"),
     "fp8 scores drop the row scale": (
-        "out[:, v0:v1] = (h @ codes[v0:v1].T) * scales[None, v0:v1]", "out[:, v0:v1] = h @ codes[v0:v1].T"),
+        "out[:, v0:v1] = (h @ codes[v0:v1].astype(np.float64).T) * scales[None, v0:v1]",
+        "out[:, v0:v1] = h @ codes[v0:v1].astype(np.float64).T"),
     "retrieval keeps the fp8 order": (
         "keep = np.lexsort((ids, -exact))[:K]", "keep = np.arange(K)"),
     "rescoring ties prefer the larger id": (
