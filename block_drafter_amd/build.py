@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdspine.so")
 SOURCES = ["dspine_api.cpp", "gemm_stream.hip", "gemm_tile.hip", "attention.hip", "rowops.hip", "propose.hip",
-           "conv.hip"]
+           "conv.hip", "bridge.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -154,6 +154,9 @@ int64_t live_lo(int S, int64_t F) { return S == 0 ? 0 : std::max<int64_t>(0, F -
 // ---------------------------------------------------------------------------
 struct Plan {
   size_t gemm_cnt;                        // u32 tile counters
+  size_t bridge_sync;                     // u32 hand-off counters of the fused bridge
+  size_t counters_end;                    // every counter lies below this offset
+  size_t ssz;                             // fused bridge: sums of squares of z per 16 columns
   size_t gemm_part, attn_part;            // f32 partials
   size_t x, act_q, act_f, qkv, z, P, P2, rope;
   size_t act_h, act_r, act_m;             // pre-scaled operands (large blocks)
@@ -185,6 +188,8 @@ Plan make_plan(const dspine_geometry& g, int64_t B, int64_t W, int64_t rows) {
     return o;
   };
   p.gemm_cnt = take(sizeof(uint32_t) * kMaxTiles);
+  p.bridge_sync = take(sizeof(uint32_t) * kBridgeSyncWords);
+  p.counters_end = off;
   p.gemm_part_floats = gemm_stream_partial_floats(gemm_rows);
   p.gemm_part = take(sizeof(float) * p.gemm_part_floats);
   p.attn_part = take(sizeof(float) * attn_partial_floats((int)std::max<int64_t>(B, 1), g.n_q_heads, g.head_dim));
@@ -204,6 +209,7 @@ Plan make_plan(const dspine_geometry& g, int64_t B, int64_t W, int64_t rows) {
   p.st1 = take(4 * (size_t)kMaxRows * stat_tiles(g.hidden));
   p.stz = take(4 * (size_t)kMaxRows * stat_tiles(r));
   p.stc = take(4 * (size_t)kMaxRows * stat_tiles(g.hidden));
+  p.ssz = take(4 * (size_t)kMaxRows * (r / 16 + 1));
   const size_t cg = g.conv_group > 0 ? (size_t)g.hidden / g.conv_group : 0;
   p.conv_da = take(4 * Mp * 4 * cg);
   p.conv_dm = take(4 * Mp * 4 * cg);
@@ -829,6 +835,39 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
   const dspine_geometry& g = m.g;
   const dspine_weights& wt = m.w;
   const int M = B * W, H = g.hidden, r = g.code_dim, a = g.msg_dim;
+  if (!pred_codes && g.dtype == DSPINE_BF16 && bridge_fused_fits(H, r, a, M, cus)) {
+    // blocks of up to 32 rows: the whole bridge in one launch
+    BridgeParams bp;
+    memset(&bp, 0, sizeof bp);
+    bp.M = M;
+    bp.W = W;
+    bp.H = H;
+    bp.r = r;
+    bp.a = a;
+    bp.eps = g.eps;
+    bp.code_scale = sqrtf((float)r);
+    bp.x = x;
+    bp.xst = xst;
+    bp.xst_lists = xst_tiles;
+    bp.st_out = st_out;
+    bp.ld = kMaxRows;
+    bp.R = m.pw.layer[layer].R;
+    bp.G = m.pw.bridge_G;
+    bp.Gp = m.pw.bridge_Gp;
+    bp.A = m.pw.bridge_A;
+    bp.Wl = m.pw.layer[layer].W_l;
+    bp.bias = wt.bridge_b;
+    bp.codebook = wt.codebook;
+    for (int b = 0; b < B; ++b) bp.anchor[b] = anchor_ids[b];
+    bp.zpart = reinterpret_cast<float*>(ws + P.gemm_part);
+    bp.z = ws + P.act_r;
+    bp.ssz = reinterpret_cast<float*>(ws + P.ssz);
+    bp.P = reinterpret_cast<float*>(ws + P.P);
+    bp.msg = ws + P.act_m;
+    bp.sync = reinterpret_cast<uint32_t*>(ws + P.bridge_sync);
+    HIP_TRY(launch_bridge_fused(bp, stream));
+    return DSPINE_OK;
+  }
   float* z = reinterpret_cast<float*>(ws + P.z);
   float* stz = reinterpret_cast<float*>(ws + P.stz);
   float* Pb = reinterpret_cast<float*>(ws + P.P);
@@ -1296,9 +1335,17 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
+// 32-bit words at the start of every workspace plan that hold counters
+size_t counter_words() {
+  dspine_geometry g0;
+  memset(&g0, 0, sizeof g0);
+  return make_plan(g0, 1, 2, 0).counters_end / sizeof(uint32_t);
+}
+
 // Device address of the current device's copy of `scratch`.  The first call
-// on a device looks it up and clears the stream-K tile counters (at the start
-// of every plan) on `stream`; every forward leaves them at zero again.
+// on a device looks it up and clears the counters (stream-K tiles, fused
+// bridge hand-offs; at the start of every plan) on `stream`; every forward
+// leaves them at zero again.
 int scratch_for_current_device(hipStream_t stream, void** out) {
   int dev = -1;
   HIP_TRY(hipGetDevice(&dev));
@@ -1308,7 +1355,7 @@ int scratch_for_current_device(hipStream_t stream, void** out) {
     void* p = nullptr;
     HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
     if (!p || ((uintptr_t)p & 255u)) return fail(DSPINE_E_HIP, "static scratch: bad device address");
-    HIP_TRY(launch_zero_words(p, kMaxTiles, stream));
+    HIP_TRY(launch_zero_words(p, counter_words(), stream));
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];

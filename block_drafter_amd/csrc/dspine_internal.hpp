@@ -251,6 +251,41 @@ struct VisibleParams {
 };
 hipError_t launch_debug_visible(const VisibleParams& p, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// fused bridge (a9-a11) for blocks of at most 32 rows: one launch whose
+// workgroups form three groups (R x, [G; G_p; A] c with gate and message,
+// W_l m with the residual add), handing results on through agent-scope
+// counters
+// ---------------------------------------------------------------------------
+struct BridgeParams {
+  int32_t M, W, H, r, a;
+  float eps, code_scale;          // sqrt(r)
+  float* x;                       // fp32 [M, H], updated in place
+  const float* xst;               // statistics lists of x: [xst_lists][ld]
+  int32_t xst_lists;
+  float* st_out;                  // statistics lists of the written x: [H / 64][ld]
+  int32_t ld;                     // list stride (kMaxRows)
+  const void* R;                  // packed [r, H] (layer)
+  const void* G;                  // packed [a, r] (shared)
+  const void* Gp;
+  const void* A;
+  const void* Wl;                 // packed [H, a] (layer)
+  const void* bias;               // [a]
+  const void* codebook;           // [vocab, r]
+  int32_t anchor[DSPINE_MAX_BATCH];
+  float* zpart;                   // [r / 16][4][2][256] partial products of the K quarters
+  void* z;                        // fp16 [M, r]: R x / (rho + eps), anchor rows sqrt(r) C[anchor]
+  float* ssz;                     // [r / 16][ld]: sums of squares of z over each 16 columns
+  float* P;                       // fp32 [M, 3a]: [G; G_p; A] c (read by the proposal tail)
+  void* msg;                      // fp16 [M, a]: gate * message, zero at anchor rows
+  uint32_t* sync;                 // [kBridgeSyncWords]: two hand-off counters, a completion counter, a
+                                  // timeout flag, then one arrival counter per block of 16 codes
+};
+hipError_t launch_bridge_fused(const BridgeParams& p, hipStream_t s);
+// true if the fused bridge takes this geometry and M rows on num_cus CUs
+bool bridge_fused_fits(int H, int r, int a, int M, int num_cus);
+constexpr int kBridgeSyncWords = 4 + 64;
+
 // words [0, n_words) of p <- 0 with a kernel
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);
 

@@ -846,6 +846,14 @@ static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipS
   }
   constexpr int NWB1 = EPI == EPI_SWIGLU ? 2 : 1;   // narrow tiles: more of them
   constexpr int PD_SMALL = PRO == PRO_BRIDGE_MSG ? 1 : (NWB1 == 2 ? 2 : 3);
+  if constexpr (kHalf && sizeof(TW) == 2 && PRO == PRO_COPY && EPI != EPI_SWIGLU) {
+    // operands already in memory as 16-bit rows: they go global -> LDS
+    // directly, the registers hold only the weight stages
+    if (p.K % 256 == 0) {
+      if (mt <= 1) return launch_t<TW, TA, 1, 1, 8, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
+      if (mt <= 2) return launch_t<TW, TA, 2, 1, 8, 2, PRO, EPI, true>(p, grid_cap, num_cus, s);
+    }
+  }
   if (mt <= 1) return launch_t<TW, TA, 1, NWB1, kHalf ? 8 : 4, PD_SMALL, PRO, EPI>(p, grid_cap, num_cus, s);
   if (mt <= 2) return launch_t<TW, TA, 2, NWB1, kHalf ? 8 : 4, PD_SMALL, PRO, EPI>(p, grid_cap, num_cus, s);
   if constexpr (PRO == PRO_COPY || PRO == PRO_GATHER) {

@@ -232,3 +232,21 @@ def test_dflash2_convolution(g, B, W):
     fr = [int(v) for v in rng.integers(5, 70, size=B)]
     run = Run(Case(g, 91 + B, B, W, fr))
     check_run(run)
+
+
+def test_counters_return_to_zero():
+    """The workspace's counters (stream-K tile arrivals, the fused bridge's
+    hand-off counters and its timeout flag: the first 8192 + 4 words of the
+    plan) are zero again after every call, as the header promises; the
+    fused bridge (blocks of up to 32 rows) and the multi-launch bridge both
+    run here."""
+    import torch
+    run = Run(Case(G_B, 86, 2, 16, [50, 70]))
+    ws = run.model.workspace(8, 16, 256)
+    for B, W in ((2, 16), (1, 16), (2, 7), (8, 16)):
+        ctxs = (run.ctxs * 4)[:B]
+        anchors = (run.anchors * 4)[:B]
+        run.model.forward(ctxs, anchors, W, workspace=ws)
+        torch.cuda.synchronize()
+        words = ws[: 4 * (8192 + 4)].view(torch.int32).cpu().numpy()
+        assert not np.any(words), f"B={B} W={W}: nonzero counter words at {np.nonzero(words)[0][:8]}"
