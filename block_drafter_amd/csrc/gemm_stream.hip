@@ -764,6 +764,7 @@ static int resident_cap(int grid_cap, int num_cus) {
 }
 
 constexpr int kMaxSplitWide = 6;   // contributors per tile for MT x NWB >= 8
+constexpr int kWholeKSteps = 16;   // MT x NWB >= 8: K iterations up to which tiles run whole-K
 constexpr int kMaxSplitSmall = 8;  // contributors per tile for MT <= 2 (one load batch of the finisher)
 
 template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA = false,
@@ -788,8 +789,11 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
   // contributors) and at most as many contributors as the finisher loads in
   // one batch (the 16-row bridge projection onto 1024 codes ran 15 us split
   // 20 ways, 10 us split 8 ways).
+  // Wide tiles over a short K (the bridge's [G; G_p; A] and W_l at 128
+  // rows): whole-K tiles; a split's partial tiles (MT x NWB x 4 KB each)
+  // would outweigh the few weights each contributor streams.
   int G;
-  if (p.tiles <= grid_cap && (p.tiles >= num_cus || p.ipt <= PD + 1)) {
+  if (p.tiles <= grid_cap && (p.tiles >= num_cus || p.ipt <= PD + 1 || (MT * NWB >= 8 && p.ipt <= kWholeKSteps))) {
     G = p.tiles;
   } else {
     int64_t g = TI < grid_cap ? TI : grid_cap;
