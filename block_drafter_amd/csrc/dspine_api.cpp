@@ -341,27 +341,29 @@ struct Proj {
   const void* dspine_weights::*global;
   const void* dspine_layer_weights::*layer;
   int rows, cols;
+  const char* name;
 };
 std::vector<Proj> projections(const dspine_geometry& g) {
   const int H = g.hidden, qd = g.n_q_heads * g.head_dim, kvd = g.n_kv_heads * g.head_dim;
   std::vector<Proj> v = {
-      {nullptr, &dspine_layer_weights::wq, qd, H},      {nullptr, &dspine_layer_weights::wk, kvd, H},
-      {nullptr, &dspine_layer_weights::wv, kvd, H},     {nullptr, &dspine_layer_weights::wo, H, qd},
-      {nullptr, &dspine_layer_weights::w_gate, g.ffn, H}, {nullptr, &dspine_layer_weights::w_up, g.ffn, H},
-      {nullptr, &dspine_layer_weights::w_down, H, g.ffn}};
+      {nullptr, &dspine_layer_weights::wq, qd, H, "wq"},      {nullptr, &dspine_layer_weights::wk, kvd, H, "wk"},
+      {nullptr, &dspine_layer_weights::wv, kvd, H, "wv"},     {nullptr, &dspine_layer_weights::wo, H, qd, "wo"},
+      {nullptr, &dspine_layer_weights::w_gate, g.ffn, H, "w_gate"},
+      {nullptr, &dspine_layer_weights::w_up, g.ffn, H, "w_up"},
+      {nullptr, &dspine_layer_weights::w_down, H, g.ffn, "w_down"}};
   if (g.code_dim > 0) {
-    v.push_back({nullptr, &dspine_layer_weights::R, g.code_dim, H});
-    v.push_back({nullptr, &dspine_layer_weights::W_l, H, g.msg_dim});
+    v.push_back({nullptr, &dspine_layer_weights::R, g.code_dim, H, "R"});
+    v.push_back({nullptr, &dspine_layer_weights::W_l, H, g.msg_dim, "W_l"});
   }
   if (g.conv_group > 0) {
-    v.push_back({nullptr, &dspine_layer_weights::attn_conv_w, 4 * (H / g.conv_group), H});
-    v.push_back({nullptr, &dspine_layer_weights::mlp_conv_w, 4 * (H / g.conv_group), H});
+    v.push_back({nullptr, &dspine_layer_weights::attn_conv_w, 4 * (H / g.conv_group), H, "attn_conv_w"});
+    v.push_back({nullptr, &dspine_layer_weights::mlp_conv_w, 4 * (H / g.conv_group), H, "mlp_conv_w"});
   }
-  v.push_back({&dspine_weights::w_feat, nullptr, H, g.n_feat_layers * H});
+  v.push_back({&dspine_weights::w_feat, nullptr, H, g.n_feat_layers * H, "w_feat"});
   if (g.code_dim > 0) {
-    v.push_back({&dspine_weights::bridge_G, nullptr, g.msg_dim, g.code_dim});
-    v.push_back({&dspine_weights::bridge_Gp, nullptr, g.msg_dim, g.code_dim});
-    v.push_back({&dspine_weights::bridge_A, nullptr, g.msg_dim, g.code_dim});
+    v.push_back({&dspine_weights::bridge_G, nullptr, g.msg_dim, g.code_dim, "bridge_G"});
+    v.push_back({&dspine_weights::bridge_Gp, nullptr, g.msg_dim, g.code_dim, "bridge_Gp"});
+    v.push_back({&dspine_weights::bridge_A, nullptr, g.msg_dim, g.code_dim, "bridge_A"});
   }
   return v;
 }
@@ -375,8 +377,17 @@ size_t packed_bytes(const dspine_geometry& g, bool head) {
   if (head) total += align256((size_t)g.vocab * g.hidden * elt_bytes(g));
   if (head && g.dtype == DSPINE_BF16)          // the head's FP8 copy and its row scales
     total += align256((size_t)g.vocab * g.hidden) + align256(sizeof(float) * (size_t)g.vocab);
+  if (g.dtype == DSPINE_BF16) total += 256;    // the range check's maxima
   return total;
 }
+
+// Projections whose bf16 weights a BF16 model's GEMMs widen to fp16 (every
+// projection but w_feat and w_down, which multiply bf16 x bf16): their
+// magnitudes must stay within fp16's range.
+bool widened_to_fp16(const Proj& pr) {
+  return pr.layer != &dspine_layer_weights::w_down && pr.global != &dspine_weights::w_feat;
+}
+constexpr float kF16Max = 65504.f;
 
 // streamed GEMM helpers -------------------------------------------------------
 GemmParams gemm_base(const Plan& P, char* ws, int K, int M) {
@@ -565,6 +576,35 @@ int dspine_pack_weights(dspine_model* model, void* dst, size_t dst_bytes, dspine
       HIP_TRY(launch_quant_head_fp8(model->w.lm_head, out, scale, g.vocab, g.hidden, s));
       model->head_fp8 = out;
       model->head_fp8_scale = scale;
+      out += align256((size_t)g.vocab * g.hidden) + align256(sizeof(float) * (size_t)g.vocab);
+    }
+  }
+  if (g.dtype == DSPINE_BF16) {
+    // range check of the weights the GEMMs widen to fp16 operands: the
+    // largest magnitude of each projection kind (and of the LM head, whose
+    // direct score GEMM widens it too); this waits for the kernels
+    const std::vector<Proj> prs = projections(g);
+    const int nk = (int)prs.size() + 1;
+    uint32_t* mx = reinterpret_cast<uint32_t*>(out);
+    HIP_TRY(launch_zero_words(mx, nk, s));
+    for (int k = 0; k < (int)prs.size(); ++k) {
+      if (!widened_to_fp16(prs[k])) continue;
+      const size_t n = (size_t)prs[k].rows * prs[k].cols;
+      if (prs[k].layer)
+        for (int l = 0; l < g.n_layers; ++l) HIP_TRY(launch_absmax_bf16(model->w.layer[l].*prs[k].layer, n, mx + k, s));
+      else
+        HIP_TRY(launch_absmax_bf16(model->w.*prs[k].global, n, mx + k, s));
+    }
+    if (model->w.lm_head) HIP_TRY(launch_absmax_bf16(model->w.lm_head, (size_t)g.vocab * g.hidden, mx + nk - 1, s));
+    std::vector<uint32_t> host(nk, 0u);
+    HIP_TRY(hipMemcpyAsync(host.data(), mx, sizeof(uint32_t) * nk, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    for (int k = 0; k < nk; ++k) {
+      float v;
+      memcpy(&v, &host[k], sizeof v);
+      if (!(v <= kF16Max))
+        return fail(DSPINE_E_UNSUPPORTED, "pack_weights: %s has a weight of magnitude %g, beyond the fp16 range "
+                    "(65504) of the GEMM operands it is widened to", k + 1 < nk ? prs[k].name : "lm_head", v);
     }
   }
   model->pw = pw;
@@ -1251,9 +1291,12 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
                                   stream))) {
       return rc;
     }
+    // the SwiGLU hidden is the one operand no norm bounds: a BF16 model keeps
+    // it in bf16 (fp32's range) and the down projection multiplies bf16 x bf16
     gp.epi = EPI_SWIGLU;
     gp.out_act = act_f;
     gp.ld_act = g.ffn;
+    gp.out_act_bf16 = g.dtype == DSPINE_BF16;
     {
       ProfScope ps(DSPINE_PROF_GEMM_GATE_UP, stream);
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
@@ -1262,6 +1305,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     set_segments(gp, {{Pw.w_down, H}});
     gp.pro = PRO_COPY;
     gp.a = act_f;
+    gp.a_bf16 = g.dtype == DSPINE_BF16;
     gp.lda = g.ffn;
     gp.epi = conv ? EPI_STORE : EPI_ADD;
     gp.out = conv ? o_tmp : x;

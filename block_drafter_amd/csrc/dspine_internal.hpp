@@ -70,7 +70,7 @@ struct GemmParams {
   // A operand: activation type of the model (fp16 for BF16 models), or bf16
   // target features when a_bf16 is set
   int32_t pro;
-  int32_t a_bf16;
+  int32_t a_bf16;                 // PRO_GATHER / PRO_COPY of a BF16 model: bf16 x bf16 MFMAs
   const void* a;                  // PRO_COPY / PRO_GATHER: row stride lda
   int32_t lda;
   const void* g_src[DSPINE_MAX_BATCH];   // PRO_GATHER: rows [g_row0[s], g_row0[s+1])
@@ -94,8 +94,9 @@ struct GemmParams {
   int32_t epi;
   float* out;                     // EPI_STORE / EPI_ADD(_ROWSCALE): fp32 [M, ldo]
   int32_t ldo;
-  void* out_act;                  // EPI_SWIGLU: model dtype [M, ld_act]
+  void* out_act;                  // EPI_SWIGLU: operand type [M, ld_act] (bf16 when out_act_bf16)
   int32_t ld_act;
+  int32_t out_act_bf16;           // EPI_SWIGLU of a BF16 model: store bf16 (the hidden's full range)
   float* stats_out;               // or NULL: [n / 64][stats_out_ld] sums of squares of the stored rows
   int32_t stats_out_ld;
   // FP8 weights (w_fp8): E4M3 codes in fragment order, read as value / 256;
@@ -288,6 +289,10 @@ constexpr int kBridgeSyncWords = 4 + 64;
 
 // words [0, n_words) of p <- 0 with a kernel
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);
+
+// *out = max(*out, max |src[i]|) over n bf16 values, as float bits (NaN
+// counts above every finite value)
+hipError_t launch_absmax_bf16(const void* src, size_t n, uint32_t* out, hipStream_t s);
 
 // projection matrix [rows, cols] row-major -> fragment order (see pack_kernel)
 hipError_t launch_pack(const void* src, void* dst, int rows, int cols, int dtype, hipStream_t s);

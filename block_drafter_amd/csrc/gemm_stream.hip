@@ -494,9 +494,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
         for (int mb = 0; mb < MT; ++mb) {
           const int m = mb * 16 + (lane & 15);
           if (m < p.M) {
-            T* o = reinterpret_cast<T*>(p.out_act) + (size_t)m * p.ld_act + j * 16 + nl;
+            const size_t e = (size_t)m * p.ld_act + j * 16 + nl;
+            if (p.out_act_bf16) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) Elt<T>::store(o, v, silu(acc[2 * i][mb][v]) * acc[2 * i + 1][mb][v]);
+              for (int v = 0; v < 4; ++v)
+                Elt<bf16_t>::store(reinterpret_cast<bf16_t*>(p.out_act) + e, v, silu(acc[2 * i][mb][v]) * acc[2 * i + 1][mb][v]);
+            } else {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                Elt<T>::store(reinterpret_cast<T*>(p.out_act) + e, v, silu(acc[2 * i][mb][v]) * acc[2 * i + 1][mb][v]);
+            }
           }
         }
       }
@@ -917,6 +924,12 @@ hipError_t launch_gemm_stream(const GemmParams& p, int dtype, int num_cus, hipSt
     if (dtype != DT_BF16 || p.epi != EPI_STORE || !p.col_scale || p.code_anchor || p.pro != PRO_COPY)
       return hipErrorInvalidValue;
     return launch_mt<fp8_t, f16_t, PRO_COPY, EPI_STORE>(p, grid_cap, num_cus, s);
+  }
+  if (p.pro == PRO_COPY && p.a_bf16) {   // bf16 rows (the SwiGLU hidden) x bf16 weights
+    if (dtype != DT_BF16) return hipErrorInvalidValue;
+    if (p.epi == EPI_ADD) return launch_mt<bf16_t, bf16_t, PRO_COPY, EPI_ADD>(p, grid_cap, num_cus, s);
+    if (p.epi == EPI_STORE) return launch_mt<bf16_t, bf16_t, PRO_COPY, EPI_STORE>(p, grid_cap, num_cus, s);
+    return hipErrorInvalidValue;
   }
   if (p.pro == PRO_GATHER) {          // target features, stored output only
     if (p.epi != EPI_STORE) return hipErrorInvalidValue;

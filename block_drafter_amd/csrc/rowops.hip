@@ -213,6 +213,25 @@ __global__ __launch_bounds__(kRowThreads) void kv_store_kernel(const KvStorePara
 // .. +8, at element offset (b*(K/32) + ks)*512 + 8*l.  This is the order in
 // which a wave's MFMA fragments are loaded, so each load reads 1 KB
 // (bf16; 2 KB for float) of consecutive memory.
+// *out = max(*out, |x|) over bf16 values, compared as float bits (for
+// non-negative floats the bit order is the value order; NaN ranks highest)
+__global__ __launch_bounds__(256) void absmax_bf16_kernel(const uint16_t* src, size_t n, uint32_t* out) {
+  uint32_t m = 0;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    m = max(m, ((uint32_t)src[i] & 0x7fffu) << 16);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, m);
+}
+
+hipError_t launch_absmax_bf16(const void* src, size_t n, uint32_t* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  DSPINE_LAUNCH(absmax_bf16_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, s,
+                static_cast<const uint16_t*>(src), n, out);
+  return hipGetLastError();
+}
+
 // words [0, n) of p <- 0 (a plain kernel, not a memset node, so that it can
 // sit in a captured graph)
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {

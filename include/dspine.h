@@ -21,8 +21,10 @@
  *   - "device" pointers address GPU memory of the current HIP device; "host"
  *     pointers address CPU memory read during the call only.
  *   - The caller owns every buffer (weights, rings, features, outputs,
- *     workspace).  The library never allocates, frees or synchronises; calls
- *     only enqueue kernels on the given stream and return.
+ *     workspace).  The library never allocates or frees; calls only enqueue
+ *     kernels on the given stream and return (dspine_pack_weights, a one-time
+ *     set-up call, also waits for its range check; dspine_profile_read waits
+ *     for its events).
  *   - Matrices are row-major [out, in] (y = W x).  BF16 tensors are IEEE
  *     bfloat16 bit patterns; FP16 is IEEE binary16.
  *   - Return value: DSPINE_OK (0) or a negative DSPINE_E_* code.  Every
@@ -182,12 +184,25 @@ void dspine_model_destroy(dspine_model* model);
  * (device, 256-byte aligned, dspine_packed_bytes bytes, caller-owned) with
  * kernels on `stream`; from then on the model reads projections only from
  * `dst`, which must outlive the model (the row-major matrices may be freed
- * once those kernels have run).  With an lm_head on a BF16 model, `dst` also
+ * once those kernels have run).
+ *
+ * Operand range (BF16 models).  The GEMMs multiply fp16 operands by the bf16
+ * weights widened to fp16, except the feature projection w_feat and the
+ * down projection w_down (bf16 x bf16: the SwiGLU hidden is the one operand
+ * no norm bounds, so it is kept in bf16).  A widened weight must therefore
+ * lie within fp16's range: dspine_pack_weights measures the largest
+ * magnitude of every widened projection (and of lm_head), waits for that
+ * check, and fails with DSPINE_E_UNSUPPORTED (naming the matrix) beyond
+ * 65504.  Weights below 2^-14 become fp16 subnormals (rounded toward zero,
+ * an absolute error below 2^-24).  This is the one call that synchronises.
+ *
+ * With an lm_head on a BF16 model, `dst` also
  * receives the head's row-scaled FP8 copy for the retrieval of
  * dspine_draft_propose (one E4M3 code per element in the same fragment order,
  * and a float32 scale per row: vocab * (hidden + 4) bytes more).  Every other
  * call returns DSPINE_E_STATE until the model is packed.  Errors: E_ARG,
- * E_WORKSPACE (dst too small).
+ * E_WORKSPACE (dst too small), E_UNSUPPORTED (a weight out of range, above),
+ * E_HIP.
  */
 size_t dspine_packed_bytes(const dspine_model* model);
 int dspine_pack_weights(dspine_model* model, void* dst, size_t dst_bytes, dspine_stream_t stream);

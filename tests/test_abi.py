@@ -212,7 +212,7 @@ def test_unpacked_model_refuses_valid_calls(L):
     that launches work; argument errors are still reported first."""
     g = synth.G_27B
     h = make_model(L, g)
-    assert L.dspine_packed_bytes(h) == sum(
+    assert L.dspine_packed_bytes(h) == 256 + sum(               # 256: the weight range check's maxima
         int(np.prod(synth.weight_shape(g, n))) * 2
         for n in synth.weight_names(g) if n.split(".")[-1] in bd._PROJECTIONS)
     c = fake_ctx(g, 4096)
@@ -279,7 +279,7 @@ def test_propose_rejections_before_any_launch(L):
     assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == 0
     head_bytes = g.vocab * g.hidden * 2
     fp8_bytes = g.vocab * g.hidden + 4 * g.vocab          # the FP8 copy and its row scales
-    assert L.dspine_packed_bytes(h) == head_bytes + fp8_bytes + sum(
+    assert L.dspine_packed_bytes(h) == head_bytes + fp8_bytes + 256 + sum(
         int(np.prod(synth.weight_shape(g, n))) * 2
         for n in synth.weight_names(g) if n.split(".")[-1] in bd._PROJECTIONS)
     need = L.dspine_propose_workspace_bytes(h, 8, 16, 16)
@@ -361,7 +361,7 @@ def test_conv_geometry_checks(L):
     assert L.dspine_model_create(ctypes.byref(gs), ctypes.byref(ws), ctypes.byref(h)) == 0
     two = sum(int(np.prod(synth.weight_shape(g, n))) * 2 for n in synth.weight_names(g)
               if n.split(".")[-1] in bd._PROJECTIONS)
-    assert L.dspine_packed_bytes(h) == two                     # W_delta of both branches packed too
+    assert L.dspine_packed_bytes(h) == two + 256               # W_delta of both branches packed too
     assert L.dspine_workspace_bytes(h, 8, 16, 0) > 0
     L.dspine_model_destroy(h)
     for bad in (6, 7, 640, -16):                               # not a multiple of 4; 8 groups; negative

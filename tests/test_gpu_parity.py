@@ -250,3 +250,47 @@ def test_counters_return_to_zero():
         torch.cuda.synchronize()
         words = ws[: 4 * (8192 + 4)].view(torch.int32).cpu().numpy()
         assert not np.any(words), f"B={B} W={W}: nonzero counter words at {np.nonzero(words)[0][:8]}"
+
+
+def test_ffn_hidden_beyond_fp16_range():
+    """The SwiGLU hidden is the one GEMM operand that no norm bounds: with
+    gate and up weights scaled by 1000 (N(0, 1000^2 / H)) the hidden rows
+    reach about 1e6, far past fp16's 65504.  A BF16 model keeps the hidden
+    in bf16 and multiplies it by the bf16 down weights, so the forward still
+    matches the oracle (fp64, no rounding of the hidden)."""
+    import block_drafter_amd as bd
+    g = G_B
+    base = synth.make_weights(g, 87)
+    big = {}
+    for l in range(g.n_layers):
+        for n in ("w_gate", "w_up"):
+            w = synth.to_float(base[f"l{l}.{n}"]) * 1000.0
+            big[f"l{l}.{n}"] = synth.f32_to_bf16_bits(w.astype(np.float32))
+    wts = synth.make_weights(g, 87, big)
+    run = Run(Case(g, 87, 2, 16, [40, 9]), wts=wts)
+    gpu = run.gpu_forward()
+    assert np.all(np.isfinite(gpu))
+    orc = run.oracle_forward()
+    for b in range(2):
+        err = rel_err(gpu[b], orc[b])
+        print(f"request {b}: rel err {err:.3e}")
+        assert err <= tol_for(g), f"request {b}: {err:.3e}"
+
+
+def test_pack_rejects_weights_beyond_fp16_range():
+    """Weights that the GEMMs widen to fp16 operands must lie within fp16's
+    range: packing refuses a larger one (E_UNSUPPORTED, naming the matrix).
+    The down projection multiplies bf16 x bf16 and takes any bf16 value."""
+    import block_drafter_amd as bd
+    g = G_A
+    wq = synth.to_float(synth.make_weights(g, 88)["l1.wq"])
+    wq[3, 5] = 1.0e5
+    wts = synth.make_weights(g, 88, {"l1.wq": synth.f32_to_bf16_bits(wq.astype(np.float32))})
+    with pytest.raises(bd.DSpineError) as e:
+        bd.Model.from_numpy(g, wts)
+    assert e.value.code == bd.E_UNSUPPORTED and "wq" in str(e.value)
+    wd = synth.to_float(synth.make_weights(g, 88)["l0.w_down"])
+    wd[1, 2] = 1.0e5
+    wts = synth.make_weights(g, 88, {"l0.w_down": synth.f32_to_bf16_bits(wd.astype(np.float32))})
+    model = bd.Model.from_numpy(g, wts)
+    model.close()
