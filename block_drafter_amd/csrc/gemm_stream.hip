@@ -131,7 +131,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
                 "direct-to-LDS activations: 16-bit copy or gather operands");
   constexpr int SLOT = MT * KSUB * 1024;        // DMA: one stage's chunk, 1 KB blocks [mb][ks]
   constexpr int DBLK = MT * KSUB / 4;           // DMA: blocks per wave per stage
-  constexpr int WLD = NWB * KSUB;               // weight loads per wave per stage
+  // weight loads per wave per stage (one 16-byte load per fragment, or per
+  // pair of FP8 fragments); the direct-to-LDS waits count them exactly
+  constexpr int WLD = sizeof(TW) == 1 ? NWB * KSUB / 2 : NWB * KSUB;
   static_assert(!DMA || (256 / MP) * MP * 4 <= SLOT, "row-scale scratch fits a ring slot");
   // WD: the weight blocks of a stage also go global -> LDS directly (1 KB
   // blocks [wave][nb][ks] after the activation chunk), so the registers hold
@@ -282,6 +284,23 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     }
 #pragma unroll
     for (int nb = 0; nb < NWB; ++nb) {
+      if constexpr (sizeof(TW) == 1) {
+        // FP8 codes: each 64-wide K step of a block is 64 lanes x 16 bytes,
+        // lane l holding its 8 codes of the two 32-wide steps in a row (one
+        // 16-byte load feeds two fragments); K is a multiple of 64
+        static_assert(KSUB % 2 == 0, "FP8 fragments come in pairs of 32-K steps");
+        const gptr<TW> wr = seg_row_ptr<TW>(p, s_seg, tile * WG_BLKS + wave * NWB + nb) + lane * 16;
+#pragma unroll
+        for (int s = 0; s < KSUB; s += 2) {
+          const int kp = k0 / 64 + s / 2;
+          const u32x4 q = gload16((gptr<void>)(wr + (size_t)(kp < p.K / 64 ? kp : p.K / 64 - 1) * 1024));
+          wf[j][nb][s].v[0] = q[0];
+          wf[j][nb][s].v[1] = q[1];
+          wf[j][nb][s + 1].v[0] = q[2];
+          wf[j][nb][s + 1].v[1] = q[3];
+        }
+        continue;
+      }
       // fragment-ordered block: 32-K step ks of the block is 64 lanes x 8
       // elements, contiguous; a step past the end of K re-reads the last one
       const gptr<TW> wr = WD ? wrow[nb] : seg_row_ptr<TW>(p, s_seg, tile * WG_BLKS + wave * NWB + nb) + lane * 8;
@@ -859,7 +878,11 @@ static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipS
   constexpr int PD_SMALL = PRO == PRO_BRIDGE_MSG ? 1 : (NWB1 == 2 ? 2 : 3);
   if constexpr (kHalf && sizeof(TW) == 2 && PRO == PRO_COPY && EPI != EPI_SWIGLU) {
     // operands already in memory as 16-bit rows: they go global -> LDS
-    // directly, the registers hold only the weight stages
+    // directly, the registers hold only the weight stages.  16 rows: two
+    // stages of 512 K (16 KB of weights per wave each; two workgroups per
+    // CU); the LM head at B=1 runs 0.69 of HBM this way against 0.59 with
+    // four stages of 256 K in registers and the operand staged by the waves
+    if (mt <= 1 && p.K % 512 == 0) return launch_t<TW, TA, 1, 1, 16, 1, PRO, EPI, true>(p, grid_cap, num_cus, s);
     if (p.K % 256 == 0) {
       if (mt <= 1) return launch_t<TW, TA, 1, 1, 8, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
       if (mt <= 2) return launch_t<TW, TA, 2, 1, 8, 2, PRO, EPI, true>(p, grid_cap, num_cus, s);
@@ -882,7 +905,7 @@ static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipS
         // weights in registers, whose stages the allocator cannot keep.
         // One-byte FP8 weights keep their (half as large) stages in registers.
         if constexpr (sizeof(TW) == 2) return launch_t<TW, TA, 8, 2, 2, 3, PRO, EPI, true, true>(p, grid_cap, num_cus, s);
-        else return launch_t<TW, TA, 8, 2, 2, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
+        else return launch_t<TW, TA, 8, 2, 4, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
       }
     }
     if (mt <= 4) return launch_t<TW, TA, 4, 2, kHalf ? 4 : 2, 1, PRO, EPI>(p, grid_cap, num_cus, s);
@@ -921,7 +944,7 @@ static hipError_t launch_kind(const GemmParams& p, int grid_cap, int num_cus, hi
 hipError_t launch_gemm_stream(const GemmParams& p, int dtype, int num_cus, hipStream_t s) {
   const int grid_cap = gemm_stream_grid_cap(num_cus);
   if (p.w_fp8) {                      // the LM head's FP8 copy: scores of fp16 rows only
-    if (dtype != DT_BF16 || p.epi != EPI_STORE || !p.col_scale || p.code_anchor || p.pro != PRO_COPY)
+    if (dtype != DT_BF16 || p.epi != EPI_STORE || !p.col_scale || p.code_anchor || p.pro != PRO_COPY || p.K % 64)
       return hipErrorInvalidValue;
     return launch_mt<fp8_t, f16_t, PRO_COPY, EPI_STORE>(p, grid_cap, num_cus, s);
   }

@@ -473,9 +473,10 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
 
 // One workgroup per block of 16 head rows: each row's absolute maximum m
 // (16 threads per row), its scale exponent k (2^k the smallest power of two
-// >= m / 448; 0 for a zero row), then the codes of E / 2^k written in the
-// fragment order of the packed projections (lane l of 32-column step ks: row
-// l % 16, columns 32 ks + 8 (l / 16) .. + 8, at byte (blk K/32 + ks) 512 + 8 l).
+// >= m / 448; 0 for a zero row), then the codes of E / 2^k in fragment order
+// with two 32-column steps per lane: for 64-column step kp, lane l holds row
+// l % 16, columns 64 kp + 8 (l / 16) .. + 8 and then 64 kp + 32 + 8 (l / 16)
+// .. + 8, 16 bytes at byte (blk K/64 + kp) 1024 + 16 l.
 __global__ __launch_bounds__(256) void quant_head_fp8_kernel(const bf16_t* head, uint8_t* codes, float* col_scale,
                                                              int H) {
   __shared__ int s_k[16];
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(256) void quant_head_fp8_kernel(const bf16_t* head,
       const uint32_t hi = e4m3_code(ldexpf(__uint_as_float(v[d] & 0xffff0000u), -k));
       w[d >> 1] |= (lo | (hi << 8)) << (16 * (d & 1));
     }
-    *reinterpret_cast<uint64_t*>(codes + ((size_t)blk * steps + ks) * 512 + 8 * lane) =
+    *reinterpret_cast<uint64_t*>(codes + ((size_t)blk * (steps / 2) + ks / 2) * 1024 + 16 * lane + 8 * (ks & 1)) =
         (uint64_t)w[0] | ((uint64_t)w[1] << 32);
   }
 }
@@ -740,7 +741,7 @@ __global__ __launch_bounds__(kMaxRetrieve) void retrieve_keep_kernel(const Propo
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_head_fp8(const void* head, void* codes, float* col_scale, int V, int H, hipStream_t s) {
-  if (V % 16 || H % 32) return hipErrorInvalidValue;
+  if (V % 16 || H % 64) return hipErrorInvalidValue;
   DSPINE_LAUNCH(quant_head_fp8_kernel, dim3(V / 16), dim3(256), 0, s, static_cast<const bf16_t*>(head),
                 static_cast<uint8_t*>(codes), col_scale, H);
   return hipGetLastError();

@@ -53,8 +53,9 @@ hipError_t launch_walk(const ProposeParams& p, hipStream_t s);
 constexpr int kMaxRetrieve = DSPINE_MAX_RETRIEVE;
 hipError_t launch_retrieve(const ProposeParams& p, hipStream_t s);
 size_t retrieve_partial_entries(int rows, int vocab);
-// Row-scaled FP8 copy of a bf16 head [V, H] (V a multiple of 16): E4M3 codes
-// in the fragment order of the packed projections (one byte per element) and
+// Row-scaled FP8 copy of a bf16 head [V, H] (V a multiple of 16, H of 64):
+// E4M3 codes in fragment order, each lane's 16 bytes holding its codes of
+// two consecutive 32-wide column steps (one byte per element), and
 // col_scale[v] = 256 s_v, s_v the smallest power of two with max|E_v| / s_v
 // <= 448 (256: the GEMM reads each code as its value / 256).
 hipError_t launch_quant_head_fp8(const void* head, void* codes, float* col_scale, int V, int H, hipStream_t s);

@@ -198,8 +198,9 @@ void dspine_model_destroy(dspine_model* model);
  *
  * With an lm_head on a BF16 model, `dst` also
  * receives the head's row-scaled FP8 copy for the retrieval of
- * dspine_draft_propose (one E4M3 code per element in the same fragment order,
- * and a float32 scale per row: vocab * (hidden + 4) bytes more).  Every other
+ * dspine_draft_propose (one E4M3 code per element, fragment order with two
+ * 32-wide column steps per lane fragment, and a float32 scale per row:
+ * vocab * (hidden + 4) bytes more).  Every other
  * call returns DSPINE_E_STATE until the model is packed.  Errors: E_ARG,
  * E_WORKSPACE (dst too small), E_UNSUPPORTED (a weight out of range, above),
  * E_HIP.
