@@ -369,31 +369,73 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       *reinterpret_cast<u32x4*>(&lds[buf][m * LDA + (c % CPR) * EPC]) = v;
     }
   };
+  // One stage's products.  Wide row tiles (64 and 128 rows) read every LDS
+  // fragment of the stage before the first MFMA: with one wave per SIMD
+  // nothing else hides an LDS round trip, and reads issued one group at a
+  // time (read, wait, multiply) stall the wave once per group and hold back
+  // the next stage's loads (128 rows: gate/up 105.6 -> 103.2 us, the B=8
+  // forward 2.021 -> 1.954 ms).  Narrow tiles keep one read per product,
+  // which the compiler interleaves with the next stage's weight loads (the
+  // batched order made the 16-row q|k|v 8 % slower).  Each accumulator sums
+  // its 32-K steps in order either way.
   auto compute = [&](int buf, int j) __attribute__((always_inline)) {
+    auto a_frag = [&](Frag<T>& af, int s, int mb) __attribute__((always_inline)) {
+      if constexpr (kFullLine)
+        af.v = *reinterpret_cast<const u32x4*>(adma + j * STG + mb * 2048 + aoff[s]);
+      else if constexpr (DMA)
+        af.v = *reinterpret_cast<const u32x4*>(adma + j * STG + (mb * KSUB + s) * 1024 + lane * 16);
+      else
+        af.load(&lds[buf][(mb * 16 + (lane & 15)) * LDA + s * 32 + 8 * (lane >> 4)]);
+    };
+    auto w_frag = [&](int s, int nb) __attribute__((always_inline)) -> Frag<TW> {
+      Frag<TW> w{};
+      if constexpr (WD)   // 16-bit weights only
+        w.v = *reinterpret_cast<const u32x4*>(adma + j * STG + SLOT + ((wave * NWB + nb) * KSUB + s) * 1024 + lane * 16);
+      return w;
+    };
+    if constexpr (MT >= 4) {
+      Frag<T> af[KSUB][MT];
+      Frag<TW> wl[WD ? KSUB : 1][NWB];
 #pragma unroll
-    for (int s = 0; s < KSUB; ++s) {
-      Frag<T> wo[NWB];
-#pragma unroll
-      for (int nb = 0; nb < NWB; ++nb) {
+      for (int s = 0; s < KSUB; ++s) {
         if constexpr (WD) {
-          Frag<TW> w;
-          w.v = *reinterpret_cast<const u32x4*>(adma + j * STG + SLOT + ((wave * NWB + nb) * KSUB + s) * 1024 + lane * 16);
-          wo[nb] = AsOperand<T, TW>::cvt(w);
-        } else {
-          wo[nb] = AsOperand<T, TW>::cvt(wf[j][nb][s]);
+#pragma unroll
+          for (int nb = 0; nb < NWB; ++nb) wl[s][nb] = w_frag(s, nb);
         }
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) a_frag(af[s][mb], s, mb);
       }
+      // keep the scheduler from sinking the reads back between the products
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mb = 0; mb < MT; ++mb) {
-        Frag<T> af;
-        if constexpr (kFullLine)
-          af.v = *reinterpret_cast<const u32x4*>(adma + j * STG + mb * 2048 + aoff[s]);
-        else if constexpr (DMA)
-          af.v = *reinterpret_cast<const u32x4*>(adma + j * STG + (mb * KSUB + s) * 1024 + lane * 16);
-        else
-          af.load(&lds[buf][(mb * 16 + (lane & 15)) * LDA + s * 32 + 8 * (lane >> 4)]);
+      for (int s = 0; s < KSUB; ++s) {
+        Frag<T> wo[NWB];
 #pragma unroll
-        for (int nb = 0; nb < NWB; ++nb) mma16(acc[nb][mb], wo[nb], af);
+        for (int nb = 0; nb < NWB; ++nb) {
+          if constexpr (WD) wo[nb] = AsOperand<T, TW>::cvt(wl[s][nb]);
+          else wo[nb] = AsOperand<T, TW>::cvt(wf[j][nb][s]);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NWB; ++nb) mma16(acc[nb][mb], wo[nb], af[s][mb]);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSUB; ++s) {
+        Frag<T> wo[NWB];
+#pragma unroll
+        for (int nb = 0; nb < NWB; ++nb) {
+          if constexpr (WD) wo[nb] = AsOperand<T, TW>::cvt(w_frag(s, nb));
+          else wo[nb] = AsOperand<T, TW>::cvt(wf[j][nb][s]);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) {
+          Frag<T> af;
+          a_frag(af, s, mb);
+#pragma unroll
+          for (int nb = 0; nb < NWB; ++nb) mma16(acc[nb][mb], wo[nb], af);
+        }
       }
     }
   };
@@ -466,6 +508,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
           for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = sum[mb];
         }
         if (tid == 0) reset_counter(p.counters + tile);
+        // the repeated loads past the last contributor are never used: wait
+        // for them here, or the compiler's wait before the next reuse of
+        // their registers (an LDS fragment read of the next tile) would
+        // also wait for every stage in flight
+        wait_vmcnt<0>();
       } else {
       constexpr int FB = NWB * MT <= 2 ? 8 : NWB * MT <= 4 ? 4 : NWB * MT <= 8 ? 2 : 1;
       f32x4 sum[NWB][MT];
@@ -499,6 +546,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 #pragma unroll
         for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = sum[nb][mb];
       if (tid == 0) reset_counter(p.counters + tile);
+      wait_vmcnt<0>();                             // as above
       }
     }
     // epilogue: lane holds D[n = 4*(lane/16) + v][m = lane%16] per (nb, mb)
