@@ -11,11 +11,12 @@
 // so as three streamed GEMMs they cost mostly fixed latency: entering, the
 // first load round trip, the split-K hand-off.  Here one grid does all three:
 //
-//   - group 1 (r/16 workgroups): 16 rows of R each, over the whole K = H,
-//     wave w taking every fourth 32-wide K step from step w (the four
-//     partial products are added through LDS in wave order); writes z
-//     (fp16) and each row's sum of squares over the 16 columns, then
-//     counts itself on sync[0];
+//   - group 1 (4 r/16 workgroups): 16 rows of R and one quarter of K = H
+//     each, wave w taking every fourth 32-wide K step of the quarter (the
+//     waves' products are added through LDS in wave order); each quarter
+//     publishes its partial, and the last of a block's four to arrive adds
+//     them in quarter order, writes z (fp16) and each row's sum of squares
+//     over the 16 columns, then counts the block on sync[0];
 //   - group 2 (a/16 workgroups): the same 16 rows of G, G_p and A each (K
 //     steps split over the waves the same way);
 //     waits for sync[0] = r/16, forms the code norm from the sums of
@@ -30,7 +31,7 @@
 // Every workgroup loads its weights into registers before it waits, so the
 // three groups' HBM reads overlap.  Results that cross workgroups travel by
 // write-through agent-scope stores, drained before the count, and are read
-// with agent-scope loads.  The grid (r/16 + a/16 + H/64 workgroups) must be
+// with agent-scope loads.  The grid (4 r/16 + a/16 + H/64 workgroups) must be
 // resident at once: the launcher checks it against the CU count, and every
 // wait is bounded (a timeout sets sync[3] and the workgroup skips its work,
 // so no wave waits forever).  The last group-3 workgroup resets the counters.
