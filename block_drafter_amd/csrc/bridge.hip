@@ -28,6 +28,10 @@
 //     waits for sync[1] = a/16, adds rho W_l m to its 64 columns of x and
 //     writes their per-row sums of squares (the next norm's statistics).
 //
+// Optionally (next_act / next_out) group 3 also forms the next RMS norm of
+// its columns once every group-3 workgroup has published its statistics (a
+// fourth wait), so that no separate norm or pre-scale kernel follows.
+//
 // Every workgroup loads its weights into registers before it waits, so the
 // three groups' HBM reads overlap.  Results that cross workgroups travel by
 // write-through agent-scope stores, drained before the count, and are read
@@ -47,6 +51,7 @@ constexpr int kF1 = 10;     // group 1: K steps of 32 per wave (H <= 5120)
 constexpr int kF2 = 8;      // group 2: K steps per wave (r <= 1024)
 constexpr int kF3 = 16;     // group 3: K steps of each wave's 16 rows (a <= 512)
 constexpr int kSpin = 1 << 17;
+constexpr int kBlk0 = 5;    // first per-block arrival counter in sync
 
 // Thread 0: wait until *c >= target (bounded); false after a timeout, which
 // is also recorded in *flag.
@@ -138,6 +143,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
   __shared__ float s_scale[MT * 16];
   __shared__ __align__(16) float s_P[3][MT * 16][16];
   __shared__ float s_sq[4][MT * 16];
+  __shared__ float s_nrm[MT * 16];
   __shared__ int s_ok;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,10 +211,10 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
       for (int mt = 0; mt < MT; ++mt) store_coherent(part + ((size_t)sp * MT + mt) * 256 + 4 * lane, acc[0][mt]);
       drain_own_stores();
       uint32_t prev = 0;
-      if (lane == 0) prev = __hip_atomic_fetch_add(sync + 4 + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) prev = __hip_atomic_fetch_add(sync + kBlk0 + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       prev = __shfl(prev, 0, 64);
       if (prev != (uint32_t)kS1 - 1) return;
-      if (lane == 0) __hip_atomic_store(sync + 4 + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_store(sync + kBlk0 + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       f32x4 q[kS1][MT];
 #pragma unroll
       for (int t = 0; t < kS1; ++t)
@@ -345,6 +351,10 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
   if (tid < MT * 16) s_scale[tid] = sqrtf(s_scale[tid] / p.H);        // rho
   if (tid == 0) s_ok = wait_count(sync + 1, (uint32_t)U2, sync + 3) ? 1 : 0;
   __syncthreads();
+  const int U3 = p.H / 64;
+  const bool fold = p.next_act != nullptr || p.next_out != nullptr;
+  const int col = 16 * (4 * c3 + wave) + nl;
+  f32x4 xn[MT];                                      // the written x of this lane's 4 columns
   if (s_ok) {
     f32x4 acc[MT];
 #pragma unroll
@@ -370,17 +380,18 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
         mma16(acc[mt], w, b);
       }
     }
-    const int col = 16 * (4 * c3 + wave) + nl;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + (lane & 15);
       float sq = 0.f;
+      xn[mt] = f32x4{0, 0, 0, 0};
       if (m < p.M) {
         f32x4* xp = reinterpret_cast<f32x4*>(p.x + (size_t)m * p.H + col);
         const float rho = s_scale[mt * 16 + (lane & 15)];
         f32x4 v = *xp;
         v = f32x4{v[0] + rho * acc[mt][0], v[1] + rho * acc[mt][1], v[2] + rho * acc[mt][2], v[3] + rho * acc[mt][3]};
         *xp = v;
+        xn[mt] = v;
         sq = ((v[0] * v[0] + v[1] * v[1]) + v[2] * v[2]) + v[3] * v[3];
       }
       sq += __shfl_xor(sq, 16, 64);
@@ -388,15 +399,90 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
       if (lane < 16) s_sq[wave][mt * 16 + lane] = sq;
     }
     __syncthreads();
-    if (tid < p.M) p.st_out[(size_t)c3 * p.ld + tid] = ((s_sq[0][tid] + s_sq[1][tid]) + s_sq[2][tid]) + s_sq[3][tid];
-    if (tid == 0) {
+    if (tid < p.M) {
+      const float st = ((s_sq[0][tid] + s_sq[1][tid]) + s_sq[2][tid]) + s_sq[3][tid];
+      if (fold) store_coherent(p.st_out + (size_t)c3 * p.ld + tid, st);   // read by the other workgroups
+      else p.st_out[(size_t)c3 * p.ld + tid] = st;
+    }
+  }
+  if (!fold) {
+    if (s_ok && tid == 0) {
       // the last group-3 workgroup resets the counters for the next launch
       const uint32_t done = __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (done == (uint32_t)(p.H / 64) - 1) {
+      if (done == (uint32_t)U3 - 1) {
         __hip_atomic_store(sync + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+    }
+    return;
+  }
+
+  // ---- fourth phase: the next RMS norm of these 64 columns ------------------
+  // Every group-3 workgroup counts itself on sync[2] (also one that timed
+  // out above, so that the wait below ends), waits for all of them, sums each
+  // row's H/64 statistics lists exactly as the pre-scale kernel does (lane t
+  // takes lists t, t + 64, ...; then a wave butterfly), and writes
+  // (x * rsqrt(S / H + eps)) * gain.  sync[4] counts the workgroups past the
+  // wait; the last one resets the counters.
+  drain_own_stores();
+  __syncthreads();
+  if (tid == 0) {
+    __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ok = (s_ok && wait_count(sync + 2, (uint32_t)U3, sync + 3)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (s_ok) {
+    // rows wave, wave + 4, ...: every row's loads go out before any is summed
+    constexpr int RPW = MT * 16 / 4;
+    float v[RPW];
+    const float* srow[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int rr = wave + 4 * i;
+      srow[i] = p.st_out + (rr < p.M ? rr : p.M - 1);
+      v[i] = 0.f;
+    }
+    for (int t = lane; t < U3; t += 64) {
+      float l[RPW];
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) l[i] = load_coherent(srow[i] + (size_t)t * p.ld);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) v[i] += l[i];
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const float S = wave_sum(v[i]);
+      if (lane == 0) s_nrm[wave + 4 * i] = rsqrtf(S / p.H + p.eps);
+    }
+    __syncthreads();
+    const gptr<bf16_t> gn = as_global(reinterpret_cast<const bf16_t*>(p.next_gain)) + col;
+    float gv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gv[e] = Elt<bf16_t>::gload(gn, e);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + (lane & 15);
+      if (m >= p.M) continue;
+      const float sc = s_nrm[m];
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = xn[mt][e] * sc * gv[e];
+      if (p.next_out) *reinterpret_cast<f32x4*>(p.next_out + (size_t)m * p.H + col) = f32x4{o[0], o[1], o[2], o[3]};
+      if (p.next_act) {
+        f16_t* d = reinterpret_cast<f16_t*>(p.next_act) + (size_t)m * p.H + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Elt<f16_t>::store(d, e, o[e]);
+      }
+    }
+  }
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(sync + 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (uint32_t)U3 - 1) {
+      __hip_atomic_store(sync + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + 4, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -419,7 +505,7 @@ static int bridge_per_cu(int M) {
 bool bridge_fused_fits(int H, int r, int a, int M, int num_cus) {
   if (M < 1 || M > 32) return false;
   if (H % 64 || H / 32 > kS1 * 4 * kF1 || r % 32 || r / 32 > 4 * kF2 || a % 32 || a / 32 > kF3 ||
-      r / 16 > kBridgeSyncWords - 4)
+      r / 16 > kBridgeSyncWords - kBlk0)
     return false;
   // the whole grid resident at once
   return bridge_fused_grid(H, r, a) <= bridge_per_cu(M) * num_cus;

@@ -899,12 +899,18 @@ namespace {
 // x [M, H] fp32 in place; `xst` holds the sums of squares of x's rows as
 // `xst_tiles` partial lists (ld kMaxRows).  Writes the new rows' statistics
 // to `st_out` (stat_tiles(H) lists).
+// The bridge (a9-a11) of `layer` on x.  With the fused kernel (blocks of up to
+// 32 rows, BF16) it can also form the next RMS norm of the written x (gain
+// next_gain): as the fp16 operand next_act and/or the fp32 rows next_out;
+// *folded then says that it did (otherwise the caller forms that norm).
 int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const float* xst, int xst_tiles,
                float* st_out, const int32_t* anchor_ids, const float* pred_codes, char* ws, const Plan& P,
-               int cus, hipStream_t stream) {
+               int cus, hipStream_t stream, const void* next_gain = nullptr, void* next_act = nullptr,
+               float* next_out = nullptr, bool* folded = nullptr) {
   const dspine_geometry& g = m.g;
   const dspine_weights& wt = m.w;
   const int M = B * W, H = g.hidden, r = g.code_dim, a = g.msg_dim;
+  if (folded) *folded = false;
   if (!pred_codes && g.dtype == DSPINE_BF16 && bridge_fused_fits(H, r, a, M, cus)) {
     // blocks of up to 32 rows: the whole bridge in one launch
     BridgeParams bp;
@@ -935,6 +941,12 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
     bp.P = reinterpret_cast<float*>(ws + P.P);
     bp.msg = ws + P.act_m;
     bp.sync = reinterpret_cast<uint32_t*>(ws + P.bridge_sync);
+    if (next_gain && (next_act || next_out)) {
+      bp.next_gain = next_gain;
+      bp.next_act = next_act;
+      bp.next_out = next_out;
+      if (folded) *folded = true;
+    }
     HIP_TRY(launch_bridge_fused(bp, stream));
     return DSPINE_OK;
   }
@@ -1124,8 +1136,11 @@ static ConvParams conv_params(const dspine_geometry& g, int M, int W, const floa
 
 // The forward's launches (arguments already checked).  save_u, when given,
 // receives the last layer's state before its bridge write [B*W, H].
+// want_head_act: also leave fp16(out) in the act_h buffer when the last
+// bridge can form it (*head_act_ready then says it did).
 static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx* ctx, const int32_t* anchor_ids,
-                       float* out, void* workspace, hipStream_t stream, float* save_u) {
+                       float* out, void* workspace, hipStream_t stream, float* save_u, bool want_head_act = false,
+                       bool* head_act_ready = nullptr) {
   int rc = DSPINE_OK;
   const dspine_geometry& g = model->g;
   const dspine_weights& wt = model->w;
@@ -1165,6 +1180,19 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
   rp.rope = rope;
   rp.head_dim = D;
   rp.rope_theta = g.rope_theta;
+  // Blocks whose q|k|v takes a pre-scaled operand (prescale_pays) get it
+  // from the kernel that writes x: the embedding for layer 0, the fused
+  // bridge for the layers after it.  act_ready: act_h holds this layer's
+  // operand.
+  const bool fold_norm = !conv && prescale_pays(g, M, H);
+  bool act_ready = false;
+  if (head_act_ready) *head_act_ready = false;
+  if (fold_norm) {
+    rp.act = ws + P.act_h;
+    rp.gain = wt.layer[0].g_in;
+    rp.eps = g.eps;
+    act_ready = true;
+  }
   {
     ProfScope ps(DSPINE_PROF_NORM, stream);
     HIP_TRY(launch_embed(rp, g.dtype, stream));
@@ -1205,10 +1233,15 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
       gp.pro = PRO_COPY;
       gp.a = ws + P.act_h;
       gp.lda = H;
+    } else if (act_ready) {
+      // the input norm as a pre-scaled operand, already formed by the kernel
+      // that wrote x: the q|k|v GEMM streams it into LDS in long stages
+      gp.pro = PRO_COPY;
+      gp.a = ws + P.act_h;
+      gp.lda = H;
     } else if (prescale_pays(g, M, H)) {
-      // the input norm as a pre-scaled operand: the q|k|v GEMM then streams
-      // it into LDS in long stages (at B=1: 142 -> 103 us per forward, the
-      // pre-scale kernels included in the saving's balance: 1.141 -> 1.125 ms)
+      // the same operand from the pre-scale kernel (at B=1 the q|k|v GEMM
+      // went 142 -> 103 us per forward with these kernels counted)
       ProfScope ps(DSPINE_PROF_NORM, stream);
       if ((rc = set_prescaled_a(gp, g, M, W, x, H, SCALE_RMSNORM, xst, xst_tiles, Lw.g_in, ws + P.act_h, stream)))
         return rc;
@@ -1223,6 +1256,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
       ProfScope ps(DSPINE_PROF_GEMM_QKV, stream);
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
     }
+    act_ready = false;                    // act_h is reused below
 
     // a6 (with the q/k head norm + RoPE of a5)
     AttnParams ap;
@@ -1368,13 +1402,29 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
 
     if (save_u && l == g.n_layers - 1)
       HIP_TRY(hipMemcpyAsync(save_u, x, sizeof(float) * (size_t)M * H, hipMemcpyDeviceToDevice, stream));
-    // a9-a11 (statistics of the written rows go to st0)
+    // a9-a11 (statistics of the written rows go to st0); the fused bridge
+    // also forms the next norm: the next layer's q|k|v operand, or after the
+    // last layer the final norm (a12) into `out` (and fp16(out) on request)
     if (g.code_dim > 0) {
       ProfScope ps(DSPINE_PROF_BRIDGE, stream);
-      rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream);
+      const bool last = l == g.n_layers - 1;
+      bool folded = false;
+      if (last)
+        rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream, wt.g_final,
+                        want_head_act ? ws + P.act_h : nullptr, out, &folded);
+      else if (fold_norm)
+        rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream,
+                        wt.layer[l + 1].g_in, ws + P.act_h, nullptr, &folded);
+      else
+        rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream);
       if (rc) return rc;
       xst = st0;                          // the write GEMM's lists, one per 64 columns
       xst_tiles = tH;
+      if (last && folded) {
+        if (head_act_ready) *head_act_ready = want_head_act;
+        return DSPINE_OK;
+      }
+      act_ready = folded;
     }
   }
   // a12
@@ -1386,6 +1436,9 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
   fp.f32_out = out;
   fp.gain = wt.g_final;
   fp.eps = g.eps;
+  fp.lists = xst;                         // the same bits as the fused bridge's folded norm
+  fp.nlists = xst_tiles;
+  fp.ld = kMaxRows;
   {
     ProfScope ps(DSPINE_PROF_NORM, stream);
     HIP_TRY(launch_rmsnorm(fp, g.dtype, true, stream));
@@ -1562,7 +1615,11 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
   float* u = reinterpret_cast<float*>(pws + PP.u);
   float* scores = prop->scores ? prop->scores : reinterpret_cast<float*>(pws + PP.scores);
 
-  if ((rc = run_forward(model, B, W, ctx, anchor_ids, out, workspace, stream, u))) return rc;
+  // the head's fp16 operand (h itself) comes from the last bridge when it can
+  const bool head_prescaled = R != 0 || prescale_pays(g, M, H);
+  bool head_act_ready = false;
+  if ((rc = run_forward(model, B, W, ctx, anchor_ids, out, workspace, stream, u, head_prescaled, &head_act_ready)))
+    return rc;
 
   // head scores E h of every row (h = the forward's final-normed output), or
   // their FP8 approximation s_v (q_v . h); one timed span holds the operand
@@ -1574,17 +1631,20 @@ int dspine_draft_propose(const dspine_model* model, int B, int W, const dspine_c
       set_segments(gp, {{model->head_fp8, V}});
       gp.w_fp8 = 1;
       gp.col_scale = model->head_fp8_scale;
-      // the FP8 GEMM reads fp16 rows (copy prologue): h converted once
-      if ((rc = set_prescaled_a(gp, g, M, W, out, H, SCALE_ONE, nullptr, 0, nullptr, ws + P.act_h, stream))) return rc;
     } else {
       set_segments(gp, {{model->pw.lm_head, V}});
-      if (prescale_pays(g, M, H)) {
-        if ((rc = set_prescaled_a(gp, g, M, W, out, H, SCALE_ONE, nullptr, 0, nullptr, ws + P.act_h, stream)))
-          return rc;
-      } else if ((rc = set_scaled_a(gp, g, M, W, out, H, H, SCALE_ONE, nullptr, 0, (float)H, nullptr, ws + P.act_h,
-                                    stream))) {
-        return rc;
-      }
+    }
+    if (head_act_ready) {
+      gp.pro = PRO_COPY;                  // fp16(h), written by the last bridge
+      gp.a = ws + P.act_h;
+      gp.lda = H;
+    } else if (head_prescaled) {
+      // h converted once to fp16 rows (the FP8 GEMM's copy prologue, and the
+      // 16-row BF16 head's direct-to-LDS stages)
+      if ((rc = set_prescaled_a(gp, g, M, W, out, H, SCALE_ONE, nullptr, 0, nullptr, ws + P.act_h, stream))) return rc;
+    } else if ((rc = set_scaled_a(gp, g, M, W, out, H, H, SCALE_ONE, nullptr, 0, (float)H, nullptr, ws + P.act_h,
+                                  stream))) {
+      return rc;
     }
     gp.epi = EPI_STORE;
     gp.out = scores;

@@ -193,6 +193,10 @@ struct RowParams {
   float rope_theta;
   float* stats;                   // [M] sum of squares of each row (one stats tile)
   int32_t act_bf16;               // rmsnorm: act is bfloat16 (the tile GEMM's bf16 x bf16 path)
+  // rmsnorm: with nlists > 0 the rows' sums of squares come from the
+  // statistics lists of x ([nlists][ld]) instead of from x itself
+  const float* lists;
+  int32_t nlists, ld;
 };
 // Operand pre-scale for large blocks: act[m, k] = x[m, k] * s[m] (* gain[k]),
 // s[m] from the row's statistics lists; or the bridge message
@@ -280,12 +284,22 @@ struct BridgeParams {
   float* P;                       // fp32 [M, 3a]: [G; G_p; A] c (read by the proposal tail)
   void* msg;                      // fp16 [M, a]: gate * message, zero at anchor rows
   uint32_t* sync;                 // [kBridgeSyncWords]: two hand-off counters, a completion counter, a
-                                  // timeout flag, then one arrival counter per block of 16 codes
+                                  // timeout flag, the fourth phase's completion counter, then one
+                                  // arrival counter per block of 16 codes
+  // Optional fourth phase, the next RMS norm folded in: once every column of
+  // x is written, each group-3 workgroup scales its 64 columns by the row's
+  // factor rsqrt(S / H + eps) (S from the statistics lists just written,
+  // summed in the pre-scale kernel's order) and by next_gain; next_act
+  // receives the result as fp16 (the next projection's operand), next_out as
+  // fp32 (the final norm).  Both NULL: no fourth phase.
+  const void* next_gain;          // [H] bf16
+  void* next_act;                 // fp16 [M, H] or NULL
+  float* next_out;                // fp32 [M, H] or NULL
 };
 hipError_t launch_bridge_fused(const BridgeParams& p, hipStream_t s);
 // true if the fused bridge takes this geometry and M rows on num_cus CUs
 bool bridge_fused_fits(int H, int r, int a, int M, int num_cus);
-constexpr int kBridgeSyncWords = 4 + 64;
+constexpr int kBridgeSyncWords = 5 + 64;
 
 // words [0, n_words) of p <- 0 with a kernel
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);

@@ -25,7 +25,8 @@ __device__ __forceinline__ void rope_pair(int64_t pos, int j, int D, float theta
 // a4 [NIF, draft input]: x[m] = embed[token(m)], row 0 of each request the
 // anchor and rows 1..W-1 the mask token.  Also the row's sum of squares (one
 // statistics tile, from which the first input norm is formed in the QKV
-// projection) and the rotation table of the row's position F + i.
+// projection, or, with `act`, that norm itself as the projection's operand)
+// and the rotation table of the row's position F + i.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void embed_kernel(const RowParams p) {
   __shared__ float red[kRowThreads / 64];
@@ -41,6 +42,17 @@ __global__ __launch_bounds__(kRowThreads) void embed_kernel(const RowParams p) {
   }
   ss = block_sum<kRowThreads>(ss, red);
   if (threadIdx.x == 0) p.stats[m] = ss;
+  if (p.act) {
+    // the first input norm as the q|k|v operand, (x * rsqrt(S / H + eps)) *
+    // gain, with the factor the pre-scale kernel forms from this one list
+    using TA = typename ActOf<T>::type;
+    const float inv = rsqrtf(ss / p.H + p.eps);
+    const gptr<T> gn = as_global(reinterpret_cast<const T*>(p.gain));
+    TA* out = reinterpret_cast<TA*>(p.act) + (size_t)m * p.H;
+#pragma unroll 4
+    for (int k = threadIdx.x; k < p.H; k += kRowThreads)
+      Elt<TA>::store(out, k, p.x_out[(size_t)m * p.H + k] * inv * Elt<T>::gload(gn, k));
+  }
   for (int j = threadIdx.x; j < p.head_dim / 2; j += kRowThreads) {
     float c, s;
     rope_pair(p.F[b] + i, j, p.head_dim, p.rope_theta, c, s);
@@ -124,9 +136,22 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const RowParams p)
   const int m = blockIdx.x;
   const gptr<float> x = as_global(p.x) + (size_t)m * p.H;
   float ss = 0.f;
+  if (p.nlists > 0) {
+    // the row's sum of squares from the statistics lists of x, summed as the
+    // pre-scale kernel and the fused bridge sum them (so that a norm formed
+    // there and one formed here are the same bits)
+    if (threadIdx.x < 64) {
+      for (int t = threadIdx.x; t < p.nlists; t += 64) ss += p.lists[(size_t)t * p.ld + m];
+      ss = wave_sum(ss);
+      if (threadIdx.x == 0) red[0] = ss;
+    }
+    __syncthreads();
+    ss = red[0];
+  } else {
 #pragma unroll 4
-  for (int k = threadIdx.x; k < p.H; k += kRowThreads) ss += x[k] * x[k];
-  ss = block_sum<kRowThreads>(ss, red);
+    for (int k = threadIdx.x; k < p.H; k += kRowThreads) ss += x[k] * x[k];
+    ss = block_sum<kRowThreads>(ss, red);
+  }
   const float inv = rsqrtf(ss / p.H + p.eps);
   const gptr<T> gw = as_global(reinterpret_cast<const T*>(p.gain));
 #pragma unroll 4

@@ -235,11 +235,12 @@ def test_dflash2_convolution(g, B, W):
 
 
 def test_counters_return_to_zero():
-    """The workspace's counters (stream-K tile arrivals, the fused bridge's
-    hand-off counters and its timeout flag: the first 8192 + 4 words of the
-    plan) are zero again after every call, as the header promises; the
-    fused bridge (blocks of up to 32 rows) and the multi-launch bridge both
-    run here."""
+    """The workspace's counters (8192 stream-K tile arrivals, then the fused
+    bridge's 69 words: its hand-off counters, timeout flag, fourth-phase
+    counter and per-block arrival counters) are zero again after every call,
+    as the header promises; the fused bridge with its folded norm (16 rows
+    and fewer), the fused bridge without it (32 rows) and the multi-launch
+    bridge all run here."""
     import torch
     run = Run(Case(G_B, 86, 2, 16, [50, 70]))
     ws = run.model.workspace(8, 16, 256)
@@ -248,7 +249,7 @@ def test_counters_return_to_zero():
         anchors = (run.anchors * 4)[:B]
         run.model.forward(ctxs, anchors, W, workspace=ws)
         torch.cuda.synchronize()
-        words = ws[: 4 * (8192 + 4)].view(torch.int32).cpu().numpy()
+        words = ws[: 4 * (8192 + 69)].view(torch.int32).cpu().numpy()
         assert not np.any(words), f"B={B} W={W}: nonzero counter words at {np.nonzero(words)[0][:8]}"
 
 
