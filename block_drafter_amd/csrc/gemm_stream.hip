@@ -873,7 +873,11 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
     int64_t g = TI < grid_cap ? TI : grid_cap;
     if (MT * NWB >= 8 && g > (int64_t)p.tiles * kMaxSplitWide) g = (int64_t)p.tiles * kMaxSplitWide;
     if (MT <= 2) {
-      if (g > num_cus) g = num_cus;
+      // one workgroup per CU (a second one only adds contributors: O and
+      // down at 16 rows ran 7 and 4 % slower with two), except for one-byte
+      // weights, whose kernel holds two (the FP8 head 1 % faster per call)
+      const int per_cu = (DMA && sizeof(TW) == 1) ? 2 : 1;
+      if (g > per_cu * num_cus) g = per_cu * num_cus;
       if (g > (int64_t)p.tiles * kMaxSplitSmall) g = (int64_t)p.tiles * kMaxSplitSmall;
     }
     G = (int)g;
@@ -952,7 +956,18 @@ static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipS
         // stages, full-line activation blocks); 1.2-1.3x faster than
         // weights in registers, whose stages the allocator cannot keep.
         // One-byte FP8 weights keep their (half as large) stages in registers.
-        if constexpr (sizeof(TW) == 2) return launch_t<TW, TA, 8, 2, 2, 3, PRO, EPI, true, true>(p, grid_cap, num_cus, s);
+        // Narrow outputs take 64-column tiles: twice the workgroups, and
+        // half the partial tile each finisher reads.  At the 27B geometry
+        // that is q|k|v, O and the bridge's three projections (B=8 forward
+        // 1.953 -> 1.79 ms; 35B B=8 1.49 -> 1.33 ms); over a long K and
+        // N > 2048 (the 27B down and feature projections) the wide tiles
+        // stay faster.
+        if constexpr (sizeof(TW) == 2) {
+          if constexpr (EPI != EPI_SWIGLU)
+            if (p.nblk <= 128 || (p.nblk <= 384 && p.K <= 8192))
+              return launch_t<TW, TA, 8, 1, 2, 3, PRO, EPI, true, true>(p, grid_cap, num_cus, s);
+          return launch_t<TW, TA, 8, 2, 2, 3, PRO, EPI, true, true>(p, grid_cap, num_cus, s);
+        }
         else return launch_t<TW, TA, 8, 2, 4, 3, PRO, EPI, true>(p, grid_cap, num_cus, s);
       }
     }
