@@ -347,14 +347,27 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
 #pragma unroll
   for (int f = 0; f < kF3; ++f)
     if (f < F) wf[f].gload(Wl + (size_t)f * 512);
+  const int U3 = p.H / 64;
+  const bool fold = p.next_act != nullptr || p.next_out != nullptr;
+  const int col = 16 * (4 * c3 + wave) + nl;
+  // this lane's 4 columns of x (the other groups do not write x) and of the
+  // next norm's gain, loaded before the wait
+  f32x4 xn[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + (lane & 15);
+    xn[mt] = *reinterpret_cast<const f32x4*>(p.x + (size_t)(m < p.M ? m : p.M - 1) * p.H + col);
+  }
+  float gv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (fold) {
+    const gptr<bf16_t> gn = as_global(reinterpret_cast<const bf16_t*>(p.next_gain)) + col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gv[e] = Elt<bf16_t>::gload(gn, e);
+  }
   row_sums<MT * 16, false>(p.xst, p.xst_lists, p.ld, p.M, s_scale, red);
   if (tid < MT * 16) s_scale[tid] = sqrtf(s_scale[tid] / p.H);        // rho
   if (tid == 0) s_ok = wait_count(sync + 1, (uint32_t)U2, sync + 3) ? 1 : 0;
   __syncthreads();
-  const int U3 = p.H / 64;
-  const bool fold = p.next_act != nullptr || p.next_out != nullptr;
-  const int col = 16 * (4 * c3 + wave) + nl;
-  f32x4 xn[MT];                                      // the written x of this lane's 4 columns
   if (s_ok) {
     f32x4 acc[MT];
 #pragma unroll
@@ -384,13 +397,11 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + (lane & 15);
       float sq = 0.f;
-      xn[mt] = f32x4{0, 0, 0, 0};
       if (m < p.M) {
-        f32x4* xp = reinterpret_cast<f32x4*>(p.x + (size_t)m * p.H + col);
         const float rho = s_scale[mt * 16 + (lane & 15)];
-        f32x4 v = *xp;
+        f32x4 v = xn[mt];
         v = f32x4{v[0] + rho * acc[mt][0], v[1] + rho * acc[mt][1], v[2] + rho * acc[mt][2], v[3] + rho * acc[mt][3]};
-        *xp = v;
+        *reinterpret_cast<f32x4*>(p.x + (size_t)m * p.H + col) = v;
         xn[mt] = v;
         sq = ((v[0] * v[0] + v[1] * v[1]) + v[2] * v[2]) + v[3] * v[3];
       }
@@ -456,10 +467,6 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
       if (lane == 0) s_nrm[wave + 4 * i] = rsqrtf(S / p.H + p.eps);
     }
     __syncthreads();
-    const gptr<bf16_t> gn = as_global(reinterpret_cast<const bf16_t*>(p.next_gain)) + col;
-    float gv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) gv[e] = Elt<bf16_t>::gload(gn, e);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + (lane & 15);
