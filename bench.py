@@ -424,9 +424,11 @@ def measure_workload(name, args, with_propose, gate_up_traffic_md=None):
         propose["roofline"]["traffic"] = None
         if wl.name == "dspine27b_b1":
             from block_drafter_amd import profsum
-            rec = profsum.read_traffic(os.path.join(ROOT, "profiles", "traffic_gemm_stream_lm_head_dspine27b_b1.md"))
-            if rec is not None and rec[1] == profsum.source_hash():
-                propose["roofline"]["traffic"] = rec[0]
+            for rec_key, md in ((None, "traffic_gemm_stream_lm_head_dspine27b_b1.md"),
+                                ("fp8_retrieval", "traffic_gemm_stream_fp8_head_dspine27b_b1.md")):
+                rec = profsum.read_traffic(os.path.join(ROOT, "profiles", md))
+                if rec is not None and rec[1] == profsum.source_hash() and (rec_key is None or rec_key in propose):
+                    (propose if rec_key is None else propose[rec_key])["roofline"]["traffic"] = rec[0]
 
     # HBM traffic of the same kernel from the PMC runs summarised under
     # profiles/ (null unless they were taken on this workload with the

@@ -3,6 +3,12 @@
   python -m block_drafter_amd.profsum stats KERNEL_STATS_CSV [--top N]
       Markdown table of a ``--kernel-trace --stats --output-format csv`` run.
 
+  python -m block_drafter_amd.profsum sequence KERNEL_TRACE_CSV --start REGEX [--nth N] [--until REGEX]
+      The kernels of one call in launch order (start, duration, gap to the
+      previous kernel's end, workgroups): from the N-th dispatch matching
+      --start (negative N counts from the end) up to the next match, or to
+      the first dispatch matching --until.
+
   python -m block_drafter_amd.profsum traffic --fetch CSV --write CSV
         --fetch-copy CSV --write-copy CSV --kernel REGEX --algorithmic BYTES
       [--min-fetch-kib KIB]
@@ -49,6 +55,36 @@ def stats_table(path: str, top: int = 20) -> str:
     for r in rows[:top]:
         out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(out)
+
+
+def sequence_table(path: str, start: str, nth: int = -1, until: str = "") -> str:
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    idx = [i for i, r in enumerate(rows) if re.search(start, r["Kernel_Name"])]
+    if not idx:
+        raise SystemExit("no dispatch matches --start")
+    k = nth if nth >= 0 else len(idx) + nth
+    i0 = idx[k]
+    i1 = idx[k + 1] if k + 1 < len(idx) else len(rows)
+    if until:
+        for i in range(i0 + 1, len(rows)):
+            if re.search(until, rows[i]["Kernel_Name"]):
+                i1 = i + 1
+                break
+    t0 = int(rows[i0]["Start_Timestamp"])
+    prev = t0
+    total = 0.0
+    out = ["| start µs | kernel | µs | gap µs | workgroups |", "|---:|---|---:|---:|---:|"]
+    for r in rows[i0:i1]:
+        st, en = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        wg = (int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])) // max(
+            1, int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+        total += (en - st) / 1e3
+        out.append(f"| {(st - t0) / 1e3:.1f} | `{short_name(r['Kernel_Name'])}` | {(en - st) / 1e3:.2f} | "
+                   f"{(st - prev) / 1e3:.1f} | {wg} |")
+        prev = en
+    out.append(f"\n{i1 - i0} kernels, {total:.1f} µs of kernel time in a {(prev - t0) / 1e3:.1f} µs span")
     return "\n".join(out)
 
 
@@ -122,6 +158,11 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--top", type=int, default=20)
+    q = sub.add_parser("sequence")
+    q.add_argument("csv")
+    q.add_argument("--start", required=True)
+    q.add_argument("--nth", type=int, default=-1)
+    q.add_argument("--until", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -134,6 +175,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv, a.top))
+    elif a.cmd == "sequence":
+        print(sequence_table(a.csv, a.start, a.nth, a.until))
     else:
         print(traffic(a))
 
