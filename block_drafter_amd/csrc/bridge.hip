@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
     Frag<bf16_t> wf[kF1];
 #pragma unroll
     for (int f = 0; f < kF1; ++f)
-      if (k_lo + wave + 4 * f < k_hi) wf[f].gload(R + (size_t)(k_lo + wave + 4 * f) * 512);
+      if (k_lo + wave + 4 * f < k_hi) wf[f].gload_nt(R + (size_t)(k_lo + wave + 4 * f) * 512);
     // activation rows (fp32 x) of every step, all in flight together
     u32x4 xv[kF1][MT][2];
 #pragma unroll
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
                               (size_t)i * 16 * p.r + 8 * lane;
 #pragma unroll
       for (int f = 0; f < kF2; ++f)
-        if (wave + 4 * f < NK) wf[s][f].gload(Wm + (size_t)(wave + 4 * f) * 512);
+        if (wave + 4 * f < NK) wf[s][f].gload_nt(Wm + (size_t)(wave + 4 * f) * 512);
     }
     if (tid == 0) s_ok = wait_count(sync + 0, (uint32_t)U1, sync + 3) ? 1 : 0;
     __syncthreads();
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
   Frag<bf16_t> wf[kF3];
 #pragma unroll
   for (int f = 0; f < kF3; ++f)
-    if (f < F) wf[f].gload(Wl + (size_t)f * 512);
+    if (f < F) wf[f].gload_nt(Wl + (size_t)f * 512);
   const int U3 = p.H / 64;
   const bool fold = p.next_act != nullptr || p.next_out != nullptr;
   const int col = 16 * (4 * c3 + wave) + nl;

@@ -64,6 +64,10 @@ __device__ __forceinline__ gptr<T> as_global(const T* p) {
   return (gptr<T>)(p);
 }
 __device__ __forceinline__ u32x4 gload16(gptr<void> p) { return *(gptr<u32x4>)(p); }
+// A load of data read once (streamed weights): non-temporal, so that the L2
+// keeps the lines that are re-read (the activations every workgroup reads)
+// instead of the stream's
+__device__ __forceinline__ u32x4 gload16_nt(gptr<void> p) { return __builtin_nontemporal_load((gptr<u32x4>)(p)); }
 
 template <typename T> struct Elt;
 template <> struct Elt<float> {
@@ -103,6 +107,7 @@ template <> struct Frag<bf16_t> {
   u32x4 v;  // 8 bf16
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
   __device__ __forceinline__ void gload(gptr<bf16_t> p) { v = gload16((gptr<void>)p); }
+  __device__ __forceinline__ void gload_nt(gptr<bf16_t> p) { v = gload16_nt((gptr<void>)p); }
   __device__ __forceinline__ void zero() { v = u32x4{0, 0, 0, 0}; }
 };
 template <> struct Frag<float> {
@@ -114,6 +119,10 @@ template <> struct Frag<float> {
   __device__ __forceinline__ void gload(gptr<float> p) {
     v[0] = gload16((gptr<void>)p);
     v[1] = gload16((gptr<void>)(p + 4));
+  }
+  __device__ __forceinline__ void gload_nt(gptr<float> p) {
+    v[0] = gload16_nt((gptr<void>)p);
+    v[1] = gload16_nt((gptr<void>)(p + 4));
   }
   __device__ __forceinline__ void zero() { v[0] = u32x4{0, 0, 0, 0}; v[1] = v[0]; }
 };
@@ -128,6 +137,11 @@ template <> struct Frag<fp8_t> {
   uint32_t v[2];
   __device__ __forceinline__ void gload(gptr<fp8_t> p) {
     const uint64_t q = *(gptr<uint64_t>)(p);
+    v[0] = (uint32_t)q;
+    v[1] = (uint32_t)(q >> 32);
+  }
+  __device__ __forceinline__ void gload_nt(gptr<fp8_t> p) {
+    const uint64_t q = __builtin_nontemporal_load((gptr<uint64_t>)(p));
     v[0] = (uint32_t)q;
     v[1] = (uint32_t)(q >> 32);
   }

@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 #pragma unroll
         for (int s = 0; s < KSUB; s += 2) {
           const int kp = k0 / 64 + s / 2;
-          const u32x4 q = gload16((gptr<void>)(wr + (size_t)(kp < p.K / 64 ? kp : p.K / 64 - 1) * 1024));
+          const u32x4 q = gload16_nt((gptr<void>)(wr + (size_t)(kp < p.K / 64 ? kp : p.K / 64 - 1) * 1024));
           wf[j][nb][s].v[0] = q[0];
           wf[j][nb][s].v[1] = q[1];
           wf[j][nb][s + 1].v[0] = q[2];
@@ -308,12 +308,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       for (int s = 0; s < KSUB; ++s) {
         const int ks = k0 / 32 + s;
         const gptr<TW> src = wr + (size_t)(ks < p.K / 32 ? ks : p.K / 32 - 1) * 512;
+        // weights are read once: non-temporal (cache policy NT), so the L2
+        // keeps the activation lines every workgroup re-reads (128 rows: the
+        // L2 missed 57 % of requests with the weights cached; B=8 forward
+        // 1.79 -> 1.69 ms)
         if constexpr (WD)
           __builtin_amdgcn_global_load_lds((const void*)src,
                                            (lds_void*)(adma + j * STG + SLOT + ((wave * NWB + nb) * KSUB + s) * 1024),
-                                           16, 0, 0);
+                                           16, 0, 2);
         else
-          wf[j][nb][s].gload(src);
+          wf[j][nb][s].gload_nt(src);
       }
     }
   };
