@@ -86,7 +86,9 @@ struct AttnShape {
   static_assert((D / 16) % NSUB == 0, "merge split of the head dimension");
 };
 
-template <typename TW, typename TQ, typename TV, int D, int GRP>
+// KVNT: the context K/V tiles are read with non-temporal loads (a layer's
+// context is read once; large ones otherwise evict lines that are re-read)
+template <typename TW, typename TQ, typename TV, int D, int GRP, bool KVNT = false>
 __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_kernel(const AttnParams p) {
   using Sh = AttnShape<TQ, TV, D, GRP>;
   static_assert(sizeof(TW) == sizeof(TQ), "stored keys and key operands have one element size");
@@ -168,13 +170,17 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
       const int c = (gtid + q * GT) % (32 * KCH);
-      kr_[q] = gload16((gptr<void>)(kring + key_row(i, c / KCH) + (c % KCH) * KEPC));
+      const gptr<void> src = (gptr<void>)(kring + key_row(i, c / KCH) + (c % KCH) * KEPC);
+      if constexpr (KVNT) kr_[q] = gload16_nt(src);
+      else kr_[q] = gload16(src);
     }
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
       int kr, part;
       if (!v_chunk(q, kr, part)) kr = part = 0;          // spare thread: re-load chunk 0
-      vr_[q] = gload16((gptr<void>)(vring + key_row(i, kr) + part * VEPC));
+      const gptr<void> src = (gptr<void>)(vring + key_row(i, kr) + part * VEPC);
+      if constexpr (KVNT) vr_[q] = gload16_nt(src);
+      else vr_[q] = gload16(src);
     }
   };
   auto store_tile = [&](const u32x4 (&kr_)[KPT], const u32x4 (&vr_)[VPT], int i) {
@@ -589,7 +595,15 @@ size_t attn_partial_floats(int max_b, int nq, int head_dim) {
 template <typename TW, typename TQ, typename TV, int D, int GRP>
 static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
   const dim3 grid(p.nsplit, p.nkv, p.B);
-  DSPINE_LAUNCH((attention_kernel<TW, TQ, TV, D, GRP>), grid, dim3(AttnShape<TQ, TV, D, GRP>::NT), 0, s, p);
+  if constexpr (sizeof(TW) == 2) {
+    if (p.kv_nt) {
+      DSPINE_LAUNCH((attention_kernel<TW, TQ, TV, D, GRP, true>), grid, dim3(AttnShape<TQ, TV, D, GRP>::NT), 0, s, p);
+    } else {
+      DSPINE_LAUNCH((attention_kernel<TW, TQ, TV, D, GRP>), grid, dim3(AttnShape<TQ, TV, D, GRP>::NT), 0, s, p);
+    }
+  } else {
+    DSPINE_LAUNCH((attention_kernel<TW, TQ, TV, D, GRP>), grid, dim3(AttnShape<TQ, TV, D, GRP>::NT), 0, s, p);
+  }
   if (p.nsplit > 1) DSPINE_LAUNCH((attn_merge_kernel<TQ, D>), dim3(p.nq * (D / 32), p.B), dim3(64), 0, s, p);
   return hipGetLastError();
 }

@@ -1288,10 +1288,16 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     }
     const int64_t spread = std::max(ceil_div(256, (int64_t)B * g.n_kv_heads), ceil_div(max_ctx, 2048));
     ap.nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({spread, ceil_div(max_ctx, 128), (int64_t)kMaxSplit}));
+    int64_t kv_bytes = 0;
     for (int b = 0; b < B; ++b) {
       const int64_t nctx = ap.F[b] - ap.lo0[b];
       ap.kps[b] = (int32_t)(ceil_div(ceil_div(nctx, ap.nsplit), 32) * 32);
+      kv_bytes += nctx * g.n_kv_heads * D * 4;
     }
+    // a layer's context K/V is read once: non-temporal loads keep it from
+    // evicting reused lines when it is large (27B B=8: 1.3 % faster, 35B
+    // B=8 2.5 %); at 27B B=1 (8.4 MB) the cached loads measured faster
+    ap.kv_nt = kv_bytes > ((int64_t)16 << 20) ? 1 : 0;
     ap.out = act_q;
     ap.ld_out = qd;
     ap.partials = reinterpret_cast<float*>(ws + P.attn_part);

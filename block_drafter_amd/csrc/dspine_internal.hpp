@@ -164,6 +164,7 @@ struct AttnParams {
   int64_t lo0[DSPINE_MAX_BATCH];  // first context position row 0 sees
   int32_t kps[DSPINE_MAX_BATCH];  // context keys per split (multiple of 32)
   int32_t nsplit;
+  int32_t kv_nt;                  // context K/V read with non-temporal loads
   void* out;                      // model dtype [M, ld_out]
   int32_t ld_out;
   float* partials;                // [B][nq][nsplit] split partials, merged by a second kernel
