@@ -1180,11 +1180,11 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
   rp.rope = rope;
   rp.head_dim = D;
   rp.rope_theta = g.rope_theta;
-  // Blocks whose q|k|v takes a pre-scaled operand (prescale_pays) get it
-  // from the kernel that writes x: the embedding for layer 0, the fused
-  // bridge for the layers after it.  act_ready: act_h holds this layer's
-  // operand.
-  const bool fold_norm = !conv && prescale_pays(g, M, H);
+  // Blocks whose q|k|v takes a pre-scaled operand (16 rows and fewer, and
+  // more than 32) get it from the kernel that writes x: the embedding for
+  // layer 0, the fused bridge (up to 32 rows) for the layers after it.
+  // act_ready: act_h holds this layer's operand.
+  const bool fold_norm = !conv && (prescale_pays(g, M, H) || M > gemm_stream_fused_rows());
   bool act_ready = false;
   if (head_act_ready) *head_act_ready = false;
   if (fold_norm) {
