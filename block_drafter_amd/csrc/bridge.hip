@@ -39,6 +39,10 @@
 // resident at once: the launcher checks it against the CU count, and every
 // wait is bounded (a timeout sets sync[3] and the workgroup skips its work,
 // so no wave waits forever).  The last group-3 workgroup resets the counters.
+// Counter i (sync[i] above) is the word i kBridgeLine: each on a 128-byte line
+// of its own, so that the 64 block arrivals, the hand-off counts and the
+// waiting workgroups' polls do not queue behind one another (packed into two
+// lines, the last block's hand-off ended about 5 us later).
 #include "dspine_device.hpp"
 #include "dspine_internal.hpp"
 
@@ -151,6 +155,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
   const int g = blockIdx.x;
   const int nl = 4 * (lane >> 4);                     // first output column of this lane's 4
   uint32_t* const sync = p.sync;
+  auto ctr = [sync](int i) { return sync + i * kBridgeLine; };   // counter i, on a line of its own
 
   if (g < kS1 * U1) {
     // ---- group 1: z = R x / (rho + eps) for 16 codes ----------------------
@@ -211,10 +216,10 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
       for (int mt = 0; mt < MT; ++mt) store_coherent(part + ((size_t)sp * MT + mt) * 256 + 4 * lane, acc[0][mt]);
       drain_own_stores();
       uint32_t prev = 0;
-      if (lane == 0) prev = __hip_atomic_fetch_add(sync + kBlk0 + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) prev = __hip_atomic_fetch_add(ctr(kBlk0 + j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       prev = __shfl(prev, 0, 64);
       if (prev != (uint32_t)kS1 - 1) return;
-      if (lane == 0) __hip_atomic_store(sync + kBlk0 + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_store(ctr(kBlk0 + j), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       f32x4 q[kS1][MT];
 #pragma unroll
       for (int t = 0; t < kS1; ++t)
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
         }
       }
       drain_own_stores();
-      if (lane == 0) __hip_atomic_fetch_add(sync + 0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_fetch_add(ctr(0), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
@@ -262,10 +267,22 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
       for (int f = 0; f < kF2; ++f)
         if (wave + 4 * f < NK) wf[s][f].gload_nt(Wm + (size_t)(wave + 4 * f) * 512);
     }
-    if (tid == 0) s_ok = wait_count(sync + 0, (uint32_t)U1, sync + 3) ? 1 : 0;
+    if (tid == 0) s_ok = wait_count(ctr(0), (uint32_t)U1, ctr(3)) ? 1 : 0;
     __syncthreads();
     const bool ok = s_ok != 0;
     if (ok) {
+      // z goes out first, the code-norm sums of squares behind it: one
+      // memory round trip for both
+      u32x4 zv[kF2][MT];
+#pragma unroll
+      for (int f = 0; f < kF2; ++f)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = mt * 16 + (lane & 15);
+          if (wave + 4 * f < NK)
+            zv[f][mt] = load_coherent_u32x4(reinterpret_cast<const f16_t*>(p.z) + (size_t)(m < p.M ? m : p.M - 1) * p.r +
+                                            32 * (wave + 4 * f) + 8 * (lane >> 4));
+        }
       // code-norm scale of each row from the sums of squares of z
       row_sums<MT * 16, true>(p.ssz, U1, p.ld, p.M, s_scale, red);
       if (tid < MT * 16) {
@@ -278,16 +295,6 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
       for (int s = 0; s < 3; ++s)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[s][mt] = f32x4{0, 0, 0, 0};
-      u32x4 zv[kF2][MT];
-#pragma unroll
-      for (int f = 0; f < kF2; ++f)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int m = mt * 16 + (lane & 15);
-          if (wave + 4 * f < NK)
-            zv[f][mt] = load_coherent_u32x4(reinterpret_cast<const f16_t*>(p.z) + (size_t)(m < p.M ? m : p.M - 1) * p.r +
-                                            32 * (wave + 4 * f) + 8 * (lane >> 4));
-        }
 #pragma unroll
       for (int f = 0; f < kF2; ++f) {
         if (wave + 4 * f >= NK) continue;
@@ -334,7 +341,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
       }
       drain_own_stores();
       __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_fetch_add(ctr(1), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
   }
   row_sums<MT * 16, false>(p.xst, p.xst_lists, p.ld, p.M, s_scale, red);
   if (tid < MT * 16) s_scale[tid] = sqrtf(s_scale[tid] / p.H);        // rho
-  if (tid == 0) s_ok = wait_count(sync + 1, (uint32_t)U2, sync + 3) ? 1 : 0;
+  if (tid == 0) s_ok = wait_count(ctr(1), (uint32_t)U2, ctr(3)) ? 1 : 0;
   __syncthreads();
   if (s_ok) {
     f32x4 acc[MT];
@@ -419,11 +426,11 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
   if (!fold) {
     if (s_ok && tid == 0) {
       // the last group-3 workgroup resets the counters for the next launch
-      const uint32_t done = __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t done = __hip_atomic_fetch_add(ctr(2), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (done == (uint32_t)U3 - 1) {
-        __hip_atomic_store(sync + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctr(0), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctr(1), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctr(2), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     return;
@@ -439,8 +446,8 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
   drain_own_stores();
   __syncthreads();
   if (tid == 0) {
-    __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_ok = (s_ok && wait_count(sync + 2, (uint32_t)U3, sync + 3)) ? 1 : 0;
+    __hip_atomic_fetch_add(ctr(2), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ok = (s_ok && wait_count(ctr(2), (uint32_t)U3, ctr(3))) ? 1 : 0;
   }
   __syncthreads();
   if (s_ok) {
@@ -484,12 +491,12 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
     }
   }
   if (tid == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(sync + 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t done = __hip_atomic_fetch_add(ctr(4), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == (uint32_t)U3 - 1) {
-      __hip_atomic_store(sync + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sync + 4, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr(0), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr(1), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr(2), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr(4), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -512,7 +519,7 @@ static int bridge_per_cu(int M) {
 bool bridge_fused_fits(int H, int r, int a, int M, int num_cus) {
   if (M < 1 || M > 32) return false;
   if (H % 64 || H / 32 > kS1 * 4 * kF1 || r % 32 || r / 32 > 4 * kF2 || a % 32 || a / 32 > kF3 ||
-      r / 16 > kBridgeSyncWords - kBlk0)
+      r / 16 > kBridgeSyncWords / kBridgeLine - kBlk0)
     return false;
   // the whole grid resident at once
   return bridge_fused_grid(H, r, a) <= bridge_per_cu(M) * num_cus;

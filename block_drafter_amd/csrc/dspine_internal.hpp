@@ -286,7 +286,7 @@ struct BridgeParams {
   void* msg;                      // fp16 [M, a]: gate * message, zero at anchor rows
   uint32_t* sync;                 // [kBridgeSyncWords]: two hand-off counters, a completion counter, a
                                   // timeout flag, the fourth phase's completion counter, then one
-                                  // arrival counter per block of 16 codes
+                                  // arrival counter per block of 16 codes, each kBridgeLine words apart
   // Optional fourth phase, the next RMS norm folded in: once every column of
   // x is written, each group-3 workgroup scales its 64 columns by the row's
   // factor rsqrt(S / H + eps) (S from the statistics lists just written,
@@ -300,7 +300,11 @@ struct BridgeParams {
 hipError_t launch_bridge_fused(const BridgeParams& p, hipStream_t s);
 // true if the fused bridge takes this geometry and M rows on num_cus CUs
 bool bridge_fused_fits(int H, int r, int a, int M, int num_cus);
-constexpr int kBridgeSyncWords = 5 + 64;
+// The fused bridge's counters sit kBridgeLine words (128 bytes) apart, so
+// that the arrivals and polls on one counter do not queue behind those on
+// another in the same line.
+constexpr int kBridgeLine = 32;
+constexpr int kBridgeSyncWords = (5 + 64) * kBridgeLine;
 
 // words [0, n_words) of p <- 0 with a kernel
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t s);

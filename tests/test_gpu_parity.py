@@ -236,8 +236,9 @@ def test_dflash2_convolution(g, B, W):
 
 def test_counters_return_to_zero():
     """The workspace's counters (8192 stream-K tile arrivals, then the fused
-    bridge's 69 words: its hand-off counters, timeout flag, fourth-phase
-    counter and per-block arrival counters) are zero again after every call,
+    bridge's 69, 32 words apart: its hand-off counters, timeout flag,
+    fourth-phase counter and per-block arrival counters) are zero again after
+    every call,
     as the header promises; the fused bridge with its folded norm (16 rows
     and fewer), the fused bridge without it (32 rows) and the multi-launch
     bridge all run here."""
@@ -249,7 +250,7 @@ def test_counters_return_to_zero():
         anchors = (run.anchors * 4)[:B]
         run.model.forward(ctxs, anchors, W, workspace=ws)
         torch.cuda.synchronize()
-        words = ws[: 4 * (8192 + 69)].view(torch.int32).cpu().numpy()
+        words = ws[: 4 * (8192 + 69 * 32)].view(torch.int32).cpu().numpy()
         assert not np.any(words), f"B={B} W={W}: nonzero counter words at {np.nonzero(words)[0][:8]}"
 
 
