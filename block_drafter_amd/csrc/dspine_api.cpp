@@ -464,7 +464,8 @@ int set_scaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, const f
 // a copy prologue: for BF16 models at 16 rows and under, whose copy GEMMs
 // stream their operand straight into LDS in long stages
 int set_prescaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, const float* x, int K, int mode,
-                    const float* st, int lists, const void* gain, void* act, hipStream_t stream) {
+                    const float* st, int lists, const void* gain, void* act, hipStream_t stream,
+                    bool round_bf16 = false) {
   ScaleParams sp;
   memset(&sp, 0, sizeof sp);
   sp.M = M;
@@ -480,6 +481,7 @@ int set_prescaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, cons
   sp.x = x;
   sp.ldx = K;
   sp.gain = gain;
+  sp.round_bf16 = round_bf16 ? 1 : 0;
   sp.act = act;
   sp.ld_act = K;
   HIP_TRY(launch_scale_rows(sp, g.dtype, stream));
@@ -843,9 +845,19 @@ int dspine_ctx_materialize(const dspine_model* model, int n_req, dspine_ctx* ctx
           gp.nseg = 2 * L;
           gp.nblk = blk;
           // c passes through bf16, as the long-block path stores it, so that
-          // both paths project the same operand values
-          int rc2 = set_scaled_a(gp, g, mr, 1, c_raw + r0 * H, H, H, SCALE_RMSNORM, stc, stat_tiles(H), (float)H,
-                                 wt.g_ctx, c_act, stream, g.dtype == DSPINE_BF16);
+          // both paths project the same operand values.  At 16 rows and
+          // under the pre-scale kernel forms it (the GEMM then streams it
+          // into LDS in long stages: 47 -> 36 us per 16-row step at the 27B
+          // geometry, the kernel counted)
+          int rc2;
+          {
+            ProfScope ps(DSPINE_PROF_CTX_GEMM, stream);
+            rc2 = prescale_pays(g, mr, H)
+                      ? set_prescaled_a(gp, g, mr, 1, c_raw + r0 * H, H, SCALE_RMSNORM, stc, stat_tiles(H), wt.g_ctx,
+                                        c_act, stream, g.dtype == DSPINE_BF16)
+                      : set_scaled_a(gp, g, mr, 1, c_raw + r0 * H, H, H, SCALE_RMSNORM, stc, stat_tiles(H), (float)H,
+                                     wt.g_ctx, c_act, stream, g.dtype == DSPINE_BF16);
+          }
           if (rc2) return rc2;
           gp.epi = EPI_STORE;
           gp.out = kv_raw + r0 * ldkv;
