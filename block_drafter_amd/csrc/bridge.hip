@@ -148,6 +148,9 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
   __shared__ __align__(16) float s_P[3][MT * 16][16];
   __shared__ float s_sq[4][MT * 16];
   __shared__ float s_nrm[MT * 16];
+  // group 3: the message rows, staged once for the four waves (row stride
+  // kF3 * 32 + 8 halves: the 16 rows of a fragment read land on distinct banks)
+  __shared__ __align__(16) f16_t s_msg[MT * 16 * (kF3 * 32 + 8)];
   __shared__ int s_ok;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -209,6 +212,19 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
     }
     reduce_waves<1, MT>(acc, red, wave, lane);
     if (wave == 0) {
+      // the anchor rows' codebook values, loaded before the arrival (only
+      // the block's last quarter uses them)
+      float cbv[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + (lane & 15);
+        if (m % p.W == 0) {
+          const gptr<bf16_t> cb = as_global(reinterpret_cast<const bf16_t*>(p.codebook)) +
+                                  (size_t)p.anchor[(m < p.M ? m : 0) / p.W] * p.r + 16 * j + nl;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) cbv[mt][v] = Elt<bf16_t>::gload(cb, v);
+        }
+      }
       // publish this quarter's partial; the last quarter of the block to
       // arrive adds the four in quarter order and finishes the block
       float* part = p.zpart + (size_t)(j * kS1) * MT * 256;
@@ -233,10 +249,8 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
 #pragma unroll
         for (int t = 1; t < kS1; ++t) z = f32x4{z[0] + q[t][mt][0], z[1] + q[t][mt][1], z[2] + q[t][mt][2], z[3] + q[t][mt][3]};
         if (m % p.W == 0) {                           // anchor code sqrt(r) C[anchor]
-          const gptr<bf16_t> cb = as_global(reinterpret_cast<const bf16_t*>(p.codebook)) +
-                                  (size_t)p.anchor[(m < p.M ? m : 0) / p.W] * p.r + col;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) z[v] = p.code_scale * Elt<bf16_t>::gload(cb, v);
+          for (int v = 0; v < 4; ++v) z[v] = p.code_scale * cbv[mt][v];
         }
         float ss = ((z[0] * z[0] + z[1] * z[1]) + z[2] * z[2]) + z[3] * z[3];
         ss += __shfl_xor(ss, 16, 64);
@@ -376,19 +390,21 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
   if (tid == 0) s_ok = wait_count(ctr(1), (uint32_t)U2, ctr(3)) ? 1 : 0;
   __syncthreads();
   if (s_ok) {
+    // every wave multiplies all of m: the workgroup reads it from memory
+    // once (8 values per thread and pass) and the waves take their
+    // fragments from LDS
+    constexpr int LDM = kF3 * 32 + 8;
+    const int cpr = p.a / 8;                          // 8-value chunks per row
+    for (int c = tid; c < MT * 16 * cpr; c += 256) {
+      const int m = c / cpr, k8 = c % cpr;
+      const u32x4 v = load_coherent_u32x4(reinterpret_cast<const f16_t*>(p.msg) + (size_t)(m < p.M ? m : p.M - 1) * p.a +
+                                          8 * k8);
+      *reinterpret_cast<u32x4*>(&s_msg[m * LDM + 8 * k8]) = v;
+    }
+    __syncthreads();
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0, 0, 0, 0};
-    u32x4 mv[kF3][MT];
-#pragma unroll
-    for (int f = 0; f < kF3; ++f)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + (lane & 15);
-        if (f < F)
-          mv[f][mt] = load_coherent_u32x4(reinterpret_cast<const f16_t*>(p.msg) + (size_t)(m < p.M ? m : p.M - 1) * p.a +
-                                          32 * f + 8 * (lane >> 4));
-      }
 #pragma unroll
     for (int f = 0; f < kF3; ++f) {
       if (f >= F) continue;
@@ -396,7 +412,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         Frag<f16_t> b;
-        b.v = mv[f][mt];
+        b.v = *reinterpret_cast<const u32x4*>(&s_msg[(mt * 16 + (lane & 15)) * LDM + 32 * f + 8 * (lane >> 4)]);
         mma16(acc[mt], w, b);
       }
     }
