@@ -232,6 +232,7 @@ hipError_t launch_rowstats(const RowParams& p, hipStream_t s);
 constexpr int kKvLayers = 8;       // draft layers stored by one K/V store launch
 struct KvStoreParams {
   int32_t rows, nkv, D, n_req, n_layers;
+  int32_t lpw;                    // layers per workgroup (set by the launcher)
   const float* kv;                // fp32 [rows, ld]: layer l's k at l*2*kvd, v at (2l+1)*kvd
   int32_t ld;
   float eps, rope_theta;

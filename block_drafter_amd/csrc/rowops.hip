@@ -173,62 +173,72 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const RowParams p)
 // its D/4 threads in a fixed butterfly order.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void kv_store_kernel(const KvStoreParams p) {
-  extern __shared__ float sm[];   // (cos, sin) x D/2, then nkv*D raw keys
-  const int row = blockIdx.x, l = blockIdx.y;
+  extern __shared__ __align__(16) float sm[];   // (cos, sin) x D/2, then nkv*D raw keys, then nkv head sums
+  const int row = blockIdx.x;
   int b = 0;
   while (b + 1 < p.n_req && row >= p.row0[b + 1]) ++b;
   const int64_t t = p.pos0[b] + (row - p.row0[b]);
-  if (t < p.keep_lo[l][b]) return;
   const int D = p.D, half = D / 2, n = p.nkv * D;
   float* cs = sm;
   float* kraw = sm + D;
-  const float* kr = p.kv + (size_t)row * p.ld + p.col[l];
-  const float* vr = kr + n;
   for (int j = threadIdx.x; j < half; j += kRowThreads) rope_pair(t, j, D, p.rope_theta, cs[2 * j], cs[2 * j + 1]);
-  const int S = p.S[l];
-  const size_t slot = (size_t)ring_slot(t, S);
-  const size_t cap = (size_t)p.cap[l][b];
-  const T* gk = reinterpret_cast<const T*>(p.gk[l]);
-  // the head sum needs the D/4 threads of a head inside one wave: 4 * 64 >= D
-  for (int e0 = 4 * threadIdx.x; e0 < n; e0 += 4 * kRowThreads) {
-    const float4 kv4 = *reinterpret_cast<const float4*>(kr + e0);
-    kraw[e0] = kv4.x;
-    kraw[e0 + 1] = kv4.y;
-    kraw[e0 + 2] = kv4.z;
-    kraw[e0 + 3] = kv4.w;
-    float ss = ((kv4.x * kv4.x + kv4.y * kv4.y) + kv4.z * kv4.z) + kv4.w * kv4.w;
-    for (int o = 1; o < D / 4; o <<= 1) ss += __shfl_xor(ss, o, 64);
-    kraw[n + e0 / D] = ss;                                  // per-head sum (same in all its threads)
-    // v: FP16_RNE(BF16(v)) (or float), 4 consecutive elements
-    const float4 v4 = *reinterpret_cast<const float4*>(vr + e0);
-    const int hh = e0 / D, d = e0 % D;
-    const size_t vi = ((size_t)hh * cap + slot) * D + d;
-    const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+  // layers [l0, l1) of this row (the rotation table is shared by them)
+  const int l0 = blockIdx.y * p.lpw, l1 = l0 + p.lpw < p.n_layers ? l0 + p.lpw : p.n_layers;
+  for (int l = l0; l < l1; ++l) {
+    if (t < p.keep_lo[l][b]) continue;                        // uniform over the workgroup
+    const float* kr = p.kv + (size_t)row * p.ld + p.col[l];
+    const float* vr = kr + n;
+    const int S = p.S[l];
+    const size_t slot = (size_t)ring_slot(t, S);
+    const size_t cap = (size_t)p.cap[l][b];
+    const T* gk = reinterpret_cast<const T*>(p.gk[l]);
+    // the head sum needs the D/4 threads of a head inside one wave: 4 * 64 >= D
+    for (int e0 = 4 * threadIdx.x; e0 < n; e0 += 4 * kRowThreads) {
+      const float4 kv4 = *reinterpret_cast<const float4*>(kr + e0);
+      *reinterpret_cast<float4*>(kraw + e0) = kv4;
+      float ss = ((kv4.x * kv4.x + kv4.y * kv4.y) + kv4.z * kv4.z) + kv4.w * kv4.w;
+      for (int o = 1; o < D / 4; o <<= 1) ss += __shfl_xor(ss, o, 64);
+      kraw[n + e0 / D] = ss;                                  // per-head sum (same in all its threads)
+      // v: FP16_RNE(BF16(v)) (or float), 4 consecutive elements in one store
+      const float4 v4 = *reinterpret_cast<const float4*>(vr + e0);
+      const int hh = e0 / D, d = e0 % D;
+      const size_t vi = ((size_t)hh * cap + slot) * D + d;
+      if constexpr (Elt<T>::kBytes == 2) {
+        auto h = [](float v) { return (uint32_t)f32_to_f16_bits(bf16_bits_to_f32(f32_to_bf16_bits(v))); };
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.vring[l][b]) + vi) =
+            uint2{h(v4.x) | (h(v4.y) << 16), h(v4.z) | (h(v4.w) << 16)};
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.vring[l][b]) + vi) = v4;
+      }
+    }
+    __syncthreads();
+    // k: head norm, rotation of the pairs (j, j + D/2), two consecutive j per thread
+    for (int e = threadIdx.x; e < p.nkv * half / 2; e += kRowThreads) {
+      const int hh = e / (half / 2), j = 2 * (e % (half / 2));
+      const float inv = rsqrtf(kraw[n + hh] / D + p.eps);
+      float lo[2], hi[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if constexpr (Elt<T>::kBytes == 2)
-        reinterpret_cast<uint16_t*>(p.vring[l][b])[vi + u] = f32_to_f16_bits(bf16_bits_to_f32(f32_to_bf16_bits(vv[u])));
-      else
-        reinterpret_cast<float*>(p.vring[l][b])[vi + u] = vv[u];
+      for (int u = 0; u < 2; ++u) {
+        const float a = kraw[hh * D + j + u] * inv * Elt<T>::load(gk, j + u);
+        const float c = kraw[hh * D + j + u + half] * inv * Elt<T>::load(gk, j + u + half);
+        const float co = cs[2 * (j + u)], si = cs[2 * (j + u) + 1];
+        lo[u] = a * co - c * si;
+        hi[u] = c * co + a * si;
+      }
+      const size_t base = ((size_t)hh * cap + slot) * D;
+      if constexpr (Elt<T>::kBytes == 2) {
+        uint16_t* K = reinterpret_cast<uint16_t*>(p.kring[l][b]);
+        *reinterpret_cast<uint32_t*>(K + base + j) =
+            (uint32_t)f32_to_bf16_bits(lo[0]) | ((uint32_t)f32_to_bf16_bits(lo[1]) << 16);
+        *reinterpret_cast<uint32_t*>(K + base + j + half) =
+            (uint32_t)f32_to_bf16_bits(hi[0]) | ((uint32_t)f32_to_bf16_bits(hi[1]) << 16);
+      } else {
+        float* K = reinterpret_cast<float*>(p.kring[l][b]);
+        *reinterpret_cast<float2*>(K + base + j) = float2{lo[0], lo[1]};
+        *reinterpret_cast<float2*>(K + base + j + half) = float2{hi[0], hi[1]};
+      }
     }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < p.nkv * half; e += kRowThreads) {
-    const int hh = e / half, j = e % half;
-    const float inv = rsqrtf(kraw[n + hh] / D + p.eps);
-    const float a = kraw[hh * D + j] * inv * Elt<T>::load(gk, j);
-    const float c = kraw[hh * D + j + half] * inv * Elt<T>::load(gk, j + half);
-    const float co = cs[2 * j], si = cs[2 * j + 1];
-    const size_t base = ((size_t)hh * cap + slot) * D;
-    if constexpr (Elt<T>::kBytes == 2) {
-      uint16_t* K = reinterpret_cast<uint16_t*>(p.kring[l][b]);
-      K[base + j] = f32_to_bf16_bits(a * co - c * si);
-      K[base + j + half] = f32_to_bf16_bits(c * co + a * si);
-    } else {
-      float* K = reinterpret_cast<float*>(p.kring[l][b]);
-      K[base + j] = a * co - c * si;
-      K[base + j + half] = c * co + a * si;
-    }
+    __syncthreads();                                          // kraw is rewritten by the next layer
   }
 }
 
@@ -340,7 +350,11 @@ hipError_t launch_rowstats(const RowParams& p, hipStream_t s) {
 hipError_t launch_kv_store(const KvStoreParams& p, int dtype, hipStream_t s) {
   if (p.n_layers < 1 || p.n_layers > kKvLayers || p.D % 4 || 4 * 64 < p.D) return hipErrorInvalidValue;
   const size_t smem = (size_t)(p.D + p.nkv * p.D + p.nkv) * sizeof(float);
-  DSPINE_DISPATCH(dtype, kv_store_kernel, dim3(p.rows, p.n_layers), dim3(kRowThreads), smem, s, p);
+  // many rows: one workgroup per row walks every layer (one rotation table,
+  // a fifth of the workgroups); few rows: one per row and layer, for width
+  KvStoreParams q = p;
+  q.lpw = p.rows >= 1024 ? p.n_layers : 1;
+  DSPINE_DISPATCH(dtype, kv_store_kernel, dim3(p.rows, (p.n_layers + q.lpw - 1) / q.lpw), dim3(kRowThreads), smem, s, q);
   return hipGetLastError();
 }
 hipError_t launch_pack(const void* src, void* dst, int rows, int cols, int dtype, hipStream_t s) {
