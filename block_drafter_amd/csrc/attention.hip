@@ -66,7 +66,10 @@ __device__ __forceinline__ void load_vt(Frag<float>& f, const float* row, int q)
 template <typename TQ, typename TV, int D, int GRP>
 struct AttnShape {
   static constexpr int EQ = (int)sizeof(TQ), EV = (int)sizeof(TV);
-  static constexpr int LDQ = D + 16 / EQ;               // padded row of Q / K tiles
+  // padded row of Q / K tiles: with 16 halves of padding (72 words at D =
+  // 128) the 16 lanes that one cycle of a 128-bit LDS read serves land on
+  // distinct banks (8 halves left pairs of them on one bank)
+  static constexpr int LDQ = D + (EQ == 2 ? 16 : 16 / EQ);
   static constexpr int LDV = 32 + 16 / EV;              // padded row of V^T tiles (32 keys)
   static constexpr int K_BYTES = 32 * LDQ * EQ;
   static constexpr int V_BYTES = D * LDV * EV;
