@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
         v = f32x4{v[0] + rho * acc[mt][0], v[1] + rho * acc[mt][1], v[2] + rho * acc[mt][2], v[3] + rho * acc[mt][3]};
         *reinterpret_cast<f32x4*>(p.x + (size_t)m * p.H + col) = v;
         xn[mt] = v;
-        sq = ((v[0] * v[0] + v[1] * v[1]) + v[2] * v[2]) + v[3] * v[3];
+        sq = sumsq4(v[0], v[1], v[2], v[3]);
       }
       sq += __shfl_xor(sq, 16, 64);
       sq += __shfl_xor(sq, 32, 64);

@@ -492,6 +492,39 @@ int set_prescaled_a(GemmParams& gp, const dspine_geometry& g, int M, int W, cons
 }
 bool prescale_pays(const dspine_geometry& g, int M, int K) { return g.dtype == DSPINE_BF16 && M <= 16 && K % 512 == 0; }
 
+// The norm of a raw-row operand applied after the product: the epilogue
+// multiplies row m's products by its row scale (mode, from the statistics
+// lists st), a per-row factor of the contraction
+void set_post_scale(GemmParams& gp, const dspine_geometry& g, int W, int mode, const float* st, int lists, float n,
+                    float mult = 1.f) {
+  gp.post_scale = 1;
+  gp.post_mult = mult;
+  gp.scale_mode = mode;
+  gp.stats_in = st;
+  gp.stats_tiles = lists;
+  gp.stats_ld = kMaxRows;
+  gp.scale_n = n;
+  gp.eps = g.eps;
+  gp.code_scale = sqrtf((float)std::max(g.code_dim, 1));
+  gp.W = W;
+}
+// The epilogue also stores a 16-bit copy of its output (times mult and
+// gain[n]) as the next GEMM's operand
+void set_copy(GemmParams& gp, void* dst, int ld, bool bf16, const void* gain, float mult = 1.f) {
+  gp.out_copy = dst;
+  gp.ld_copy = ld;
+  gp.copy_bf16 = bf16 ? 1 : 0;
+  gp.copy_gain = gain;
+  gp.copy_mult = mult;
+}
+// Raw residual rows (not yet normalised) travel as fp16 times 2^-8: fp16's
+// 11-bit precision (bf16 copies, with 8 bits, took the 27B B=8 forward's
+// error against the oracle from about 0.009 to 0.021) with headroom up to
+// |x g| of about 1.7e7;
+// entries below 2^-6 lose relative precision but keep an absolute error
+// under 2^-16.  The consuming GEMM multiplies its products back by 2^8.
+constexpr float kRawCopy = 1.f / 256.f, kRawPost = 256.f;
+
 }  // namespace
 
 const LaunchTimer* dspine::take_launch_timer() {
@@ -918,7 +951,8 @@ namespace {
 int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const float* xst, int xst_tiles,
                float* st_out, const int32_t* anchor_ids, const float* pred_codes, char* ws, const Plan& P,
                int cus, hipStream_t stream, const void* next_gain = nullptr, void* next_act = nullptr,
-               float* next_out = nullptr, bool* folded = nullptr) {
+               float* next_out = nullptr, bool* folded = nullptr, const void* x16 = nullptr,
+               void* copy_out = nullptr, const void* copy_gain = nullptr) {
   const dspine_geometry& g = m.g;
   const dspine_weights& wt = m.w;
   const int M = B * W, H = g.hidden, r = g.code_dim, a = g.msg_dim;
@@ -971,8 +1005,19 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
   // sqrt(r) C[anchor] (their code); statistics of z for the code norm
   GemmParams gp = gemm_base(P, ws, H, M);
   set_segments(gp, {{m.pw.layer[layer].R, r}});
-  int rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RHO_INV, xst, xst_tiles, (float)H, nullptr, ws + P.act_h, stream);
-  if (rc) return rc;
+  int rc = DSPINE_OK;
+  if (x16) {
+    // fp16 rows of x (stored by the down projection); 1 / (rho + eps) after
+    // the product, and fp16(z) stored beside z as the next operand
+    gp.pro = PRO_COPY;
+    gp.a = x16;
+    gp.lda = H;
+    set_post_scale(gp, g, W, SCALE_RHO_INV, xst, xst_tiles, (float)H, kRawPost);
+    set_copy(gp, ws + P.act_r, r, false, nullptr);
+  } else if ((rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RHO_INV, xst, xst_tiles, (float)H, nullptr, ws + P.act_h,
+                                stream))) {
+    return rc;
+  }
   gp.epi = EPI_STORE;
   gp.out = z;
   gp.ldo = r;
@@ -988,8 +1033,16 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
   // [G; G_p; A] c with c = sqrt(r) z / (||z|| + eps) (anchor rows: z as is)
   gp = gemm_base(P, ws, r, M);
   set_segments(gp, {{m.pw.bridge_G, a}, {m.pw.bridge_Gp, a}, {m.pw.bridge_A, a}});
-  rc = set_scaled_a(gp, g, M, W, z, r, r, SCALE_CODE, stz, stat_tiles(r), (float)r, nullptr, ws + P.act_r, stream);
-  if (rc) return rc;
+  if (x16) {
+    // fp16(z) from the R projection; the code norm after the product
+    gp.pro = PRO_COPY;
+    gp.a = ws + P.act_r;
+    gp.lda = r;
+    set_post_scale(gp, g, W, SCALE_CODE, stz, stat_tiles(r), (float)r);
+  } else if ((rc = set_scaled_a(gp, g, M, W, z, r, r, SCALE_CODE, stz, stat_tiles(r), (float)r, nullptr,
+                                ws + P.act_r, stream))) {
+    return rc;
+  }
   gp.epi = EPI_STORE;
   gp.out = Pb;
   gp.ldo = 3 * a;
@@ -1048,6 +1101,7 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
   gp.ldo = H;
   gp.stats_out = st_out;
   gp.stats_out_ld = kMaxRows;
+  if (copy_out) set_copy(gp, copy_out, H, false, copy_gain, kRawCopy);   // the next layer's operand
   HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
   return DSPINE_OK;
 }
@@ -1198,6 +1252,14 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
   // act_ready: act_h holds this layer's operand.
   const bool fold_norm = !conv && (prescale_pays(g, M, H) || M > gemm_stream_fused_rows());
   bool act_ready = false;
+  // Blocks of more than 32 rows of a BF16 model (no convolution): after
+  // layer 0, every norm is applied after the product that consumes it (a
+  // per-row factor of the contraction), to raw rows times the norm's gain
+  // that the GEMM writing those rows stores beside them as fp16 (scaled by
+  // 2^-8), so no pre-scale kernel runs.  copy_ready: act_h holds that copy
+  // of x g_in for this layer.
+  const bool post = !conv && g.dtype == DSPINE_BF16 && M > gemm_stream_fused_rows();
+  bool copy_ready = false;
   if (head_act_ready) *head_act_ready = false;
   if (fold_norm) {
     rp.act = ws + P.act_h;
@@ -1251,6 +1313,11 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
       gp.pro = PRO_COPY;
       gp.a = ws + P.act_h;
       gp.lda = H;
+    } else if (copy_ready) {
+      gp.pro = PRO_COPY;
+      gp.a = ws + P.act_h;
+      gp.lda = H;
+      set_post_scale(gp, g, W, SCALE_RMSNORM, xst, xst_tiles, (float)H, kRawPost);
     } else if (prescale_pays(g, M, H)) {
       // the same operand from the pre-scale kernel (at B=1 the q|k|v GEMM
       // went 142 -> 103 us per forward with these kernels counted)
@@ -1269,6 +1336,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
     }
     act_ready = false;                    // act_h is reused below
+    copy_ready = false;
 
     // a6 (with the q/k head norm + RoPE of a5)
     AttnParams ap;
@@ -1329,6 +1397,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     gp.ldo = H;
     gp.stats_out = conv ? nullptr : st0;
     gp.stats_out_ld = kMaxRows;
+    if (post) set_copy(gp, ws + P.act_h, H, false, Lw.g_post, kRawCopy);     // y g_post for gate/up
     {
       ProfScope ps(DSPINE_PROF_GEMM_O, stream);
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
@@ -1376,6 +1445,11 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
       gp.pro = PRO_COPY;
       gp.a = ws + P.act_h;
       gp.lda = H;
+    } else if (post) {
+      gp.pro = PRO_COPY;
+      gp.a = ws + P.act_h;
+      gp.lda = H;
+      set_post_scale(gp, g, W, SCALE_RMSNORM, st0, tH, (float)H, kRawPost);
     } else if ((rc = set_scaled_a(gp, g, M, W, x, H, H, SCALE_RMSNORM, st0, tH, (float)H, Lw.g_post, ws + P.act_h,
                                   stream))) {
       return rc;
@@ -1401,12 +1475,16 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     gp.ldo = H;
     gp.stats_out = conv ? nullptr : st1;
     gp.stats_out_ld = kMaxRows;
+    const bool more = l + 1 < g.n_layers;
+    if (post && g.code_dim > 0) set_copy(gp, ws + P.act_h, H, false, nullptr, kRawCopy);   // x for R
+    else if (post && more) set_copy(gp, ws + P.act_h, H, false, wt.layer[l + 1].g_in, kRawCopy);
     {
       ProfScope ps(DSPINE_PROF_GEMM_DOWN, stream);
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
     }
     xst = st1;
     xst_tiles = tH;
+    copy_ready = post && g.code_dim == 0 && more;
     if (conv) {
       // x_next = y + Conv_1(z) with the MLP prepare's delta
       ConvParams cp = conv_params(g, M, W, conv_dm, Lw.mlp_conv_base);
@@ -1429,7 +1507,10 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
       bool folded = false;
       if (last)
         rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream, wt.g_final,
-                        want_head_act ? ws + P.act_h : nullptr, out, &folded);
+                        want_head_act ? ws + P.act_h : nullptr, out, &folded, post ? ws + P.act_h : nullptr);
+      else if (post)
+        rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream, nullptr,
+                        nullptr, nullptr, nullptr, ws + P.act_h, ws + P.act_h, wt.layer[l + 1].g_in);
       else if (fold_norm)
         rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream,
                         wt.layer[l + 1].g_in, ws + P.act_h, nullptr, &folded);
@@ -1443,6 +1524,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
         return DSPINE_OK;
       }
       act_ready = folded;
+      copy_ready = post && !last;
     }
   }
   // a12

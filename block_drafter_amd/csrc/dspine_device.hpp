@@ -38,6 +38,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 }
 // float -> the nearest bfloat16 value (RNE), as a float
 __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
+// Sum of squares of four values in one fixed evaluation (explicit fused
+// multiply-adds): the kernels whose row statistics must agree bit for bit
+// (a GEMM epilogue and the fused bridge) do not depend on how the compiler
+// would contract the plain expression in each of them
+__device__ __forceinline__ float sumsq4(float a, float b, float c, float d) {
+  return __builtin_fmaf(d, d, __builtin_fmaf(c, c, __builtin_fmaf(b, b, a * a)));
+}
 // float -> IEEE half bits, round to nearest even (hardware conversion).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   _Float16 h = (_Float16)f;

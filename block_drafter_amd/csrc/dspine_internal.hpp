@@ -99,6 +99,19 @@ struct GemmParams {
   int32_t out_act_bf16;           // EPI_SWIGLU of a BF16 model: store bf16 (the hidden's full range)
   float* stats_out;               // or NULL: [n / 64][stats_out_ld] sums of squares of the stored rows
   int32_t stats_out_ld;
+  // EPI_STORE / EPI_SWIGLU with post_scale: the products of row m times its
+  // row scale (scale_mode, from stats_in) before the epilogue's operation;
+  // the norm of an operand applied after the contraction (it is a per-row
+  // factor), so that the operand can be the raw rows
+  int32_t post_scale;
+  float post_mult;                // and times post_mult (the inverse of the operand copy's copy_mult)
+  // EPI_STORE / EPI_ADD / EPI_ADD_ROWSCALE: a 16-bit copy of the stored
+  // values times copy_mult (and copy_gain[n] when given) into out_copy
+  // [M, ld_copy], bf16 when copy_bf16 (else fp16): the next GEMM's operand
+  void* out_copy;
+  int32_t ld_copy, copy_bf16;
+  float copy_mult;
+  const void* copy_gain;          // [N] bf16, or NULL
   // FP8 weights (w_fp8): E4M3 codes in fragment order, read as value / 256;
   // EPI_STORE multiplies output column n by col_scale[n]
   int32_t w_fp8;

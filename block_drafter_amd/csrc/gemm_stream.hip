@@ -566,14 +566,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
           const int m = mb * 16 + (lane & 15);
           if (m < p.M) {
             const size_t e = (size_t)m * p.ld_act + j * 16 + nl;
+            const float rs = p.post_scale ? s_scale[m] * p.post_mult : 1.f;   // the norm after the product
             if (p.out_act_bf16) {
 #pragma unroll
               for (int v = 0; v < 4; ++v)
-                Elt<bf16_t>::store(reinterpret_cast<bf16_t*>(p.out_act) + e, v, silu(acc[2 * i][mb][v]) * acc[2 * i + 1][mb][v]);
+                Elt<bf16_t>::store(reinterpret_cast<bf16_t*>(p.out_act) + e, v,
+                                   silu(rs * acc[2 * i][mb][v]) * (rs * acc[2 * i + 1][mb][v]));
             } else {
 #pragma unroll
               for (int v = 0; v < 4; ++v)
-                Elt<T>::store(reinterpret_cast<T*>(p.out_act) + e, v, silu(acc[2 * i][mb][v]) * acc[2 * i + 1][mb][v]);
+                Elt<T>::store(reinterpret_cast<T*>(p.out_act) + e, v,
+                              silu(rs * acc[2 * i][mb][v]) * (rs * acc[2 * i + 1][mb][v]));
             }
           }
         }
@@ -586,6 +589,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       for (int nb = 0; nb < NWB; ++nb) {
         const int vb = tile * WG_BLKS + wave * NWB + nb;
         if (vb >= p.nblk) continue;
+        // the copy's gains go out with the residual loads below
+        float cg[4] = {1.f, 1.f, 1.f, 1.f};
+        if (p.out_copy && p.copy_gain) {
+          const gptr<bf16_t> gp = as_global(reinterpret_cast<const bf16_t*>(p.copy_gain)) + vb * 16 + nl;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) cg[v] = Elt<bf16_t>::gload(gp, v);
+        }
 #pragma unroll
         for (int mb = 0; mb < MT; ++mb) {
           const int m = mb * 16 + (lane & 15);
@@ -598,6 +608,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
             val = *o + s_scale[m] * acc[nb][mb];
           } else {
             val = acc[nb][mb];
+            if (p.post_scale) {                       // the operand's row norm, after the product
+              const float rs = s_scale[m] * p.post_mult;
+              val = f32x4{val[0] * rs, val[1] * rs, val[2] * rs, val[3] * rs};
+            }
             if constexpr (sizeof(TW) == 1) {          // FP8 rows: codes read as value / 256
               const f32x4 cs = *as_global(reinterpret_cast<const f32x4*>(p.col_scale + vb * 16 + nl));
               val = f32x4{val[0] * cs[0], val[1] * cs[1], val[2] * cs[2], val[3] * cs[3]};
@@ -610,7 +624,22 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
             }
           }
           *o = val;
-          sq[mb] += ((val[0] * val[0] + val[1] * val[1]) + val[2] * val[2]) + val[3] * val[3];
+          if (p.out_copy) {                           // the next GEMM's 16-bit operand
+            float cv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cv[v] = val[v] * p.copy_mult * cg[v];
+            const size_t e = (size_t)m * p.ld_copy + vb * 16 + nl;
+            uint32_t w0, w1;
+            if (p.copy_bf16) {
+              w0 = (uint32_t)f32_to_bf16_bits(cv[0]) | ((uint32_t)f32_to_bf16_bits(cv[1]) << 16);
+              w1 = (uint32_t)f32_to_bf16_bits(cv[2]) | ((uint32_t)f32_to_bf16_bits(cv[3]) << 16);
+            } else {
+              w0 = (uint32_t)f32_to_f16_bits(cv[0]) | ((uint32_t)f32_to_f16_bits(cv[1]) << 16);
+              w1 = (uint32_t)f32_to_f16_bits(cv[2]) | ((uint32_t)f32_to_f16_bits(cv[3]) << 16);
+            }
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out_copy) + e) = uint2{w0, w1};
+          }
+          sq[mb] += sumsq4(val[0], val[1], val[2], val[3]);
         }
       }
       // Sums of squares per row over each 64 output columns, in a fixed
@@ -652,7 +681,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   // out before the weight stages, so that waiting for it does not wait for
   // the weights (the memory counter retires in issue order).
   constexpr int Q = 256 / MP;
-  constexpr int LB = 8;                             // statistics loads per batch
+  // statistics loads per batch: with 64 rows and more a thread takes 40 of
+  // its row's lists at once (80 lists at H = 5120 otherwise cost five
+  // serial round trips before the first weight stage)
+  constexpr int LB = MP >= 64 ? 40 : 8;
   const bool scaled = p.scale_mode != SCALE_NONE && p.scale_mode != SCALE_ONE;
   const int sm = tid % MP, sq0 = tid / MP;
   const gptr<float> st = as_global(p.stats_in) + (sm < p.M ? sm : 0);
