@@ -30,7 +30,9 @@
 //
 // Optionally (next_act / next_out) group 3 also forms the next RMS norm of
 // its columns once every group-3 workgroup has published its statistics (a
-// fourth wait), so that no separate norm or pre-scale kernel follows.
+// fourth wait), so that no separate norm or pre-scale kernel follows; or
+// (copy_out) it stores its columns of x times the next norm's gain as fp16
+// at once, and the next q|k|v GEMM applies the norm after its product.
 //
 // Every workgroup loads its weights into registers before it waits, so the
 // three groups' HBM reads overlap.  Results that cross workgroups travel by
@@ -380,8 +382,8 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
     xn[mt] = *reinterpret_cast<const f32x4*>(p.x + (size_t)(m < p.M ? m : p.M - 1) * p.H + col);
   }
   float gv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (fold) {
-    const gptr<bf16_t> gn = as_global(reinterpret_cast<const bf16_t*>(p.next_gain)) + col;
+  if (fold || p.copy_out) {
+    const gptr<bf16_t> gn = as_global(reinterpret_cast<const bf16_t*>(fold ? p.next_gain : p.copy_gain)) + col;
 #pragma unroll
     for (int e = 0; e < 4; ++e) gv[e] = Elt<bf16_t>::gload(gn, e);
   }
@@ -426,6 +428,13 @@ __global__ __launch_bounds__(256) void bridge_fused_kernel(const BridgeParams p)
         v = f32x4{v[0] + rho * acc[mt][0], v[1] + rho * acc[mt][1], v[2] + rho * acc[mt][2], v[3] + rho * acc[mt][3]};
         *reinterpret_cast<f32x4*>(p.x + (size_t)m * p.H + col) = v;
         xn[mt] = v;
+        if (p.copy_out) {                             // the next layer's raw operand
+          float c[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c[e] = v[e] * p.copy_mult * gv[e];
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.copy_out) + (size_t)m * p.H + col) =
+              uint2{pack_f16x2(c[0], c[1]), pack_f16x2(c[2], c[3])};
+        }
         sq = sumsq4(v[0], v[1], v[2], v[3]);
       }
       sq += __shfl_xor(sq, 16, 64);

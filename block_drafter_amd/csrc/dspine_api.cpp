@@ -992,6 +992,10 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
       bp.next_act = next_act;
       bp.next_out = next_out;
       if (folded) *folded = true;
+    } else if (copy_out) {
+      bp.copy_out = copy_out;
+      bp.copy_gain = copy_gain;
+      bp.copy_mult = kRawCopy;
     }
     HIP_TRY(launch_bridge_fused(bp, stream));
     return DSPINE_OK;
@@ -1259,6 +1263,10 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
   // 2^-8), so no pre-scale kernel runs.  copy_ready: act_h holds that copy
   // of x g_in for this layer.
   const bool post = !conv && g.dtype == DSPINE_BF16 && M > gemm_stream_fused_rows();
+  // 16 rows and fewer (BF16): the bridge stores the same kind of copy for
+  // the layers after the first, instead of waiting for every column to form
+  // the next norm itself
+  const bool copy16 = !conv && prescale_pays(g, M, H);
   bool copy_ready = false;
   if (head_act_ready) *head_act_ready = false;
   if (fold_norm) {
@@ -1511,9 +1519,11 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
       else if (post)
         rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream, nullptr,
                         nullptr, nullptr, nullptr, ws + P.act_h, ws + P.act_h, wt.layer[l + 1].g_in);
-      else if (fold_norm)
-        rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream,
-                        wt.layer[l + 1].g_in, ws + P.act_h, nullptr, &folded);
+      else if (copy16)
+        // the next layer's operand as a raw copy: its norm is applied after
+        // the q|k|v product, so the bridge does not wait for every column
+        rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream, nullptr,
+                        nullptr, nullptr, nullptr, nullptr, ws + P.act_h, wt.layer[l + 1].g_in);
       else
         rc = run_bridge(*model, l, B, W, x, xst, xst_tiles, st0, anchor_ids, nullptr, ws, P, cus, stream);
       if (rc) return rc;
@@ -1524,7 +1534,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
         return DSPINE_OK;
       }
       act_ready = folded;
-      copy_ready = post && !last;
+      copy_ready = (post || copy16) && !last;
     }
   }
   // a12

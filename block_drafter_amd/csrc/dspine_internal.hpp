@@ -310,6 +310,12 @@ struct BridgeParams {
   const void* next_gain;          // [H] bf16
   void* next_act;                 // fp16 [M, H] or NULL
   float* next_out;                // fp32 [M, H] or NULL
+  // Or (copy_out): group 3 stores fp16(x * copy_gain * copy_mult) of its
+  // columns, the next layer's raw operand, whose norm its q|k|v GEMM applies
+  // after the product; no fourth phase
+  void* copy_out;                 // fp16 [M, H] or NULL
+  const void* copy_gain;          // [H] bf16
+  float copy_mult;
 };
 hipError_t launch_bridge_fused(const BridgeParams& p, hipStream_t s);
 // true if the fused bridge takes this geometry and M rows on num_cus CUs
