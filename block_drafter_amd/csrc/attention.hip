@@ -77,15 +77,19 @@ struct AttnShape {
   static constexpr int Q_BYTES = GRP * 16 * LDQ * EQ;
   static constexpr int PART = 64 * (D / 4 + 2) * 4;     // one wave's (o, m, l) in LDS
   static constexpr int LIMIT = 156 * 1024;
-  static constexpr bool fits(int n) {
-    return Q_BYTES + (n + 1) * TILE <= LIMIT && GRP * (n - 1) * PART <= Q_BYTES + (n + 1) * TILE;
+  // slots tile slots per key sub-stream and the block's tile
+  static constexpr bool fits(int n, int slots) {
+    return Q_BYTES + (slots * n + 1) * TILE <= LIMIT && GRP * (n - 1) * PART <= Q_BYTES + (slots * n + 1) * TILE;
   }
   // at most 8 waves (512 threads): 256 registers per wave, two workgroups per CU
   static constexpr int NSUB_MAX = 8 / GRP < 1 ? 1 : 8 / GRP < 4 ? 8 / GRP : 4;
-  static constexpr int NSUB = (NSUB_MAX >= 4 && fits(4)) ? 4 : (NSUB_MAX >= 2 && fits(2)) ? 2 : 1;
+  static constexpr int NSUB = (NSUB_MAX >= 4 && fits(4, 1)) ? 4 : (NSUB_MAX >= 2 && fits(2, 1)) ? 2 : 1;
+  // two slots per sub-stream where they fit: a round stages its tile while
+  // other waves may still read the previous round's (one barrier a round)
+  static constexpr int NSLOT = fits(NSUB, 2) ? 2 : 1;
   static constexpr int NT = 64 * GRP * NSUB;
-  static constexpr int SMEM = Q_BYTES + (NSUB + 1) * TILE;
-  static_assert(fits(NSUB), "attention LDS");
+  static constexpr int SMEM = Q_BYTES + (NSLOT * NSUB + 1) * TILE;
+  static_assert(fits(NSUB, NSLOT), "attention LDS");
   static_assert((D / 16) % NSUB == 0, "merge split of the head dimension");
 };
 
@@ -96,7 +100,7 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
   using Sh = AttnShape<TQ, TV, D, GRP>;
   static_assert(sizeof(TW) == sizeof(TQ), "stored keys and key operands have one element size");
   constexpr int EQ = Sh::EQ, EV = Sh::EV, LDQ = Sh::LDQ, LDV = Sh::LDV;
-  constexpr int NSUB = Sh::NSUB;
+  constexpr int NSUB = Sh::NSUB, NSLOT = Sh::NSLOT;
   constexpr int GT = 64 * GRP;                          // threads of one sub-stream
   constexpr int PSZ = 64 * (D / 4) + 32;                // floats of one split partial in HBM
 
@@ -186,9 +190,9 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
       else vr_[q] = gload16(src);
     }
   };
-  auto store_tile = [&](const u32x4 (&kr_)[KPT], const u32x4 (&vr_)[VPT], int i) {
-    TQ* k_t = sK(sub);
-    TV* v_t = sVt(sub);
+  auto store_tile = [&](const u32x4 (&kr_)[KPT], const u32x4 (&vr_)[VPT], int i, int slot) {
+    TQ* k_t = sK(NSLOT * sub + slot);
+    TV* v_t = sVt(NSLOT * sub + slot);
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
       const int c = gtid + q * GT;
@@ -308,8 +312,8 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
   if (do_q) prep_store(pin, sQ + hl * 16 * LDQ);
   if (do_k) {
     if (do_q) prep_load(kcol, p.gk, pin);        // (only with one sub-stream)
-    prep_store(pin, sK(NSUB));
-    for (int e = lane; e < 16 * D; e += 64) Elt<TQ>::store(sK(NSUB), (16 + e / D) * LDQ + e % D, 0.f);
+    prep_store(pin, sK(NSLOT * NSUB));
+    for (int e = lane; e < 16 * D; e += 64) Elt<TQ>::store(sK(NSLOT * NSUB), (16 + e / D) * LDQ + e % D, 0.f);
   }
   if (do_v) {
     const int r = lane >> 2, part = lane & 3;
@@ -321,8 +325,8 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
       for (int d = 0; d < D / 4; ++d) vv[d] = src[d];
     }
 #pragma unroll
-    for (int d = 0; d < D / 4; ++d) put_v(&sVt(NSUB)[(part * (D / 4) + d) * LDV + r], live ? vv[d] : 0.f);
-    for (int e = lane; e < 16 * D; e += 64) put_v(&sVt(NSUB)[(e / 16) * LDV + 16 + (e % 16)], 0.f);
+    for (int d = 0; d < D / 4; ++d) put_v(&sVt(NSLOT * NSUB)[(part * (D / 4) + d) * LDV + r], live ? vv[d] : 0.f);
+    for (int e = lane; e < 16 * D; e += 64) put_v(&sVt(NSLOT * NSUB)[(e / 16) * LDV + 16 + (e % 16)], 0.f);
   }
   __syncthreads();
 
@@ -411,9 +415,12 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
     }
   };
 
-  // Round r stages slot r % PF and refills it with round r + PF while there
-  // is one (the number of rounds is the same for every sub-stream of the
-  // workgroup, so the barriers match).  Passes whose refills are all needed
+  // Round r stages register slot r % PF and refills it with round r + PF
+  // while there is one (the number of rounds is the same for every
+  // sub-stream of the workgroup, so the barriers match).  Its tile goes to
+  // LDS slot r % NSLOT of the sub-stream.  With two slots one barrier per
+  // round suffices: the slot a round overwrites was last read two rounds
+  // before, and every wave has passed the barrier of the round in between.  Passes whose refills are all needed
   // run without any exit or condition around the loads: with a break or a
   // skipped refill inside the unrolled pass, the compiler routes every slot
   // through one set of registers, and the copy waits for the load just
@@ -425,15 +432,15 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
       const int r = r0 + j;
       const int i = r * NSUB + sub;
       const bool live = i < n_tiles;
-      if (live) store_tile(kreg[j], vreg[j], i);
+      if (live) store_tile(kreg[j], vreg[j], i, r % NSLOT);
       __syncthreads();
       const int inext = (r + PF) * NSUB + sub;
       load_tile(kreg[j], vreg[j], inext < n_tiles ? inext : n_tiles - 1);
       if (live) {
         const bool edge = 32 * i + 32 > nkeys || 32 * i < lo_rel_max;
-        process(sub, 32 * i, false, edge);
+        process(NSLOT * sub + r % NSLOT, 32 * i, false, edge);
       }
-      __syncthreads();
+      if constexpr (NSLOT == 1) __syncthreads();   // the one slot is rewritten next round
     }
   }
   for (; r0 < rounds; r0 += PF) {
@@ -443,7 +450,7 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
       if (r >= rounds) break;
       const int i = r * NSUB + sub;
       const bool live = i < n_tiles;
-      if (live) store_tile(kreg[j], vreg[j], i);
+      if (live) store_tile(kreg[j], vreg[j], i, r % NSLOT);
       __syncthreads();
       if (r + PF < rounds) {
         const int inext = (r + PF) * NSUB + sub;
@@ -451,12 +458,12 @@ __global__ __launch_bounds__((AttnShape<TQ, TV, D, GRP>::NT)) void attention_ker
       }
       if (live) {
         const bool edge = 32 * i + 32 > nkeys || 32 * i < lo_rel_max;
-        process(sub, 32 * i, false, edge);
+        process(NSLOT * sub + r % NSLOT, 32 * i, false, edge);
       }
-      __syncthreads();
+      if constexpr (NSLOT == 1) __syncthreads();   // the one slot is rewritten next round
     }
   }
-  if (has_block && sub == NSUB - 1) process(NSUB, -1, true, true);
+  if (has_block && sub == NSUB - 1) process(NSLOT * NSUB, -1, true, true);
   __syncthreads();                                      // all tiles and Q done: LDS reused below
 
   // ---- combine the sub-streams of each head (lane-wise, through LDS) ------
