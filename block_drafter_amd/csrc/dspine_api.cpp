@@ -517,6 +517,17 @@ void set_copy(GemmParams& gp, void* dst, int ld, bool bf16, const void* gain, fl
   gp.copy_gain = gain;
   gp.copy_mult = mult;
 }
+// Blocks of more than 32 rows (BF16): GEMMs with at most 24 MB of weights
+// run as row blocks of 32 rows side by side, each with a stream-K split of
+// its own, instead of one 128-row tile row whose few column tiles are split
+// deep over K.  Every row block reads the weights again (from L2 or the
+// Infinity Cache), which larger matrices pay for: at the 27B geometry the
+// bridge's R, [G; G_p; A] and W_l went 315 -> 240 us per B=8 forward while
+// q|k|v (63 MB) and O (42 MB) went 167 -> 261 and 152 -> 204; the 35B-style
+// O (17 MB) 140 -> 119.
+void set_row_blocks(GemmParams& gp, const dspine_geometry& g, int M, int64_t N, int64_t K) {
+  if (g.dtype == DSPINE_BF16 && M > gemm_stream_fused_rows() && N * K * 2 <= ((int64_t)24 << 20)) gp.rb_rows = 32;
+}
 // Raw residual rows (not yet normalised) travel as fp16 times 2^-8: fp16's
 // 11-bit precision (bf16 copies, with 8 bits, took the 27B B=8 forward's
 // error against the oracle from about 0.009 to 0.021) with headroom up to
@@ -1027,6 +1038,7 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
   gp.ldo = r;
   gp.stats_out = stz;
   gp.stats_out_ld = kMaxRows;
+  if (x16) set_row_blocks(gp, g, M, r, H);
   gp.code_anchor = 1;
   gp.codebook = wt.codebook;
   gp.code_scale = sqrtf((float)r);
@@ -1050,6 +1062,7 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
   gp.epi = EPI_STORE;
   gp.out = Pb;
   gp.ldo = 3 * a;
+  if (x16) set_row_blocks(gp, g, M, 3 * a, r);
   HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
 
   const float* Ppred = Pb;
@@ -1106,6 +1119,7 @@ int run_bridge(const dspine_model& m, int layer, int B, int W, float* x, const f
   gp.stats_out = st_out;
   gp.stats_out_ld = kMaxRows;
   if (copy_out) set_copy(gp, copy_out, H, false, copy_gain, kRawCopy);   // the next layer's operand
+  if (x16) set_row_blocks(gp, g, M, H, a);
   HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
   return DSPINE_OK;
 }
@@ -1339,6 +1353,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     gp.epi = EPI_STORE;
     gp.out = qkv;
     gp.ldo = qd + 2 * kvd;
+    if (post) set_row_blocks(gp, g, M, qd + 2 * kvd, H);
     {
       ProfScope ps(DSPINE_PROF_GEMM_QKV, stream);
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));
@@ -1406,6 +1421,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     gp.stats_out = conv ? nullptr : st0;
     gp.stats_out_ld = kMaxRows;
     if (post) set_copy(gp, ws + P.act_h, H, false, Lw.g_post, kRawCopy);     // y g_post for gate/up
+    if (post) set_row_blocks(gp, g, M, H, qd);
     {
       ProfScope ps(DSPINE_PROF_GEMM_O, stream);
       HIP_TRY(launch_gemm_stream(gp, g.dtype, cus, stream));

@@ -67,6 +67,10 @@ struct GemmParams {
   int32_t interleave;             // 1: block vb -> segment vb&1, row block vb>>1
   int32_t nblk;                   // 16-row blocks in N
   int32_t K, M;
+  // rows per row block (16 or 32), or 0: all M rows in one tile row.  Row
+  // blocks run side by side (grid y), each with its own stream-K split:
+  // small outputs of many rows get more independent tiles
+  int32_t rb_rows;
   // A operand: activation type of the model (fp16 for BF16 models), or bf16
   // target features when a_bf16 is set
   int32_t pro;

@@ -173,6 +173,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   int g = blockIdx.x;
   if (p.xcd_remap) g = (g % 8) * (G / 8) + g / 8;   // neighbours in k-space share an XCD
 
+  // row block of this workgroup (blocks of MP rows along y; one block: 0)
+  const int m_base = blockIdx.y * MP;
   const int ipt = p.ipt;
   const int TI = p.tiles * ipt;
   const int it_beg = iter_begin(g, TI, G);
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   const void* arow[NCH];
 #pragma unroll
   for (int q = 0; q < NCH; ++q) {
-    const int m = (tid + q * 256) / CPR;
+    const int m = m_base + (tid + q * 256) / CPR;
     if constexpr (kScaledA) arow[q] = p.xa + (size_t)(m < p.M ? m : p.M - 1) * p.lda;
     else if constexpr (PRO == PRO_BRIDGE_MSG) arow[q] = nullptr;
     else arow[q] = a_row_ptr<PRO, TA>(p, m);
@@ -207,9 +209,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       const int bi = wave + 4 * q;
       if constexpr (kFullLine) {
         const int r = lane >> 3;
-        drow[q] = a_row_ptr<PRO, TA>(p, bi * 8 + r) + ((lane & 7) ^ act_swz(r, bi & 1)) * 8;
+        drow[q] = a_row_ptr<PRO, TA>(p, m_base + bi * 8 + r) + ((lane & 7) ^ act_swz(r, bi & 1)) * 8;
       } else {
-        drow[q] = a_row_ptr<PRO, TA>(p, (bi / KSUB) * 16 + (lane & 15)) + (bi % KSUB) * 32 + 8 * (lane >> 4);
+        drow[q] = a_row_ptr<PRO, TA>(p, m_base + (bi / KSUB) * 16 + (lane & 15)) + (bi % KSUB) * 32 + 8 * (lane >> 4);
       }
     }
   }
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
           areg[j][q][AR - 1] = gload16((gptr<void>)(as_global(reinterpret_cast<const TW*>(p.gain)) + kc));
       } else if constexpr (PRO == PRO_BRIDGE_MSG) {
         // A[t, k] = sigmoid(P[t, k] + Pp[tp, a + k] + b[k]) * Pp[tp, 2a + k]
-        int m = c / CPR;
+        int m = m_base + c / CPR;
         m = m < p.M ? m : p.M - 1;
         int tp = p.pred_shift ? m - 1 : m;
         tp = tp < 0 ? 0 : tp;
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
         }
       } else if constexpr (PRO == PRO_BRIDGE_MSG) {
         // receivers only: zero at anchors (m % W == 0) and past M / K
-        if (k < p.K && m < p.M && m % p.W != 0) {
+        if (k < p.K && m_base + m < p.M && (m_base + m) % p.W != 0) {
           constexpr int H4 = EPC / 4;
           alignas(16) float P[EPC], Pg[EPC], Pm[EPC];
 #pragma unroll
@@ -451,9 +453,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       const int g_first = owner_of(t0, TI, G);
       const int g_last = owner_of(t0 + ipt - 1, TI, G);
       const int ncontrib = g_last - g_first + 1;
+      // two slots per workgroup of each row block
       auto slot_of = [&](int gg) __attribute__((always_inline)) {
         const int first_tile = iter_begin(gg, TI, G) / ipt;
-        return 2 * gg + (first_tile == tile ? 0 : 1);
+        return 2 * ((int)blockIdx.y * G + gg) + (first_tile == tile ? 0 : 1);
       };
       float* mine = p.partials + (size_t)slot_of(g) * (NWB * MT * 256 * 4);
 #pragma unroll
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
         for (int mb = 0; mb < MT; ++mb) store_coherent(mine + ((nb * MT + mb) * 256 + tid) * 4, acc[nb][mb]);
       drain_own_stores();
       __syncthreads();
-      if (tid == 0) s_flag = count_arrival(p.counters + tile);
+      if (tid == 0) s_flag = count_arrival(p.counters + blockIdx.y * p.tiles + tile);
       __syncthreads();
       if ((int)s_flag != ncontrib - 1) {
 #pragma unroll
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 #pragma unroll
           for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = sum[mb];
         }
-        if (tid == 0) reset_counter(p.counters + tile);
+        if (tid == 0) reset_counter(p.counters + blockIdx.y * p.tiles + tile);
         // the repeated loads past the last contributor are never used: wait
         // for them here, or the compiler's wait before the next reuse of
         // their registers (an LDS fragment read of the next tile) would
@@ -549,7 +552,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       for (int nb = 0; nb < NWB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = sum[nb][mb];
-      if (tid == 0) reset_counter(p.counters + tile);
+      if (tid == 0) reset_counter(p.counters + blockIdx.y * p.tiles + tile);
       wait_vmcnt<0>();                             // as above
       }
     }
@@ -564,8 +567,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 #pragma unroll
         for (int mb = 0; mb < MT; ++mb) {
           const int m = mb * 16 + (lane & 15);
-          if (m < p.M) {
-            const size_t e = (size_t)m * p.ld_act + j * 16 + nl;
+          if (m_base + m < p.M) {
+            const size_t e = (size_t)(m_base + m) * p.ld_act + j * 16 + nl;
             const float rs = p.post_scale ? s_scale[m] * p.post_mult : 1.f;   // the norm after the product
             if (p.out_act_bf16) {
 #pragma unroll
@@ -598,9 +601,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
         }
 #pragma unroll
         for (int mb = 0; mb < MT; ++mb) {
-          const int m = mb * 16 + (lane & 15);
-          if (m >= p.M) continue;
-          f32x4* o = reinterpret_cast<f32x4*>(p.out + (size_t)m * p.ldo + vb * 16 + nl);
+          const int m = mb * 16 + (lane & 15);               // row in the block (s_scale)
+          const int mg = m_base + m;                            // row of the matrix
+          if (mg >= p.M) continue;
+          f32x4* o = reinterpret_cast<f32x4*>(p.out + (size_t)mg * p.ldo + vb * 16 + nl);
           f32x4 val;
           if constexpr (EPI == EPI_ADD) {
             val = *o + acc[nb][mb];
@@ -616,9 +620,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
               const f32x4 cs = *as_global(reinterpret_cast<const f32x4*>(p.col_scale + vb * 16 + nl));
               val = f32x4{val[0] * cs[0], val[1] * cs[1], val[2] * cs[2], val[3] * cs[3]};
             }
-            if (p.code_anchor && m % p.W == 0) {      // anchor code: sqrt(r) C[anchor]
+            if (p.code_anchor && mg % p.W == 0) {     // anchor code: sqrt(r) C[anchor]
               const gptr<TW> cb = as_global(reinterpret_cast<const TW*>(p.codebook)) +
-                                  (size_t)p.anchor[m / p.W] * p.ldo + vb * 16 + nl;
+                                  (size_t)p.anchor[mg / p.W] * p.ldo + vb * 16 + nl;
 #pragma unroll
               for (int v = 0; v < 4; ++v) val[v] = p.code_scale * Elt<TW>::gload(cb, v);
             }
@@ -628,7 +632,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
             float cv[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) cv[v] = val[v] * p.copy_mult * cg[v];
-            const size_t e = (size_t)m * p.ld_copy + vb * 16 + nl;
+            const size_t e = (size_t)mg * p.ld_copy + vb * 16 + nl;
             uint32_t w0, w1;
             if (p.copy_bf16) {
               w0 = (uint32_t)f32_to_bf16_bits(cv[0]) | ((uint32_t)f32_to_bf16_bits(cv[1]) << 16);
@@ -654,7 +658,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
         __syncthreads();
         constexpr int WPL = 4 / NWB;                   // waves per 64-column list
         const int nlists = (p.nblk + 3) / 4;
-        if (tid < p.M) {
+        if (m_base + tid < p.M && tid < MP) {
 #pragma unroll
           for (int jl = 0; jl < NWB; ++jl) {
             const int list = tile * NWB + jl;
@@ -662,7 +666,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
             float sum = s_red[jl * WPL][tid];
 #pragma unroll
             for (int w = 1; w < WPL; ++w) sum += s_red[jl * WPL + w][tid];
-            p.stats_out[(size_t)list * p.stats_out_ld + tid] = sum;
+            p.stats_out[(size_t)list * p.stats_out_ld + m_base + tid] = sum;
           }
         }
         __syncthreads();
@@ -687,7 +691,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   constexpr int LB = MP >= 64 ? 40 : 8;
   const bool scaled = p.scale_mode != SCALE_NONE && p.scale_mode != SCALE_ONE;
   const int sm = tid % MP, sq0 = tid / MP;
-  const gptr<float> st = as_global(p.stats_in) + (sm < p.M ? sm : 0);
+  const gptr<float> st = as_global(p.stats_in) + (m_base + sm < p.M ? m_base + sm : 0);
   float sv[LB];
   if (scaled) {
 #pragma unroll
@@ -725,7 +729,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
       float S = 0.f;
 #pragma unroll
       for (int q = 0; q < Q; ++q) S += s_part[q * MP + tid];
-      s_scale[tid] = tid < p.M ? row_scale_of(p, tid, S) : 0.f;
+      s_scale[tid] = m_base + tid < p.M ? row_scale_of(p, m_base + tid, S) : 0.f;
     }
     __syncthreads();
   }
@@ -884,6 +888,11 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
   static_assert(EPI != EPI_SWIGLU || NWB % 2 == 0, "SwiGLU pairs gate and up blocks");
   constexpr int KS = 32 * KSUB;
   grid_cap = resident_cap<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>(grid_cap, num_cus);
+  // row blocks share the resident grid and the CUs
+  const int RB = p.rb_rows > 0 ? (p.M + MT * 16 - 1) / (MT * 16) : 1;
+  if (p.rb_rows > 0 && p.rb_rows != MT * 16) return hipErrorInvalidValue;
+  grid_cap = (grid_cap + RB - 1) / RB;
+  num_cus = (num_cus + RB - 1) / RB;
   p.ipt = (p.K + KS - 1) / KS;
   p.tiles = (p.nblk + 4 * NWB - 1) / (4 * NWB);
   const int64_t TI = (int64_t)p.tiles * p.ipt;
@@ -918,10 +927,13 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
     }
     G = (int)g;
   }
-  // two partial slots per workgroup, each NWB * MT * 4 KB
-  if ((size_t)2 * G * (NWB * MT * 256 * 4) > p.partial_floats) return hipErrorInvalidValue;
+  // two partial slots per workgroup, each NWB * MT * 4 KB; a counter per
+  // tile of every row block
+  if ((size_t)2 * G * RB * (NWB * MT * 256 * 4) > p.partial_floats || (int64_t)RB * p.tiles > kMaxTiles)
+    return hipErrorInvalidValue;
   p.xcd_remap = (G % 8 == 0) ? 1 : 0;
-  DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>), dim3(G), dim3(256), 0, s, p);
+  DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>), dim3(G, RB), dim3(256), 0, s,
+                p);
   return hipGetLastError();
 }
 
@@ -950,7 +962,7 @@ int gemm_stream_fused_rows() { return 32; }
 // accumulators and the activation stages instead.
 template <typename TW, typename TA, int PRO, int EPI>
 static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipStream_t s) {
-  const int mt = (p.M + 15) / 16;
+  const int mt = ((p.rb_rows > 0 ? p.rb_rows : p.M) + 15) / 16;
   constexpr bool kHalf = Elt<TA>::kBytes == 2;
   if constexpr (sizeof(TW) == 1 && PRO == PRO_COPY) {
     // One-byte FP8 weights: 512-K stages (16 fragments of 8 bytes per
