@@ -318,6 +318,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
           __builtin_amdgcn_global_load_lds((const void*)src,
                                            (lds_void*)(adma + j * STG + SLOT + ((wave * NWB + nb) * KSUB + s) * 1024),
                                            16, 0, 2);
+        else if (gridDim.y > 1)   // row blocks: the siblings of this tile read the same lines from L2
+          wf[j][nb][s].gload(src);
         else
           wf[j][nb][s].gload_nt(src);
       }
