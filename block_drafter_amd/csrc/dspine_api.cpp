@@ -518,17 +518,22 @@ void set_copy(GemmParams& gp, void* dst, int ld, bool bf16, const void* gain, fl
   gp.copy_mult = mult;
 }
 // Blocks of more than 32 rows (BF16): GEMMs with at most 32 MB of weights
-// run as row blocks of 32 rows side by side, each with a stream-K split of
-// its own, instead of one 128-row tile row whose few column tiles are split
-// deep over K.  The row blocks of one column range run on one XCD (grid
-// widths that are multiples of 8) and read
-// the weights through its L2 (ordinary loads, not non-temporal ones);
-// larger matrices still pay for the extra reads.  B=8 per forward: at the
-// 27B geometry the bridge's R, [G; G_p; A] and W_l 315 -> 240 us, while
-// q|k|v (63 MB) went 167 -> 195 and O (42 MB) 149 -> 157; at the
-// 35B-style geometry q|k|v (25 MB) 141 -> 119 and O (17 MB) 140 -> 119.
+// run as row blocks side by side, each with a stream-K split of its own,
+// instead of one 128-row tile row whose few column tiles are split deep over
+// K: blocks of 16 rows up to 12 MB of weights, of 32 rows above.  The row
+// blocks of one column range run on one XCD (grid widths that are multiples
+// of 8) and read the weights through its L2 (ordinary loads, not
+// non-temporal ones); larger matrices still pay for the extra reads.  B=8
+// per forward: at the 27B geometry the bridge's R, [G; G_p; A] and W_l
+// 315 -> 239 us in 32-row blocks, 216 in 16-row ones, while q|k|v (63 MB)
+// went 167 -> 195 and O (42 MB) 149 -> 157 in 32-row blocks; at the
+// 35B-style geometry q|k|v (25 MB) 141 -> 121 in 32-row blocks (161 in
+// 16-row ones) and O (17 MB) 140 -> 120.
 void set_row_blocks(GemmParams& gp, const dspine_geometry& g, int M, int64_t N, int64_t K) {
-  if (g.dtype == DSPINE_BF16 && M > gemm_stream_fused_rows() && N * K * 2 <= ((int64_t)32 << 20)) gp.rb_rows = 32;
+  if (g.dtype != DSPINE_BF16 || M <= gemm_stream_fused_rows()) return;
+  const int64_t bytes = N * K * 2;
+  if (bytes <= ((int64_t)12 << 20)) gp.rb_rows = 16;
+  else if (bytes <= ((int64_t)32 << 20)) gp.rb_rows = 32;
 }
 // Raw residual rows (not yet normalised) travel as fp16 times 2^-8: fp16's
 // 11-bit precision (bf16 copies, with 8 bits, took the 27B B=8 forward's
