@@ -890,11 +890,17 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
   static_assert(EPI != EPI_SWIGLU || NWB % 2 == 0, "SwiGLU pairs gate and up blocks");
   constexpr int KS = 32 * KSUB;
   grid_cap = resident_cap<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>(grid_cap, num_cus);
-  // row blocks share the resident grid and the CUs
+  // row blocks share the resident grid and the CUs; over at most 20 MB of
+  // weights they take two workgroups per CU between them (B=8 per forward:
+  // the 27B bridge's three GEMMs 217 -> 208 us, the 35B-style O 119 -> 112;
+  // the 25 MB q|k|v went 118 -> 135 and keeps one)
   const int RB = p.rb_rows > 0 ? (p.M + MT * 16 - 1) / (MT * 16) : 1;
   if (p.rb_rows > 0 && p.rb_rows != MT * 16) return hipErrorInvalidValue;
   grid_cap = (grid_cap + RB - 1) / RB;
-  num_cus = (num_cus + RB - 1) / RB;
+  if (RB > 1) {
+    const int64_t wbytes = (int64_t)p.nblk * 16 * p.K * (int64_t)sizeof(TW);
+    num_cus = ((wbytes <= ((int64_t)20 << 20) ? 2 : 1) * num_cus + RB - 1) / RB;
+  }
   p.ipt = (p.K + KS - 1) / KS;
   p.tiles = (p.nblk + 4 * NWB - 1) / (4 * NWB);
   const int64_t TI = (int64_t)p.tiles * p.ipt;
