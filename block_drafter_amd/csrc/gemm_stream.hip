@@ -108,7 +108,9 @@ constexpr int a_regs() {
 
 }  // namespace
 
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA, bool WD>
+// TL: row-block launches, whose blocks read the same weights, load them
+// with the ordinary cache policy (single-block launches: non-temporal)
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA, bool WD, bool TL>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   using T = TA;                                 // LDS / MFMA operand type
   constexpr int EB = Elt<TA>::kBytes;
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
           __builtin_amdgcn_global_load_lds((const void*)src,
                                            (lds_void*)(adma + j * STG + SLOT + ((wave * NWB + nb) * KSUB + s) * 1024),
                                            16, 0, 2);
-        else if (gridDim.y > 1)   // row blocks: the siblings of this tile read the same lines from L2
+        else if constexpr (TL)    // row blocks: the siblings of this tile read the same lines from L2
           wf[j][nb][s].gload(src);
         else
           wf[j][nb][s].gload_nt(src);
@@ -864,12 +866,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 // Stream-K and whole-K tiles both assume every workgroup of the grid is
 // resident at once: the grid is capped at what the kernel's occupancy
 // allows on all CUs.
-template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA, bool WD>
+template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA, bool WD, bool TL>
 static int resident_cap(int grid_cap, int num_cus) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD, TL>,
                                                       256, 0) != hipSuccess ||
         n < 1)
       n = 1;
@@ -884,18 +886,18 @@ constexpr int kWholeKSteps = 16;   // MT x NWB >= 8: K iterations up to which ti
 constexpr int kMaxSplitSmall = 8;  // contributors per tile for MT <= 2 (one load batch of the finisher)
 
 template <typename TW, typename TA, int MT, int NWB, int KSUB, int PD, int PRO, int EPI, bool DMA = false,
-          bool WD = false>
+          bool WD = false, bool TL = false>
 static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t s) {
   static_assert(NWB == 1 || NWB == 2 || (WD && NWB == 4), "tile widths");
   static_assert(EPI != EPI_SWIGLU || NWB % 2 == 0, "SwiGLU pairs gate and up blocks");
   constexpr int KS = 32 * KSUB;
-  grid_cap = resident_cap<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>(grid_cap, num_cus);
+  grid_cap = resident_cap<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD, TL>(grid_cap, num_cus);
   // row blocks share the resident grid and the CUs; over at most 20 MB of
   // weights they take two workgroups per CU between them (B=8 per forward:
   // the 27B bridge's three GEMMs 217 -> 208 us, the 35B-style O 119 -> 112;
   // the 25 MB q|k|v went 118 -> 135 and keeps one)
   const int RB = p.rb_rows > 0 ? (p.M + MT * 16 - 1) / (MT * 16) : 1;
-  if (p.rb_rows > 0 && p.rb_rows != MT * 16) return hipErrorInvalidValue;
+  if (p.rb_rows > 0 && (p.rb_rows != MT * 16 || !TL)) return hipErrorInvalidValue;
   grid_cap = (grid_cap + RB - 1) / RB;
   if (RB > 1) {
     const int64_t wbytes = (int64_t)p.nblk * 16 * p.K * (int64_t)sizeof(TW);
@@ -940,7 +942,7 @@ static hipError_t launch_t(GemmParams p, int grid_cap, int num_cus, hipStream_t 
   if ((size_t)2 * G * RB * (NWB * MT * 256 * 4) > p.partial_floats || (int64_t)RB * p.tiles > kMaxTiles)
     return hipErrorInvalidValue;
   p.xcd_remap = (G % 8 == 0) ? 1 : 0;
-  DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD>), dim3(G, RB), dim3(256), 0, s,
+  DSPINE_LAUNCH((gemm_stream_kernel<TW, TA, MT, NWB, KSUB, PD, PRO, EPI, DMA, WD, TL>), dim3(G, RB), dim3(256), 0, s,
                 p);
   return hipGetLastError();
 }
@@ -972,6 +974,22 @@ template <typename TW, typename TA, int PRO, int EPI>
 static hipError_t launch_mt(const GemmParams& p, int grid_cap, int num_cus, hipStream_t s) {
   const int mt = ((p.rb_rows > 0 ? p.rb_rows : p.M) + 15) / 16;
   constexpr bool kHalf = Elt<TA>::kBytes == 2;
+  // row blocks (16 or 32 rows each): 16-bit copy operands, the small tile
+  // shapes, weights loaded with the ordinary cache policy
+  if (p.rb_rows > 0) {
+    if constexpr (kHalf && sizeof(TW) == 2 && PRO == PRO_COPY && EPI != EPI_SWIGLU) {
+      if (mt <= 1) {
+        if (p.K % 512 == 0) return launch_t<TW, TA, 1, 1, 16, 1, PRO, EPI, true, false, true>(p, grid_cap, num_cus, s);
+        if (p.K % 256 == 0) return launch_t<TW, TA, 1, 1, 8, 3, PRO, EPI, true, false, true>(p, grid_cap, num_cus, s);
+        return launch_t<TW, TA, 1, 1, 8, 3, PRO, EPI, false, false, true>(p, grid_cap, num_cus, s);
+      }
+      if (mt <= 2) {
+        if (p.K % 256 == 0) return launch_t<TW, TA, 2, 1, 8, 2, PRO, EPI, true, false, true>(p, grid_cap, num_cus, s);
+        return launch_t<TW, TA, 2, 1, 8, 3, PRO, EPI, false, false, true>(p, grid_cap, num_cus, s);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   if constexpr (sizeof(TW) == 1 && PRO == PRO_COPY) {
     // One-byte FP8 weights: 512-K stages (16 fragments of 8 bytes per
     // lane, as many bytes in flight as 16-bit weights in 256-K stages) with
