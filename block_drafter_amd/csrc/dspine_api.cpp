@@ -520,7 +520,10 @@ void set_copy(GemmParams& gp, void* dst, int ld, bool bf16, const void* gain, fl
 // Blocks of more than 32 rows (BF16): GEMMs with at most 32 MB of weights
 // run as row blocks side by side, each with a stream-K split of its own,
 // instead of one 128-row tile row whose few column tiles are split deep over
-// K: blocks of 16 rows up to 12 MB of weights, of 32 rows above.  The row
+// K: blocks of 16 rows up to 12 MB of weights, of 32 rows above and where K
+// is a single 512-K stage (W_l: the 16-row blocks left 80 column tiles to 64
+// workgroups a block, 32-row blocks give each its own; bridge 208 -> 204 us
+// per B=8 forward).  The row
 // blocks of one column range run on one XCD (grid widths that are multiples
 // of 8) and read the weights through its L2 (ordinary loads, not
 // non-temporal ones); larger matrices still pay for the extra reads.  B=8
@@ -532,7 +535,7 @@ void set_copy(GemmParams& gp, void* dst, int ld, bool bf16, const void* gain, fl
 void set_row_blocks(GemmParams& gp, const dspine_geometry& g, int M, int64_t N, int64_t K) {
   if (g.dtype != DSPINE_BF16 || M <= gemm_stream_fused_rows()) return;
   const int64_t bytes = N * K * 2;
-  if (bytes <= ((int64_t)12 << 20)) gp.rb_rows = 16;
+  if (bytes <= ((int64_t)12 << 20) && K > 512) gp.rb_rows = 16;
   else if (bytes <= ((int64_t)32 << 20)) gp.rb_rows = 32;
 }
 // Raw residual rows (not yet normalised) travel as fp16 times 2^-8: fp16's
