@@ -1401,6 +1401,20 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     }
     const int64_t spread = std::max(ceil_div(256, (int64_t)B * g.n_kv_heads), ceil_div(max_ctx, 2048));
     ap.nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({spread, ceil_div(max_ctx, 128), (int64_t)kMaxSplit}));
+    {
+      // One workgroup fills a CU (its LDS), so a grid of several waves runs
+      // a whole number of them: the split count goes to the nearest multiple
+      // of the splits that fill one wave (35B-style full layer at B=8: 17 ->
+      // 16 splits, 1088 -> 1024 workgroups, instead of a quarter-full fifth
+      // wave)
+      const int64_t heads = (int64_t)B * g.n_kv_heads;
+      const int64_t per = cus % heads == 0 ? cus / heads : 0;
+      if (per > 0 && ap.nsplit > per) {
+        int64_t n = (ap.nsplit + per / 2) / per * per;
+        while (n > kMaxSplit || n > ceil_div(max_ctx, 128)) n -= per;
+        if (n >= per) ap.nsplit = (int)n;
+      }
+    }
     int64_t kv_bytes = 0;
     for (int b = 0; b < B; ++b) {
       const int64_t nctx = ap.F[b] - ap.lo0[b];
