@@ -1289,7 +1289,9 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
   const bool post = !conv && g.dtype == DSPINE_BF16 && M > gemm_stream_fused_rows();
   // 16 rows and fewer (BF16): the bridge stores the same kind of copy for
   // the layers after the first, instead of waiting for every column to form
-  // the next norm itself
+  // the next norm itself, and O stores y g_post for gate/up, which then reads
+  // 16-bit rows instead of forming the norm from fp32 ones (27B B=1 gate/up
+  // 384 -> 345 us per forward, O 85 -> 87)
   const bool copy16 = !conv && prescale_pays(g, M, H);
   bool copy_ready = false;
   if (head_act_ready) *head_act_ready = false;
@@ -1444,7 +1446,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     gp.ldo = H;
     gp.stats_out = conv ? nullptr : st0;
     gp.stats_out_ld = kMaxRows;
-    if (post) set_copy(gp, ws + P.act_h, H, false, Lw.g_post, kRawCopy);     // y g_post for gate/up
+    if (post || copy16) set_copy(gp, ws + P.act_h, H, false, Lw.g_post, kRawCopy);     // y g_post for gate/up
     if (post) set_row_blocks(gp, g, M, H, qd);
     {
       ProfScope ps(DSPINE_PROF_GEMM_O, stream);
@@ -1493,7 +1495,7 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
       gp.pro = PRO_COPY;
       gp.a = ws + P.act_h;
       gp.lda = H;
-    } else if (post) {
+    } else if (post || copy16) {
       gp.pro = PRO_COPY;
       gp.a = ws + P.act_h;
       gp.lda = H;
