@@ -32,7 +32,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # sources whose change invalidates a traffic figure of the streamed GEMM
-GEMM_SOURCES = ["csrc/gemm_stream.hip", "csrc/dspine_device.hpp", "csrc/dspine_internal.hpp"]
+# (the kernel, and the launcher that picks its configuration and operands)
+GEMM_SOURCES = ["csrc/gemm_stream.hip", "csrc/dspine_device.hpp", "csrc/dspine_internal.hpp", "csrc/dspine_api.cpp"]
 
 
 def source_hash(paths=GEMM_SOURCES) -> str:
