@@ -1390,9 +1390,9 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
     ap.S = g.window[l];
     ap.causal = g.block_causal;
     // Key splits: enough workgroups to spread the reads over the CUs (about
-    // 256, or one split per 2048 keys on long contexts) but at least 128 keys
-    // per split, so that each of a workgroup's key sub-streams has a tile.
-    int64_t max_ctx = 0;
+    // 256, or more on long contexts, below) but at least 128 keys per split,
+    // so that each of a workgroup's key sub-streams has a tile.
+    int64_t max_ctx = 0, min_ctx = INT64_MAX;
     for (int b = 0; b < B; ++b) {
       ap.kring[b] = ctx[b].k_ring[l];
       ap.vring[b] = ctx[b].v_ring[l];
@@ -1400,8 +1400,15 @@ static int run_forward(const dspine_model* model, int B, int W, const dspine_ctx
       ap.F[b] = ctx[b].frontier;
       ap.lo0[b] = row0_lo(ctx[b].frontier, g.window[l]);
       max_ctx = std::max(max_ctx, ap.F[b] - ap.lo0[b]);
+      min_ctx = std::min(min_ctx, ap.F[b] - ap.lo0[b]);
     }
-    const int64_t spread = std::max(ceil_div(256, (int64_t)B * g.n_kv_heads), ceil_div(max_ctx, 2048));
+    // Long contexts: splits of up to 8192 keys when the requests' contexts
+    // are within a factor of two (each wave then holds like work, and fewer
+    // waves pay fewer prologues: 35B-style full layer at B=8 in one wave of
+    // 256 workgroups, attention 512 -> 483 us per forward), else of 2048 so
+    // that the short requests' workgroups fill in behind the long ones
+    const int64_t per_split = 2 * min_ctx >= max_ctx ? 8192 : 2048;
+    const int64_t spread = std::max(ceil_div(256, (int64_t)B * g.n_kv_heads), ceil_div(max_ctx, per_split));
     ap.nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({spread, ceil_div(max_ctx, 128), (int64_t)kMaxSplit}));
     {
       // One workgroup fills a CU (its LDS), so a grid of several waves runs
